@@ -1,0 +1,180 @@
+"""Benchmark of the NVFP4 W4A4 MoE expert layer on one MI355X.
+
+One step = one moe_expert_forward call: routing metadata + per-token NVFP4
+quantize-permute, FC1 grouped GEMM with the weighted SwiGLU + row-amax
+epilogue, requantization of D, FC2 grouped GEMM, combine.  Weights are
+quantized once before timing (static weights).  Inputs are seeded synthetic
+tensors with the shapes of the Qwen3-30B-A3B expert layer (T=8192 tokens,
+hidden 2048, 128 experts, top-8, intermediate 768, Zipf(1.1)-biased router),
+resident in HBM before the timed region.
+
+Prints one JSON line (rank 0):
+  value        tokens/s of the whole layer
+  roofline     the FC1 kernel (dominant): algorithmic FLOPs per launch over its
+               average duration from HIP events recorded on the launch stream
+  cpu_baseline the CPU oracle timed on a bounded token sample of the workload
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="qwen3_30b_a3b_moe_t8192")
+    p.add_argument("--cpu-tokens", type=int, default=512,
+                   help="tokens of the oracle's CPU-baseline sample (0 = skip)")
+    p.add_argument("--traffic", default=None,
+                   help="JSON file with measured HBM bytes per FC1 launch (rocprof PMC)")
+    return p.parse_args()
+
+
+def moe_algorithmic(w):
+    R = w.routed_rows
+    H, I, T, k = w.hidden, w.inter, w.tokens, w.topk
+    fc1 = 2.0 * R * 2 * I * H
+    fc2 = 2.0 * R * H * I
+    # quantize + permute: read x and routing, write codes/scales/s_g and maps
+    qbytes = T * H * 2 + T * k * 8 + R * (H // 2 + H // 16 + 4) + R * 8 + T * k * 4
+    return fc1, fc2, qbytes
+
+
+def cpu_baseline(w, n_tokens):
+    from oracle import oracle as O
+    E, I, H = w.experts, w.inter, w.hidden
+    log(f"cpu baseline: oracle weight quantization (offline, untimed), sample {n_tokens} tokens")
+    ow1 = O.quantize(w.w1.reshape(E * 2 * I, H), domain=1,
+                     group_offsets=np.arange(E + 1, dtype=np.int32) * 2 * I)
+    ow2 = O.quantize(w.w2.reshape(E * H, I), domain=1,
+                     group_offsets=np.arange(E + 1, dtype=np.int32) * H)
+    W1 = (ow1[0].reshape(E, 2 * I, H // 2), ow1[1].reshape(E, 2 * I, H // 16), ow1[2])
+    W2 = (ow2[0].reshape(E, H, I // 2), ow2[1].reshape(E, H, I // 16), ow2[2])
+    t0 = time.perf_counter()
+    O.moe_forward(w.x[:n_tokens], w.topk_idx[:n_tokens], w.topk_prob[:n_tokens], E, I, W1, W2)
+    dt = time.perf_counter() - t0
+    log(f"cpu baseline: {n_tokens} tokens in {dt:.2f} s on {O.num_threads()} threads")
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+            "sample": f"first {n_tokens} of {w.tokens} tokens of the same workload (same routing "
+                      f"and weights), whole layer: route+quantize, FC1, SwiGLU, requantize, FC2, "
+                      f"combine; {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the sharded path is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from nvfp4_w4a4_quantized_amd.ops import (NvFp4Weights, StageTimer, moe_expert_forward,
+                                              moe_expert_forward_workspace_size)
+    from nvfp4_w4a4_quantized_amd.workloads import make_moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    log(f"generating workload {args.workload}")
+    w = make_moe(args.workload)
+    fc1_flops, fc2_flops, qbytes = moe_algorithmic(w)
+
+    def bf(u16):
+        return torch.from_numpy(u16.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x = bf(w.x)
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    prob = torch.from_numpy(w.topk_prob).to(dev)
+    log("quantizing weights (a0, offline)")
+    W1 = NvFp4Weights.quantize(bf(w.w1))
+    W2 = NvFp4Weights.quantize(bf(w.w2))
+    ws = torch.empty(moe_expert_forward_workspace_size(w.tokens, w.hidden, w.inter, w.topk,
+                                                       w.experts), dtype=torch.uint8, device=dev)
+    y = torch.empty((w.tokens, w.hidden), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def step(timer=None):
+        moe_expert_forward(x, idx, prob, w.experts, w.inter, W1, W2, workspace=ws, y=y,
+                           timer=timer)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timers = [StageTimer() for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(timers[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = {n: float(np.mean([t.elapsed_ms()[n] for t in timers])) for n in StageTimer.NAMES}
+    for t in timers:
+        t.close()
+    ms = wall * 1e3 / args.steps
+    tokens_per_s = w.tokens * args.steps / wall
+    total_flops = fc1_flops + fc2_flops
+    fc1_ms = stages["fc1_swiglu"]
+    fc1_tflops = fc1_flops / (fc1_ms * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("fc1_hbm_bytes_per_launch")
+    log("stages (ms, HIP events): " + ", ".join(f"{k}={v:.4f}" for k, v in stages.items()))
+    result = {
+        "metric": "MoE W4A4 expert-layer tokens/s",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 e2m1/e4m3 operands decoded exactly to f16 for f16 MFMA, f32 accumulate",
+        "data": "synthetic (seeded; Qwen3-30B-A3B expert-layer shapes, random N(0,0.02) weights)",
+        "config": {"workload": w.name, "tokens": w.tokens, "hidden": w.hidden,
+                   "moe_intermediate": w.inter, "experts": w.experts, "topk": w.topk,
+                   "router": f"softmax(N(0,1) + Zipf(s={w.meta['zipf_s']}) bias), top-k renormalised",
+                   "routed_rows": w.routed_rows, "active_experts": w.meta["active_experts"],
+                   "cv_rows_per_expert": round(w.meta["cv_rows_per_expert"], 3),
+                   "parallelism": "single GPU"},
+        "effective_tflops": total_flops / (ms * 1e-3) / 1e12,
+        "effective_frac_of_f16_peak": total_flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "stage_ms": stages,
+        "quantize_permute_gbps": qbytes / (stages["route_quantize"] * 1e-3) / 1e9,
+        "roofline": {"kernel": "FC1 grouped GEMM + SwiGLU/amax epilogue",
+                     "bound": "mfma", "achieved": fc1_tflops, "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": fc1_tflops / PEAK_F16_TFLOPS,
+                     "traffic": traffic,
+                     "per_launch_flops": fc1_flops},
+    }
+    if args.cpu_tokens > 0:
+        result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.tokens))
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

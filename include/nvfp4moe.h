@@ -1,0 +1,257 @@
+/*
+ * nvfp4moe.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 MoE expert path.
+ *
+ * The path: per-token NVFP4 quantization of activations fused with the MoE
+ * routing permutation, a W4A4 grouped GEMM over every expert's FC1 (gate|up)
+ * and FC2 (down) projections, and a router-weighted SwiGLU whose bf16 output
+ * and row amax feed the FC2 requantization.
+ *
+ * Sources, cited by page title and section:
+ *   [miniTE]   "miniTE Technical Report: Stable and Efficient Reinforcement
+ *              Learning with Native NVFP4"
+ *   [miniTE-S] "miniTE: Diagnosing and Bridging the Execution Gap in Native
+ *              NVFP4 Reinforcement Learning" (source-linked summary)
+ *   [4BIT]     "The 4-bitter Lesson"
+ *
+ * NVFP4 format ([miniTE] §2.2, §5.1; [4BIT] "Baseline recipe",
+ * "Four-Over-Six"): a value is x^ = q * s_b * s_g with q an E2M1 code on the
+ * grid {0, 0.5, 1, 1.5, 2, 3, 4, 6} (bit 3 = sign), s_b an OCP E4M3 scale
+ * shared by 16 consecutive elements along K, and s_g an FP32 outer scale:
+ * one per token (row) for activations, one per expert matrix for weights.
+ * Quantization (bit-exact contract):
+ *   s_g  = fl32(amax / 2688)                               ([miniTE] §5.6)
+ *   s_b  = E4M3_rne_satfinite(fl32(bmax / fl32(6 * s_g))), 0 when s_g == 0
+ *   d    = fl32(s_b * s_g); code = sign(x) | E2M1_rne_satfinite(fl32(x / d)),
+ *          magnitude 0 when d == 0
+ * with IEEE binary32 round-to-nearest-even at every step.
+ *
+ * Layouts (all row-major, K contiguous):
+ *   codes        uint8 [rows, k/2]   element 2j in the low nibble of byte j
+ *   block_scales uint8 [rows, k/16]  E4M3 bytes (bias 7, max 0x7E = 448)
+ *   global scale float [rows] (per row) or [groups] (per group)
+ *   bf16 tensors travel as uint16_t bit patterns.
+ * Weight matrices are [G, N, K] (one [N, K] matrix per expert, K contiguous):
+ *   codes [G, N, K/2], block scales [G, N, K/16], outer scales [G].
+ *
+ * Ownership and execution: every pointer argument is a DEVICE pointer unless
+ * stated otherwise, owned by the caller; the library allocates no device or
+ * host memory on these calls.  All calls are asynchronous on `stream`
+ * (a hipStream_t passed as void*, NULL = the null stream): the host returns
+ * after enqueueing the kernels, with no host<->device synchronisation, and
+ * nothing is read back to the host.  Calls that share a workspace must be
+ * ordered by the caller.  No C++ exception crosses this interface.
+ *
+ * Errors: arguments are validated on the host before any HIP call; a failed
+ * check returns NVFP4_INVALID_ARGUMENT (or NVFP4_UNSUPPORTED for shapes the
+ * kernels do not handle) and enqueues nothing.  Launch failures return
+ * NVFP4_HIP_ERROR.  Data-dependent preconditions (finite inputs, expert ids
+ * of one token distinct) are the caller's contract; expert ids outside
+ * [0, num_experts) are legal and mean "not routed".
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_OK 0
+#define NVFP4_INVALID_ARGUMENT 1
+#define NVFP4_UNSUPPORTED 2
+#define NVFP4_HIP_ERROR 3
+#define NVFP4_WORKSPACE_TOO_SMALL 4
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * nvfp4_quantize -- NVFP4 quantization of a bf16 matrix.
+ * [miniTE] §2.2 (two-level scaling; the recipe chooses the outer-scale
+ * domain), §5.1 (per-token outer scale), §5.3 (amax reuse); [4BIT] "Baseline
+ * recipe" (per-token activation scale, one FP32 scale per weight tensor).
+ *
+ *   x            bf16 [rows, ld_x], first k columns used; k % 16 == 0,
+ *                ld_x >= k, ld_x % 8 == 0, 16-byte aligned
+ *   scale_domain 0: one outer scale per row (activations);
+ *                1: one outer scale per group of rows
+ *                   [group_offsets[g], group_offsets[g+1]) (expert weights)
+ *   group_offsets int32 [num_groups + 1], non-decreasing, within [0, rows]
+ *                (domain 1 only; device pointer)
+ *   amax_in      nullable float [rows] (domain 0) or [num_groups] (domain 1):
+ *                use these amax values instead of reducing |x|
+ *   codes        out uint8 [rows, k/2];  block_scales out uint8 [rows, k/16]
+ *   global_scales out float [rows] (domain 0) or [num_groups] (domain 1);
+ *                in domain 1 without amax_in it also serves as the scratch
+ *                for the group amax reduction (no other memory is used).
+ * Limits: 1 <= k <= 16384; rows, num_groups < 2^31.
+ * ---------------------------------------------------------------------- */
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
+                   int scale_domain, const int32_t* group_offsets, int32_t num_groups,
+                   const float* amax_in,
+                   uint8_t* codes, uint8_t* block_scales, float* global_scales,
+                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * MoE routing permutation fused with per-token quantization.
+ * [miniTE] §5.2 (contiguous buffers with expert offsets, device-side metadata,
+ * zero-token experts and padding in the same grouped path), §5.3 (row amax
+ * collected during the permutation and reused by the quantizer);
+ * [miniTE-S] §4.3.
+ *
+ * Layout of the routed rows: expert-major; expert e owns rows
+ * [expert_offsets[e], expert_offsets[e+1]) whose length is its entry count
+ * rounded up to `align`.  Inside an expert, rows follow ascending flattened
+ * entry index t*topk + j (ascending token).  Row r of entry (t, j) holds
+ * token t quantized with its own per-token scale; dst_row[t*topk + j] = r,
+ * row_src[r] = t, row_prob[r] = topk_prob[t*topk + j].  Padding rows have
+ * row_src = -1, row_prob = 0, zero codes, zero scales and s_g = 0.  Entries
+ * with an expert id outside [0, num_experts) get dst_row = -1.  Rows at or
+ * beyond expert_offsets[num_experts] are not written.
+ *
+ *   x            nullable bf16 [tokens, hidden]: NULL computes the metadata only
+ *   topk_idx     int32 [tokens, topk];  topk_prob float [tokens, topk]
+ *   align        power of two in [1, 256]
+ *   expert_offsets out int32 [num_experts + 1]
+ *   dst_row      out int32 [tokens, topk]
+ *   row_src, row_prob  out [moe_rows_capacity(...)]
+ *   codes, block_scales, global_scales  out [capacity, hidden/2],
+ *                [capacity, hidden/16], [capacity] (unused when x is NULL)
+ *   workspace    device scratch of moe_permute_workspace_size() bytes,
+ *                16-byte aligned
+ * Limits: 1 <= topk <= num_experts <= 1024; hidden % 16 == 0,
+ * hidden <= 16384; tokens * topk + num_experts * align < 2^31.
+ * ---------------------------------------------------------------------- */
+int64_t moe_rows_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int32_t align);
+size_t moe_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_experts);
+int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
+                const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                int32_t num_experts, int32_t align,
+                int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
+                uint8_t* codes, uint8_t* block_scales, float* global_scales,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * w4a4_grouped_gemm -- one grouped call over all experts.
+ * [miniTE] §5.2 (dense grouped GEMM fed by contiguous buffers and device
+ * offsets), §5.4 (block-scaled GEMM; ACC * alpha_a[m] * alpha_b in an FP32
+ * epilogue); [miniTE-S] §4.2 (FP32 epilogue rescaling).
+ *
+ * For each group g and row r in [group_offsets[g], group_offsets[g+1]):
+ *   out[r, n] = s_ga[r] * s_gb[g] * sum_k (q_a s_a)[r, k] * (q_b s_b)[g, n, k]
+ * Operands are decoded exactly to fp16 (q * s_b has at most 6 significant
+ * bits), multiplied on the fp16 matrix cores and accumulated in fp32.
+ * Accuracy: |out - exact| <= 2^-10 * sum_k |a_k b_k| + 1e-6 (fp32 output).
+ *
+ *   a_*          A rows: codes [rows_cap, k/2], scales [rows_cap, k/16],
+ *                outer scales [rows_cap]
+ *   b_*          B: codes [G, n, k/2], scales [G, n, k/16], outer scales [G]
+ *   group_offsets int32 [num_groups + 1] on the device, non-decreasing,
+ *                group_offsets[0] >= 0, group_offsets[G] <= rows_cap; empty
+ *                groups are legal; the host never reads it
+ *   out_dtype    0: float32, 1: bf16 (round-to-nearest-even)
+ *   out          [rows_cap, n]; rows outside [off[0], off[G]) are not written
+ * Limits: k % 128 == 0, k <= 16384; n % 32 == 0; 1 <= num_groups <= 1024.
+ * ---------------------------------------------------------------------- */
+int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                      int64_t rows_cap,
+                      const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gscale,
+                      const int32_t* group_offsets, int32_t num_groups, int64_t n, int64_t k,
+                      int out_dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * w4a4_grouped_gemm_swiglu -- FC1 with the fused router-weighted SwiGLU
+ * epilogue and the row amax of its output.
+ * [miniTE] §5.3 (weighted SwiGLU with row amax: the statistic of exactly the
+ * tensor FC2 quantizes), §5.4 ("C = gate | up", "D = act(gate, up) x prob",
+ * "reduce D amax concurrently").
+ *
+ * B holds the fused [G, 2*inter, k] gate|up weights (gate = rows [0, inter)).
+ * For every routed row r and j < inter, with C the grouped GEMM above:
+ *   D[r, j]  = bf16(silu(C[r, j]) * C[r, inter + j] * row_prob[r])
+ *   amax[r]  = max_j |D[r, j]|   (over the bf16 values; bit-exact)
+ *   c_out    nullable float [rows_cap, 2*inter]: also store C
+ * amax must be zero-filled by the caller for the rows of the call (the
+ * kernel takes an order-independent maximum into it).
+ * Limits: as w4a4_grouped_gemm, with inter % 64 == 0.
+ * ---------------------------------------------------------------------- */
+int w4a4_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                             int64_t rows_cap,
+                             const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gscale,
+                             const int32_t* group_offsets, int32_t num_groups, int64_t inter,
+                             int64_t k, const float* row_prob,
+                             uint16_t* d_out, float* amax, float* c_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_combine -- unpermute: y[t, :] = bf16(sum_j Y[dst_row[t, j], :]) with a
+ * fixed j order and fp32 accumulation; entries with dst_row < 0 add nothing.
+ * The router weight is already inside D ([miniTE] §5.4), so this is a plain
+ * sum.  y_rows_dtype 0: float32 rows, 1: bf16 rows.  hidden % 8 == 0.
+ * ---------------------------------------------------------------------- */
+int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
+                int64_t tokens, int32_t topk, int64_t hidden, uint16_t* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_expert_forward -- the whole expert layer in one call:
+ *   moe_permute -> FC1 grouped GEMM + SwiGLU + amax -> requantize D with that
+ *   amax -> FC2 grouped GEMM -> moe_combine.
+ * [miniTE] §5.2-§5.4 (the fused FC1 and FC2 flows).
+ *
+ *   x            bf16 [tokens, hidden];  y out bf16 [tokens, hidden]
+ *   w1           NVFP4 gate|up weights [E, 2*inter, hidden] (+ scales, [E])
+ *   w2           NVFP4 down weights    [E, hidden, inter]
+ *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned
+ *   debug        nullable: every non-NULL member receives that intermediate
+ *                (in place of the workspace copy); fc1_out and y_rows_f32
+ *                are only produced when requested (y_rows_f32 switches the
+ *                FC2 output to fp32)
+ *   stage_events nullable array of 6 hipEvent_t (as void*), recorded on
+ *                `stream` before route, FC1, requantize, FC2, combine and
+ *                after combine (profiling; see nvfp4_event_*).
+ * Limits: hidden % 128 == 0, inter % 128 == 0, hidden, inter <= 16384, plus
+ * the limits of moe_permute.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* gscale;
+} nvfp4_weights;
+
+typedef struct {
+  int32_t* expert_offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
+  uint8_t* a1_codes; uint8_t* a1_scales; float* a1_gscale;
+  float* fc1_out;                 /* [cap, 2*inter] fp32, optional */
+  uint16_t* d;                    /* [cap, inter] bf16 */
+  float* amax_d;                  /* [cap] */
+  uint8_t* a2_codes; uint8_t* a2_scales; float* a2_gscale;
+  uint16_t* y_rows;               /* [cap, hidden] bf16 FC2 output */
+  float* y_rows_f32;              /* [cap, hidden] fp32 FC2 output, optional */
+} nvfp4_moe_intermediates;
+
+size_t moe_expert_forward_workspace_size(int64_t tokens, int64_t hidden, int64_t inter,
+                                         int32_t topk, int32_t num_experts, int32_t align);
+int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
+                       const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                       int32_t num_experts, int32_t align,
+                       const nvfp4_weights* w1, const nvfp4_weights* w2, uint16_t* y,
+                       void* workspace, size_t workspace_bytes,
+                       const nvfp4_moe_intermediates* debug, void* const* stage_events,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * Profiling helpers: thin wrappers over hipEventCreate / hipEventRecord /
+ * hipEventElapsedTime / hipEventDestroy so a caller without HIP headers can
+ * time the stages of moe_expert_forward on its stream.  (These allocate a
+ * HIP event; they are not on the hot path.)
+ * ---------------------------------------------------------------------- */
+int nvfp4_event_create(void** event);
+int nvfp4_event_record(void* event, void* stream);
+int nvfp4_event_elapsed_ms(void* start, void* stop, float* ms);
+int nvfp4_event_destroy(void* event);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,342 @@
+// capi.hip -- the C ABI declared in include/nvfp4moe.h: host-side argument
+// validation (before any HIP call), workspace carving and kernel launches.
+#include "nvfp4moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "launch.h"
+
+using namespace nvfp4;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_HIP_ERROR; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool valid_align(int32_t align) {
+  return align >= 1 && align <= 256 && (align & (align - 1)) == 0;
+}
+
+constexpr int64_t kMaxK = 16384;
+constexpr int32_t kMaxExperts = 1024;
+
+// Sequential carve of 256-byte aligned regions out of one workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += round_up(count * sizeof(T), 256);
+    return p;
+  }
+};
+
+struct MoeLayout {
+  int32_t* route_ws_i; int32_t* offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
+  uint8_t* a1c; uint8_t* a1s; float* a1g;
+  uint16_t* d; float* amax_d;
+  uint8_t* a2c; uint8_t* a2s; float* a2g;
+  uint16_t* y_rows;
+  size_t bytes;
+};
+
+MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_t E, int32_t align) {
+  const int64_t cap = moe_rows_capacity(T, k, E, align);
+  Carver c(ws);
+  MoeLayout L;
+  L.route_ws_i = c.take<int32_t>(route_workspace_bytes(T, E) / 4);
+  L.offsets = c.take<int32_t>(E + 1);
+  L.dst_row = c.take<int32_t>((size_t)(T * k));
+  L.row_src = c.take<int32_t>((size_t)cap);
+  L.row_prob = c.take<float>((size_t)cap);
+  L.a1c = c.take<uint8_t>((size_t)(cap * H / 2));
+  L.a1s = c.take<uint8_t>((size_t)(cap * H / 16));
+  L.a1g = c.take<float>((size_t)cap);
+  L.d = c.take<uint16_t>((size_t)(cap * I));
+  L.amax_d = c.take<float>((size_t)cap);
+  L.a2c = c.take<uint8_t>((size_t)(cap * I / 2));
+  L.a2s = c.take<uint8_t>((size_t)(cap * I / 16));
+  L.a2g = c.take<float>((size_t)cap);
+  L.y_rows = c.take<uint16_t>((size_t)(cap * H));
+  L.bytes = c.used;
+  return L;
+}
+
+bool route_args_ok(int64_t tokens, int32_t topk, int32_t num_experts, int32_t align) {
+  if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > kMaxExperts) return false;
+  if (topk > num_experts || !valid_align(align)) return false;
+  const int64_t cap = (int64_t)tokens * topk + (int64_t)num_experts * align;
+  return cap < 0x7FFFFFFFLL;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_INVALID_ARGUMENT: return "invalid argument";
+    case NVFP4_UNSUPPORTED: return "unsupported shape";
+    case NVFP4_HIP_ERROR: return "HIP launch/runtime error";
+    case NVFP4_WORKSPACE_TOO_SMALL: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x, int scale_domain,
+                   const int32_t* group_offsets, int32_t num_groups, const float* amax_in,
+                   uint8_t* codes, uint8_t* block_scales, float* global_scales, void* stream) {
+  if (rows < 0 || rows >= 0x7FFFFFFFLL || k < 16 || k % 16 != 0 || ld_x < k || ld_x % 8 != 0)
+    return NVFP4_INVALID_ARGUMENT;
+  if (k > kMaxK) return NVFP4_UNSUPPORTED;
+  if (!x || !codes || !block_scales || !global_scales) return NVFP4_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(global_scales, 4))
+    return NVFP4_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  QuantRowsArgs a{x, rows, k, ld_x, 0, amax_in, group_offsets, num_groups,
+                  codes, block_scales, global_scales};
+  if (scale_domain == 0) {
+    a.amax_kind = amax_in ? 1 : 0;
+    return hip_status(launch_quantize_rows(a, s));
+  }
+  if (scale_domain != 1) return NVFP4_INVALID_ARGUMENT;
+  if (!group_offsets || num_groups < 1 || num_groups >= 0x7FFFFFFF) return NVFP4_INVALID_ARGUMENT;
+  // group amax: reduce into global_scales (as bits) unless given
+  const float* amax_src = amax_in;
+  if (!amax_src) {
+    hipError_t e = launch_group_amax(x, rows, k, ld_x, group_offsets, num_groups,
+                                     reinterpret_cast<uint32_t*>(global_scales), s);
+    if (e != hipSuccess) return NVFP4_HIP_ERROR;
+    amax_src = global_scales;
+  }
+  a.amax_kind = 2;
+  a.amax_in = amax_src;
+  hipError_t e = launch_quantize_rows(a, s);
+  if (e != hipSuccess) return NVFP4_HIP_ERROR;
+  return hip_status(launch_group_finalize(amax_src, global_scales, num_groups, s));
+}
+
+int64_t moe_rows_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int32_t align) {
+  if (tokens < 0 || topk < 1 || num_experts < 1 || align < 1) return 0;
+  return tokens * (int64_t)topk + (int64_t)num_experts * (int64_t)(align - 1);
+}
+
+size_t moe_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_experts) {
+  (void)topk;
+  if (tokens < 0 || num_experts < 1) return 0;
+  return route_workspace_bytes(tokens, num_experts);
+}
+
+int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden, const int32_t* topk_idx,
+                const float* topk_prob, int32_t topk, int32_t num_experts, int32_t align,
+                int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
+                uint8_t* codes, uint8_t* block_scales, float* global_scales, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!route_args_ok(tokens, topk, num_experts, align)) return NVFP4_INVALID_ARGUMENT;
+  if (!expert_offsets || !row_src || !row_prob || !workspace) return NVFP4_INVALID_ARGUMENT;
+  if (tokens > 0 && (!topk_idx || !topk_prob || !dst_row)) return NVFP4_INVALID_ARGUMENT;
+  if (!aligned(workspace, 16)) return NVFP4_INVALID_ARGUMENT;
+  if (x) {
+    if (hidden < 16 || hidden % 16 != 0) return NVFP4_INVALID_ARGUMENT;
+    if (hidden > kMaxK) return NVFP4_UNSUPPORTED;
+    if (!codes || !block_scales || !global_scales) return NVFP4_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_INVALID_ARGUMENT;
+  }
+  if (workspace_bytes < route_workspace_bytes(tokens, num_experts)) return NVFP4_WORKSPACE_TOO_SMALL;
+  RouteArgs a{x, tokens, x ? hidden : 0, topk_idx, topk_prob, topk, num_experts, align,
+              expert_offsets, dst_row, row_src, row_prob, codes, block_scales, global_scales,
+              nullptr, workspace};
+  return hip_status(launch_route(a, static_cast<hipStream_t>(stream)));
+}
+
+static int gemm_args_ok(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                        int64_t rows_cap, const uint8_t* b_codes, const uint8_t* b_scales,
+                        const float* b_gscale, const int32_t* group_offsets, int32_t num_groups,
+                        int64_t k) {
+  if (!a_codes || !a_scales || !a_gscale || !b_codes || !b_scales || !b_gscale || !group_offsets)
+    return NVFP4_INVALID_ARGUMENT;
+  if (rows_cap < 0 || rows_cap >= 0x7FFFFFFFLL || num_groups < 1 || num_groups > kMaxExperts)
+    return NVFP4_INVALID_ARGUMENT;
+  if (k < 16 || k % 16 != 0) return NVFP4_INVALID_ARGUMENT;
+  if (k % 128 != 0 || k > kMaxK) return NVFP4_UNSUPPORTED;
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) ||
+      !aligned(b_scales, 4))
+    return NVFP4_INVALID_ARGUMENT;
+  return NVFP4_OK;
+}
+
+int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                      int64_t rows_cap, const uint8_t* b_codes, const uint8_t* b_scales,
+                      const float* b_gscale, const int32_t* group_offsets, int32_t num_groups,
+                      int64_t n, int64_t k, int out_dtype, void* out, void* stream) {
+  int st = gemm_args_ok(a_codes, a_scales, a_gscale, rows_cap, b_codes, b_scales, b_gscale,
+                        group_offsets, num_groups, k);
+  if (st != NVFP4_OK) return st;
+  if (!out || (out_dtype != 0 && out_dtype != 1)) return NVFP4_INVALID_ARGUMENT;
+  if (n < 32 || n % 32 != 0) return NVFP4_UNSUPPORTED;
+  if ((int64_t)num_groups * n >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;
+  GemmArgs a{};
+  a.a_codes = a_codes; a.a_scales = a_scales; a.a_gscale = a_gscale;
+  a.b_codes = b_codes; a.b_scales = b_scales; a.b_gscale = b_gscale;
+  a.offsets = group_offsets; a.num_groups = num_groups; a.rows_cap = rows_cap;
+  a.n = n; a.k = k; a.out_dtype = out_dtype; a.out = out;
+  return hip_status(launch_gemm_plain(a, static_cast<hipStream_t>(stream)));
+}
+
+int w4a4_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
+                             int64_t rows_cap, const uint8_t* b_codes, const uint8_t* b_scales,
+                             const float* b_gscale, const int32_t* group_offsets,
+                             int32_t num_groups, int64_t inter, int64_t k, const float* row_prob,
+                             uint16_t* d_out, float* amax, float* c_out, void* stream) {
+  int st = gemm_args_ok(a_codes, a_scales, a_gscale, rows_cap, b_codes, b_scales, b_gscale,
+                        group_offsets, num_groups, k);
+  if (st != NVFP4_OK) return st;
+  if (!row_prob || !d_out || !amax) return NVFP4_INVALID_ARGUMENT;
+  if (inter < 64 || inter % 64 != 0) return NVFP4_UNSUPPORTED;
+  if ((int64_t)num_groups * 2 * inter >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;
+  GemmArgs a{};
+  a.a_codes = a_codes; a.a_scales = a_scales; a.a_gscale = a_gscale;
+  a.b_codes = b_codes; a.b_scales = b_scales; a.b_gscale = b_gscale;
+  a.offsets = group_offsets; a.num_groups = num_groups; a.rows_cap = rows_cap;
+  a.n = 2 * inter; a.k = k; a.inter = inter;
+  a.row_prob = row_prob; a.d_out = d_out; a.amax = amax; a.c_out = c_out;
+  return hip_status(launch_gemm_swiglu(a, static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row, int64_t tokens,
+                int32_t topk, int64_t hidden, uint16_t* y, void* stream) {
+  if (tokens < 0 || topk < 1 || hidden < 8 || hidden % 8 != 0) return NVFP4_INVALID_ARGUMENT;
+  if (y_rows_dtype != 0 && y_rows_dtype != 1) return NVFP4_INVALID_ARGUMENT;
+  if (tokens > 0 && (!y_rows || !dst_row || !y)) return NVFP4_INVALID_ARGUMENT;
+  if (!aligned(y_rows, 16) || !aligned(y, 16)) return NVFP4_INVALID_ARGUMENT;
+  return hip_status(launch_combine(y_rows, y_rows_dtype, dst_row, tokens, topk, hidden, y,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_expert_forward_workspace_size(int64_t tokens, int64_t hidden, int64_t inter,
+                                         int32_t topk, int32_t num_experts, int32_t align) {
+  if (!route_args_ok(tokens, topk, num_experts, align) || hidden < 0 || inter < 0) return 0;
+  return carve_moe(nullptr, tokens, hidden, inter, topk, num_experts, align).bytes;
+}
+
+int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
+                       const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                       int32_t num_experts, int32_t align, const nvfp4_weights* w1,
+                       const nvfp4_weights* w2, uint16_t* y, void* workspace,
+                       size_t workspace_bytes, const nvfp4_moe_intermediates* debug,
+                       void* const* stage_events, void* stream) {
+  if (!route_args_ok(tokens, topk, num_experts, align)) return NVFP4_INVALID_ARGUMENT;
+  if (hidden < 128 || hidden % 128 != 0 || inter < 128 || inter % 128 != 0)
+    return NVFP4_UNSUPPORTED;
+  if (hidden > kMaxK || inter > kMaxK) return NVFP4_UNSUPPORTED;
+  if (!w1 || !w2 || !w1->codes || !w1->scales || !w1->gscale || !w2->codes || !w2->scales ||
+      !w2->gscale || !workspace)
+    return NVFP4_INVALID_ARGUMENT;
+  if (tokens > 0 && (!x || !y || !topk_idx || !topk_prob)) return NVFP4_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256) || (x && !aligned(x, 16)) || (y && !aligned(y, 16)) ||
+      !aligned(w1->codes, 16) || !aligned(w2->codes, 16) || !aligned(w1->scales, 4) ||
+      !aligned(w2->scales, 4))
+    return NVFP4_INVALID_ARGUMENT;
+  if ((int64_t)num_experts * 2 * inter >= 0x7FFFFFFFLL ||
+      (int64_t)num_experts * hidden >= 0x7FFFFFFFLL)
+    return NVFP4_INVALID_ARGUMENT;
+  MoeLayout L = carve_moe(workspace, tokens, hidden, inter, topk, num_experts, align);
+  if (workspace_bytes < L.bytes) return NVFP4_WORKSPACE_TOO_SMALL;
+  float* c_out = nullptr;
+  float* y_f32 = nullptr;
+  if (debug) {
+    if (debug->expert_offsets) L.offsets = debug->expert_offsets;
+    if (debug->dst_row) L.dst_row = debug->dst_row;
+    if (debug->row_src) L.row_src = debug->row_src;
+    if (debug->row_prob) L.row_prob = debug->row_prob;
+    if (debug->a1_codes) L.a1c = debug->a1_codes;
+    if (debug->a1_scales) L.a1s = debug->a1_scales;
+    if (debug->a1_gscale) L.a1g = debug->a1_gscale;
+    if (debug->d) L.d = debug->d;
+    if (debug->amax_d) L.amax_d = debug->amax_d;
+    if (debug->a2_codes) L.a2c = debug->a2_codes;
+    if (debug->a2_scales) L.a2s = debug->a2_scales;
+    if (debug->a2_gscale) L.a2g = debug->a2_gscale;
+    if (debug->y_rows) L.y_rows = debug->y_rows;
+    c_out = debug->fc1_out;
+    y_f32 = debug->y_rows_f32;
+    const void* ptrs16[] = {L.a1c, L.a2c, L.d, L.y_rows, y_f32};
+    for (const void* p : ptrs16)
+      if (p && !aligned(p, 16)) return NVFP4_INVALID_ARGUMENT;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t cap = moe_rows_capacity(tokens, topk, num_experts, align);
+  auto mark = [&](int i) -> hipError_t {
+    if (!stage_events || !stage_events[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s);
+  };
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return NVFP4_HIP_ERROR;
+  // a1 + a2: routing metadata and per-token quantize-scatter (zeroes amax_d rows)
+  RouteArgs ra{x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
+               L.offsets, L.dst_row, L.row_src, L.row_prob, L.a1c, L.a1s, L.a1g,
+               L.amax_d, L.route_ws_i};
+  if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
+  // a3 + a4: FC1 with the weighted SwiGLU epilogue and D's row amax
+  GemmArgs g1{};
+  g1.a_codes = L.a1c; g1.a_scales = L.a1s; g1.a_gscale = L.a1g;
+  g1.b_codes = w1->codes; g1.b_scales = w1->scales; g1.b_gscale = w1->gscale;
+  g1.offsets = L.offsets; g1.num_groups = num_experts; g1.rows_cap = cap;
+  g1.n = 2 * inter; g1.k = hidden; g1.inter = inter;
+  g1.row_prob = L.row_prob; g1.d_out = L.d; g1.amax = L.amax_d; g1.c_out = c_out;
+  if ((e = launch_gemm_swiglu(g1, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if ((e = mark(2)) != hipSuccess) return NVFP4_HIP_ERROR;
+  // a5: requantize D reusing its amax (rows up to offsets[E] live on device:
+  // quantize the whole capacity; rows past the end are ignored downstream)
+  QuantRowsArgs q{L.d, cap, inter, inter, 1, L.amax_d, nullptr, 0, L.a2c, L.a2s, L.a2g};
+  if ((e = launch_quantize_rows(q, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if ((e = mark(3)) != hipSuccess) return NVFP4_HIP_ERROR;
+  // a6: FC2
+  GemmArgs g2{};
+  g2.a_codes = L.a2c; g2.a_scales = L.a2s; g2.a_gscale = L.a2g;
+  g2.b_codes = w2->codes; g2.b_scales = w2->scales; g2.b_gscale = w2->gscale;
+  g2.offsets = L.offsets; g2.num_groups = num_experts; g2.rows_cap = cap;
+  g2.n = hidden; g2.k = inter;
+  g2.out_dtype = y_f32 ? 0 : 1;
+  g2.out = y_f32 ? static_cast<void*>(y_f32) : static_cast<void*>(L.y_rows);
+  if ((e = launch_gemm_plain(g2, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if ((e = mark(4)) != hipSuccess) return NVFP4_HIP_ERROR;
+  // a7: combine
+  if ((e = launch_combine(y_f32 ? static_cast<const void*>(y_f32) : L.y_rows, y_f32 ? 0 : 1,
+                          L.dst_row, tokens, topk, hidden, y, s)) != hipSuccess)
+    return NVFP4_HIP_ERROR;
+  if ((e = mark(5)) != hipSuccess) return NVFP4_HIP_ERROR;
+  return NVFP4_OK;
+}
+
+int nvfp4_event_create(void** event) {
+  if (!event) return NVFP4_INVALID_ARGUMENT;
+  hipEvent_t ev;
+  if (hipEventCreate(&ev) != hipSuccess) return NVFP4_HIP_ERROR;
+  *event = ev;
+  return NVFP4_OK;
+}
+
+int nvfp4_event_record(void* event, void* stream) {
+  if (!event) return NVFP4_INVALID_ARGUMENT;
+  return hip_status(hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(stream)));
+}
+
+int nvfp4_event_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return NVFP4_INVALID_ARGUMENT;
+  return hip_status(hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)));
+}
+
+int nvfp4_event_destroy(void* event) {
+  if (!event) return NVFP4_INVALID_ARGUMENT;
+  return hip_status(hipEventDestroy(static_cast<hipEvent_t>(event)));
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// launch.h -- host-side launchers of the gfx950 kernels (internal to the
+// library; the public interface is include/nvfp4moe.h).  Every launcher
+// enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Blocks (16 elements) per lane needed for a row of k elements, rounded up to
+// a supported power of two (1, 2, 4, 8, 16); 0 if k is too large.
+int blocks_per_lane(int64_t k);
+
+// ---- quantize.hip ----
+// amax source of a row: reduce |x| (kind 0), amax_in[row] (kind 1), or
+// group_amax[group(row)] (kind 2, groups given by offsets).
+struct QuantRowsArgs {
+  const uint16_t* x; int64_t rows; int64_t k; int64_t ld_x;
+  int amax_kind; const float* amax_in; const int32_t* group_offsets; int32_t num_groups;
+  uint8_t* codes; uint8_t* scales; float* gscale;  // gscale written for kinds 0, 1
+};
+hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
+// Group amax: zero `amax_bits[num_groups]`, then atomic max of every row's amax.
+hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
+                             const int32_t* group_offsets, int32_t num_groups,
+                             uint32_t* amax_bits, hipStream_t s);
+// gscale[g] = amax[g] / 2688 (in place allowed: amax may alias gscale).
+hipError_t launch_group_finalize(const float* amax, float* gscale, int32_t num_groups,
+                                 hipStream_t s);
+
+// ---- route.hip ----
+int64_t route_num_chunks(int64_t tokens);
+size_t route_workspace_bytes(int64_t tokens, int32_t num_experts);
+struct RouteArgs {
+  const uint16_t* x; int64_t tokens; int64_t hidden;
+  const int32_t* topk_idx; const float* topk_prob; int32_t topk; int32_t num_experts;
+  int32_t align;
+  int32_t* offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
+  uint8_t* codes; uint8_t* scales; float* gscale;
+  float* zero_per_row;  // nullable: set to 0 for every routed and padding row
+  void* workspace;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// ---- gemm.hip ----
+struct GemmArgs {
+  const uint8_t* a_codes; const uint8_t* a_scales; const float* a_gscale;
+  const uint8_t* b_codes; const uint8_t* b_scales; const float* b_gscale;
+  const int32_t* offsets; int32_t num_groups;
+  int64_t rows_cap;
+  int64_t n;      // B rows per group (2*inter for the SwiGLU epilogue)
+  int64_t k;
+  // plain epilogue
+  int out_dtype; void* out;
+  // SwiGLU epilogue
+  const float* row_prob; uint16_t* d_out; float* amax; float* c_out; int64_t inter;
+};
+hipError_t launch_gemm_plain(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
+
+// ---- combine.hip ----
+hipError_t launch_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
+                          int64_t tokens, int32_t topk, int64_t hidden, uint16_t* y,
+                          hipStream_t s);
+
+}  // namespace nvfp4

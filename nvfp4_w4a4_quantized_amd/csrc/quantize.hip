@@ -1,0 +1,162 @@
+// quantize.hip -- NVFP4 quantization of bf16 rows on gfx950.
+//
+// One wavefront per row.  Lane l owns the 16-element blocks l, l+64, ...
+// (BPL blocks), so each load instruction of the wave reads a contiguous
+// 2 KiB span (coalesced), and the row stays in registers between the amax
+// reduction and the encoding.  The row amax is a wave-wide max of the |bf16|
+// bit patterns; the per-token outer scale is s_g = amax / 2688 (miniTE
+// Technical Report §5.6).  Group (per-expert) scales take an atomic max of
+// the row amaxes first (order independent, so deterministic).
+#include "launch.h"
+#include "nvfp4_device.h"
+
+namespace nvfp4 {
+
+int blocks_per_lane(int64_t k) {
+  int64_t nb = (k + 15) / 16;
+  int64_t per = (nb + kWave - 1) / kWave;
+  if (per <= 1) return 1;
+  if (per <= 2) return 2;
+  if (per <= 4) return 4;
+  if (per <= 8) return 8;
+  if (per <= 16) return 16;
+  return 0;
+}
+
+// Loads the lane's blocks of one bf16 row (zeros for blocks past the row end)
+// and returns the lane's max |x| as bits of a bf16 magnitude.
+template <int BPL>
+__device__ __forceinline__ uint32_t load_row_blocks(const uint16_t* row, int nblocks, int lane,
+                                                    uint32_t (&w)[BPL][8]) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = lane + kWave * i;
+    if (b < nblocks) {
+      const uint16_t* p = row + (int64_t)b * 16;
+      u32x4_t u0 = load_stream16(p);
+      u32x4_t u1 = load_stream16(p + 8);
+      w[i][0] = u0.x; w[i][1] = u0.y; w[i][2] = u0.z; w[i][3] = u0.w;
+      w[i][4] = u1.x; w[i][5] = u1.y; w[i][6] = u1.z; w[i][7] = u1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[i][j] = 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t a = w[i][j] & 0x7FFF7FFFu;
+      uint32_t lo = a & 0xFFFFu, hi = a >> 16;
+      m = m > lo ? m : lo;
+      m = m > hi ? m : hi;
+    }
+  }
+  return m;
+}
+
+// Group of `row` given non-decreasing offsets (the last g with off[g] <= row).
+__device__ __forceinline__ int find_group(const int32_t* off, int num_groups, int64_t row) {
+  int lo = 0, hi = num_groups - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)off[mid] <= row) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int BPL>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (row >= a.rows) return;
+  const int nblocks = (int)(a.k / 16);
+  const uint16_t* xr = a.x + row * a.ld_x;
+  uint32_t w[BPL][8];
+  uint32_t mbits = load_row_blocks<BPL>(xr, nblocks, lane, w);
+  float amax;
+  if (a.amax_kind == 0) {
+    amax = __uint_as_float(wave_max_u32(mbits) << 16);
+  } else if (a.amax_kind == 1) {
+    amax = a.amax_in[row];
+  } else {
+    int g = find_group(a.group_offsets, a.num_groups, row);
+    amax = a.amax_in[g];
+  }
+  const float s_g = amax / 2688.0f;
+  uint8_t* crow = a.codes + row * (a.k / 2);
+  uint8_t* srow = a.scales + row * (a.k / 16);
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = lane + kWave * i;
+    if (b < nblocks) {
+      uint32_t sb;
+      uint2 c = quantize_block16(w[i], s_g, &sb);
+      *reinterpret_cast<uint2*>(crow + (int64_t)b * 8) = c;
+      srow[b] = (uint8_t)sb;
+    }
+  }
+  if (a.amax_kind != 2 && lane == 0) a.gscale[row] = s_g;
+}
+
+template <int BPL>
+__global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* x, int64_t rows, int64_t k,
+                                                         int64_t ld_x, const int32_t* off,
+                                                         int32_t num_groups, uint32_t* amax_bits) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (row >= rows) return;
+  if (row < off[0] || row >= off[num_groups]) return;
+  uint32_t w[BPL][8];
+  uint32_t m = wave_max_u32(load_row_blocks<BPL>(x + row * ld_x, (int)(k / 16), lane, w));
+  if (lane == 0) {
+    int g = find_group(off, num_groups, row);
+    atomicMax(amax_bits + g, m << 16);
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void group_finalize_kernel(const float* amax, float* gscale, int32_t n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) gscale[i] = amax[i] / 2688.0f;
+}
+
+hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s) {
+  if (a.rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  switch (blocks_per_lane(a.k)) {
+    case 1: quantize_rows_kernel<1><<<grid, block, 0, s>>>(a); break;
+    case 2: quantize_rows_kernel<2><<<grid, block, 0, s>>>(a); break;
+    case 4: quantize_rows_kernel<4><<<grid, block, 0, s>>>(a); break;
+    case 8: quantize_rows_kernel<8><<<grid, block, 0, s>>>(a); break;
+    case 16: quantize_rows_kernel<16><<<grid, block, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
+                             const int32_t* off, int32_t num_groups, uint32_t* amax_bits,
+                             hipStream_t s) {
+  fill_u32_kernel<<<(num_groups + 255) / 256, 256, 0, s>>>(amax_bits, num_groups, 0u);
+  if (rows == 0) return hipGetLastError();
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  switch (blocks_per_lane(k)) {
+    case 1: group_amax_kernel<1><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
+    case 2: group_amax_kernel<2><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
+    case 4: group_amax_kernel<4><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
+    case 8: group_amax_kernel<8><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
+    case 16: group_amax_kernel<16><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_group_finalize(const float* amax, float* gscale, int32_t n, hipStream_t s) {
+  group_finalize_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, gscale, n);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,99 @@
+"""The C-ABI library loads, exports every function include/nvfp4moe.h
+declares, and rejects invalid arguments on the host before any HIP call (no
+GPU needed: these calls return before touching the device)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+LIB = os.path.join(ROOT, "nvfp4_w4a4_quantized_amd", "libnvfp4moe.so")
+
+INVALID, UNSUPPORTED, WS_SMALL = 1, 2, 4
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "sizeof")))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} not built (run __graft_entry__.build())")
+    from nvfp4_w4a4_quantized_amd import _lib
+    return _lib.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ("nvfp4_quantize", "moe_permute", "w4a4_grouped_gemm", "w4a4_grouped_gemm_swiglu",
+              "moe_combine", "moe_expert_forward", "moe_rows_capacity",
+              "moe_permute_workspace_size", "moe_expert_forward_workspace_size",
+              "nvfp4_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    missing = [n for n in _declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in _declared_functions():
+        getattr(L, n)   # resolvable through ctypes
+
+
+def test_host_side_sizes(L):
+    assert L.moe_rows_capacity(8192, 8, 128, 1) == 65536
+    assert L.moe_rows_capacity(100, 4, 7, 16) == 100 * 4 + 7 * 15
+    assert L.moe_permute_workspace_size(8192, 8, 128) >= 128 * 128 * 4
+    ws = L.moe_expert_forward_workspace_size(8192, 2048, 768, 8, 128, 1)
+    cap = 65536
+    assert ws >= cap * (2048 // 2 + 2048 // 16 + 768 * 2 + 768 // 2 + 768 // 16 + 2048 * 2)
+    assert L.nvfp4_status_string(0) == b"ok"
+    assert L.nvfp4_status_string(4) == b"workspace too small"
+
+
+def test_invalid_arguments_rejected_before_any_device_call(L):
+    fake = C.c_void_p(0x1000)   # never dereferenced: validation fails first
+    # k not a multiple of 16
+    assert L.nvfp4_quantize(fake, 4, 24, 24, 0, None, 0, None, fake, fake, fake, None) == INVALID
+    # missing output
+    assert L.nvfp4_quantize(fake, 4, 32, 32, 0, None, 0, None, None, fake, fake, None) == INVALID
+    # unknown domain / domain 1 without offsets
+    assert L.nvfp4_quantize(fake, 4, 32, 32, 1, None, 2, None, fake, fake, fake, None) == INVALID
+    # k beyond the supported maximum
+    assert L.nvfp4_quantize(fake, 4, 32768, 32768, 0, None, 0, None, fake, fake, fake, None) == UNSUPPORTED
+    # misaligned x
+    assert L.nvfp4_quantize(C.c_void_p(0x1002), 4, 32, 32, 0, None, 0, None, fake, fake, fake, None) == INVALID
+    # topk > experts, bad align, too many experts
+    args = (fake, 16, 64, fake, fake)
+    assert L.moe_permute(*args, 5, 4, 1, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
+    assert L.moe_permute(*args, 2, 4, 3, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
+    assert L.moe_permute(*args, 2, 2048, 1, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
+    # workspace too small
+    assert L.moe_permute(*args, 2, 4, 1, fake, fake, fake, fake, fake, fake, fake, fake, 4, None) == WS_SMALL
+    # GEMM: k not a multiple of 128, n not a multiple of 32, bad dtype
+    g = (fake, fake, fake, 64, fake, fake, fake, fake, 2)
+    assert L.w4a4_grouped_gemm(*g, 64, 96, 0, fake, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm(*g, 48, 128, 0, fake, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm(*g, 64, 128, 7, fake, None) == INVALID
+    assert L.w4a4_grouped_gemm(*g, 64, 120, 0, fake, None) == INVALID
+    assert L.w4a4_grouped_gemm_swiglu(*g, 96, 128, fake, fake, fake, None, None) == UNSUPPORTED
+    # combine: hidden not a multiple of 8
+    assert L.moe_combine(fake, 0, fake, 4, 2, 12, fake, None) == INVALID
+    # expert layer: hidden not a multiple of 128, missing weights
+    from nvfp4_w4a4_quantized_amd._lib import Weights
+    w = Weights(0x1000, 0x1000, 0x1000)
+    assert L.moe_expert_forward(fake, 8, 200, 128, fake, fake, 2, 4, 1, C.byref(w), C.byref(w),
+                                fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == UNSUPPORTED
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, None, C.byref(w),
+                                fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, C.byref(w), C.byref(w),
+                                fake, C.c_void_p(0x10000), 16, None, None, None) == WS_SMALL

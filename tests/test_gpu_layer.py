@@ -1,0 +1,147 @@
+"""moe_expert_forward end to end (through the C ABI), checked as a replay
+chain against the oracle: every step is compared on the inputs the GPU itself
+produced upstream, so one rounding flip is not compounded.
+  a1/a2  routing + quantized A1: bit-exact vs the oracle
+  a3     FC1 C (fp32) vs the oracle GEMM on A1: GEMM tolerance
+  a4     D within one bf16 ulp of the oracle SwiGLU of the GPU's C;
+         amax_d == max |D| bit-exact
+  a5     A2 == oracle quantize(D_gpu, amax_gpu): bit-exact
+  a6     FC2 rows vs the oracle GEMM on A2: GEMM tolerance
+  a7     y vs the oracle combine of the GPU's FC2 rows: sum of tolerances
+and, loosely, y against a pure oracle run (relative L2)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import assert_gemm_close, bf16_ulp, dev, dev_bf16, host, moe_case, say
+from nvfp4_w4a4_quantized_amd.workloads import bf16_bits_to_f32
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+def _weights(W):
+    from nvfp4_w4a4_quantized_amd.ops import NvFp4Weights
+    return NvFp4Weights(dev(W[0]), dev(W[1]), dev(W[2]))
+
+
+def _forward(w, W1, W2, align=1, **kw):
+    from nvfp4_w4a4_quantized_amd.ops import moe_expert_forward
+    say("moe_expert_forward", w.name, "align", align, kw)
+    y, it = moe_expert_forward(dev_bf16(w.x), dev(w.topk_idx), dev(w.topk_prob), w.experts,
+                               w.inter, _weights(W1), _weights(W2), align=align, debug=True, **kw)
+    torch.cuda.synchronize()
+    return host(y), {k: host(v) for k, v in it.items()}
+
+
+def _replay_chain(w, W1, W2, align, full, rng):
+    y, it = _forward(w, W1, W2, align=align, fc1_out=True, y_rows_f32=True)
+    ref = O.moe_permute(w.x, w.topk_idx, w.topk_prob, w.experts, align)
+    off = it["expert_offsets"]
+    assert np.array_equal(off, ref["offsets"])
+    assert np.array_equal(it["dst_row"], ref["dst_row"])
+    R = int(off[-1])
+    assert np.array_equal(it["row_src"][:R], ref["row_src"][:R])
+    assert np.array_equal(it["row_prob"][:R].view(np.uint32), ref["row_prob"][:R].view(np.uint32))
+    for a, b in (("a1_codes", "codes"), ("a1_scales", "scales"), ("a1_gscale", "gscale")):
+        assert np.array_equal(it[a][:R].view(np.uint8), ref[b][:R].view(np.uint8)), a
+    A1 = (it["a1_codes"], it["a1_scales"], it["a1_gscale"])
+    C = it["fc1_out"][:R]
+    if full:
+        cref, cb = O.grouped_gemm(*A1, *W1, off, with_bound=True)
+        assert_gemm_close(C, cref[:R], cb[:R], "FC1")
+    else:
+        rows = rng.integers(0, R, 20000)
+        cols = rng.integers(0, C.shape[1], 20000)
+        cref, cb = O.grouped_gemm_at(*A1, *W1, off, rows, cols)
+        assert_gemm_close(C[rows, cols], cref, cb, "FC1 sampled")
+    D = it["d"][:R]
+    dref, _ = O.swiglu(C, it["row_prob"][:R])
+    dv = bf16_bits_to_f32(D).astype(np.float64)
+    rv = bf16_bits_to_f32(dref).astype(np.float64)
+    assert np.all(np.abs(dv - rv) <= bf16_ulp(rv) * 1.0001 + 1e-40), "SwiGLU D"
+    amax = it["amax_d"][:R]
+    assert np.array_equal(amax, np.abs(bf16_bits_to_f32(D)).max(axis=1)), "amax_d"
+    a2 = O.quantize(D, amax_in=amax)
+    for name, r in zip(("a2_codes", "a2_scales", "a2_gscale"), a2):
+        assert np.array_equal(it[name][:R].view(np.uint8), r.view(np.uint8)), name
+    A2 = (it["a2_codes"], it["a2_scales"], it["a2_gscale"])
+    Y = it["y_rows_f32"][:R]
+    if full:
+        yref, yb = O.grouped_gemm(*A2, *W2, off, with_bound=True)
+        assert_gemm_close(Y, yref[:R], yb[:R], "FC2")
+        ybound = yb[:R]
+    else:
+        rows = rng.integers(0, R, 20000)
+        cols = rng.integers(0, Y.shape[1], 20000)
+        yref, yb = O.grouped_gemm_at(*A2, *W2, off, rows, cols)
+        assert_gemm_close(Y[rows, cols], yref, yb, "FC2 sampled")
+        ybound = None
+    # combine: y vs the oracle combine of the GPU's own rows
+    ycomb = bf16_bits_to_f32(O.combine(Y, it["dst_row"])).astype(np.float64)
+    yv = bf16_bits_to_f32(y).astype(np.float64)
+    # fp32 accumulation of k terms + one bf16 rounding on each side
+    absum = np.zeros_like(yv)
+    dst = it["dst_row"]
+    for j in range(dst.shape[1]):
+        ok = dst[:, j] >= 0
+        absum[ok] += np.abs(Y[dst[ok, j]])
+    tol = absum * 2.0 ** -20 + bf16_ulp(ycomb) * 1.0001 + 1e-30
+    assert np.all(np.abs(yv - ycomb) <= tol), "combine"
+    return y, it, ybound
+
+
+@pytest.mark.parametrize("align", [1, 16])
+def test_tiny_layer_replay_chain_and_end_to_end(align):
+    w, W1, W2 = moe_case(0)
+    rng = np.random.default_rng(1)
+    y, it, _ = _replay_chain(w, W1, W2, align, True, rng)
+    yo, _ = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2, align=align)
+    a = bf16_bits_to_f32(y).astype(np.float64)
+    b = bf16_bits_to_f32(yo).astype(np.float64)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    print(f"tiny layer end-to-end rel L2 vs pure oracle: {rel:.3e}")
+    assert rel < 1e-2
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4])
+def test_workload_layer_replay_chain(wid):
+    w, W1, W2 = moe_case(wid)
+    rng = np.random.default_rng(wid)
+    _replay_chain(w, W1, W2, 1, wid == 3, rng)
+
+
+def test_decode_layer_end_to_end():
+    w, W1, W2 = moe_case(3)
+    y, _ = _forward(w, W1, W2)
+    yo, _ = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2)
+    a = bf16_bits_to_f32(y).astype(np.float64)
+    b = bf16_bits_to_f32(yo).astype(np.float64)
+    rel = np.linalg.norm(a - b) / np.linalg.norm(b)
+    print(f"decode layer end-to-end rel L2 vs pure oracle: {rel:.3e}")
+    assert rel < 1e-2
+
+
+def test_perf_path_bf16_rows_and_determinism():
+    """The benchmarked configuration (bf16 FC2 rows, no debug outputs) gives
+    the same y on repeated calls, and its FC2 rows are the bf16 rounding of
+    values within the GEMM tolerance."""
+    from nvfp4_w4a4_quantized_amd.ops import moe_expert_forward
+    w, W1, W2 = moe_case(2)
+    args = (dev_bf16(w.x), dev(w.topk_idx), dev(w.topk_prob), w.experts, w.inter, _weights(W1),
+            _weights(W2))
+    say("moe_expert_forward perf path x2")
+    y1 = moe_expert_forward(*args)
+    y2 = moe_expert_forward(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y, it = _forward(w, W1, W2)
+    assert np.array_equal(y, host(y1))
+    R = int(it["expert_offsets"][-1])
+    rng = np.random.default_rng(5)
+    rows = rng.integers(0, R, 20000)
+    cols = rng.integers(0, w.hidden, 20000)
+    A2 = (it["a2_codes"], it["a2_scales"], it["a2_gscale"])
+    yref, yb = O.grouped_gemm_at(*A2, *W2, it["expert_offsets"], rows, cols)
+    got = bf16_bits_to_f32(it["y_rows"][rows, cols]).astype(np.float64)
+    assert np.all(np.abs(got - yref) <= 2.0 ** -10 * yb + 1e-6 + bf16_ulp(yref) * 0.5001)

@@ -1,0 +1,148 @@
+"""GPU parity of nvfp4_quantize (through the C ABI) against the oracle:
+codes, E4M3 block scales and FP32 outer scales must match bit for bit."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import dev, dev_bf16, host, moe_case, oracle_weights, say
+from nvfp4_w4a4_quantized_amd.workloads import make_dense, to_bf16_bits
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _ops():
+    from nvfp4_w4a4_quantized_amd import ops
+    return ops
+
+
+def _check_rows(xb: np.ndarray, what: str, amax_in=None):
+    say("nvfp4_quantize", what, xb.shape)
+    c, s, g = _ops().nvfp4_quantize(dev_bf16(xb), amax_in=None if amax_in is None else dev(amax_in))
+    torch.cuda.synchronize()
+    rc, rs, rg = O.quantize(xb, amax_in=amax_in)
+    assert np.array_equal(host(s), rs), f"{what}: scales differ"
+    assert np.array_equal(host(g).view(np.uint32), rg.view(np.uint32)), f"{what}: outer scales differ"
+    hc = host(c)
+    if not np.array_equal(hc, rc):
+        bad = np.argwhere(hc != rc)
+        r, b = bad[0]
+        raise AssertionError(f"{what}: {len(bad)} code bytes differ; first row {r} byte {b}: "
+                             f"gpu {hc[r, b]:02x} oracle {rc[r, b]:02x}")
+
+
+def test_golden_rows():
+    for name in ("worked_row.json", "tie_row.json"):
+        with open(os.path.join(GOLD, name)) as f:
+            gold = json.load(f)
+        xb = to_bf16_bits(np.array(gold["x_values"], np.float32))[None]
+        c, s, g = _ops().nvfp4_quantize(dev_bf16(xb))
+        torch.cuda.synchronize()
+        assert [f"{b:02x}" for b in host(c)[0]] == gold["expected_codes_hex"], name
+        assert [f"{b:02x}" for b in host(s)[0]] == gold["expected_scales_hex"], name
+        assert f"{host(g).view(np.uint32)[0]:08x}" == gold["expected_gscale_hex"], name
+
+
+@pytest.mark.parametrize("wid", [0, 2, 3, 4])
+def test_moe_activations(wid):
+    w, _, _ = moe_case(wid, with_weights=False)
+    _check_rows(w.x, f"moe workload {wid} activations")
+
+
+def test_dense_projection_inputs():
+    d = make_dense()
+    for pname, x, _ in d.projections:
+        _check_rows(x, f"dense {pname} input")
+
+
+@pytest.mark.parametrize("k", [16, 32, 48, 144, 768, 1040, 2048, 4096, 16384])
+def test_shapes_and_distributions(k):
+    rng = np.random.default_rng(100 + k)
+    rows = 67
+    x = (rng.standard_normal((rows, k)) * np.exp(rng.uniform(-30, 30, (rows, 1)))).astype(np.float32)
+    x[3] = 0.0
+    x[4] = -0.0
+    x[5, ::7] = 1e-38
+    x[6] = rng.standard_t(3, size=k) * 100
+    x[7, : min(k, 16)] = 3.3895314e38
+    _check_rows(to_bf16_bits(x), f"random k={k}")
+
+
+def test_lattice_ties_and_extremes():
+    """Exact grid points and quotient ties exercise the exact-division path."""
+    rng = np.random.default_rng(7)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5])
+    rows = []
+    for j in (-120, -60, -8, 0, 9, 100):
+        for sb in (0x01, 0x07, 0x08, 0x0F, 0x33, 0x63, 0x7E):
+            sv = float(torch.tensor([sb], dtype=torch.uint8).view(torch.float8_e4m3fn).float())
+            q = rng.choice(grid, size=256) * rng.choice([-1, 1], size=256)
+            q[0] = 6.0
+            row = q * sv * 2.0 ** j
+            row[16] = 6 * 448 * 2.0 ** j          # fixes amax: s_g = 2^j
+            rows.append(row)
+    x = np.array(rows)
+    x = np.where(np.isfinite(x) & (np.abs(x) < 3e38), x, 0.0).astype(np.float32)
+    _check_rows(to_bf16_bits(x), "lattice and ties")
+
+
+def test_amax_in_and_leading_dimension():
+    rng = np.random.default_rng(8)
+    xb = to_bf16_bits(rng.standard_normal((40, 256)).astype(np.float32))
+    am = (np.abs(rng.standard_normal(40)) * 5).astype(np.float32)
+    am[0] = 0.0
+    _check_rows(xb, "amax_in", amax_in=am)
+    # ld_x > k through the C ABI directly
+    from nvfp4_w4a4_quantized_amd import _lib
+    big = to_bf16_bits(rng.standard_normal((40, 384)).astype(np.float32))
+    xd = dev_bf16(big)
+    c = torch.empty((40, 128), dtype=torch.uint8, device="cuda")
+    s = torch.empty((40, 16), dtype=torch.uint8, device="cuda")
+    g = torch.empty(40, dtype=torch.float32, device="cuda")
+    say("nvfp4_quantize ld_x=384 k=256")
+    _lib.check(_lib.lib().nvfp4_quantize(_lib.ptr(xd), 40, 256, 384, 0, None, 0, None,
+                                         _lib.ptr(c), _lib.ptr(s), _lib.ptr(g),
+                                         _lib.stream_handle()), "quantize ld")
+    torch.cuda.synchronize()
+    rc, rs, rg = O.quantize(np.ascontiguousarray(big[:, :256]))
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs) and np.array_equal(host(g), rg)
+
+
+def test_group_domain_with_empty_groups():
+    rng = np.random.default_rng(9)
+    xb = to_bf16_bits((rng.standard_normal((50, 512)) * rng.uniform(0.01, 100, (50, 1))).astype(np.float32))
+    offs = np.array([0, 7, 7, 30, 30, 50], np.int32)
+    say("nvfp4_quantize groups")
+    c, s, g = _ops().nvfp4_quantize(dev_bf16(xb), scale_domain=1, group_offsets=dev(offs))
+    torch.cuda.synchronize()
+    rc, rs, rg = O.quantize(xb, domain=1, group_offsets=offs)
+    assert np.array_equal(host(c), rc) and np.array_equal(host(s), rs)
+    assert np.array_equal(host(g), rg)
+
+
+@pytest.mark.parametrize("wid", [0, 2])
+def test_expert_weights(wid):
+    """a0: per-expert weight quantization of the gate|up and down matrices."""
+    w, W1, W2 = moe_case(wid)
+    for name, wb, ref in (("w1", w.w1, W1), ("w2", w.w2, W2)):
+        say("weights", wid, name, wb.shape)
+        from nvfp4_w4a4_quantized_amd.ops import NvFp4Weights
+        q = NvFp4Weights.quantize(dev_bf16(wb))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(q.gscale), ref[2]), name
+        assert np.array_equal(host(q.scales), ref[1]), name
+        assert np.array_equal(host(q.codes), ref[0]), name
+
+
+def test_deterministic_repeat():
+    w, _, _ = moe_case(2, with_weights=False)
+    xd = dev_bf16(w.x)
+    a = _ops().nvfp4_quantize(xd)
+    b = _ops().nvfp4_quantize(xd)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
