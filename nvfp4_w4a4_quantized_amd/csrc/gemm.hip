@@ -12,16 +12,10 @@
 // the epilogue (miniTE §5.4 "ACC x alpha_a[m] (x alpha_b[n])"; miniTE summary
 // §4.2 "FP32 epilogue rescaling").
 //
-// Structure.  A workgroup owns a BM x BN output tile of one group; each wave
-// a (32*WM) x (32*WN) sub-tile kept in accumulator registers.  Every lane
-// loads its own operand fragments straight from global memory (16 bytes of
-// codes and 2 scale bytes per fragment per 64-deep K step), prefetching the
-// next K step while decoding and multiplying the current one.  The K order
-// inside a 64-step is permuted identically for A and B (lane half g takes
-// elements [32g, 32g+32)), which leaves the sum unchanged and gives each lane
-// contiguous bytes.  Group boundaries come from the device offsets: every
-// workgroup derives its (group, m-tile) from a wave-wide scan of the per-group
-// tile counts, so the host never reads them; surplus workgroups exit.
+// Structure: see the kernel comment below.  Group boundaries come from the
+// device offsets: every workgroup derives its (group, m-tile) from a
+// wave-wide scan of the per-group tile counts, so the host never reads them;
+// surplus workgroups exit.
 #include "launch.h"
 #include "nvfp4_device.h"
 
@@ -95,69 +89,184 @@ __device__ __forceinline__ bool locate_mtile(const int32_t* off, int G, int BM, 
 }
 
 // ---- kernel --------------------------------------------------------------
+//
+// Workgroup = NW waves side by side along N.  The workgroup owns a BM x BN
+// output tile of one group (BM = 32*WM rows, BN = NW*32*WN columns); each
+// wave a BM x (32*WN) sub-tile held in accumulator registers
+// (WM x WN v_mfma_f32_32x32x16_f16 tiles).  K advances in stages of 128 with
+// two LDS buffers: while the waves multiply stage i, they fill stage i+1.
+//   A (activations, shared by all waves): each thread decodes half a row of
+//     the stage (64 elements) once, straight from its global load, and stores
+//     the fp16 values in MFMA-fragment order: for fragment m and substep s the
+//     64 lanes' 16-byte operands are one contiguous 1 KiB block, so both the
+//     writes and the per-substep reads are bank-conflict free.
+//   B (weights, distinct per wave): copied packed (64 code bytes + the 8
+//     scale bytes per row, rows padded to 80 bytes) and decoded by each wave
+//     into registers right before its MFMAs.
+// K order: inside a 128 stage, lane half h covers elements [64h, 64h+64)
+// and substep s takes [64h + 8s, 64h + 8s + 8); A and B use the same order,
+// so the dot products are unchanged.
+// The epilogue goes through LDS, one 32-row block at a time, so that each
+// lane writes contiguous bytes of one output row.
+constexpr int kKS = 128;          // K per stage
+constexpr int kRowB = 80;         // LDS bytes per staged B row
+constexpr int kEpiLd = 136;       // fp32 words per epilogue LDS row (128 + pad)
 
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2 };
 
-template <int WM, int WN, int WGM, int WGN, int EPI>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_w4a4_kernel(GemmArgs a) {
-  constexpr int BM = 32 * WM * WGM;
-  constexpr int BN = 32 * WN * WGN;          // B rows (output columns) per tile
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int wm = wave / WGN, wn = wave % WGN;
+// Workgroups are dealt to the 8 XCDs round robin; renumber them so that each
+// XCD walks a contiguous range of tiles (consecutive tiles share A rows and,
+// inside an expert, B rows, which then stay in that XCD's L2).
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
+  const int64_t x = bid % 8, pos = bid / 8, q = n / 8, r = n % 8;
+  return (x < r) ? x * (q + 1) + pos : r * (q + 1) + (x - r) * q + pos;
+}
+
+// SwiGLU weighted by the router probability, in binary32; below g = -80
+// binary32 exp(-g) overflows while g e^g u p may still be a normal bf16, so
+// that rare tail is evaluated in binary64.
+__device__ __noinline__ float swiglu_tail(float g, float u, float p) {
+  const double eg = exp((double)g);
+  return (float)(((double)g * eg / (1.0 + eg)) * (double)u * (double)p);
+}
+
+__device__ __forceinline__ float swiglu_weighted(float g, float u, float p) {
+  if (g >= -80.0f) {
+    const float silu = g / (1.0f + __expf(-g));
+    return (silu * u) * p;
+  }
+  return swiglu_tail(g, u, p);
+}
+
+template <int WM, int WN, int NW, int EPI>
+__global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
+  constexpr int BM = 32 * WM;
+  constexpr int BN = 32 * WN * NW;
+  constexpr int NT = 64 * NW;                       // threads
+  constexpr int A_BYTES = WM * 8 * 64 * 16;         // fp16 A stage (fragment order)
+  constexpr int B_BYTES = BN * kRowB;               // packed B stage
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_UNITS = BM * 2;                   // half rows of 64 elements
+  constexpr int APT = (A_UNITS + NT - 1) / NT;      // A units per thread
+  constexpr int B_CHUNKS = BN * 4;                  // 16-byte code chunks
+  constexpr int BPT = (B_CHUNKS + NT - 1) / NT;
+  constexpr int BSPT = (BN + NT - 1) / NT;          // B scale rows per thread
+  static_assert(EPI != EPI_SWIGLU || WN % 2 == 0, "SwiGLU pairs gate and up blocks");
+  extern __shared__ __align__(16) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int64_t K = a.k;
   const int64_t N = a.n;
 
-  // output-column tiles: plain -> N / BN; SwiGLU -> inter / (BN/2) gate|up pairs
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  const int64_t mt = (int64_t)blockIdx.x / ntn;
-  const int64_t nt = (int64_t)blockIdx.x % ntn;
+  const int64_t logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t mt = logical / ntn;
+  const int64_t nt = logical % ntn;
   int g;
   int64_t row0, row1;
   if (!locate_mtile(a.offsets, a.num_groups, BM, mt, &g, &row0, &row1)) return;
 
-  // ---- operand rows of this lane
-  const int half = lane >> 5;                // K half of the 64-step
-  const int l32 = lane & 31;
-  int64_t arow[WM];
-#pragma unroll
-  for (int m = 0; m < WM; ++m) {
-    int64_t r = row0 + wm * 32 * WM + m * 32 + l32;
-    arow[m] = r < row1 ? r : row1 - 1;        // clamp (results discarded)
-  }
-  int64_t bcol[WN];                           // output column of each n-block (lane)
-  int64_t brow[WN];                           // B row inside the group
-#pragma unroll
-  for (int n = 0; n < WN; ++n) {
-    int64_t c;
+  // output column of B-tile row j (gate|up pairing for SwiGLU)
+  auto b_col = [&](int j) -> int64_t {
+    const int w = j / (32 * WN), n = (j / 32) % WN, c = j % 32;
     if (EPI == EPI_SWIGLU) {
       constexpr int HALF = WN / 2;
-      const int64_t gate0 = nt * (BN / 2) + wn * 32 * HALF;
-      c = (n < HALF) ? gate0 + 32 * n + l32 : a.inter + gate0 + 32 * (n - HALF) + l32;
-      bcol[n] = c;
-      const int64_t cmax = (n < HALF) ? a.inter - 1 : 2 * a.inter - 1;
-      brow[n] = c < cmax ? c : cmax;
-    } else {
-      c = nt * BN + wn * 32 * WN + 32 * n + l32;
-      bcol[n] = c;
-      brow[n] = c < N ? c : N - 1;
+      const int64_t gate0 = nt * (BN / 2) + (int64_t)w * 32 * HALF;
+      return (n < HALF) ? gate0 + 32 * n + c : a.inter + gate0 + 32 * (n - HALF) + c;
     }
-  }
-  const uint8_t* ac_ptr[WM];
-  const uint8_t* as_ptr[WM];
+    return nt * BN + (int64_t)w * 32 * WN + 32 * n + c;
+  };
+  auto b_src_row = [&](int j) -> int64_t {     // B row inside the [G*N, K] matrix
+    int64_t c = b_col(j);
+    int64_t cmax = N - 1;
+    if (EPI == EPI_SWIGLU) cmax = (((j / 32) % WN) < WN / 2) ? a.inter - 1 : 2 * a.inter - 1;
+    return (int64_t)g * N + (c < cmax ? c : cmax);
+  };
+
+  // ---- per-thread copy plan (fixed for the tile; the stage moves K)
+  int64_t a_src[APT], a_ssrc[APT];
+  int a_dst[APT];
+  bool a_ok[APT];
 #pragma unroll
-  for (int m = 0; m < WM; ++m) {
-    ac_ptr[m] = a.a_codes + arow[m] * (K / 2) + 16 * half;
-    as_ptr[m] = a.a_scales + arow[m] * (K / 16) + 2 * half;
+  for (int j = 0; j < APT; ++j) {
+    const int u = tid + NT * j;
+    a_ok[j] = u < A_UNITS;
+    const int r = a_ok[j] ? u / 2 : 0, h = u % 2;
+    int64_t ar = row0 + r;
+    ar = ar < row1 ? ar : row1 - 1;
+    a_src[j] = ar * (K / 2) + 32 * h;
+    a_ssrc[j] = ar * (K / 16) + 4 * h;
+    // fragment m = r/32, lane (r%32) + 32h; substep s adds s*1024 bytes
+    a_dst[j] = ((r / 32) * 8 * 64 + (r % 32) + 32 * h) * 16;
   }
-  const uint8_t* bc_ptr[WN];
-  const uint8_t* bs_ptr[WN];
+  int64_t b_src[BPT];
+  int b_dst[BPT];
+  bool b_ok[BPT];
 #pragma unroll
-  for (int n = 0; n < WN; ++n) {
-    const int64_t r = (int64_t)g * N + brow[n];
-    bc_ptr[n] = a.b_codes + r * (K / 2) + 16 * half;
-    bs_ptr[n] = a.b_scales + r * (K / 16) + 2 * half;
+  for (int j = 0; j < BPT; ++j) {
+    const int c = tid + NT * j;
+    b_ok[j] = c < B_CHUNKS;
+    const int row = b_ok[j] ? c / 4 : 0, part = c % 4;
+    b_src[j] = b_src_row(row) * (K / 2) + part * 16;
+    b_dst[j] = A_BYTES + row * kRowB + part * 16;
   }
+  int64_t bs_src[BSPT];
+  int bs_dst[BSPT];
+  bool bs_ok[BSPT];
+#pragma unroll
+  for (int j = 0; j < BSPT; ++j) {
+    const int row = tid + NT * j;
+    bs_ok[j] = row < BN;
+    const int rr = bs_ok[j] ? row : 0;
+    bs_src[j] = b_src_row(rr) * (K / 16);
+    bs_dst[j] = A_BYTES + rr * kRowB + 64;
+  }
+
+  u32x4_t ar0[APT], ar1[APT];
+  uint32_t asr[APT];
+  u32x4_t breg[BPT];
+  uint2 bsreg[BSPT];
+  auto gload = [&](int64_t st) {
+#pragma unroll
+    for (int j = 0; j < APT; ++j)
+      if (a_ok[j]) {
+        const uint8_t* p = a.a_codes + a_src[j] + st * 64;
+        ar0[j] = *reinterpret_cast<const u32x4_t*>(p);
+        ar1[j] = *reinterpret_cast<const u32x4_t*>(p + 16);
+        asr[j] = *reinterpret_cast<const uint32_t*>(a.a_scales + a_ssrc[j] + st * 8);
+      }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      if (b_ok[j]) breg[j] = *reinterpret_cast<const u32x4_t*>(a.b_codes + b_src[j] + st * 64);
+#pragma unroll
+    for (int j = 0; j < BSPT; ++j)
+      if (bs_ok[j]) bsreg[j] = *reinterpret_cast<const uint2*>(a.b_scales + bs_src[j] + st * 8);
+  };
+  // decode the A half rows and copy the packed B rows into stage buffer `buf`
+  auto fill = [&](int buf) {
+    uint8_t* sb = smem + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < APT; ++j)
+      if (a_ok[j]) {
+        const half2_t s01 = e4m3x2_to_half2(asr[j]);
+        const half2_t s23 = e4m3x2_to_half2(asr[j] >> 16);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const uint32_t c = s < 4 ? ar0[j][s] : ar1[j][s - 4];
+          const _Float16 sc = (s < 2) ? s01[0] : (s < 4) ? s01[1] : (s < 6) ? s23[0] : s23[1];
+          const half8_t v = decode8(c, half2_t{sc, sc});
+          *reinterpret_cast<half8_t*>(sb + a_dst[j] + s * 1024) = v;
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      if (b_ok[j]) *reinterpret_cast<u32x4_t*>(sb + b_dst[j]) = breg[j];
+#pragma unroll
+    for (int j = 0; j < BSPT; ++j)
+      if (bs_ok[j]) *reinterpret_cast<uint2*>(sb + bs_dst[j]) = bsreg[j];
+  };
 
   float16_t acc[WM][WN];
 #pragma unroll
@@ -167,55 +276,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_w4a4_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.0f;
 
-  const int64_t nk = K / 64;
-  uint4 ca[WM], cb[WN];
-  uint32_t sa[WM], sbv[WN];
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  int b_off[WN];
 #pragma unroll
-  for (int m = 0; m < WM; ++m) {
-    ca[m] = *reinterpret_cast<const uint4*>(ac_ptr[m]);
-    sa[m] = *reinterpret_cast<const uint16_t*>(as_ptr[m]);
-  }
-#pragma unroll
-  for (int n = 0; n < WN; ++n) {
-    cb[n] = *reinterpret_cast<const uint4*>(bc_ptr[n]);
-    sbv[n] = *reinterpret_cast<const uint16_t*>(bs_ptr[n]);
-  }
+  for (int n = 0; n < WN; ++n) b_off[n] = A_BYTES + (wave * 32 * WN + 32 * n + l32) * kRowB;
 
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    uint4 na[WM], nb[WN];
-    uint32_t nsa[WM], nsb[WN];
-    const bool more = kt + 1 < nk;
-    if (more) {
+  auto compute = [&](int buf) {
+    const uint8_t* sb = smem + buf * STAGE;
+    u32x4_t rb0[WN], rb1[WN];
+    half2_t bsc[WN][2];
 #pragma unroll
-      for (int m = 0; m < WM; ++m) {
-        na[m] = *reinterpret_cast<const uint4*>(ac_ptr[m] + (kt + 1) * 32);
-        nsa[m] = *reinterpret_cast<const uint16_t*>(as_ptr[m] + (kt + 1) * 4);
-      }
-#pragma unroll
-      for (int n = 0; n < WN; ++n) {
-        nb[n] = *reinterpret_cast<const uint4*>(bc_ptr[n] + (kt + 1) * 32);
-        nsb[n] = *reinterpret_cast<const uint16_t*>(bs_ptr[n] + (kt + 1) * 4);
-      }
+    for (int n = 0; n < WN; ++n) {
+      rb0[n] = *reinterpret_cast<const u32x4_t*>(sb + b_off[n] + 32 * half);
+      rb1[n] = *reinterpret_cast<const u32x4_t*>(sb + b_off[n] + 32 * half + 16);
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + b_off[n] + 64 + 4 * half);
+      bsc[n][0] = e4m3x2_to_half2(sw);
+      bsc[n][1] = e4m3x2_to_half2(sw >> 16);
     }
-    half2_t sah[WM], sbh[WN];
 #pragma unroll
-    for (int m = 0; m < WM; ++m) sah[m] = e4m3x2_to_half2(sa[m]);
-#pragma unroll
-    for (int n = 0; n < WN; ++n) sbh[n] = e4m3x2_to_half2(sbv[n]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 8; ++s) {
       half8_t fa[WM], fb[WN];
 #pragma unroll
-      for (int m = 0; m < WM; ++m) {
-        const uint32_t c = s == 0 ? ca[m].x : s == 1 ? ca[m].y : s == 2 ? ca[m].z : ca[m].w;
-        const half2_t sc = (s < 2) ? half2_t{sah[m][0], sah[m][0]} : half2_t{sah[m][1], sah[m][1]};
-        fa[m] = decode8(c, sc);
-      }
+      for (int m = 0; m < WM; ++m)
+        fa[m] = *reinterpret_cast<const half8_t*>(sb + ((m * 8 + s) * 64 + lane) * 16);
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
-        const uint32_t c = s == 0 ? cb[n].x : s == 1 ? cb[n].y : s == 2 ? cb[n].z : cb[n].w;
-        const half2_t sc = (s < 2) ? half2_t{sbh[n][0], sbh[n][0]} : half2_t{sbh[n][1], sbh[n][1]};
-        fb[n] = decode8(c, sc);
+        const uint32_t c = s < 4 ? rb0[n][s] : rb1[n][s - 4];
+        const _Float16 sc = bsc[n][s / 4][(s / 2) % 2];
+        fb[n] = decode8(c, half2_t{sc, sc});
       }
 #pragma unroll
       for (int m = 0; m < WM; ++m)
@@ -223,113 +312,140 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_w4a4_kernel(GemmArgs a) {
         for (int n = 0; n < WN; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[m], fb[n], acc[m][n], 0, 0, 0);
     }
-    if (more) {
-#pragma unroll
-      for (int m = 0; m < WM; ++m) { ca[m] = na[m]; sa[m] = nsa[m]; }
-#pragma unroll
-      for (int n = 0; n < WN; ++n) { cb[n] = nb[n]; sbv[n] = nsb[n]; }
-    }
+  };
+
+  // ---- main loop: stage it computes from buffer it&1 while stage it+1 is
+  // decoded/copied into the other buffer and stage it+2 is loaded.
+  const int64_t nst = K / kKS;
+  gload(0);
+  fill(0);
+  gload(nst > 1 ? 1 : 0);
+  __syncthreads();
+  for (int64_t it = 0; it < nst; ++it) {
+    compute((int)(it & 1));
+    fill((int)((it + 1) & 1));               // harmless on the last stage
+    gload(it + 2 < nst ? it + 2 : nst - 1);
+    __syncthreads();
   }
 
-  // ---- epilogue: acc[m][n][r] is C[row, col] with
-  //   row = 32m + 8(r/4) + 4(lane/32) + r%4,  col = 32n + lane%32
+  // ---- epilogue through LDS, one 32-row block at a time.  acc[m][n][r] is
+  // C[32m + 8(r/4) + 4(lane/32) + r%4][32n + lane%32] of this wave's tile.
+  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * kEpiLd;
   const float sgb = a.b_gscale[g];
-  const int64_t wrow0 = row0 + wm * 32 * WM;
-  if (EPI != EPI_SWIGLU) {
+  const int er = lane >> 1;                     // row of the block this lane finishes
+  const int eh = lane & 1;                      // which half of the columns
 #pragma unroll
-    for (int m = 0; m < WM; ++m) {
+  for (int m = 0; m < WM; ++m) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = wrow0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
-        if (row >= row1) continue;
-        const float sga = a.a_gscale[row];
+    for (int n = 0; n < WN; ++n)
 #pragma unroll
-        for (int n = 0; n < WN; ++n) {
-          const int64_t col = bcol[n];
-          if (col >= N) continue;
-          const float v = (acc[m][n][r] * sga) * sgb;
-          if (EPI == EPI_F32)
-            static_cast<float*>(a.out)[row * N + col] = v;
-          else
-            static_cast<uint16_t*>(a.out)[row * N + col] = (uint16_t)f32_to_bf16_bits(v);
+      for (int r = 0; r < 16; ++r)
+        ep[(8 * (r / 4) + 4 * half + (r % 4)) * kEpiLd + 32 * n + l32] = acc[m][n][r];
+    __syncthreads();                             // the block is in LDS (every wave loops WM times)
+    const int64_t row = row0 + 32 * m + er;
+    const bool rv = row < row1;
+    const int64_t rr = rv ? row : row1 - 1;
+    const float sga = a.a_gscale[rr];
+    const float* src = ep + er * kEpiLd;
+    if (EPI == EPI_SWIGLU) {
+      constexpr int GC = 32 * WN / 2;            // gate columns of this wave
+      const int64_t I = a.inter;
+      const int64_t gate0 = nt * (BN / 2) + (int64_t)wave * GC;
+      const float p = a.row_prob[rr];
+      uint32_t mx = 0u;
+      if (rv && gate0 < I) {
+#pragma unroll
+        for (int c8 = 0; c8 < GC / 2; c8 += 8) {
+          const int c = eh * (GC / 2) + c8;      // column inside the gate half
+          uint32_t packed[4];
+          float gv[8], uv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            gv[i] = (src[c + i] * sga) * sgb;
+            uv[i] = (src[GC + c + i] * sga) * sgb;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            const uint32_t d0 = f32_to_bf16_bits(swiglu_weighted(gv[i], uv[i], p));
+            const uint32_t d1 = f32_to_bf16_bits(swiglu_weighted(gv[i + 1], uv[i + 1], p));
+            packed[i / 2] = d0 | (d1 << 16);
+            const uint32_t m0 = d0 & 0x7FFFu, m1 = d1 & 0x7FFFu;
+            mx = mx > m0 ? mx : m0;
+            mx = mx > m1 ? mx : m1;
+          }
+          const int64_t col = gate0 + c;
+          *reinterpret_cast<uint4*>(a.d_out + rr * I + col) =
+              make_uint4(packed[0], packed[1], packed[2], packed[3]);
+          if (a.c_out) {
+            float* cg = a.c_out + rr * 2 * I + col;
+            float* cu = cg + I;
+            *reinterpret_cast<float4*>(cg) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+            *reinterpret_cast<float4*>(cg + 4) = make_float4(gv[4], gv[5], gv[6], gv[7]);
+            *reinterpret_cast<float4*>(cu) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+            *reinterpret_cast<float4*>(cu + 4) = make_float4(uv[4], uv[5], uv[6], uv[7]);
+          }
         }
       }
-    }
-  } else {
-    constexpr int HALF = WN / 2;
-    const int64_t I = a.inter;
+      const uint32_t other = (uint32_t)__shfl_xor((int)mx, 1, kWave);
+      mx = mx > other ? mx : other;
+      if (rv && eh == 0 && mx != 0u)
+        atomicMax(reinterpret_cast<uint32_t*>(a.amax) + row, mx << 16);
+    } else {
+      constexpr int WC = 32 * WN;                // columns of this wave
+      const int64_t col0 = nt * BN + (int64_t)wave * WC + eh * (WC / 2);
+      if (rv) {
 #pragma unroll
-    for (int m = 0; m < WM; ++m) {
+        for (int c8 = 0; c8 < WC / 2; c8 += 8) {
+          const int64_t col = col0 + c8;
+          if (col >= N) break;                   // N % 32 == 0: 8-column runs are whole
+          float v[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = wrow0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
-        const bool rv = row < row1;
-        const int64_t rr = rv ? row : row1 - 1;
-        const float sga = a.a_gscale[rr];
-        const float p = a.row_prob[rr];
-        uint32_t mx = 0u;
-#pragma unroll
-        for (int n = 0; n < HALF; ++n) {
-          const int64_t col = bcol[n];                  // gate column (< inter if valid)
-          const bool cv = rv && col < I;
-          const float gv = (acc[m][n][r] * sga) * sgb;
-          const float uv = (acc[m][n + HALF][r] * sga) * sgb;
-          float dv;
-          if (gv >= -80.0f) {
-            const float silu = gv / (1.0f + __expf(-gv));
-            dv = (silu * uv) * p;
+          for (int i = 0; i < 8; ++i) v[i] = (src[eh * (WC / 2) + c8 + i] * sga) * sgb;
+          if (EPI == EPI_F32) {
+            float* o = static_cast<float*>(a.out) + rr * N + col;
+            *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
           } else {
-            // exp(-g) overflows binary32 below g = -88.7 while g e^g u p can
-            // still be a normal bf16: evaluate this rare tail in binary64.
-            const double eg = exp((double)gv);
-            dv = (float)(((double)gv * eg / (1.0 + eg)) * (double)uv * (double)p);
-          }
-          const uint32_t db = f32_to_bf16_bits(dv);
-          if (cv) {
-            a.d_out[rr * I + col] = (uint16_t)db;
-            if (a.c_out) {
-              a.c_out[rr * 2 * I + col] = gv;
-              a.c_out[rr * 2 * I + I + col] = uv;
-            }
-            const uint32_t mag = db & 0x7FFFu;
-            mx = mx > mag ? mx : mag;
+            uint16_t* o = static_cast<uint16_t*>(a.out) + rr * N + col;
+            *reinterpret_cast<uint4*>(o) = make_uint4(
+                f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16),
+                f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16),
+                f32_to_bf16_bits(v[4]) | (f32_to_bf16_bits(v[5]) << 16),
+                f32_to_bf16_bits(v[6]) | (f32_to_bf16_bits(v[7]) << 16));
           }
         }
-        // max over the 32 lanes that hold this row (same lane half)
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) {
-          uint32_t y = (uint32_t)__shfl_xor((int)mx, o, kWave);
-          mx = mx > y ? mx : y;
-        }
-        if (rv && l32 == 0 && mx != 0u)
-          atomicMax(reinterpret_cast<uint32_t*>(a.amax) + row, mx << 16);
       }
     }
+    __syncthreads();                             // block consumed before it is overwritten
   }
 }
 
 // ---- launchers -------------------------------------------------------------
 
-template <int WM, int WN, int WGM, int WGN, int EPI>
+template <int WM, int WN, int NW, int EPI>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int BM = 32 * WM * WGM, BN = 32 * WN * WGN;
+  constexpr int BM = 32 * WM, BN = 32 * WN * NW;
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (a.n + BN - 1) / BN;
   // upper bound on the m-tiles of all groups: sum ceil(n_g/BM) <= cap/BM + G
   const int64_t mtiles = (a.rows_cap + BM - 1) / BM + a.num_groups;
   const int64_t blocks = mtiles * ntn;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  gemm_w4a4_kernel<WM, WN, WGM, WGN, EPI><<<(unsigned)blocks, 64 * WGM * WGN, 0, s>>>(a);
+  const size_t stage = (size_t)WM * 8 * 64 * 16 + (size_t)BN * kRowB;
+  size_t lds = 2 * stage;
+  const size_t epi = (size_t)NW * 32 * kEpiLd * 4;
+  if (epi > lds) lds = epi;
+  gemm_w4a4_kernel<WM, WN, NW, EPI><<<(unsigned)blocks, 64 * NW, lds, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_plain(const GemmArgs& a, hipStream_t s) {
-  if (a.out_dtype == 0) return launch_cfg<4, 2, 1, 4, EPI_F32>(a, s);
-  return launch_cfg<4, 2, 1, 4, EPI_BF16>(a, s);
+  if (a.out_dtype == 0) return launch_cfg<4, 4, 4, EPI_F32>(a, s);
+  return launch_cfg<4, 4, 4, EPI_BF16>(a, s);
 }
 
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s) {
-  return launch_cfg<4, 2, 1, 4, EPI_SWIGLU>(a, s);
+  return launch_cfg<4, 4, 4, EPI_SWIGLU>(a, s);
 }
 
 }  // namespace nvfp4
