@@ -44,8 +44,12 @@ def parse():
     p.add_argument("--workload", default="qwen3_30b_a3b_moe_t8192")
     p.add_argument("--cpu-tokens", type=int, default=512,
                    help="tokens of the oracle's CPU-baseline sample (0 = skip)")
-    p.add_argument("--traffic", default=None,
-                   help="JSON file with measured HBM bytes per FC1 launch (rocprof PMC)")
+    p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fc1_traffic.json"),
+                   help="JSON record of measured HBM bytes per FC1 launch (rocprof PMC); "
+                        "ignored when the GEMM source changed since it was taken")
+    p.add_argument("--copy-calib-mib", type=int, default=0,
+                   help="after timing, run plain device copies of this many MiB (a known-size "
+                        "kernel for scaling the rocprof FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -137,8 +141,20 @@ def main():
     fc1_tflops = fc1_flops / (fc1_ms * 1e-3) / 1e12
     traffic = None
     if args.traffic and os.path.exists(args.traffic):
+        from nvfp4_w4a4_quantized_amd.traffic import gemm_source_hash
         with open(args.traffic) as f:
-            traffic = json.load(f).get("fc1_hbm_bytes_per_launch")
+            rec = json.load(f)
+        if rec.get("gemm_source_sha256") == gemm_source_hash() and rec.get("workload") == w.name:
+            traffic = rec.get("fc1_hbm_bytes_per_launch")
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.empty(n, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty(n, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(3):   # a plain elementwise kernel: reads n*4 bytes, writes n*4 bytes
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 elementwise copies of {args.copy_calib_mib} MiB")
     log("stages (ms, HIP events): " + ", ".join(f"{k}={v:.4f}" for k, v in stages.items()))
     result = {
         "metric": "MoE W4A4 expert-layer tokens/s",

@@ -140,25 +140,29 @@ __device__ __forceinline__ float swiglu_weighted(float g, float u, float p) {
   return swiglu_tail(g, u, p);
 }
 
-template <int WM, int WN, int NW, int EPI>
-__global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
-  constexpr int BM = 32 * WM;
-  constexpr int BN = 32 * WN * NW;
+template <int WM, int WN, int WGM, int WGN, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_w4a4_kernel(GemmArgs a) {
+  constexpr int NW = WGM * WGN;                     // waves: WGM along M x WGN along N
+  constexpr int BM = 32 * WM * WGM;
+  constexpr int BN = 32 * WN * WGN;
   constexpr int NT = 64 * NW;                       // threads
-  constexpr int A_BYTES = WM * 8 * 64 * 16;         // fp16 A stage (fragment order)
-  constexpr int B_BYTES = BN * kRowB;               // packed B stage
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_UNITS = BM * 2;                   // half rows of 64 elements
+  constexpr int A_BYTES = (BM / 32) * 8 * 64 * 16;  // fp16 A stage (fragment order)
+  constexpr int BC_BYTES = BN * 64;                 // packed B codes (swizzled rows)
+  constexpr int BS_BYTES = BN * 8;                  // B block scales
+  constexpr int STAGE = A_BYTES + BC_BYTES + BS_BYTES;
+  constexpr int A_UNITS = BM * 4;                   // quarter rows of 32 elements
   constexpr int APT = (A_UNITS + NT - 1) / NT;      // A units per thread
-  constexpr int B_CHUNKS = BN * 4;                  // 16-byte code chunks
-  constexpr int BPT = (B_CHUNKS + NT - 1) / NT;
-  constexpr int BSPT = (BN + NT - 1) / NT;          // B scale rows per thread
+  constexpr bool A_FULL = (A_UNITS % NT) == 0;      // every thread owns APT units
+  constexpr int BC_INSTR = BN / 16 / NW;            // 1 KiB code loads per wave
+  constexpr int BS_INSTR = BN / 32 / NW;            // 256-byte scale loads per wave
   static_assert(EPI != EPI_SWIGLU || WN % 2 == 0, "SwiGLU pairs gate and up blocks");
+  static_assert(BC_INSTR * 16 * NW == BN && BS_INSTR * 32 * NW == BN, "B tile split across waves");
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int64_t K = a.k;
   const int64_t N = a.n;
 
@@ -186,8 +190,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
     if (EPI == EPI_SWIGLU) cmax = (((j / 32) % WN) < WN / 2) ? a.inter - 1 : 2 * a.inter - 1;
     return (int64_t)g * N + (c < cmax ? c : cmax);
   };
+  // 16-byte slot of part p in staged B row r: XOR swizzle keeps the fragment
+  // reads (32 consecutive rows, one part) on distinct LDS banks
+  auto bslot = [](int r, int p) { return p ^ ((r >> 2) & 3); };
 
-  // ---- per-thread copy plan (fixed for the tile; the stage moves K)
+  // ---- A: thread-owned quarter rows (32 elements = 16 code bytes + 2 scales)
   int64_t a_src[APT], a_ssrc[APT];
   int a_dst[APT];
   bool a_ok[APT];
@@ -195,79 +202,65 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
   for (int j = 0; j < APT; ++j) {
     const int u = tid + NT * j;
     a_ok[j] = u < A_UNITS;
-    const int r = a_ok[j] ? u / 2 : 0, h = u % 2;
+    const int r = a_ok[j] ? u / 4 : 0, q = u % 4, h = q / 2;
     int64_t ar = row0 + r;
     ar = ar < row1 ? ar : row1 - 1;
-    a_src[j] = ar * (K / 2) + 32 * h;
-    a_ssrc[j] = ar * (K / 16) + 4 * h;
-    // fragment m = r/32, lane (r%32) + 32h; substep s adds s*1024 bytes
-    a_dst[j] = ((r / 32) * 8 * 64 + (r % 32) + 32 * h) * 16;
+    a_src[j] = ar * (K / 2) + 16 * q;
+    a_ssrc[j] = ar * (K / 16) + 2 * q;
+    // fragment r/32, lane (r%32) + 32h, substeps 4(q%2) .. 4(q%2)+3
+    a_dst[j] = (((r / 32) * 8 + 4 * (q % 2)) * 64 + (r % 32) + 32 * h) * 16;
   }
-  int64_t b_src[BPT];
-  int b_dst[BPT];
-  bool b_ok[BPT];
+  // ---- B: global -> LDS copies issued by every wave (no registers involved)
+  int64_t bc_src[BC_INSTR], bs_src[BS_INSTR];
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    const int c = tid + NT * j;
-    b_ok[j] = c < B_CHUNKS;
-    const int row = b_ok[j] ? c / 4 : 0, part = c % 4;
-    b_src[j] = b_src_row(row) * (K / 2) + part * 16;
-    b_dst[j] = A_BYTES + row * kRowB + part * 16;
+  for (int j = 0; j < BC_INSTR; ++j) {
+    const int c = wave + NW * j;                 // 16-row chunk: 1 KiB of LDS
+    const int r = c * 16 + lane / 4, q = lane % 4;
+    bc_src[j] = b_src_row(r) * (K / 2) + 16 * bslot(r, q);
   }
-  int64_t bs_src[BSPT];
-  int bs_dst[BSPT];
-  bool bs_ok[BSPT];
 #pragma unroll
-  for (int j = 0; j < BSPT; ++j) {
-    const int row = tid + NT * j;
-    bs_ok[j] = row < BN;
-    const int rr = bs_ok[j] ? row : 0;
-    bs_src[j] = b_src_row(rr) * (K / 16);
-    bs_dst[j] = A_BYTES + rr * kRowB + 64;
+  for (int j = 0; j < BS_INSTR; ++j) {
+    const int c = wave + NW * j;                 // 32-row chunk: 256 bytes of LDS
+    const int r = c * 32 + lane / 2;
+    bs_src[j] = b_src_row(r) * (K / 16) + 4 * (lane % 2);
   }
-
-  u32x4_t ar0[APT], ar1[APT];
-  uint32_t asr[APT];
-  u32x4_t breg[BPT];
-  uint2 bsreg[BSPT];
-  auto gload = [&](int64_t st) {
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+  auto b_issue = [&](int64_t st, int buf) {
+    uint8_t* sb = smem + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < BC_INSTR; ++j) {
+      const int c = wave + NW * j;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a.b_codes + bc_src[j] + st * 64),
+                                       (lds_ptr_t)(sb + A_BYTES + c * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < BS_INSTR; ++j) {
+      const int c = wave + NW * j;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a.b_scales + bs_src[j] + st * 8),
+                                       (lds_ptr_t)(sb + A_BYTES + BC_BYTES + c * 256), 4, 0, 0);
+    }
+  };
+  u32x4_t araw[APT];
+  uint32_t asc[APT];
+  auto a_load = [&](int64_t st) {
 #pragma unroll
     for (int j = 0; j < APT; ++j)
-      if (a_ok[j]) {
-        const uint8_t* p = a.a_codes + a_src[j] + st * 64;
-        ar0[j] = *reinterpret_cast<const u32x4_t*>(p);
-        ar1[j] = *reinterpret_cast<const u32x4_t*>(p + 16);
-        asr[j] = *reinterpret_cast<const uint32_t*>(a.a_scales + a_ssrc[j] + st * 8);
+      if (A_FULL || a_ok[j]) {
+        araw[j] = *reinterpret_cast<const u32x4_t*>(a.a_codes + a_src[j] + st * 64);
+        asc[j] = *reinterpret_cast<const uint16_t*>(a.a_scales + a_ssrc[j] + st * 8);
       }
-#pragma unroll
-    for (int j = 0; j < BPT; ++j)
-      if (b_ok[j]) breg[j] = *reinterpret_cast<const u32x4_t*>(a.b_codes + b_src[j] + st * 64);
-#pragma unroll
-    for (int j = 0; j < BSPT; ++j)
-      if (bs_ok[j]) bsreg[j] = *reinterpret_cast<const uint2*>(a.b_scales + bs_src[j] + st * 8);
   };
-  // decode the A half rows and copy the packed B rows into stage buffer `buf`
-  auto fill = [&](int buf) {
+  // decode chunk c (8 elements) of the thread's quarter rows into buffer buf
+  auto a_decode = [&](int c, int buf) {
     uint8_t* sb = smem + buf * STAGE;
 #pragma unroll
     for (int j = 0; j < APT; ++j)
-      if (a_ok[j]) {
-        const half2_t s01 = e4m3x2_to_half2(asr[j]);
-        const half2_t s23 = e4m3x2_to_half2(asr[j] >> 16);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const uint32_t c = s < 4 ? ar0[j][s] : ar1[j][s - 4];
-          const _Float16 sc = (s < 2) ? s01[0] : (s < 4) ? s01[1] : (s < 6) ? s23[0] : s23[1];
-          const half8_t v = decode8(c, half2_t{sc, sc});
-          *reinterpret_cast<half8_t*>(sb + a_dst[j] + s * 1024) = v;
-        }
+      if (A_FULL || a_ok[j]) {
+        const half2_t s2 = e4m3x2_to_half2(asc[j]);
+        const _Float16 sc = (c < 2) ? s2[0] : s2[1];
+        *reinterpret_cast<half8_t*>(sb + a_dst[j] + c * 1024) = decode8(araw[j][c], half2_t{sc, sc});
       }
-#pragma unroll
-    for (int j = 0; j < BPT; ++j)
-      if (b_ok[j]) *reinterpret_cast<u32x4_t*>(sb + b_dst[j]) = breg[j];
-#pragma unroll
-    for (int j = 0; j < BSPT; ++j)
-      if (bs_ok[j]) *reinterpret_cast<uint2*>(sb + bs_dst[j]) = bsreg[j];
   };
 
   float16_t acc[WM][WN];
@@ -280,19 +273,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
 
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  int b_off[WN];
+  int b_row[WN];
 #pragma unroll
-  for (int n = 0; n < WN; ++n) b_off[n] = A_BYTES + (wave * 32 * WN + 32 * n + l32) * kRowB;
+  for (int n = 0; n < WN; ++n) b_row[n] = wn * 32 * WN + 32 * n + l32;
 
-  auto compute = [&](int buf) {
+  // multiplies stage buffer `buf`; substeps 4..7 also decode the next stage's
+  // A (raw registers loaded at the start of the stage) into buffer `nxt`
+  auto compute = [&](int buf, int nxt) {
     const uint8_t* sb = smem + buf * STAGE;
     u32x4_t rb0[WN], rb1[WN];
     half2_t bsc[WN][2];
 #pragma unroll
     for (int n = 0; n < WN; ++n) {
-      rb0[n] = *reinterpret_cast<const u32x4_t*>(sb + b_off[n] + 32 * half);
-      rb1[n] = *reinterpret_cast<const u32x4_t*>(sb + b_off[n] + 32 * half + 16);
-      const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + b_off[n] + 64 + 4 * half);
+      const int r = b_row[n];
+      rb0[n] = *reinterpret_cast<const u32x4_t*>(sb + A_BYTES + r * 64 + 16 * bslot(r, 2 * half));
+      rb1[n] = *reinterpret_cast<const u32x4_t*>(sb + A_BYTES + r * 64 + 16 * bslot(r, 2 * half + 1));
+      const uint32_t sw = *reinterpret_cast<const uint32_t*>(sb + A_BYTES + BC_BYTES + r * 8 + 4 * half);
       bsc[n][0] = e4m3x2_to_half2(sw);
       bsc[n][1] = e4m3x2_to_half2(sw >> 16);
     }
@@ -301,7 +297,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
       half8_t fa[WM], fb[WN];
 #pragma unroll
       for (int m = 0; m < WM; ++m)
-        fa[m] = *reinterpret_cast<const half8_t*>(sb + ((m * 8 + s) * 64 + lane) * 16);
+        fa[m] = *reinterpret_cast<const half8_t*>(sb + (((wm * WM + m) * 8 + s) * 64 + lane) * 16);
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
         const uint32_t c = s < 4 ? rb0[n][s] : rb1[n][s - 4];
@@ -313,22 +309,40 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
 #pragma unroll
         for (int n = 0; n < WN; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+      if (s >= 4) a_decode(s - 4, nxt);
     }
   };
 
-  // ---- main loop: stage it computes from buffer it&1 while stage it+1 is
-  // decoded/copied into the other buffer and stage it+2 is loaded.
+  // ---- main loop.  Stage it is multiplied from buffer it&1.  At the start
+  // of the stage the next stage's B is requested straight into the other
+  // buffer; the next stage's A codes (already in registers, loaded one stage
+  // earlier) are decoded into it between the MFMAs of substeps 4-7, after
+  // which the registers receive the A codes of the stage after that.  Vector
+  // memory loads complete in issue order, so waiting until only the A loads
+  // (issued last) may be outstanding guarantees the B copy has landed before
+  // the barrier.  The tail stages re-fetch the last stage into the idle
+  // buffer, which nothing reads: the loop stays branch-free.
+  constexpr int A_LOADS = 2 * APT;              // VMEM ops issued by a_load
+  static_assert(A_LOADS <= 15, "vmcnt immediate");
   const int64_t nst = K / kKS;
-  gload(0);
-  fill(0);
-  gload(nst > 1 ? 1 : 0);
+  a_load(0);
+  b_issue(0, 0);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) a_decode(c, 0);
+  a_load(nst > 1 ? 1 : 0);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | A_LOADS); // vmcnt(A_LOADS): B of stage 0 is in LDS
   __syncthreads();
   for (int64_t it = 0; it < nst; ++it) {
-    compute((int)(it & 1));
-    fill((int)((it + 1) & 1));               // harmless on the last stage
-    gload(it + 2 < nst ? it + 2 : nst - 1);
+    const int cur = (int)(it & 1), nxt = cur ^ 1;
+    const int64_t st1 = it + 1 < nst ? it + 1 : it;
+    const int64_t st2 = it + 2 < nst ? it + 2 : nst - 1;
+    b_issue(st1, nxt);
+    compute(cur, nxt);
+    a_load(st2);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | A_LOADS);
     __syncthreads();
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0) before LDS is reused
 
   // ---- epilogue through LDS, one 32-row block at a time.  acc[m][n][r] is
   // C[32m + 8(r/4) + 4(lane/32) + r%4][32n + lane%32] of this wave's tile.
@@ -344,7 +358,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r)
         ep[(8 * (r / 4) + 4 * half + (r % 4)) * kEpiLd + 32 * n + l32] = acc[m][n][r];
     __syncthreads();                             // the block is in LDS (every wave loops WM times)
-    const int64_t row = row0 + 32 * m + er;
+    const int64_t row = row0 + 32 * (wm * WM + m) + er;
     const bool rv = row < row1;
     const int64_t rr = rv ? row : row1 - 1;
     const float sga = a.a_gscale[rr];
@@ -352,7 +366,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
     if (EPI == EPI_SWIGLU) {
       constexpr int GC = 32 * WN / 2;            // gate columns of this wave
       const int64_t I = a.inter;
-      const int64_t gate0 = nt * (BN / 2) + (int64_t)wave * GC;
+      const int64_t gate0 = nt * (BN / 2) + (int64_t)wn * GC;
       const float p = a.row_prob[rr];
       uint32_t mx = 0u;
       if (rv && gate0 < I) {
@@ -394,7 +408,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
         atomicMax(reinterpret_cast<uint32_t*>(a.amax) + row, mx << 16);
     } else {
       constexpr int WC = 32 * WN;                // columns of this wave
-      const int64_t col0 = nt * BN + (int64_t)wave * WC + eh * (WC / 2);
+      const int64_t col0 = nt * BN + (int64_t)wn * WC + eh * (WC / 2);
       if (rv) {
 #pragma unroll
         for (int c8 = 0; c8 < WC / 2; c8 += 8) {
@@ -424,30 +438,38 @@ __global__ __launch_bounds__(64 * NW, 1) void gemm_w4a4_kernel(GemmArgs a) {
 
 // ---- launchers -------------------------------------------------------------
 
-template <int WM, int WN, int NW, int EPI>
+template <int WM, int WN, int WGM, int WGN, int EPI>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  constexpr int BM = 32 * WM, BN = 32 * WN * NW;
+  constexpr int NW = WGM * WGN, BM = 32 * WM * WGM, BN = 32 * WN * WGN;
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (a.n + BN - 1) / BN;
   // upper bound on the m-tiles of all groups: sum ceil(n_g/BM) <= cap/BM + G
   const int64_t mtiles = (a.rows_cap + BM - 1) / BM + a.num_groups;
   const int64_t blocks = mtiles * ntn;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const size_t stage = (size_t)WM * 8 * 64 * 16 + (size_t)BN * kRowB;
+  const size_t stage = (size_t)(BM / 32) * 8 * 64 * 16 + (size_t)BN * (64 + 8);
   size_t lds = 2 * stage;
   const size_t epi = (size_t)NW * 32 * kEpiLd * 4;
   if (epi > lds) lds = epi;
-  gemm_w4a4_kernel<WM, WN, NW, EPI><<<(unsigned)blocks, 64 * NW, lds, s>>>(a);
+  gemm_w4a4_kernel<WM, WN, WGM, WGN, EPI><<<(unsigned)blocks, 64 * NW, lds, s>>>(a);
   return hipGetLastError();
 }
 
+// Tile: MFMA blocks per wave (M, N) and waves per workgroup (M, N).
+#ifndef NVFP4_GEMM_TILE
+#define NVFP4_GEMM_TILE 4, 2, 1, 8
+#endif
+#ifndef NVFP4_GEMM_TILE_FC1
+#define NVFP4_GEMM_TILE_FC1 NVFP4_GEMM_TILE
+#endif
+
 hipError_t launch_gemm_plain(const GemmArgs& a, hipStream_t s) {
-  if (a.out_dtype == 0) return launch_cfg<4, 2, 8, EPI_F32>(a, s);
-  return launch_cfg<4, 2, 8, EPI_BF16>(a, s);
+  if (a.out_dtype == 0) return launch_cfg<NVFP4_GEMM_TILE, EPI_F32>(a, s);
+  return launch_cfg<NVFP4_GEMM_TILE, EPI_BF16>(a, s);
 }
 
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s) {
-  return launch_cfg<4, 2, 8, EPI_SWIGLU>(a, s);
+  return launch_cfg<NVFP4_GEMM_TILE_FC1, EPI_SWIGLU>(a, s);
 }
 
 }  // namespace nvfp4

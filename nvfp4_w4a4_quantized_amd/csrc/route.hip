@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* hist,
   }
 }
 
-template <int BPL>
+template <int BPL, int KMAX>
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const int32_t* base,
                                                             const int32_t* counts) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -205,19 +205,13 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     }
   }
 
-  for (int j = 0; j < k; ++j) {
-    const int e = a.topk_idx[t * k + j];
-    int64_t dst = -1;
-    if (e >= 0 && e < E) {
-      bool hit = false;
-      if (lane_valid)
-        for (int i = 0; i < k; ++i) hit |= (a.topk_idx[tl * k + i] == e);
-      const uint64_t mask = __ballot(hit);
-      const uint64_t below = pos == 0 ? 0ull : (mask & ((1ull << pos) - 1ull));
-      dst = (int64_t)base[chunk * E + e] + __popcll(below);
-    }
+  // Destination row of each of the token's k entries.  With KMAX > 0 every
+  // lane first holds the k expert ids of its own chunk token in registers, so
+  // the ballots need no memory traffic; the current token's ids come from
+  // lane `pos` by a shuffle.
+  auto store_row = [&](int j, int64_t dst) {
     if (lane == 0) a.dst_row[t * k + j] = (int32_t)dst;
-    if (dst < 0) continue;
+    if (dst < 0) return;
     if (lane == 0) {
       a.row_src[dst] = (int32_t)t;
       a.row_prob[dst] = a.topk_prob[t * k + j];
@@ -236,6 +230,43 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
         }
       }
     }
+  };
+  const uint64_t below_mask = pos == 0 ? 0ull : ((1ull << pos) - 1ull);
+  if constexpr (KMAX > 0) {
+    int ids[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) ids[i] = (lane_valid && i < k) ? a.topk_idx[tl * k + i] : -1;
+    int64_t dsts[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      dsts[j] = -1;
+      if (j < k) {
+        const int e = __shfl(ids[j], pos, kWave);
+        if (e >= 0 && e < E) {
+          bool hit = false;
+#pragma unroll
+          for (int i = 0; i < KMAX; ++i) hit |= (ids[i] == e);
+          const uint64_t mask = __ballot(hit);
+          dsts[j] = (int64_t)base[chunk * E + e] + __popcll(mask & below_mask);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (j < k) store_row(j, dsts[j]);
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const int e = a.topk_idx[t * k + j];
+      int64_t dst = -1;
+      if (e >= 0 && e < E) {
+        bool hit = false;
+        if (lane_valid)
+          for (int i = 0; i < k; ++i) hit |= (a.topk_idx[tl * k + i] == e);
+        const uint64_t mask = __ballot(hit);
+        dst = (int64_t)base[chunk * E + e] + __popcll(mask & below_mask);
+      }
+      store_row(j, dst);
+    }
   }
 }
 
@@ -253,12 +284,14 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int64_t waves = a.tokens + E;
   dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   int bpl = a.x ? blocks_per_lane(a.hidden) : 1;
-  switch (bpl) {
-    case 1: route_scatter_kernel<1><<<grid, block, 0, s>>>(a, base, counts); break;
-    case 2: route_scatter_kernel<2><<<grid, block, 0, s>>>(a, base, counts); break;
-    case 4: route_scatter_kernel<4><<<grid, block, 0, s>>>(a, base, counts); break;
-    case 8: route_scatter_kernel<8><<<grid, block, 0, s>>>(a, base, counts); break;
-    case 16: route_scatter_kernel<16><<<grid, block, 0, s>>>(a, base, counts); break;
+  const int kmax = a.topk <= 8 ? 8 : (a.topk <= 16 ? 16 : 0);
+  switch (bpl * 100 + kmax) {
+#define NVFP4_SCATTER(B, KM) \
+    case B * 100 + KM: route_scatter_kernel<B, KM><<<grid, block, 0, s>>>(a, base, counts); break;
+    NVFP4_SCATTER(1, 8) NVFP4_SCATTER(2, 8) NVFP4_SCATTER(4, 8) NVFP4_SCATTER(8, 8) NVFP4_SCATTER(16, 8)
+    NVFP4_SCATTER(1, 16) NVFP4_SCATTER(2, 16) NVFP4_SCATTER(4, 16) NVFP4_SCATTER(8, 16) NVFP4_SCATTER(16, 16)
+    NVFP4_SCATTER(1, 0) NVFP4_SCATTER(2, 0) NVFP4_SCATTER(4, 0) NVFP4_SCATTER(8, 0) NVFP4_SCATTER(16, 0)
+#undef NVFP4_SCATTER
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -113,3 +113,16 @@ def test_deterministic_repeat():
     torch.cuda.synchronize()
     for key in a:
         assert torch.equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("k,E", [(12, 40), (20, 64)])
+def test_wide_topk(k, E):
+    """top-k beyond 8 (16-id register path) and beyond 16 (generic path)."""
+    rng = np.random.default_rng(k)
+    T = 200
+    idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[3, 2] = -1
+    prob = rng.random((T, k)).astype(np.float32)
+    x = random_bf16(rng, (T, 128))
+    for align in (1, 8):
+        _permute_and_compare(x, idx, prob, E, align, f"k={k} E={E}")
