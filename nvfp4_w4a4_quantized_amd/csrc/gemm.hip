@@ -16,6 +16,9 @@
 // device offsets: every workgroup derives its (group, m-tile) from a
 // wave-wide scan of the per-group tile counts, so the host never reads them;
 // surplus workgroups exit.
+#include <type_traits>
+#include <algorithm>
+
 #include "launch.h"
 #include "nvfp4_device.h"
 
@@ -95,14 +98,16 @@ __device__ __forceinline__ bool locate_mtile(const int32_t* off, int G, int BM, 
 // wave a BM x (32*WN) sub-tile held in accumulator registers
 // (WM x WN v_mfma_f32_32x32x16_f16 tiles).  K advances in stages of 128 with
 // two LDS buffers: while the waves multiply stage i, they fill stage i+1.
-//   A (activations, shared by all waves): each thread decodes half a row of
-//     the stage (64 elements) once, straight from its global load, and stores
-//     the fp16 values in MFMA-fragment order: for fragment m and substep s the
-//     64 lanes' 16-byte operands are one contiguous 1 KiB block, so both the
-//     writes and the per-substep reads are bank-conflict free.
-//   B (weights, distinct per wave): copied packed (64 code bytes + the 8
-//     scale bytes per row, rows padded to 80 bytes) and decoded by each wave
-//     into registers right before its MFMAs.
+//   A (activations, shared by all waves): each thread decodes a quarter row
+//     of the stage (32 elements) once, straight from its global load, and
+//     stores the fp16 values in MFMA-fragment order: for fragment m and
+//     substep s the 64 lanes' 16-byte operands are one 1 KiB block (lane
+//     slots XOR-swizzled inside groups of 16), so both the writes and the
+//     per-substep reads are bank-conflict free.
+//   B (weights, distinct per wave): copied packed by global->LDS loads (64
+//     code bytes per row in swizzled 16-byte slots, the 8 scale bytes in a
+//     separate array) and decoded by each wave into registers right before
+//     its MFMAs.
 // K order: inside a 128 stage, lane half h covers elements [64h, 64h+64)
 // and substep s takes [64h + 8s, 64h + 8s + 8); A and B use the same order,
 // so the dot products are unchanged.
@@ -194,6 +199,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_w4a4_kernel(GemmArgs a
   // reads (32 consecutive rows, one part) on distinct LDS banks
   auto bslot = [](int r, int p) { return p ^ ((r >> 2) & 3); };
 
+  // 16-byte slot of MFMA lane l in an A fragment block of substeps 4sq..4sq+3:
+  // flipping bits 2-3 keeps the slot inside its group of 16 (reads stay
+  // conflict free) and spreads the writers of one row over four bank groups
+  auto aslot = [](int l, int sq) { return l ^ (4 * (sq + 2 * (l >> 5))); };
   // ---- A: thread-owned quarter rows (32 elements = 16 code bytes + 2 scales)
   int64_t a_src[APT], a_ssrc[APT];
   int a_dst[APT];
@@ -207,8 +216,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_w4a4_kernel(GemmArgs a
     ar = ar < row1 ? ar : row1 - 1;
     a_src[j] = ar * (K / 2) + 16 * q;
     a_ssrc[j] = ar * (K / 16) + 2 * q;
-    // fragment r/32, lane (r%32) + 32h, substeps 4(q%2) .. 4(q%2)+3
-    a_dst[j] = (((r / 32) * 8 + 4 * (q % 2)) * 64 + (r % 32) + 32 * h) * 16;
+    // fragment r/32, lane (r%32) + 32h, substeps 4(q%2) .. 4(q%2)+3; the
+    // lane slot is XOR-swizzled (aslot) so that the four threads of one row
+    // write to distinct banks
+    a_dst[j] = (((r / 32) * 8 + 4 * (q % 2)) * 64 + aslot((r % 32) + 32 * h, q % 2)) * 16;
   }
   // ---- B: global -> LDS copies issued by every wave (no registers involved)
   int64_t bc_src[BC_INSTR], bs_src[BS_INSTR];
@@ -277,9 +288,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_w4a4_kernel(GemmArgs a
 #pragma unroll
   for (int n = 0; n < WN; ++n) b_row[n] = wn * 32 * WN + 32 * n + l32;
 
-  // multiplies stage buffer `buf`; substeps 4..7 also decode the next stage's
-  // A (raw registers loaded at the start of the stage) into buffer `nxt`
-  auto compute = [&](int buf, int nxt) {
+  // multiplies stage buffer `buf` for the first MV 32-row blocks of the
+  // wave's rows (the others are all padding); substeps 4..7 also decode the
+  // next stage's A (raw registers loaded at the start of the stage) into
+  // buffer `nxt`
+  auto compute = [&](auto mv_c, int buf, int nxt) {
+    constexpr int MV = decltype(mv_c)::value;
     const uint8_t* sb = smem + buf * STAGE;
     u32x4_t rb0[WN], rb1[WN];
     half2_t bsc[WN][2];
@@ -292,23 +306,37 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_w4a4_kernel(GemmArgs a
       bsc[n][0] = e4m3x2_to_half2(sw);
       bsc[n][1] = e4m3x2_to_half2(sw >> 16);
     }
+    // software pipeline: the operands of substep s+1 (A fragments from LDS,
+    // B decoded in registers) are produced while the MFMAs of substep s run
+    auto load_a = [&](half8_t (&fa)[WM], int s) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      half8_t fa[WM], fb[WN];
-#pragma unroll
-      for (int m = 0; m < WM; ++m)
-        fa[m] = *reinterpret_cast<const half8_t*>(sb + (((wm * WM + m) * 8 + s) * 64 + lane) * 16);
+      for (int m = 0; m < MV; ++m)
+        fa[m] = *reinterpret_cast<const half8_t*>(sb + (((wm * WM + m) * 8 + s) * 64 + aslot(lane, s / 4)) * 16);
+    };
+    auto decode_b = [&](half8_t (&fb)[WN], int s) {
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
         const uint32_t c = s < 4 ? rb0[n][s] : rb1[n][s - 4];
         const _Float16 sc = bsc[n][s / 4][(s / 2) % 2];
         fb[n] = decode8(c, half2_t{sc, sc});
       }
+    };
+    half8_t fa0[WM], fa1[WM], fb0[WN], fb1[WN];
+    load_a(fa0, 0);
+    decode_b(fb0, 0);
 #pragma unroll
-      for (int m = 0; m < WM; ++m)
+    for (int s = 0; s < 8; ++s) {
+      half8_t (&fa)[WM] = (s & 1) ? fa1 : fa0;
+      half8_t (&fb)[WN] = (s & 1) ? fb1 : fb0;
+      half8_t (&fan)[WM] = (s & 1) ? fa0 : fa1;
+      half8_t (&fbn)[WN] = (s & 1) ? fb0 : fb1;
+      if (s < 7) load_a(fan, s + 1);
+#pragma unroll
+      for (int m = 0; m < MV; ++m)
 #pragma unroll
         for (int n = 0; n < WN; ++n)
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+      if (s < 7) decode_b(fbn, s + 1);
       if (s >= 4) a_decode(s - 4, nxt);
     }
   };
@@ -325,24 +353,39 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_w4a4_kernel(GemmArgs a
   constexpr int A_LOADS = 2 * APT;              // VMEM ops issued by a_load
   static_assert(A_LOADS <= 15, "vmcnt immediate");
   const int64_t nst = K / kKS;
-  a_load(0);
-  b_issue(0, 0);
+  auto main_loop = [&](auto mv_c) {
+    a_load(0);
+    b_issue(0, 0);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) a_decode(c, 0);
-  a_load(nst > 1 ? 1 : 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70 | A_LOADS); // vmcnt(A_LOADS): B of stage 0 is in LDS
-  __syncthreads();
-  for (int64_t it = 0; it < nst; ++it) {
-    const int cur = (int)(it & 1), nxt = cur ^ 1;
-    const int64_t st1 = it + 1 < nst ? it + 1 : it;
-    const int64_t st2 = it + 2 < nst ? it + 2 : nst - 1;
-    b_issue(st1, nxt);
-    compute(cur, nxt);
-    a_load(st2);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | A_LOADS);
+    for (int c = 0; c < 4; ++c) a_decode(c, 0);
+    a_load(nst > 1 ? 1 : 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | A_LOADS); // vmcnt(A_LOADS): B of stage 0 is in LDS
     __syncthreads();
+    for (int64_t it = 0; it < nst; ++it) {
+      const int cur = (int)(it & 1), nxt = cur ^ 1;
+      const int64_t st1 = it + 1 < nst ? it + 1 : it;
+      const int64_t st2 = it + 2 < nst ? it + 2 : nst - 1;
+      b_issue(st1, nxt);
+      compute(mv_c, cur, nxt);
+      a_load(st2);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | A_LOADS);
+      __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0) before LDS is reused
+  };
+  // 32-row blocks of this wave's rows that hold at least one valid row; the
+  // tile's last rows are padding when the group ends inside it.  The count is
+  // the same for every wave of a row of waves, so barriers stay uniform.
+  const int mv = __builtin_amdgcn_readfirstlane((int)std::min<int64_t>(
+      WM, std::max<int64_t>(0, (row1 - row0 - 32 * WM * wm + 31) / 32)));
+  static_assert(WM <= 4, "main loop instances");
+  switch (mv) {
+    case 0: break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    case 2: if constexpr (WM >= 2) main_loop(std::integral_constant<int, 2 <= WM ? 2 : 1>{}); break;
+    case 3: if constexpr (WM >= 3) main_loop(std::integral_constant<int, 3 <= WM ? 3 : 1>{}); break;
+    default: main_loop(std::integral_constant<int, WM>{}); break;
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0) before LDS is reused
 
   // ---- epilogue through LDS, one 32-row block at a time.  acc[m][n][r] is
   // C[32m + 8(r/4) + 4(lane/32) + r%4][32n + lane%32] of this wave's tile.
@@ -352,11 +395,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_w4a4_kernel(GemmArgs a
   const int eh = lane & 1;                      // which half of the columns
 #pragma unroll
   for (int m = 0; m < WM; ++m) {
+    if (m < mv) {
 #pragma unroll
-    for (int n = 0; n < WN; ++n)
+      for (int n = 0; n < WN; ++n)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ep[(8 * (r / 4) + 4 * half + (r % 4)) * kEpiLd + 32 * n + l32] = acc[m][n][r];
+        for (int r = 0; r < 16; ++r)
+          ep[(8 * (r / 4) + 4 * half + (r % 4)) * kEpiLd + 32 * n + l32] = acc[m][n][r];
+    }
     __syncthreads();                             // the block is in LDS (every wave loops WM times)
     const int64_t row = row0 + 32 * (wm * WM + m) + er;
     const bool rv = row < row1;
