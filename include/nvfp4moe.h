@@ -153,7 +153,8 @@ int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
  *                groups are legal; the host never reads it
  *   out_dtype    0: float32, 1: bf16 (round-to-nearest-even)
  *   out          [rows_cap, n]; rows outside [off[0], off[G]) are not written
- * Limits: k % 128 == 0, k <= 16384; n % 32 == 0; 1 <= num_groups <= 1024.
+ * Limits: k % 128 == 0, k <= 16384; n % 32 == 0; 1 <= num_groups <= 1024;
+ * one group's B codes (n * k / 2 bytes) below 4 GiB (NVFP4_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                       int64_t rows_cap,

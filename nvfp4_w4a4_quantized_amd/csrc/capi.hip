@@ -181,6 +181,7 @@ int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   if (!out || (out_dtype != 0 && out_dtype != 1)) return NVFP4_INVALID_ARGUMENT;
   if (n < 32 || n % 32 != 0) return NVFP4_UNSUPPORTED;
   if ((int64_t)num_groups * n >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;
+  if (n * (k / 2) > 0xFFFFFFFFLL) return NVFP4_UNSUPPORTED;   // 32-bit offsets inside a group
   GemmArgs a{};
   a.a_codes = a_codes; a.a_scales = a_scales; a.a_gscale = a_gscale;
   a.b_codes = b_codes; a.b_scales = b_scales; a.b_gscale = b_gscale;
@@ -200,6 +201,7 @@ int w4a4_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales, co
   if (!row_prob || !d_out || !amax) return NVFP4_INVALID_ARGUMENT;
   if (inter < 64 || inter % 64 != 0) return NVFP4_UNSUPPORTED;
   if ((int64_t)num_groups * 2 * inter >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;
+  if (2 * inter * (k / 2) > 0xFFFFFFFFLL) return NVFP4_UNSUPPORTED;   // 32-bit offsets inside a group
   GemmArgs a{};
   a.a_codes = a_codes; a.a_scales = a_scales; a.a_gscale = a_gscale;
   a.b_codes = b_codes; a.b_scales = b_scales; a.b_gscale = b_gscale;

@@ -86,6 +86,10 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     assert L.w4a4_grouped_gemm(*g, 64, 128, 7, fake, None) == INVALID
     assert L.w4a4_grouped_gemm(*g, 64, 120, 0, fake, None) == INVALID
     assert L.w4a4_grouped_gemm_swiglu(*g, 96, 128, fake, fake, fake, None, None) == UNSUPPORTED
+    # one group's B codes of 4 GiB or more (32-bit offsets inside a group)
+    g1 = (fake, fake, fake, 64, fake, fake, fake, fake, 1)
+    assert L.w4a4_grouped_gemm(*g1, 1 << 20, 8192, 0, fake, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm_swiglu(*g1, 1 << 19, 8192, fake, fake, fake, None, None) == UNSUPPORTED
     # combine: hidden not a multiple of 8
     assert L.moe_combine(fake, 0, fake, 4, 2, 12, fake, None) == INVALID
     # expert layer: hidden not a multiple of 128, missing weights
