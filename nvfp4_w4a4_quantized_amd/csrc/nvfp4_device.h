@@ -30,6 +30,23 @@ constexpr int kWave = 64;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Largest |bf16| bit pattern (0..0x7FFF) among N dwords of packed bf16
+// pairs: packed unsigned 16-bit maxima of the magnitudes (for non-negative
+// values the bit patterns order like the values).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+template <int N>
+__device__ __forceinline__ uint32_t bf16_absmax_bits(const uint32_t (&w)[N]) {
+  u16x2_t m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t a = w[i] & 0x7FFF7FFFu;
+    u16x2_t v;
+    __builtin_memcpy(&v, &a, 4);
+    m = __builtin_elementwise_max(m, v);
+  }
+  return m[0] > m[1] ? (uint32_t)m[0] : (uint32_t)m[1];
+}
+
 // Round-to-nearest-even fp32 -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t b = __float_as_uint(f);
@@ -78,9 +95,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // only where x/d lies within that distance of a rounding threshold
 // (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, i.e. 4*|r| an integer).  Elements
 // whose 4*|r'| is within 2^-16 of an integer in [1, 23] (a band about 50x
-// wider than the error) recompute r with the IEEE division; so does every
-// element of a block with d < 2^-126.  d == 0 (s_b underflowed or s_g == 0)
-// gives r = x * 0 = +-0: magnitude 0, sign kept.
+// wider than the error) need the IEEE division; when a block holds one, the
+// whole block is recomputed that way (for the other elements both quotients
+// give the same code), and so is every block with d < 2^-126.  d == 0 (s_b
+// underflowed or s_g == 0) gives r = x * 0 = +-0: magnitude 0, sign kept.
 template <int SEL>
 __device__ __forceinline__ uint32_t pack_fp4_pair(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
@@ -90,14 +108,17 @@ __device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
   const bool full_div = (d != 0.0f) && (d < 1.17549435e-38f);
   const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
   float r[16];
+  bool near = false;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float ri = x[i] * inv;
-    float f = __builtin_fabsf(ri) * 4.0f;
-    bool near = (f >= 0.5f) && (f < 23.5f) &&
-                (__builtin_fabsf(f - __builtin_rintf(f)) < 1.52587890625e-05f);
-    if (full_div || near) ri = x[i] / d;
-    r[i] = ri;
+    r[i] = x[i] * inv;
+    const float f = __builtin_fabsf(r[i]) * 4.0f;
+    near |= (f >= 0.5f) && (f < 23.5f) &&
+            (__builtin_fabsf(f - __builtin_rintf(f)) < 1.52587890625e-05f);
+  }
+  if (full_div || near) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = x[i] / d;
   }
   uint32_t w0 = pack_fp4_pair<0>(0u, r[0], r[1]);
   w0 = pack_fp4_pair<1>(w0, r[2], r[3]);
@@ -117,17 +138,12 @@ __device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
 __device__ __forceinline__ uint2 quantize_block16(const uint32_t (&w)[8], float s_g,
                                                   uint32_t* scale) {
   float x[16];
-  uint32_t bmax_bits = 0u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     x[2 * i] = bf16_lo(w[i]);
     x[2 * i + 1] = bf16_hi(w[i]);
-    uint32_t a = w[i] & 0x7FFF7FFFu;
-    uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-    bmax_bits = bmax_bits > lo ? bmax_bits : lo;
-    bmax_bits = bmax_bits > hi ? bmax_bits : hi;
   }
-  const float bmax = __uint_as_float(bmax_bits << 16);
+  const float bmax = __uint_as_float(bf16_absmax_bits(w) << 16);
   uint32_t sb = 0u;
   if (s_g != 0.0f) {
     const float t = 6.0f * s_g;

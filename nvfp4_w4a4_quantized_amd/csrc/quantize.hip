@@ -42,13 +42,8 @@ __device__ __forceinline__ uint32_t load_row_blocks(const uint16_t* row, int nbl
 #pragma unroll
       for (int j = 0; j < 8; ++j) w[i][j] = 0u;
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t a = w[i][j] & 0x7FFF7FFFu;
-      uint32_t lo = a & 0xFFFFu, hi = a >> 16;
-      m = m > lo ? m : lo;
-      m = m > hi ? m : hi;
-    }
+    const uint32_t mi = bf16_absmax_bits(w[i]);
+    m = m > mi ? m : mi;
   }
   return m;
 }
@@ -97,6 +92,29 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
   if (a.amax_kind != 2 && lane == 0) a.gscale[row] = s_g;
 }
 
+// Outer scale given per row (amax kind 1) or per group (kind 2): one thread
+// per 16-element block, consecutive threads on consecutive blocks of a row
+// (32-byte reads and 8-byte writes side by side), so short rows leave no
+// lane idle and no reduction is needed.  Rows * blocks < 2^32.
+__global__ __launch_bounds__(256) void quantize_blocks_kernel(QuantRowsArgs a) {
+  const uint32_t nb = (uint32_t)(a.k / 16);
+  const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  if (i >= (uint64_t)a.rows * nb) return;
+  const uint32_t row = (uint32_t)i / nb, b = (uint32_t)i - row * nb;
+  const float amax = a.amax_kind == 1 ? a.amax_in[row]
+                                      : a.amax_in[find_group(a.group_offsets, a.num_groups, row)];
+  const float s_g = amax / 2688.0f;
+  const uint16_t* p = a.x + (int64_t)row * a.ld_x + (int64_t)b * 16;
+  const u32x4_t u0 = load_stream16(p);
+  const u32x4_t u1 = load_stream16(p + 8);
+  const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+  uint32_t sb;
+  const uint2 c = quantize_block16(w, s_g, &sb);
+  *reinterpret_cast<uint2*>(a.codes + (int64_t)row * (a.k / 2) + (int64_t)b * 8) = c;
+  a.scales[(int64_t)row * (a.k / 16) + b] = (uint8_t)sb;
+  if (a.amax_kind == 1 && b == 0) a.gscale[row] = s_g;
+}
+
 template <int BPL>
 __global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* x, int64_t rows, int64_t k,
                                                          int64_t ld_x, const int32_t* off,
@@ -125,6 +143,11 @@ __global__ void group_finalize_kernel(const float* amax, float* gscale, int32_t 
 
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
+  const int64_t total = a.rows * (a.k / 16);
+  if (a.amax_kind != 0 && total < 0xFFFFFFFFll) {
+    quantize_blocks_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
   switch (blocks_per_lane(a.k)) {
     case 1: quantize_rows_kernel<1><<<grid, block, 0, s>>>(a); break;

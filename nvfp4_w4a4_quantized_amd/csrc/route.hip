@@ -189,14 +189,10 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     }
     uint32_t m = 0u;
 #pragma unroll
-    for (int i = 0; i < BPL; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t v = w[i][j] & 0x7FFF7FFFu;
-        uint32_t lo = v & 0xFFFFu, hi = v >> 16;
-        m = m > lo ? m : lo;
-        m = m > hi ? m : hi;
-      }
+    for (int i = 0; i < BPL; ++i) {
+      const uint32_t mi = bf16_absmax_bits(w[i]);
+      m = m > mi ? m : mi;
+    }
     const float amax = __uint_as_float(wave_max_u32(m) << 16);
     s_g = amax / 2688.0f;
 #pragma unroll
