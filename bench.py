@@ -3,7 +3,8 @@
 One step = one moe_expert_forward call: routing metadata + per-token NVFP4
 quantize-permute, FC1 grouped GEMM with the weighted SwiGLU + row-amax
 epilogue, requantization of D, FC2 grouped GEMM, combine.  Weights are
-quantized once before timing (static weights).  Inputs are seeded synthetic
+quantized once before timing and stored in the grouped GEMM's tiled layout
+(static weights).  Inputs are seeded synthetic
 tensors with the shapes of the Qwen3-30B-A3B expert layer (T=8192 tokens,
 hidden 2048, 128 experts, top-8, intermediate 768, Zipf(1.1)-biased router),
 resident in HBM before the timed region.
@@ -39,8 +40,8 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen3_30b_a3b_moe_t8192")
     p.add_argument("--cpu-tokens", type=int, default=512,
                    help="tokens of the oracle's CPU-baseline sample (0 = skip)")
@@ -107,9 +108,9 @@ def main():
     x = bf(w.x)
     idx = torch.from_numpy(w.topk_idx).to(dev)
     prob = torch.from_numpy(w.topk_prob).to(dev)
-    log("quantizing weights (a0, offline)")
-    W1 = NvFp4Weights.quantize(bf(w.w1))
-    W2 = NvFp4Weights.quantize(bf(w.w2))
+    log("quantizing weights and moving them to the GEMM's tiled layout (a0, offline)")
+    W1 = NvFp4Weights.quantize(bf(w.w1)).packed()
+    W2 = NvFp4Weights.quantize(bf(w.w2)).packed()
     ws = torch.empty(moe_expert_forward_workspace_size(w.tokens, w.hidden, w.inter, w.topk,
                                                        w.experts), dtype=torch.uint8, device=dev)
     y = torch.empty((w.tokens, w.hidden), dtype=torch.bfloat16, device=dev)

@@ -148,6 +148,8 @@ int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
  *   a_*          A rows: codes [rows_cap, k/2], scales [rows_cap, k/16],
  *                outer scales [rows_cap]
  *   b_*          B: codes [G, n, k/2], scales [G, n, k/16], outer scales [G]
+ *   b_layout     0: B codes and scales row-major as above; 1: the same bytes
+ *                rearranged by nvfp4_pack_weights (faster loads)
  *   group_offsets int32 [num_groups + 1] on the device, non-decreasing,
  *                group_offsets[0] >= 0, group_offsets[G] <= rows_cap; empty
  *                groups are legal; the host never reads it
@@ -160,7 +162,7 @@ int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const flo
                       int64_t rows_cap,
                       const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gscale,
                       const int32_t* group_offsets, int32_t num_groups, int64_t n, int64_t k,
-                      int out_dtype, void* out, void* stream);
+                      int b_layout, int out_dtype, void* out, void* stream);
 
 /* ------------------------------------------------------------------------
  * w4a4_grouped_gemm_swiglu -- FC1 with the fused router-weighted SwiGLU
@@ -182,8 +184,27 @@ int w4a4_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales, co
                              int64_t rows_cap,
                              const uint8_t* b_codes, const uint8_t* b_scales, const float* b_gscale,
                              const int32_t* group_offsets, int32_t num_groups, int64_t inter,
-                             int64_t k, const float* row_prob,
+                             int64_t k, int b_layout, const float* row_prob,
                              uint16_t* d_out, float* amax, float* c_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * nvfp4_pack_weights -- scale-layout transfer for static weights: rearranges
+ * row-major NVFP4 B (codes [G, n, k/2], scales [G, n, k/16]) into the tiled
+ * layout the grouped GEMM reads with whole-wavefront contiguous loads
+ * (b_layout 1).  [miniTE] §5.4 (scale-layout transfer ahead of the GEMM).
+ * A pure byte permutation into buffers of the same sizes (outer scales are
+ * unchanged).  Tile t = (g*(n/32) + rb)*(k/128) + st covers rows
+ * 32rb..32rb+31 of group g and K stage st (128 elements):
+ *   packed_codes[t*2048 + c*1024 + 16*L + i]
+ *       = codes[g, 32rb + L%32, 64st + 32(L/32) + 16c + i]   c < 2, L < 64, i < 16
+ *   packed_scales[t*256 + 4*L + i]
+ *       = scales[g, 32rb + L%32, 8st + 4(L/32) + i]           L < 64, i < 4
+ * Outputs must not overlap the inputs.  Limits: n % 32 == 0, k % 128 == 0,
+ * k <= 16384.
+ * ---------------------------------------------------------------------- */
+int nvfp4_pack_weights(const uint8_t* codes, const uint8_t* scales, int32_t num_groups,
+                       int64_t n, int64_t k, uint8_t* packed_codes, uint8_t* packed_scales,
+                       void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- unpermute: y[t, :] = bf16(sum_j Y[dst_row[t, j], :]) with a
@@ -203,6 +224,7 @@ int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
  *   x            bf16 [tokens, hidden];  y out bf16 [tokens, hidden]
  *   w1           NVFP4 gate|up weights [E, 2*inter, hidden] (+ scales, [E])
  *   w2           NVFP4 down weights    [E, hidden, inter]
+ *                (each row-major or tiled, per its layout member)
  *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned
  *   debug        nullable: every non-NULL member receives that intermediate
  *                (in place of the workspace copy); fc1_out and y_rows_f32
@@ -218,6 +240,7 @@ typedef struct {
   const uint8_t* codes;
   const uint8_t* scales;
   const float* gscale;
+  int32_t layout;                 /* b_layout of w4a4_grouped_gemm: 0 or 1 */
 } nvfp4_weights;
 
 typedef struct {

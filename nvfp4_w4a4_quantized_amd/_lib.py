@@ -24,7 +24,7 @@ class NvFp4Error(RuntimeError):
 
 
 class Weights(C.Structure):
-    _fields_ = [("codes", _vp), ("scales", _vp), ("gscale", _vp)]
+    _fields_ = [("codes", _vp), ("scales", _vp), ("gscale", _vp), ("layout", C.c_int32)]
 
 
 class Intermediates(C.Structure):
@@ -57,10 +57,12 @@ def lib():
                               _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     L.w4a4_grouped_gemm.restype = C.c_int
     L.w4a4_grouped_gemm.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
-                                    C.c_int, _vp, _vp]
+                                    C.c_int, C.c_int, _vp, _vp]
     L.w4a4_grouped_gemm_swiglu.restype = C.c_int
     L.w4a4_grouped_gemm_swiglu.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i64,
-                                           _i64, _vp, _vp, _vp, _vp, _vp]
+                                           _i64, C.c_int, _vp, _vp, _vp, _vp, _vp]
+    L.nvfp4_pack_weights.restype = C.c_int
+    L.nvfp4_pack_weights.argtypes = [_vp, _vp, _i32, _i64, _i64, _vp, _vp, _vp]
     L.moe_combine.restype = C.c_int
     L.moe_combine.argtypes = [_vp, C.c_int, _vp, _i64, _i32, _i64, _vp, _vp]
     L.moe_expert_forward_workspace_size.restype = C.c_size_t

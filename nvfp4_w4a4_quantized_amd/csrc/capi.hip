@@ -174,11 +174,13 @@ static int gemm_args_ok(const uint8_t* a_codes, const uint8_t* a_scales, const f
 int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                       int64_t rows_cap, const uint8_t* b_codes, const uint8_t* b_scales,
                       const float* b_gscale, const int32_t* group_offsets, int32_t num_groups,
-                      int64_t n, int64_t k, int out_dtype, void* out, void* stream) {
+                      int64_t n, int64_t k, int b_layout, int out_dtype, void* out,
+                      void* stream) {
   int st = gemm_args_ok(a_codes, a_scales, a_gscale, rows_cap, b_codes, b_scales, b_gscale,
                         group_offsets, num_groups, k);
   if (st != NVFP4_OK) return st;
   if (!out || (out_dtype != 0 && out_dtype != 1)) return NVFP4_INVALID_ARGUMENT;
+  if (b_layout != 0 && b_layout != 1) return NVFP4_INVALID_ARGUMENT;
   if (n < 32 || n % 32 != 0) return NVFP4_UNSUPPORTED;
   if ((int64_t)num_groups * n >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;
   if (n * (k / 2) > 0xFFFFFFFFLL) return NVFP4_UNSUPPORTED;   // 32-bit offsets inside a group
@@ -186,19 +188,21 @@ int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   a.a_codes = a_codes; a.a_scales = a_scales; a.a_gscale = a_gscale;
   a.b_codes = b_codes; a.b_scales = b_scales; a.b_gscale = b_gscale;
   a.offsets = group_offsets; a.num_groups = num_groups; a.rows_cap = rows_cap;
-  a.n = n; a.k = k; a.out_dtype = out_dtype; a.out = out;
+  a.n = n; a.k = k; a.b_layout = b_layout; a.out_dtype = out_dtype; a.out = out;
   return hip_status(launch_gemm_plain(a, static_cast<hipStream_t>(stream)));
 }
 
 int w4a4_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_gscale,
                              int64_t rows_cap, const uint8_t* b_codes, const uint8_t* b_scales,
                              const float* b_gscale, const int32_t* group_offsets,
-                             int32_t num_groups, int64_t inter, int64_t k, const float* row_prob,
+                             int32_t num_groups, int64_t inter, int64_t k, int b_layout,
+                             const float* row_prob,
                              uint16_t* d_out, float* amax, float* c_out, void* stream) {
   int st = gemm_args_ok(a_codes, a_scales, a_gscale, rows_cap, b_codes, b_scales, b_gscale,
                         group_offsets, num_groups, k);
   if (st != NVFP4_OK) return st;
   if (!row_prob || !d_out || !amax) return NVFP4_INVALID_ARGUMENT;
+  if (b_layout != 0 && b_layout != 1) return NVFP4_INVALID_ARGUMENT;
   if (inter < 64 || inter % 64 != 0) return NVFP4_UNSUPPORTED;
   if ((int64_t)num_groups * 2 * inter >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;
   if (2 * inter * (k / 2) > 0xFFFFFFFFLL) return NVFP4_UNSUPPORTED;   // 32-bit offsets inside a group
@@ -206,7 +210,7 @@ int w4a4_grouped_gemm_swiglu(const uint8_t* a_codes, const uint8_t* a_scales, co
   a.a_codes = a_codes; a.a_scales = a_scales; a.a_gscale = a_gscale;
   a.b_codes = b_codes; a.b_scales = b_scales; a.b_gscale = b_gscale;
   a.offsets = group_offsets; a.num_groups = num_groups; a.rows_cap = rows_cap;
-  a.n = 2 * inter; a.k = k; a.inter = inter;
+  a.n = 2 * inter; a.k = k; a.inter = inter; a.b_layout = b_layout;
   a.row_prob = row_prob; a.d_out = d_out; a.amax = amax; a.c_out = c_out;
   return hip_status(launch_gemm_swiglu(a, static_cast<hipStream_t>(stream)));
 }
@@ -239,6 +243,8 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   if (hidden > kMaxK || inter > kMaxK) return NVFP4_UNSUPPORTED;
   if (!w1 || !w2 || !w1->codes || !w1->scales || !w1->gscale || !w2->codes || !w2->scales ||
       !w2->gscale || !workspace)
+    return NVFP4_INVALID_ARGUMENT;
+  if ((w1->layout != 0 && w1->layout != 1) || (w2->layout != 0 && w2->layout != 1))
     return NVFP4_INVALID_ARGUMENT;
   if (tokens > 0 && (!x || !y || !topk_idx || !topk_prob)) return NVFP4_INVALID_ARGUMENT;
   if (!aligned(workspace, 256) || (x && !aligned(x, 16)) || (y && !aligned(y, 16)) ||
@@ -291,7 +297,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   g1.a_codes = L.a1c; g1.a_scales = L.a1s; g1.a_gscale = L.a1g;
   g1.b_codes = w1->codes; g1.b_scales = w1->scales; g1.b_gscale = w1->gscale;
   g1.offsets = L.offsets; g1.num_groups = num_experts; g1.rows_cap = cap;
-  g1.n = 2 * inter; g1.k = hidden; g1.inter = inter;
+  g1.n = 2 * inter; g1.k = hidden; g1.inter = inter; g1.b_layout = w1->layout;
   g1.row_prob = L.row_prob; g1.d_out = L.d; g1.amax = L.amax_d; g1.c_out = c_out;
   if ((e = launch_gemm_swiglu(g1, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(2)) != hipSuccess) return NVFP4_HIP_ERROR;
@@ -305,7 +311,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   g2.a_codes = L.a2c; g2.a_scales = L.a2s; g2.a_gscale = L.a2g;
   g2.b_codes = w2->codes; g2.b_scales = w2->scales; g2.b_gscale = w2->gscale;
   g2.offsets = L.offsets; g2.num_groups = num_experts; g2.rows_cap = cap;
-  g2.n = hidden; g2.k = inter;
+  g2.n = hidden; g2.k = inter; g2.b_layout = w2->layout;
   g2.out_dtype = y_f32 ? 0 : 1;
   g2.out = y_f32 ? static_cast<void*>(y_f32) : static_cast<void*>(L.y_rows);
   if ((e = launch_gemm_plain(g2, s)) != hipSuccess) return NVFP4_HIP_ERROR;
@@ -316,6 +322,20 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
     return NVFP4_HIP_ERROR;
   if ((e = mark(5)) != hipSuccess) return NVFP4_HIP_ERROR;
   return NVFP4_OK;
+}
+
+int nvfp4_pack_weights(const uint8_t* codes, const uint8_t* scales, int32_t num_groups,
+                       int64_t n, int64_t k, uint8_t* packed_codes, uint8_t* packed_scales,
+                       void* stream) {
+  if (!codes || !scales || !packed_codes || !packed_scales) return NVFP4_INVALID_ARGUMENT;
+  if (num_groups < 1 || n < 0 || k < 0) return NVFP4_INVALID_ARGUMENT;
+  if (n % 32 != 0 || k % 128 != 0 || k > kMaxK) return NVFP4_UNSUPPORTED;
+  if ((int64_t)num_groups * n >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;
+  if (!aligned(codes, 16) || !aligned(packed_codes, 16) || !aligned(scales, 4) ||
+      !aligned(packed_scales, 4))
+    return NVFP4_INVALID_ARGUMENT;
+  return hip_status(launch_pack_b(codes, scales, (int64_t)num_groups * n, k, packed_codes,
+                                  packed_scales, static_cast<hipStream_t>(stream)));
 }
 
 int nvfp4_event_create(void** event) {

@@ -195,9 +195,16 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
 
   // ---- B: this lane's column j = 32*WN*wave + 32n + l32 of the tile.
   // Addresses are a scalar base (the group's matrix) plus a 32-bit lane
-  // offset; the launcher rejects groups of 4 GiB or more.
+  // offset; the launcher rejects groups of 4 GiB or more.  Row-major B keeps
+  // a row's stage in 64 code bytes + 8 scale bytes; the tiled layout
+  // (nvfp4_pack_weights) stores each (32-row block, stage) as the 64 lanes'
+  // operands side by side, so every load of a wave is one contiguous span.
+  const bool tiled = a.b_layout == 1;
   const uint8_t* b_cbase = a.b_codes + (int64_t)g * N * (K / 2);
   const uint8_t* b_sbase = a.b_scales + (int64_t)g * N * (K / 16);
+  const int64_t b_cstage = tiled ? 2048 : 64;    // bytes between stages
+  const int64_t b_sstage = tiled ? 256 : 8;
+  const int64_t b_c1 = tiled ? 1024 : 16;        // codes of substeps 4-7
   uint32_t bco[WN], bso[WN];
 #pragma unroll
   for (int n = 0; n < WN; ++n) {
@@ -211,8 +218,14 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
       c = nt * BN + (int64_t)wave * 32 * WN + 32 * n + l32;
     }
     const int64_t row = c < cmax ? c : cmax;     // B row inside the group
-    bco[n] = (uint32_t)(row * (K / 2) + 32 * half);
-    bso[n] = (uint32_t)(row * (K / 16) + 4 * half);
+    if (tiled) {                                 // (clamped columns read some valid row)
+      const int64_t tile0 = (row / 32) * (K / kKS);
+      bco[n] = (uint32_t)(tile0 * 2048 + 16 * lane);
+      bso[n] = (uint32_t)(tile0 * 256 + 4 * lane);
+    } else {
+      bco[n] = (uint32_t)(row * (K / 2) + 32 * half);
+      bso[n] = (uint32_t)(row * (K / 16) + 4 * half);
+    }
   }
   // one stage of the lane's B columns, reloaded in place a part at a time:
   // codes of substeps 0-3 (bc0), 4-7 (bc1) and the four block scales (bs)
@@ -220,15 +233,15 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   uint32_t bs[WN];
   auto b_load_c0 = [&](int64_t st) {
 #pragma unroll
-    for (int n = 0; n < WN; ++n) bc0[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * 64 + bco[n]);
+    for (int n = 0; n < WN; ++n) bc0[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * b_cstage + bco[n]);
   };
   auto b_load_c1 = [&](int64_t st) {
 #pragma unroll
-    for (int n = 0; n < WN; ++n) bc1[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * 64 + 16 + bco[n]);
+    for (int n = 0; n < WN; ++n) bc1[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * b_cstage + b_c1 + bco[n]);
   };
   auto b_load_s = [&](int64_t st) {
 #pragma unroll
-    for (int n = 0; n < WN; ++n) bs[n] = *reinterpret_cast<const uint32_t*>(b_sbase + st * 8 + bso[n]);
+    for (int n = 0; n < WN; ++n) bs[n] = *reinterpret_cast<const uint32_t*>(b_sbase + st * b_sstage + bso[n]);
   };
 
   // 16-byte slot of MFMA lane l in an A fragment block of substeps 4sq..4sq+3:
@@ -459,6 +472,41 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
       __syncthreads();                           // rows consumed before they are overwritten
     }
   }
+}
+
+// ---- B layout transfer ---------------------------------------------------
+//
+// Row-major B ([G*N rows, K/2 code bytes], [G*N, K/16] scales) -> the tiled
+// layout read above.  Tile t = (g*(N/32) + rb) * (K/128) + st holds rows
+// 32rb..32rb+31 of group g over K stage st:
+//   codes  t*2048 + c*1024 + 16*L : row 32rb + L%32, code bytes
+//          [64st + 32(L/32) + 16c, +16)            (c = 0, 1; L = 0..63)
+//   scales t*256 + 4*L            : row 32rb + L%32, scale bytes [8st + 4(L/32), +4)
+// One thread per 16-byte code piece; the c == 0 threads also move the scales.
+__global__ __launch_bounds__(256) void pack_b_kernel(const uint8_t* codes, const uint8_t* scales,
+                                                     int64_t rows, int64_t k, uint8_t* pcodes,
+                                                     uint8_t* pscales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nst = k / kKS;
+  if (i >= (rows / 32) * nst * 128) return;
+  const int64_t t = i / 128;
+  const int piece = (int)(i % 128), c = piece / 64, L = piece % 64;
+  const int64_t rb = t / nst, st = t % nst;
+  const int64_t row = rb * 32 + L % 32;
+  const u32x4_t v =
+      *reinterpret_cast<const u32x4_t*>(codes + row * (k / 2) + 64 * st + 32 * (L / 32) + 16 * c);
+  *reinterpret_cast<u32x4_t*>(pcodes + t * 2048 + c * 1024 + 16 * L) = v;
+  if (c == 0)
+    *reinterpret_cast<uint32_t*>(pscales + t * 256 + 4 * L) =
+        *reinterpret_cast<const uint32_t*>(scales + row * (k / 16) + 8 * st + 4 * (L / 32));
+}
+
+hipError_t launch_pack_b(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                         uint8_t* pcodes, uint8_t* pscales, hipStream_t s) {
+  const int64_t n = (rows / 32) * (k / kKS) * 128;
+  if (n == 0) return hipSuccess;
+  pack_b_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(codes, scales, rows, k, pcodes, pscales);
+  return hipGetLastError();
 }
 
 // ---- launchers -------------------------------------------------------------

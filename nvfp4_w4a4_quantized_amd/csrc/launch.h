@@ -51,6 +51,7 @@ struct GemmArgs {
   int64_t rows_cap;
   int64_t n;      // B rows per group (2*inter for the SwiGLU epilogue)
   int64_t k;
+  int b_layout;   // 0 row-major B, 1 tiled (launch_pack_b)
   // plain epilogue
   int out_dtype; void* out;
   // SwiGLU epilogue
@@ -58,6 +59,9 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_plain(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
+// Row-major B (rows % 32 == 0, k % 128 == 0) -> the tiled layout.
+hipError_t launch_pack_b(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
+                         uint8_t* pcodes, uint8_t* pscales, hipStream_t s);
 
 // ---- combine.hip ----
 hipError_t launch_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,

@@ -33,10 +33,24 @@ def _need(t, dtypes, name):
 
 class NvFp4Weights:
     """NVFP4 expert weights: codes [G, N, K/2] u8, scales [G, N, K/16] u8,
-    gscale [G] f32 (one outer scale per expert matrix)."""
+    gscale [G] f32 (one outer scale per expert matrix).  layout 0 is
+    row-major; layout 1 holds the same bytes in the grouped GEMM's tiled
+    order (nvfp4_pack_weights), the tensor shapes unchanged."""
 
-    def __init__(self, codes, scales, gscale):
+    def __init__(self, codes, scales, gscale, layout: int = 0):
         self.codes, self.scales, self.gscale = codes, scales, gscale
+        self.layout = layout
+
+    def packed(self) -> "NvFp4Weights":
+        """The tiled copy of row-major weights (static weights: done once)."""
+        if self.layout != 0:
+            raise ValueError("weights are already in the tiled layout")
+        G, N, kh = self.codes.shape
+        pc = torch.empty_like(self.codes)
+        ps = torch.empty_like(self.scales)
+        check(lib().nvfp4_pack_weights(ptr(self.codes), ptr(self.scales), G, N, kh * 2, ptr(pc),
+                                       ptr(ps), stream_handle()), "nvfp4_pack_weights")
+        return NvFp4Weights(pc, ps, self.gscale, layout=1)
 
     @classmethod
     def quantize(cls, w_bf16: torch.Tensor) -> "NvFp4Weights":
@@ -48,7 +62,8 @@ class NvFp4Weights:
         return cls(codes.view(G, N, K // 2), scales.view(G, N, K // 16), gscale)
 
     def c_struct(self) -> Weights:
-        return Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr())
+        return Weights(self.codes.data_ptr(), self.scales.data_ptr(), self.gscale.data_ptr(),
+                       self.layout)
 
 
 def nvfp4_quantize(x, scale_domain: int = 0, group_offsets=None, amax_in=None):
@@ -126,7 +141,8 @@ def w4a4_grouped_gemm(a_codes, a_scales, a_gscale, b: NvFp4Weights, group_offset
         out = torch.empty((rows_cap, N), dtype=out_dtype, device=a_codes.device)
     check(lib().w4a4_grouped_gemm(ptr(a_codes), ptr(a_scales), ptr(a_gscale), rows_cap,
                                   ptr(b.codes), ptr(b.scales), ptr(b.gscale), ptr(group_offsets),
-                                  G, N, K, code, ptr(out), stream_handle()), "w4a4_grouped_gemm")
+                                  G, N, K, b.layout, code, ptr(out), stream_handle()),
+          "w4a4_grouped_gemm")
     return out
 
 
@@ -143,7 +159,8 @@ def w4a4_grouped_gemm_swiglu(a_codes, a_scales, a_gscale, b: NvFp4Weights, group
     c = torch.empty((rows_cap, N2), dtype=torch.float32, device=dev) if with_c else None
     check(lib().w4a4_grouped_gemm_swiglu(ptr(a_codes), ptr(a_scales), ptr(a_gscale), rows_cap,
                                          ptr(b.codes), ptr(b.scales), ptr(b.gscale),
-                                         ptr(group_offsets), G, inter, K, ptr(row_prob), ptr(d),
+                                         ptr(group_offsets), G, inter, K, b.layout,
+                                         ptr(row_prob), ptr(d),
                                          ptr(amax), ptr(c), stream_handle()),
           "w4a4_grouped_gemm_swiglu")
     return d, amax, c

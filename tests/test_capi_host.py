@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     for n in ("nvfp4_quantize", "moe_permute", "w4a4_grouped_gemm", "w4a4_grouped_gemm_swiglu",
               "moe_combine", "moe_expert_forward", "moe_rows_capacity",
               "moe_permute_workspace_size", "moe_expert_forward_workspace_size",
-              "nvfp4_status_string"):
+              "nvfp4_status_string", "nvfp4_pack_weights"):
         assert n in names
 
 
@@ -81,15 +81,22 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     assert L.moe_permute(*args, 2, 4, 1, fake, fake, fake, fake, fake, fake, fake, fake, 4, None) == WS_SMALL
     # GEMM: k not a multiple of 128, n not a multiple of 32, bad dtype
     g = (fake, fake, fake, 64, fake, fake, fake, fake, 2)
-    assert L.w4a4_grouped_gemm(*g, 64, 96, 0, fake, None) == UNSUPPORTED
-    assert L.w4a4_grouped_gemm(*g, 48, 128, 0, fake, None) == UNSUPPORTED
-    assert L.w4a4_grouped_gemm(*g, 64, 128, 7, fake, None) == INVALID
-    assert L.w4a4_grouped_gemm(*g, 64, 120, 0, fake, None) == INVALID
-    assert L.w4a4_grouped_gemm_swiglu(*g, 96, 128, fake, fake, fake, None, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm(*g, 64, 96, 0, 0, fake, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm(*g, 48, 128, 0, 0, fake, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm(*g, 64, 128, 0, 7, fake, None) == INVALID
+    assert L.w4a4_grouped_gemm(*g, 64, 120, 0, 0, fake, None) == INVALID
+    # unknown B layout
+    assert L.w4a4_grouped_gemm(*g, 64, 128, 2, 0, fake, None) == INVALID
+    assert L.w4a4_grouped_gemm_swiglu(*g, 64, 128, 5, fake, fake, fake, None, None) == INVALID
+    assert L.w4a4_grouped_gemm_swiglu(*g, 96, 128, 0, fake, fake, fake, None, None) == UNSUPPORTED
+    # weight packing: n not a multiple of 32, k not a multiple of 128, missing output
+    assert L.nvfp4_pack_weights(fake, fake, 2, 48, 128, fake, fake, None) == UNSUPPORTED
+    assert L.nvfp4_pack_weights(fake, fake, 2, 64, 96, fake, fake, None) == UNSUPPORTED
+    assert L.nvfp4_pack_weights(fake, fake, 2, 64, 128, None, fake, None) == INVALID
     # one group's B codes of 4 GiB or more (32-bit offsets inside a group)
     g1 = (fake, fake, fake, 64, fake, fake, fake, fake, 1)
-    assert L.w4a4_grouped_gemm(*g1, 1 << 20, 8192, 0, fake, None) == UNSUPPORTED
-    assert L.w4a4_grouped_gemm_swiglu(*g1, 1 << 19, 8192, fake, fake, fake, None, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm(*g1, 1 << 20, 8192, 0, 0, fake, None) == UNSUPPORTED
+    assert L.w4a4_grouped_gemm_swiglu(*g1, 1 << 19, 8192, 0, fake, fake, fake, None, None) == UNSUPPORTED
     # combine: hidden not a multiple of 8
     assert L.moe_combine(fake, 0, fake, 4, 2, 12, fake, None) == INVALID
     # expert layer: hidden not a multiple of 128, missing weights
@@ -101,3 +108,6 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
     assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, C.byref(w), C.byref(w),
                                 fake, C.c_void_p(0x10000), 16, None, None, None) == WS_SMALL
+    wbad = Weights(0x1000, 0x1000, 0x1000, 3)   # unknown layout
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, C.byref(w), C.byref(wbad),
+                                fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID

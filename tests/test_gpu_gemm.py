@@ -14,9 +14,10 @@ from oracle import oracle as O
 pytestmark = pytest.mark.gpu
 
 
-def _weights(W):
+def _weights(W, tiled=False):
     from nvfp4_w4a4_quantized_amd.ops import NvFp4Weights
-    return NvFp4Weights(dev(W[0]), dev(W[1]), dev(W[2]))
+    w = NvFp4Weights(dev(W[0]), dev(W[1]), dev(W[2]))
+    return w.packed() if tiled else w
 
 
 def _operands(rng, rows, G, n, k, scale=1.0):
@@ -26,9 +27,10 @@ def _operands(rng, rows, G, n, k, scale=1.0):
     return A, W
 
 
-def _run_plain(A, W, offs, dtype=torch.float32):
+def _run_plain(A, W, offs, dtype=torch.float32, tiled=False):
     from nvfp4_w4a4_quantized_amd.ops import w4a4_grouped_gemm
-    out = w4a4_grouped_gemm(dev(A[0]), dev(A[1]), dev(A[2]), _weights(W), dev(offs), out_dtype=dtype)
+    out = w4a4_grouped_gemm(dev(A[0]), dev(A[1]), dev(A[2]), _weights(W, tiled), dev(offs),
+                            out_dtype=dtype)
     torch.cuda.synchronize()
     return host(out) if dtype == torch.float32 else bf16_bits_to_f32(host(out))
 
@@ -52,6 +54,40 @@ def test_plain_fp32_full_compare(shape):
     ref, bound = O.grouped_gemm(*A, *W, offs, with_bound=True)
     r0, r1 = offs[0], offs[-1]
     assert_gemm_close(gpu[r0:r1], ref[r0:r1], bound[r0:r1], f"plain {shape}")
+    # the tiled weight layout computes the same bits
+    say("gemm fp32 tiled B", rows, offs.tolist(), n, k)
+    gpu_t = _run_plain(A, W, offs, tiled=True)
+    assert np.array_equal(gpu_t[r0:r1].view(np.uint32), gpu[r0:r1].view(np.uint32))
+
+
+def test_pack_weights_is_the_documented_permutation():
+    """nvfp4_pack_weights against the byte map stated in the header, written
+    out here with numpy index arithmetic."""
+    rng = np.random.default_rng(21)
+    G, n, k = 3, 96, 384
+    codes = rng.integers(0, 256, (G, n, k // 2)).astype(np.uint8)
+    scales = rng.integers(0, 256, (G, n, k // 16)).astype(np.uint8)
+    say("pack weights", G, n, k)
+    w = _weights((codes, scales, np.ones(G, np.float32)), tiled=True)
+    torch.cuda.synchronize()
+    pc, ps = host(w.codes).reshape(-1), host(w.scales).reshape(-1)
+    nst, nrb = k // 128, n // 32
+    exp_c = np.empty(G * n * k // 2, np.uint8)
+    exp_s = np.empty(G * n * k // 16, np.uint8)
+    for g in range(G):
+        for rb in range(nrb):
+            for st in range(nst):
+                t = (g * nrb + rb) * nst + st
+                for L in range(64):
+                    row = 32 * rb + L % 32
+                    for c in range(2):
+                        src = 64 * st + 32 * (L // 32) + 16 * c
+                        dst = t * 2048 + c * 1024 + 16 * L
+                        exp_c[dst:dst + 16] = codes[g, row, src:src + 16]
+                    src = 8 * st + 4 * (L // 32)
+                    exp_s[t * 256 + 4 * L:t * 256 + 4 * L + 4] = scales[g, row, src:src + 4]
+    assert np.array_equal(pc, exp_c)
+    assert np.array_equal(ps, exp_s)
 
 
 def test_plain_bf16_output():
@@ -118,22 +154,22 @@ def test_moe_fc1_fc2_shapes_sampled(wid):
     A1 = (p["codes"], p["scales"], p["gscale"])
     rng = np.random.default_rng(12 + wid)
     say("moe fc1 plain", wid)
-    gpu = _run_plain(A1, W1, offs)
+    gpu = _run_plain(A1, W1, offs, tiled=(wid == 2))
     _sampled_check(A1, W1, offs, gpu, rng, 20000, f"FC1 workload {wid}")
     # FC2 on oracle-quantized synthetic activations of the FC2 input shape
     R = offs[-1]
     dx = random_bf16(rng, (R, w.inter), 0.05)
     A2 = O.quantize(dx)
     say("moe fc2 plain", wid)
-    gpu2 = _run_plain(A2, W2, offs)
+    gpu2 = _run_plain(A2, W2, offs, tiled=(wid == 2))
     _sampled_check(A2, W2, offs, gpu2, rng, 20000, f"FC2 workload {wid}")
 
 
-def _swiglu_case(A, W, offs, prob, what):
+def _swiglu_case(A, W, offs, prob, what, tiled=False):
     from nvfp4_w4a4_quantized_amd.ops import w4a4_grouped_gemm_swiglu
-    say("gemm swiglu", what)
-    d, amax, c = w4a4_grouped_gemm_swiglu(dev(A[0]), dev(A[1]), dev(A[2]), _weights(W), dev(offs),
-                                          dev(prob), with_c=True)
+    say("gemm swiglu", what, "tiled" if tiled else "")
+    d, amax, c = w4a4_grouped_gemm_swiglu(dev(A[0]), dev(A[1]), dev(A[2]), _weights(W, tiled),
+                                          dev(offs), dev(prob), with_c=True)
     torch.cuda.synchronize()
     r0, r1 = int(offs[0]), int(offs[-1])
     c = host(c)[r0:r1]
@@ -159,6 +195,10 @@ def test_swiglu_epilogue_full_compare():
     assert np.all(np.abs(dv - rv) <= bf16_ulp(rv) * 1.0001 + 1e-40)
     # amax is exactly the max |D| of the GPU's own D
     assert np.array_equal(amax, np.abs(bf16_bits_to_f32(d)).max(axis=1))
+    # the tiled weight layout computes the same bits
+    ct, dt, at = _swiglu_case(A, W, offs, prob, "small", tiled=True)
+    assert np.array_equal(ct.view(np.uint32), c.view(np.uint32))
+    assert np.array_equal(dt, d) and np.array_equal(at.view(np.uint32), amax.view(np.uint32))
 
 
 @pytest.mark.parametrize("wid", [0, 2])

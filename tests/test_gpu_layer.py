@@ -137,6 +137,11 @@ def test_perf_path_bf16_rows_and_determinism():
     assert torch.equal(y1, y2)
     y, it = _forward(w, W1, W2)
     assert np.array_equal(y, host(y1))
+    # static weights in the tiled layout: the same bits
+    say("moe_expert_forward tiled weights")
+    yt = moe_expert_forward(*args[:5], _weights(W1).packed(), _weights(W2).packed())
+    torch.cuda.synchronize()
+    assert torch.equal(yt, y1)
     R = int(it["expert_offsets"][-1])
     rng = np.random.default_rng(5)
     rows = rng.integers(0, R, 20000)
