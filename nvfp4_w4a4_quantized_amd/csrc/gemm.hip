@@ -120,12 +120,34 @@ constexpr int kKS = 128;          // K per stage
 
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2 };
 
-// Workgroups are dealt to the 8 XCDs round robin; renumber them so that each
-// XCD walks a contiguous range of tiles (consecutive tiles share A rows and,
-// inside an expert, B rows, which then stay in that XCD's L2).
-__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t n) {
+// Number of BM-row tiles over all groups (the same value in every lane).
+__device__ __forceinline__ int64_t count_mtiles(const int32_t* off, int G, int BM) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int64_t total = 0;
+  for (int base = 0; base < G; base += kWave) {
+    const int g = base + lane;
+    int64_t cnt = 0;
+    if (g < G) {
+      const int64_t n = (int64_t)off[g + 1] - (int64_t)off[g];
+      cnt = n > 0 ? (n + BM - 1) / BM : 0;
+    }
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) cnt += __shfl_xor(cnt, o, kWave);
+    total += cnt;
+  }
+  return total;
+}
+
+// Workgroups are dealt to the 8 XCDs round robin (workgroup b runs on XCD
+// b % 8).  Of the n real tiles (counted on the device; the grid is an upper
+// bound), XCD x takes an equal contiguous range: consecutive tiles share A
+// rows and, inside an expert, B rows, which then stay in that XCD's L2.
+// Returns false for the surplus workgroups.
+__device__ __forceinline__ bool xcd_remap(int64_t bid, int64_t n, int64_t* logical) {
   const int64_t x = bid % 8, pos = bid / 8, q = n / 8, r = n % 8;
-  return (x < r) ? x * (q + 1) + pos : r * (q + 1) + (x - r) * q + pos;
+  if (pos >= ((x < r) ? q + 1 : q)) return false;
+  *logical = (x < r) ? x * (q + 1) + pos : r * (q + 1) + (x - r) * q + pos;
+  return true;
 }
 
 // SwiGLU weighted by the router probability, in binary32; below g = -80
@@ -180,7 +202,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   const int64_t N = a.n;
 
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  const int64_t logical = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t logical;
+  if (!xcd_remap(blockIdx.x, count_mtiles(a.offsets, a.num_groups, BM) * ntn, &logical)) return;
   const int64_t mt = logical / ntn;
   const int64_t nt = logical % ntn;
   int g;

@@ -89,37 +89,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // binary32 quotient r = fl(x / d), rounded to E2M1 with ties to the even code
 // and saturation at 6 by the gfx950 FP4 conversion (scale 1.0).
 //
-// Fast path: r' = fl(x * fl(1/d)) differs from x/d by less than 2^-22.9
-// relative (two roundings of 2^-24 each, 1/d normal because
-// 2^-126 <= d < 2^126).  The E2M1 decision of r' and of fl(x/d) can differ
-// only where x/d lies within that distance of a rounding threshold
-// (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, i.e. 4*|r| an integer).  Elements
-// whose 4*|r'| is within 2^-16 of an integer in [1, 23] (a band about 50x
-// wider than the error) need the IEEE division; when a block holds one, the
-// whole block is recomputed that way (for the other elements both quotients
-// give the same code), and so is every block with d < 2^-126.  d == 0 (s_b
-// underflowed or s_g == 0) gives r = x * 0 = +-0: magnitude 0, sign kept.
+// Fast path: with inv = fl(1/d) (1/d normal because 2^-126 <= d < 2^126),
+// lo = fl(x * fl(inv * (1 - 2^-20))) and hi = fl(x * fl(inv * (1 + 2^-20)))
+// bracket both x/d and fl(x/d) strictly: each carries at most three binary32
+// roundings (relative error below 3.1 * 2^-24), far inside the 2^-20 offset,
+// and fl(x/d) itself is within 2^-24 of x/d.  E2M1 rounding is monotonic, so
+// when lo and hi get the same code, every value between them, fl(x/d)
+// included, gets that code.  A block where any element's two codes differ
+// (its quotient lies near a rounding threshold), and every block with
+// d < 2^-126, recomputes all 16 quotients with the IEEE division.  d == 0
+// (s_b underflowed or s_g == 0) gives r = x * 0 = +-0: magnitude 0, sign
+// kept.  Overflowing products (huge x/d) saturate to code 7 on both sides.
 template <int SEL>
 __device__ __forceinline__ uint32_t pack_fp4_pair(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
 }
 
-__device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
-  const bool full_div = (d != 0.0f) && (d < 1.17549435e-38f);
-  const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
-  float r[16];
-  bool near = false;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    r[i] = x[i] * inv;
-    const float f = __builtin_fabsf(r[i]) * 4.0f;
-    near |= (f >= 0.5f) && (f < 23.5f) &&
-            (__builtin_fabsf(f - __builtin_rintf(f)) < 1.52587890625e-05f);
-  }
-  if (full_div || near) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) r[i] = x[i] / d;
-  }
+__device__ __forceinline__ uint2 pack_fp4_block(const float (&r)[16]) {
   uint32_t w0 = pack_fp4_pair<0>(0u, r[0], r[1]);
   w0 = pack_fp4_pair<1>(w0, r[2], r[3]);
   w0 = pack_fp4_pair<2>(w0, r[4], r[5]);
@@ -129,6 +115,26 @@ __device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
   w1 = pack_fp4_pair<2>(w1, r[12], r[13]);
   w1 = pack_fp4_pair<3>(w1, r[14], r[15]);
   return make_uint2(w0, w1);
+}
+
+__device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
+  const bool full_div = (d != 0.0f) && (d < 1.17549435e-38f);
+  const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
+  const float inv_lo = inv * 0.99999904632568359375f;   // 1 - 2^-20
+  const float inv_hi = inv * 1.00000095367431640625f;   // 1 + 2^-20
+  float r[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = x[i] * inv_lo;
+  const uint2 lo = pack_fp4_block(r);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r[i] = x[i] * inv_hi;
+  const uint2 hi = pack_fp4_block(r);
+  if (full_div || lo.x != hi.x || lo.y != hi.y) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = x[i] / d;
+    return pack_fp4_block(r);
+  }
+  return lo;
 }
 
 // Quantizes one 16-element block of bf16 values (two uint4 words = 8 dwords,

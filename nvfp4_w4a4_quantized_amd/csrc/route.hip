@@ -6,18 +6,20 @@
 //
 // Three launches, no host synchronisation:
 //   1. hist:    one wave per chunk of 64 tokens counts its entries per expert
-//               (LDS histogram) -> hist[chunk][e].
-//   2. scan:    one workgroup turns the chunk histograms into
-//               base[chunk][e] = offsets[e] + #entries of e in earlier chunks,
-//               counts[e], and offsets[] (exclusive scan of counts rounded up
-//               to `align`).
-//   3. scatter: one wave per token quantizes the token once (row amax, block
-//               scales, codes in registers) and writes it to each of its k
-//               destination rows.  The rank of token t inside expert e is
-//               base[chunk][e] + popcount of the chunk's ballot mask of
-//               tokens choosing e below t: a stable order (ascending token)
-//               without any order-dependent atomics.  Extra waves (one per
-//               expert) fill the padding rows.
+//               (LDS histogram) -> hist[e][chunk] (expert-major).
+//   2. scan:    one workgroup; each wave takes whole experts: the expert's
+//               total is a wave sum over its chunk counts, offsets[] are the
+//               exclusive scan of the totals rounded up to `align`, and
+//               base[e][chunk] = offsets[e] + #entries of e in earlier chunks
+//               is a wave scan along the expert's contiguous row.
+//   3. scatter: each wave takes TPW consecutive tokens of one chunk.  It
+//               quantizes a token once (row amax, block scales, codes in
+//               registers) while the next token's row is already loading, and
+//               writes it to each of the token's k destination rows.  The
+//               rank of token t inside expert e is base[e][chunk] + popcount
+//               of the chunk's ballot mask of tokens choosing e below t: a
+//               stable order (ascending token) without any order-dependent
+//               atomics.  Extra waves (one per expert) fill the padding rows.
 #include "launch.h"
 #include "nvfp4_device.h"
 
@@ -28,7 +30,7 @@ constexpr int kScanThreads = 1024;
 
 int64_t route_num_chunks(int64_t tokens) { return (tokens + kChunk - 1) / kChunk; }
 
-// workspace: base[nchunks][E] int32, counts[E] int32 (each 256-byte aligned)
+// workspace: base[E][nchunks] int32, counts[E] int32 (each 256-byte aligned)
 size_t route_workspace_bytes(int64_t tokens, int32_t num_experts) {
   size_t base = (size_t)route_num_chunks(tokens) * (size_t)num_experts * 4u;
   base = (base + 255u) & ~(size_t)255u;
@@ -56,60 +58,76 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int
   }
   __syncthreads();
   if (chunk < nchunks)
-    for (int e = lane; e < E; e += kWave) hist[chunk * E + e] = h[e];
+    for (int e = lane; e < E; e += kWave) hist[(int64_t)e * nchunks + chunk] = h[e];
 }
 
-// Single workgroup.  Thread (part, e) handles chunks [part*L, (part+1)*L).
+__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int32_t y = __shfl_up(v, o, kWave);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// Single workgroup of kScanThreads.  Wave w handles experts w + 16i, EPW of
+// them at a time so that their loads are in flight together; the counts of
+// the first EPW experts' first CPL*64 chunks stay in registers between the
+// totals pass and the base pass (the whole matrix for E <= 128, T <= 8192).
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* hist, int64_t nchunks,
                                                                   int32_t E, int32_t align,
                                                                   int32_t* counts,
                                                                   int32_t* offsets) {
-  __shared__ int32_t partial[kScanThreads];
+  constexpr int NWAVES = kScanThreads / kWave;
+  constexpr int EPW = 8, CPL = 2;
   __shared__ int32_t cnt[1024];
-  __shared__ int32_t off[1025];
-  __shared__ int32_t wsum[kScanThreads / kWave];
-  const int tid = threadIdx.x;
-  const int parts = kScanThreads / E;            // >= 1 since E <= 1024
-  const int e = tid % E, part = tid / E;
-  const bool active = part < parts;
-  const int64_t L = (nchunks + parts - 1) / parts;
-  const int64_t c0 = active ? (int64_t)part * L : 0;
-  const int64_t c1 = active ? ((c0 + L < nchunks) ? c0 + L : nchunks) : 0;
-  int32_t s = 0;
-  for (int64_t c = c0; c < c1; ++c) s += hist[c * E + e];
-  partial[tid] = active ? s : 0;
-  __syncthreads();
-  int32_t before = 0;
-  if (active) {
-    for (int p = 0; p < part; ++p) before += partial[p * E + e];
-    if (part == 0) {
-      int32_t total = 0;
-      for (int p = 0; p < parts; ++p) total += partial[p * E + e];
-      cnt[e] = total;
+  __shared__ int32_t off[1024];
+  __shared__ int32_t wsum[NWAVES];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  int32_t xv[EPW][CPL];                        // cached counts of the first expert group
+  auto cnt_at = [&](int e, int64_t c) -> int32_t {
+    return (e < E && c < nchunks) ? hist[(int64_t)e * nchunks + c] : 0;
+  };
+  // expert totals
+  for (int e0 = w; e0 < E; e0 += NWAVES * EPW) {
+    const bool first = e0 == w;
+    int32_t s[EPW];
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) s[i] = 0;
+#pragma unroll
+    for (int cb = 0; cb < CPL; ++cb)
+#pragma unroll
+      for (int i = 0; i < EPW; ++i) {
+        const int32_t v = cnt_at(e0 + NWAVES * i, (int64_t)cb * kWave + lane);
+        if (first) xv[i][cb] = v;
+        s[i] += v;
+      }
+    for (int64_t c = (int64_t)CPL * kWave + lane; c < nchunks; c += kWave)
+#pragma unroll
+      for (int i = 0; i < EPW; ++i) s[i] += cnt_at(e0 + NWAVES * i, c);
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) {
+      const int e = e0 + NWAVES * i;
+      const int32_t t = wave_sum_i32(s[i]);
+      if (e < E && lane == 0) cnt[e] = t;
     }
   }
   __syncthreads();
   // exclusive scan of padded counts over experts (E <= 1024 = block size)
-  int32_t v = 0;
-  if (tid < E) v = (cnt[tid] + align - 1) / align * align;
-  const int lane = tid & (kWave - 1), w = tid / kWave;
-  int32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int32_t y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
-  }
+  const int32_t v = (tid < E) ? (cnt[tid] + align - 1) / align * align : 0;
+  const int32_t incl = wave_incl_scan_i32(v, lane);
   if (lane == kWave - 1) wsum[w] = incl;
   __syncthreads();
   if (w == 0) {
-    int32_t ws = (lane < kScanThreads / kWave) ? wsum[lane] : 0;
-    int32_t wi = ws;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      int32_t y = __shfl_up(wi, o, kWave);
-      if (lane >= o) wi += y;
-    }
-    if (lane < kScanThreads / kWave) wsum[lane] = wi - ws;   // exclusive
+    const int32_t ws = (lane < NWAVES) ? wsum[lane] : 0;
+    const int32_t wi = wave_incl_scan_i32(ws, lane);
+    if (lane < NWAVES) wsum[lane] = wi - ws;    // exclusive
   }
   __syncthreads();
   const int32_t excl = incl - v + wsum[w];
@@ -117,29 +135,78 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* hist,
     off[tid] = excl;
     offsets[tid] = excl;
     counts[tid] = cnt[tid];
-    if (tid == E - 1) { off[E] = excl + v; offsets[E] = excl + v; }
+    if (tid == E - 1) offsets[E] = excl + v;
   }
   __syncthreads();
-  if (active) {
-    int32_t run = off[e] + before;
-    for (int64_t c = c0; c < c1; ++c) {
-      int32_t h = hist[c * E + e];
-      hist[c * E + e] = run;
-      run += h;
+  // base[e][c] = offsets[e] + entries of e in chunks before c
+  for (int e0 = w; e0 < E; e0 += NWAVES * EPW) {
+    const bool first = e0 == w;
+    int32_t carry[EPW];
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) carry[i] = (e0 + NWAVES * i < E) ? off[e0 + NWAVES * i] : 0;
+    auto scan_block = [&](int64_t c0, const int32_t (&x)[EPW]) {
+      const int64_t c = c0 + lane;
+#pragma unroll
+      for (int i = 0; i < EPW; ++i) {
+        const int e = e0 + NWAVES * i;
+        const int32_t in = wave_incl_scan_i32(x[i], lane);
+        if (e < E && c < nchunks) hist[(int64_t)e * nchunks + c] = carry[i] + in - x[i];
+        carry[i] += __shfl(in, kWave - 1, kWave);
+      }
+    };
+#pragma unroll
+    for (int cb = 0; cb < CPL; ++cb) {
+      int32_t x[EPW];
+#pragma unroll
+      for (int i = 0; i < EPW; ++i)
+        x[i] = first ? xv[i][cb] : cnt_at(e0 + NWAVES * i, (int64_t)cb * kWave + lane);
+      scan_block((int64_t)cb * kWave, x);
+    }
+    for (int64_t c0 = (int64_t)CPL * kWave; c0 < nchunks; c0 += kWave) {
+      int32_t x[EPW];
+#pragma unroll
+      for (int i = 0; i < EPW; ++i) x[i] = cnt_at(e0 + NWAVES * i, c0 + lane);
+      scan_block(c0, x);
+    }
+  }
+}
+
+// tokens per scatter wave (a divisor of kChunk): two while the double-buffered
+// row fits the register budget, one for the longest rows
+constexpr int tokens_per_wave(int bpl) { return bpl <= 4 ? 2 : 1; }
+
+template <int BPL>
+__device__ __forceinline__ void load_token_row(const uint16_t* xr, int nblocks, int lane,
+                                               uint32_t (&w)[BPL][8]) {
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = lane + kWave * i;
+    if (b < nblocks) {
+      const uint16_t* p = xr + (int64_t)b * 16;
+      const u32x4_t u0 = load_stream16(p);
+      const u32x4_t u1 = load_stream16(p + 8);
+      w[i][0] = u0.x; w[i][1] = u0.y; w[i][2] = u0.z; w[i][3] = u0.w;
+      w[i][4] = u1.x; w[i][5] = u1.y; w[i][6] = u1.z; w[i][7] = u1.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[i][j] = 0u;
     }
   }
 }
 
 template <int BPL, int KMAX>
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const int32_t* base,
-                                                            const int32_t* counts) {
+                                                            const int32_t* counts,
+                                                            int64_t token_waves, int64_t nchunks) {
+  constexpr int TPW = tokens_per_wave(BPL);
+  static_assert(kChunk % TPW == 0, "a wave's tokens share one chunk");
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int k = a.topk, E = a.num_experts;
   const int64_t H = a.hidden;
-  if (wid >= a.tokens) {
+  if (wid >= token_waves) {
     // padding rows of expert e: [offsets[e] + counts[e], offsets[e+1])
-    const int64_t e = wid - a.tokens;
+    const int64_t e = wid - token_waves;
     if (e >= E) return;
     const int64_t r0 = (int64_t)a.offsets[e] + counts[e], r1 = a.offsets[e + 1];
     for (int64_t r = r0; r < r1; ++r) {
@@ -159,62 +226,79 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     }
     return;
   }
-  const int64_t t = wid;
-  const int64_t chunk = t / kChunk;
-  const int pos = (int)(t % kChunk);
-  const int64_t tl = chunk * kChunk + lane;            // token of this lane in the chunk
+  const int64_t t0 = wid * TPW;                      // TPW consecutive tokens of one chunk
+  const int nt = (int)(a.tokens - t0 < TPW ? a.tokens - t0 : TPW);
+  const int64_t chunk = t0 / kChunk;
+  const int64_t tl = chunk * kChunk + lane;          // token of this lane in the chunk
   const bool lane_valid = tl < a.tokens;
-
-  // quantize the token once
   const int nblocks = (int)(H / 16);
-  uint32_t w[BPL][8];
-  uint2 codes[BPL];
-  uint32_t sbytes[BPL];
-  float s_g = 0.0f;
+
+  // Phase 1: every load of the wave is issued before any store (a store may
+  // alias a later load as far as the compiler knows): the tokens' rows, the
+  // chunk's expert ids, and the destinations with their base counters.
+  uint32_t w[TPW][BPL][8];
   if (a.x) {
-    const uint16_t* xr = a.x + t * H;
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const int b = lane + kWave * i;
-      if (b < nblocks) {
-        const uint16_t* p = xr + (int64_t)b * 16;
-        u32x4_t u0 = load_stream16(p);
-        u32x4_t u1 = load_stream16(p + 8);
-        w[i][0] = u0.x; w[i][1] = u0.y; w[i][2] = u0.z; w[i][3] = u0.w;
-        w[i][4] = u1.x; w[i][5] = u1.y; w[i][6] = u1.z; w[i][7] = u1.w;
-      } else {
+    for (int ti = 0; ti < TPW; ++ti)
+      if (ti < nt) load_token_row<BPL>(a.x + (t0 + ti) * H, nblocks, lane, w[ti]);
+  }
+  // destination of entry j of token ti is held by lane j (lanes < k)
+  int64_t dst_l[TPW];
+  if constexpr (KMAX > 0) {
+    // every lane holds the k expert ids of its own chunk token, so the
+    // ballots need no memory traffic; a token's ids come from its lane
+    int ids[KMAX];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w[i][j] = 0u;
+    for (int i = 0; i < KMAX; ++i) ids[i] = (lane_valid && i < k) ? a.topk_idx[tl * k + i] : -1;
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) {
+      dst_l[ti] = -1;
+      const int pos = (int)((t0 + ti) % kChunk);
+      const uint64_t below_mask = pos == 0 ? 0ull : ((1ull << pos) - 1ull);
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k && ti < nt) {
+          const int e = __shfl(ids[j], pos, kWave);
+          if (e >= 0 && e < E) {
+            bool hit = false;
+#pragma unroll
+            for (int i = 0; i < KMAX; ++i) hit |= (ids[i] == e);
+            const uint64_t mask = __ballot(hit);
+            const int64_t d = (int64_t)base[(int64_t)e * nchunks + chunk] + __popcll(mask & below_mask);
+            if (lane == j) dst_l[ti] = d;
+          }
+        }
       }
     }
-    uint32_t m = 0u;
+  } else {
+    // any k: the entries are resolved one by one in phase 2
 #pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      const uint32_t mi = bf16_absmax_bits(w[i]);
-      m = m > mi ? m : mi;
-    }
-    const float amax = __uint_as_float(wave_max_u32(m) << 16);
-    s_g = amax / 2688.0f;
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      codes[i] = quantize_block16(w[i], s_g, &sbytes[i]);
-    }
+    for (int ti = 0; ti < TPW; ++ti) dst_l[ti] = -1;
   }
 
-  // Destination row of each of the token's k entries.  With KMAX > 0 every
-  // lane first holds the k expert ids of its own chunk token in registers, so
-  // the ballots need no memory traffic; the current token's ids come from
-  // lane `pos` by a shuffle.
-  auto store_row = [&](int j, int64_t dst) {
-    if (lane == 0) a.dst_row[t * k + j] = (int32_t)dst;
-    if (dst < 0) return;
-    if (lane == 0) {
-      a.row_src[dst] = (int32_t)t;
-      a.row_prob[dst] = a.topk_prob[t * k + j];
-      if (a.zero_per_row) a.zero_per_row[dst] = 0.0f;
-      if (a.x) a.gscale[dst] = s_g;
-    }
+  // Phase 2: quantize each token once, then write its k rows and maps
+#pragma unroll
+  for (int ti = 0; ti < TPW; ++ti) {
+    if (ti >= nt) break;
+    const int64_t t = t0 + ti;
+    uint2 codes[BPL];
+    uint32_t sbytes[BPL];
+    float s_g = 0.0f;
     if (a.x) {
+      uint32_t m = 0u;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        const uint32_t mi = bf16_absmax_bits(w[ti][i]);
+        m = m > mi ? m : mi;
+      }
+      const float amax = __uint_as_float(wave_max_u32(m) << 16);
+      s_g = amax / 2688.0f;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) codes[i] = quantize_block16(w[ti][i], s_g, &sbytes[i]);
+    }
+    // the quantized token into row dst (all lanes)
+    auto store_row = [&](int64_t dst) {
+      if (dst < 0 || !a.x) return;
       uint8_t* cr = a.codes + dst * (H / 2);
       uint8_t* sr = a.scales + dst * (H / 16);
 #pragma unroll
@@ -225,43 +309,37 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
           sr[b] = (uint8_t)sbytes[i];
         }
       }
-    }
-  };
-  const uint64_t below_mask = pos == 0 ? 0ull : ((1ull << pos) - 1ull);
-  if constexpr (KMAX > 0) {
-    int ids[KMAX];
+    };
+    // the maps of entry j, by the lane that holds it
+    auto store_meta = [&](int j, int64_t dst) {
+      a.dst_row[t * k + j] = (int32_t)dst;
+      if (dst < 0) return;
+      a.row_src[dst] = (int32_t)t;
+      a.row_prob[dst] = a.topk_prob[t * k + j];
+      if (a.zero_per_row) a.zero_per_row[dst] = 0.0f;
+      if (a.x) a.gscale[dst] = s_g;
+    };
+    if constexpr (KMAX > 0) {
+      if (lane < k) store_meta(lane, dst_l[ti]);
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) ids[i] = (lane_valid && i < k) ? a.topk_idx[tl * k + i] : -1;
-    int64_t dsts[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      dsts[j] = -1;
-      if (j < k) {
-        const int e = __shfl(ids[j], pos, kWave);
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) store_row(__shfl(dst_l[ti], j, kWave));
+    } else {
+      const int pos = (int)(t % kChunk);
+      const uint64_t below_mask = pos == 0 ? 0ull : ((1ull << pos) - 1ull);
+      for (int j = 0; j < k; ++j) {
+        const int e = a.topk_idx[t * k + j];
+        int64_t dst = -1;
         if (e >= 0 && e < E) {
           bool hit = false;
-#pragma unroll
-          for (int i = 0; i < KMAX; ++i) hit |= (ids[i] == e);
+          if (lane_valid)
+            for (int i = 0; i < k; ++i) hit |= (a.topk_idx[tl * k + i] == e);
           const uint64_t mask = __ballot(hit);
-          dsts[j] = (int64_t)base[chunk * E + e] + __popcll(mask & below_mask);
+          dst = (int64_t)base[(int64_t)e * nchunks + chunk] + __popcll(mask & below_mask);
         }
+        if (lane == 0) store_meta(j, dst);
+        store_row(dst);
       }
-    }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (j < k) store_row(j, dsts[j]);
-  } else {
-    for (int j = 0; j < k; ++j) {
-      const int e = a.topk_idx[t * k + j];
-      int64_t dst = -1;
-      if (e >= 0 && e < E) {
-        bool hit = false;
-        if (lane_valid)
-          for (int i = 0; i < k; ++i) hit |= (a.topk_idx[tl * k + i] == e);
-        const uint64_t mask = __ballot(hit);
-        dst = (int64_t)base[chunk * E + e] + __popcll(mask & below_mask);
-      }
-      store_row(j, dst);
     }
   }
 }
@@ -277,13 +355,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
         a.topk_idx, a.tokens, a.topk, E, nchunks, base);
   }
   route_scan_kernel<<<1, kScanThreads, 0, s>>>(base, nchunks, E, a.align, counts, a.offsets);
-  const int64_t waves = a.tokens + E;
+  const int bpl = a.x ? blocks_per_lane(a.hidden) : 1;
+  if (bpl == 0) return hipErrorInvalidValue;
+  const int tpw = tokens_per_wave(bpl);
+  const int64_t token_waves = (a.tokens + tpw - 1) / tpw;
+  const int64_t waves = token_waves + E;
   dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-  int bpl = a.x ? blocks_per_lane(a.hidden) : 1;
   const int kmax = a.topk <= 8 ? 8 : (a.topk <= 16 ? 16 : 0);
   switch (bpl * 100 + kmax) {
 #define NVFP4_SCATTER(B, KM) \
-    case B * 100 + KM: route_scatter_kernel<B, KM><<<grid, block, 0, s>>>(a, base, counts); break;
+    case B * 100 + KM: route_scatter_kernel<B, KM><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks); break;
     NVFP4_SCATTER(1, 8) NVFP4_SCATTER(2, 8) NVFP4_SCATTER(4, 8) NVFP4_SCATTER(8, 8) NVFP4_SCATTER(16, 8)
     NVFP4_SCATTER(1, 16) NVFP4_SCATTER(2, 16) NVFP4_SCATTER(4, 16) NVFP4_SCATTER(8, 16) NVFP4_SCATTER(16, 16)
     NVFP4_SCATTER(1, 0) NVFP4_SCATTER(2, 0) NVFP4_SCATTER(4, 0) NVFP4_SCATTER(8, 0) NVFP4_SCATTER(16, 0)
