@@ -117,56 +117,125 @@ float orc_row_amax(const uint16_t* x, int64_t k) {
   return amax;
 }
 
+/* One block's E4M3 scale byte and its 16 codes, with the block maximum
+ * mapped to the E2M1 value `top` (6 for the standard rule; 4 for the second
+ * Four-Over-Six candidate). */
+static unsigned quantize_block(const uint16_t* blk, float s_g, float top, unsigned codes16[16]) {
+  float bmax = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    float a = fabsf(orc_bf16_to_f32(blk[i]));
+    if (a > bmax) bmax = a;
+  }
+  /* block scale: maps the block maximum to `top` */
+  unsigned sb_byte = 0;
+  if (s_g != 0.0f) {
+    float t = top * s_g;
+    float q = bmax / t;
+    sb_byte = orc_e4m3_encode(q);
+  }
+  float s_b = (float)orc_e4m3_value(sb_byte);  /* exact in binary32 */
+  float d = s_b * s_g;                          /* per-block decode step */
+  for (int i = 0; i < 16; ++i) {
+    float xv = orc_bf16_to_f32(blk[i]);
+    unsigned code;
+    if (d == 0.0f) {
+      code = signbit(xv) ? 8u : 0u;             /* underflowed block */
+    } else {
+      float r = xv / d;                         /* IEEE binary32 division */
+      code = orc_e2m1_encode(r);
+      if (signbit(xv)) code |= 8u; else code &= 7u;
+    }
+    codes16[i] = code;
+  }
+  return sb_byte;
+}
+
+/* Packs a block's codes: element 2j in the low nibble of byte j. */
+static void pack_block(int64_t b, const unsigned codes16[16], uint8_t* codes) {
+  for (int i = 0; i < 16; ++i) {
+    int64_t e = b * 16 + i;
+    unsigned code = codes16[i];
+    codes[e / 2] |= (uint8_t)((e % 2) ? (code << 4) : code);
+  }
+}
+
 float orc_quantize_row_with_amax(const uint16_t* x, int64_t k, float amax,
                                  uint8_t* codes, uint8_t* scales) {
   /* outer (second-level) scale: [miniTE] §5.6 "gs = gamax / 2688" */
   float s_g = amax / 2688.0f;
   memset(codes, 0, (size_t)(k / 2));
   for (int64_t b = 0; b < k / 16; ++b) {
-    const uint16_t* blk = x + b * 16;
-    float bmax = 0.0f;
-    for (int i = 0; i < 16; ++i) {
-      float a = fabsf(orc_bf16_to_f32(blk[i]));
-      if (a > bmax) bmax = a;
-    }
-    /* block scale: maps the block maximum to the largest E2M1 value 6 */
-    unsigned sb_byte = 0;
-    if (s_g != 0.0f) {
-      float t = 6.0f * s_g;
-      float q = bmax / t;
-      sb_byte = orc_e4m3_encode(q);
-    }
-    scales[b] = (uint8_t)sb_byte;
-    float s_b = (float)orc_e4m3_value(sb_byte);  /* exact in binary32 */
-    float d = s_b * s_g;                          /* per-block decode step */
-    for (int i = 0; i < 16; ++i) {
-      float xv = orc_bf16_to_f32(blk[i]);
-      unsigned code;
-      if (d == 0.0f) {
-        code = signbit(xv) ? 8u : 0u;             /* underflowed block */
-      } else {
-        float r = xv / d;                         /* IEEE binary32 division */
-        code = orc_e2m1_encode(r);
-        if (signbit(xv)) code |= 8u; else code &= 7u;
-      }
-      int64_t e = b * 16 + i;
-      codes[e / 2] |= (uint8_t)((e % 2) ? (code << 4) : code);
-    }
+    unsigned c[16];
+    /* the block maximum maps to the largest E2M1 value, 6 */
+    scales[b] = (uint8_t)quantize_block(x + b * 16, s_g, 6.0f, c);
+    pack_block(b, c, codes);
   }
   return s_g;
+}
+
+/* Block error of a candidate: the values q * s_b * s_g against x, summed
+ * left to right in binary32 (metric 1: squares, 2: absolute values). */
+static float block_error(const uint16_t* blk, const unsigned codes16[16], unsigned sb_byte,
+                         float s_g, int metric) {
+  float s_b = (float)orc_e4m3_value(sb_byte);
+  float acc = 0.0f;
+  for (int i = 0; i < 16; ++i) {
+    float xv = orc_bf16_to_f32(blk[i]);
+    float qs = (float)(orc_e2m1_value(codes16[i]) * (double)s_b);  /* exact */
+    float v = qs * s_g;
+    float e = xv - v;
+    float term = (metric == 1) ? e * e : fabsf(e);
+    acc = acc + term;
+  }
+  return acc;
+}
+
+float orc_quantize_row_rule(const uint16_t* x, int64_t k, float amax, int rule,
+                            uint8_t* codes, uint8_t* scales) {
+  if (rule == 0) return orc_quantize_row_with_amax(x, k, amax, codes, scales);
+  /* 4/6: the outer scale leaves room for blocks mapped to 4, whose scale is
+   * 1.5x that of the same block mapped to 6: s_g = amax / (6 * 256) */
+  float s_g = amax / 1536.0f;
+  memset(codes, 0, (size_t)(k / 2));
+  for (int64_t b = 0; b < k / 16; ++b) {
+    const uint16_t* blk = x + b * 16;
+    unsigned c6[16], c4[16];
+    unsigned sb6 = quantize_block(blk, s_g, 6.0f, c6);
+    unsigned sb4 = quantize_block(blk, s_g, 4.0f, c4);
+    float e6 = block_error(blk, c6, sb6, s_g, rule);
+    float e4 = block_error(blk, c4, sb4, s_g, rule);
+    /* the reduced range only where it lowers the block error; ties keep 6 */
+    int four = e4 < e6;
+    scales[b] = (uint8_t)(four ? sb4 : sb6);
+    pack_block(b, four ? c4 : c6, codes);
+  }
+  return s_g;
+}
+
+float orc_outer_scale(float amax, int rule) {
+  return rule == 0 ? amax / 2688.0f : amax / 1536.0f;
 }
 
 int orc_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
                  int domain, const int32_t* group_offsets, int32_t num_groups,
                  const float* amax_in,
                  uint8_t* codes, uint8_t* scales, float* gscale) {
+  return orc_quantize_rule(x, rows, k, ld_x, domain, group_offsets, num_groups, amax_in, 0,
+                           codes, scales, gscale);
+}
+
+int orc_quantize_rule(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
+                      int domain, const int32_t* group_offsets, int32_t num_groups,
+                      const float* amax_in, int rule,
+                      uint8_t* codes, uint8_t* scales, float* gscale) {
   if (rows < 0 || k < 0 || k % 16 != 0 || ld_x < k) return 1;
+  if (rule < 0 || rule > 2) return 1;
   if (domain == 0) {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
       const uint16_t* xr = x + r * ld_x;
       float amax = amax_in ? amax_in[r] : orc_row_amax(xr, k);
-      gscale[r] = orc_quantize_row_with_amax(xr, k, amax, codes + r * (k / 2), scales + r * (k / 16));
+      gscale[r] = orc_quantize_row_rule(xr, k, amax, rule, codes + r * (k / 2), scales + r * (k / 16));
     }
     return 0;
   }
@@ -186,9 +255,9 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
       }
 #pragma omp parallel for schedule(static)
       for (int64_t r = r0; r < r1; ++r)
-        (void)orc_quantize_row_with_amax(x + r * ld_x, k, amax, codes + r * (k / 2),
-                                         scales + r * (k / 16));
-      gscale[g] = amax / 2688.0f; /* the s_g every row of the group used */
+        (void)orc_quantize_row_rule(x + r * ld_x, k, amax, rule, codes + r * (k / 2),
+                                    scales + r * (k / 16));
+      gscale[g] = orc_outer_scale(amax, rule); /* the s_g every row of the group used */
     }
     return 0;
   }
@@ -258,7 +327,16 @@ int orc_moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
                     int32_t num_experts, int32_t align,
                     int32_t* offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
                     uint8_t* codes, uint8_t* scales, float* gscale) {
-  if (hidden < 0 || hidden % 16 != 0) return 1;
+  return orc_moe_permute_rule(x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
+                              0, offsets, dst_row, row_src, row_prob, codes, scales, gscale);
+}
+
+int orc_moe_permute_rule(const uint16_t* x, int64_t tokens, int64_t hidden,
+                         const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                         int32_t num_experts, int32_t align, int rule,
+                         int32_t* offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
+                         uint8_t* codes, uint8_t* scales, float* gscale) {
+  if (hidden < 0 || hidden % 16 != 0 || rule < 0 || rule > 2) return 1;
   int st = orc_route(topk_idx, topk_prob, tokens, topk, num_experts, align,
                      offsets, dst_row, row_src, row_prob);
   if (st != 0 || !x) return st;
@@ -277,7 +355,7 @@ int orc_moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
       continue;
     }
     const uint16_t* xr = x + (int64_t)t * hidden;
-    gscale[r] = orc_quantize_row_with_amax(xr, hidden, orc_row_amax(xr, hidden), c, s);
+    gscale[r] = orc_quantize_row_rule(xr, hidden, orc_row_amax(xr, hidden), rule, c, s);
   }
   return 0;
 }
@@ -426,11 +504,22 @@ int orc_moe_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t i
                     const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_gscale,
                     const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gscale,
                     const orc_moe_buffers* b, uint16_t* y, double* stage_seconds) {
+  return orc_moe_forward_rule(x, tokens, hidden, inter, topk_idx, topk_prob, topk, num_experts,
+                              align, 0, w1_codes, w1_scales, w1_gscale, w2_codes, w2_scales,
+                              w2_gscale, b, y, stage_seconds);
+}
+
+int orc_moe_forward_rule(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
+                         const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                         int32_t num_experts, int32_t align, int act_rule,
+                         const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_gscale,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gscale,
+                         const orc_moe_buffers* b, uint16_t* y, double* stage_seconds) {
   if (!b || hidden % 16 != 0 || inter % 16 != 0) return 1;
   double t0 = now_seconds();
-  int st = orc_moe_permute(x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
-                           b->offsets, b->dst_row, b->row_src, b->row_prob,
-                           b->a1_codes, b->a1_scales, b->a1_gscale);
+  int st = orc_moe_permute_rule(x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
+                                act_rule, b->offsets, b->dst_row, b->row_src, b->row_prob,
+                                b->a1_codes, b->a1_scales, b->a1_gscale);
   if (st) return st;
   int64_t rows = b->offsets[num_experts];
   double t1 = now_seconds();
@@ -441,8 +530,8 @@ int orc_moe_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t i
   orc_swiglu(b->c_fc1, b->row_prob, rows, inter, b->d, b->amax_d);
   double t3 = now_seconds();
   /* FC2 input: requantize D with the amax produced alongside it ([miniTE] §5.3) */
-  st = orc_quantize(b->d, rows, inter, inter, 0, NULL, 0, b->amax_d,
-                    b->a2_codes, b->a2_scales, b->a2_gscale);
+  st = orc_quantize_rule(b->d, rows, inter, inter, 0, NULL, 0, b->amax_d, act_rule,
+                         b->a2_codes, b->a2_scales, b->a2_gscale);
   if (st) return st;
   double t4 = now_seconds();
   st = orc_grouped_gemm(b->a2_codes, b->a2_scales, b->a2_gscale, w2_codes, w2_scales, w2_gscale,

@@ -78,6 +78,30 @@ uint16_t orc_f64_to_bf16(double v);   /* round-to-nearest-even, finite inputs */
 float orc_quantize_row_with_amax(const uint16_t* x, int64_t k, float amax,
                                  uint8_t* codes, uint8_t* scales);
 
+/* Four-Over-Six ([4BIT] "Four-Over-Six for RL Weights and Activations"):
+ * every block is quantized twice, with its maximum mapped to the E2M1 value
+ * 6 and to 4, and keeps the candidate with the smaller block error; ties keep
+ * 6.  rule 1 measures the error as a sum of squares, rule 2 as a sum of
+ * absolute values ("MSE or MAE").  Readings of the pages (their formula
+ * names an FP8 maximum E4M3_4OVER6_MAXVAL without giving it):
+ *   s_g   = fl32(amax / 1536), 1536 = 6 * 256: the FP8 maximum is lowered to
+ *           256 so that the 4-candidate's block scale (1.5x the 6-candidate's,
+ *           at most 384) stays inside E4M3;
+ *   candidate c in {6, 4}: s_b = E4M3(fl32(bmax / fl32(c * s_g))),
+ *           d = fl32(s_b * s_g), codes E2M1(fl32(x / d)) as in rule 0;
+ *   error = sum over the 16 elements, in order, of e^2 (rule 1) or |e|
+ *           (rule 2), e = fl32(x - fl32((q * s_b) * s_g)), in binary32 (the
+ *           page's "candidate = fp4_value * fp8_scale * amax / (E2M1_MAXVAL *
+ *           E4M3_4OVER6_MAXVAL)" with fp32 error accumulation);
+ *   the 4-candidate is kept only if its error is strictly smaller.
+ * rule 0 is orc_quantize_row_with_amax.  Returns s_g. */
+float orc_quantize_row_rule(const uint16_t* x, int64_t k, float amax, int rule,
+                            uint8_t* codes, uint8_t* scales);
+
+/* The outer scale of a domain with maximum amax under a rule:
+ * amax / 2688 (rule 0) or amax / 1536 (rules 1, 2). */
+float orc_outer_scale(float amax, int rule);
+
 /* Row amax = max |x| over k bf16 values (exact). */
 float orc_row_amax(const uint16_t* x, int64_t k);
 
@@ -96,6 +120,11 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
                  int domain, const int32_t* group_offsets, int32_t num_groups,
                  const float* amax_in,
                  uint8_t* codes, uint8_t* scales, float* gscale);
+/* orc_quantize with a block rule (0 standard, 1 4/6 MSE, 2 4/6 MAE). */
+int orc_quantize_rule(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
+                      int domain, const int32_t* group_offsets, int32_t num_groups,
+                      const float* amax_in, int rule,
+                      uint8_t* codes, uint8_t* scales, float* gscale);
 
 /* O5: x^ = q * s_b * s_g in fp64 for one quantized row. */
 void orc_dequantize_row(const uint8_t* codes, const uint8_t* scales, float gscale,
@@ -126,6 +155,12 @@ int orc_moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
                     int32_t num_experts, int32_t align,
                     int32_t* offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
                     uint8_t* codes, uint8_t* scales, float* gscale);
+/* orc_moe_permute quantizing with a block rule (see orc_quantize_row_rule). */
+int orc_moe_permute_rule(const uint16_t* x, int64_t tokens, int64_t hidden,
+                         const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                         int32_t num_experts, int32_t align, int rule,
+                         int32_t* offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
+                         uint8_t* codes, uint8_t* scales, float* gscale);
 
 /* ---- O7: W4A4 grouped GEMM -------------------------------------------- */
 
@@ -192,6 +227,14 @@ int orc_moe_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t i
                     const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_gscale,
                     const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gscale,
                     const orc_moe_buffers* buf, uint16_t* y, double* stage_seconds);
+/* orc_moe_forward with a block rule for both activation quantizations (the
+ * routed tokens and the requantized D); the weights come pre-quantized. */
+int orc_moe_forward_rule(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
+                         const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                         int32_t num_experts, int32_t align, int act_rule,
+                         const uint8_t* w1_codes, const uint8_t* w1_scales, const float* w1_gscale,
+                         const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gscale,
+                         const orc_moe_buffers* buf, uint16_t* y, double* stage_seconds);
 
 /* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */
 int orc_num_threads(void);

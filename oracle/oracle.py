@@ -65,6 +65,11 @@ def lib():
     L.orc_quantize.restype = C.c_int
     L.orc_quantize.argtypes = [_u16p, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_void_p,
                                C.c_int32, C.c_void_p, _u8p, _u8p, _f32p]
+    L.orc_quantize_rule.restype = C.c_int
+    L.orc_quantize_rule.argtypes = [_u16p, C.c_int64, C.c_int64, C.c_int64, C.c_int, C.c_void_p,
+                                    C.c_int32, C.c_void_p, C.c_int, _u8p, _u8p, _f32p]
+    L.orc_outer_scale.restype = C.c_float
+    L.orc_outer_scale.argtypes = [C.c_float, C.c_int]
     L.orc_dequantize_row.restype = None
     L.orc_dequantize_row.argtypes = [_u8p, _u8p, C.c_float, C.c_int64, _f64p]
     L.orc_rows_capacity.restype = C.c_int64
@@ -76,6 +81,10 @@ def lib():
     L.orc_moe_permute.argtypes = [C.c_void_p, C.c_int64, C.c_int64, _i32p, _f32p, C.c_int32,
                                   C.c_int32, C.c_int32, _i32p, _i32p, _i32p, _f32p,
                                   C.c_void_p, C.c_void_p, C.c_void_p]
+    L.orc_moe_permute_rule.restype = C.c_int
+    L.orc_moe_permute_rule.argtypes = [C.c_void_p, C.c_int64, C.c_int64, _i32p, _f32p, C.c_int32,
+                                       C.c_int32, C.c_int32, C.c_int, _i32p, _i32p, _i32p, _f32p,
+                                       C.c_void_p, C.c_void_p, C.c_void_p]
     L.orc_grouped_gemm.restype = C.c_int
     L.orc_grouped_gemm.argtypes = [_u8p, _u8p, _f32p, _u8p, _u8p, _f32p, _i32p, C.c_int32,
                                    C.c_int64, C.c_int64, _f32p, C.c_void_p]
@@ -92,6 +101,11 @@ def lib():
                                   C.c_int32, C.c_int32, C.c_int32,
                                   _u8p, _u8p, _f32p, _u8p, _u8p, _f32p,
                                   C.POINTER(_MoeBuffers), _u16p, C.c_void_p]
+    L.orc_moe_forward_rule.restype = C.c_int
+    L.orc_moe_forward_rule.argtypes = [_u16p, C.c_int64, C.c_int64, C.c_int64, _i32p, _f32p,
+                                       C.c_int32, C.c_int32, C.c_int32, C.c_int,
+                                       _u8p, _u8p, _f32p, _u8p, _u8p, _f32p,
+                                       C.POINTER(_MoeBuffers), _u16p, C.c_void_p]
     L.orc_num_threads.restype = C.c_int
     L.orc_num_threads.argtypes = []
     _libs[path] = L
@@ -135,7 +149,11 @@ def num_threads() -> int:
 
 # ---- quantization ---------------------------------------------------------
 
-def quantize(x_bf16: np.ndarray, domain: int = 0, group_offsets=None, amax_in=None):
+def outer_scale(amax: float, rule: int = 0) -> float:
+    return lib().orc_outer_scale(amax, rule)
+
+
+def quantize(x_bf16: np.ndarray, domain: int = 0, group_offsets=None, amax_in=None, rule: int = 0):
     """NVFP4 quantization of a bf16 [rows, k] matrix (uint16 bit patterns).
 
     Returns (codes u8 [rows, k/2], scales u8 [rows, k/16], gscale f32 [rows] or
@@ -153,8 +171,12 @@ def quantize(x_bf16: np.ndarray, domain: int = 0, group_offsets=None, amax_in=No
         ng = offs.size - 1
         gscale = np.zeros(ng, np.float32)
     am = None if amax_in is None else np.ascontiguousarray(amax_in, dtype=np.float32)
-    _check(lib().orc_quantize(x, rows, k, k, domain, _ptr(offs), ng, _ptr(am),
-                              codes, scales, gscale), "quantize")
+    if rule == 0:
+        _check(lib().orc_quantize(x, rows, k, k, domain, _ptr(offs), ng, _ptr(am),
+                                  codes, scales, gscale), "quantize")
+    else:
+        _check(lib().orc_quantize_rule(x, rows, k, k, domain, _ptr(offs), ng, _ptr(am), rule,
+                                       codes, scales, gscale), "quantize")
     return codes, scales, gscale
 
 
@@ -194,7 +216,7 @@ def route(topk_idx: np.ndarray, topk_prob: np.ndarray, num_experts: int, align: 
     return offsets, dst, src, rp
 
 
-def moe_permute(x_bf16, topk_idx, topk_prob, num_experts: int, align: int = 1):
+def moe_permute(x_bf16, topk_idx, topk_prob, num_experts: int, align: int = 1, rule: int = 0):
     """Route + per-token quantize-scatter.  Returns a dict of numpy arrays."""
     idx = np.ascontiguousarray(topk_idx, np.int32)
     prob = np.ascontiguousarray(topk_prob, np.float32)
@@ -213,8 +235,9 @@ def moe_permute(x_bf16, topk_idx, topk_prob, num_experts: int, align: int = 1):
     codes = np.zeros((cap, H // 2), np.uint8)
     scales = np.zeros((cap, H // 16), np.uint8)
     gs = np.zeros(cap, np.float32)
-    _check(lib().orc_moe_permute(_ptr(x), T, H, idx, prob, k, num_experts, align, offsets, dst,
-                                 src, rp, _ptr(codes), _ptr(scales), _ptr(gs)), "moe_permute")
+    _check(lib().orc_moe_permute_rule(_ptr(x), T, H, idx, prob, k, num_experts, align, rule,
+                                      offsets, dst, src, rp, _ptr(codes), _ptr(scales), _ptr(gs)),
+           "moe_permute")
     return dict(offsets=offsets, dst_row=dst, row_src=src, row_prob=rp,
                 codes=codes, scales=scales, gscale=gs)
 
@@ -287,7 +310,7 @@ def combine(y_rows: np.ndarray, dst_row: np.ndarray):
 # ---- whole layer ----------------------------------------------------------
 
 def moe_forward(x_bf16, topk_idx, topk_prob, num_experts, inter, w1, w2, align: int = 1,
-                stage_times: bool = False):
+                stage_times: bool = False, act_rule: int = 0):
     """Whole expert layer.  w1 / w2 are (codes, scales, gscale) NVFP4 triples with
     shapes [E, 2I, H/2] ... and [E, H, I/2] ....  Returns (y bf16 [T, H], dict of
     intermediates[, stage seconds])."""
@@ -311,7 +334,7 @@ def moe_forward(x_bf16, topk_idx, topk_prob, num_experts, inter, w1, w2, align: 
     secs = np.zeros(6, np.float64)
     w1c, w1s, w1g = (np.ascontiguousarray(a) for a in w1)
     w2c, w2s, w2g = (np.ascontiguousarray(a) for a in w2)
-    _check(lib().orc_moe_forward(x, T, H, I, idx, prob, k, num_experts, align,
+    _check(lib().orc_moe_forward_rule(x, T, H, I, idx, prob, k, num_experts, align, act_rule,
                                  w1c.astype(np.uint8, copy=False), w1s.astype(np.uint8, copy=False),
                                  w1g.astype(np.float32, copy=False),
                                  w2c.astype(np.uint8, copy=False), w2s.astype(np.uint8, copy=False),

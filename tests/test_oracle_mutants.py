@@ -9,6 +9,7 @@ import pytest
 
 from oracle import oracle as O
 import test_oracle_codecs as TC
+import test_oracle_four_over_six as T46
 import test_oracle_quantize as TQ
 import test_oracle_route_gemm as TR
 
@@ -18,7 +19,7 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
 # (name, original text, planted mistake)
 MUTANTS = [
     ("outer_scale_divisor", "float s_g = amax / 2688.0f;", "float s_g = amax / 2687.0f;"),
-    ("block_target_code", "float t = 6.0f * s_g;", "float t = 4.0f * s_g;"),
+    ("block_target_code", "quantize_block(x + b * 16, s_g, 6.0f, c)", "quantize_block(x + b * 16, s_g, 4.0f, c)"),
     ("nibble_order", "codes[e / 2] |= (uint8_t)((e % 2) ? (code << 4) : code);",
      "codes[e / 2] |= (uint8_t)((e % 2) ? code : (code << 4));"),
     ("e2m1_ties_to_odd", "(dist == best_dist && (i % 2u) == 0u && (best % 2u) != 0u)",
@@ -26,8 +27,8 @@ MUTANTS = [
     ("e4m3_ties_to_odd", "(dist == best_dist && (b % 2u) == 0u)", "(dist == best_dist && (b % 2u) != 0u)"),
     ("e4m3_subnormal_step", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
     ("e4m3_bias", "v = ldexp(1.0 + (double)m / 8.0, (int)e - 7);", "v = ldexp(1.0 + (double)m / 8.0, (int)e - 8);"),
-    ("block_max_half_block", "    for (int i = 0; i < 16; ++i) {\n      float a = fabsf(orc_bf16_to_f32(blk[i]));",
-     "    for (int i = 0; i < 8; ++i) {\n      float a = fabsf(orc_bf16_to_f32(blk[i]));"),
+    ("block_max_half_block", "  for (int i = 0; i < 16; ++i) {\n    float a = fabsf(orc_bf16_to_f32(blk[i]));",
+     "  for (int i = 0; i < 8; ++i) {\n    float a = fabsf(orc_bf16_to_f32(blk[i]));"),
     ("no_underflow_guard", "if (d == 0.0f) {", "if (0) {"),
     ("sign_dropped", "if (signbit(xv)) code |= 8u; else code &= 7u;", "code &= 7u;"),
     ("reciprocal_instead_of_division", "float r = xv / d;", "float r = xv * (1.0f / d);"),
@@ -50,6 +51,14 @@ MUTANTS = [
     ("combine_skips_first_slot", "for (int32_t j = 0; j < topk; ++j) {\n        int32_t r = dst_row",
      "for (int32_t j = 1; j < topk; ++j) {\n        int32_t r = dst_row"),
     ("bf16_ties_to_odd", "(dist == best_dist && (c & 1u) == 0u)", "(dist == best_dist && (c & 1u) != 0u)"),
+    ("four_six_ties_pick_four", "int four = e4 < e6;", "int four = e4 <= e6;"),
+    ("four_six_outer_divisor", "float s_g = amax / 1536.0f;", "float s_g = amax / 1792.0f;"),
+    ("four_six_metrics_swapped", "float term = (metric == 1) ? e * e : fabsf(e);",
+     "float term = (metric == 1) ? fabsf(e) : e * e;"),
+    ("four_six_second_top", "quantize_block(blk, s_g, 4.0f, c4)", "quantize_block(blk, s_g, 3.0f, c4)"),
+    ("four_six_error_without_outer_scale", "float v = qs * s_g;", "float v = qs;"),
+    ("four_six_last_element_dropped", "  for (int i = 0; i < 16; ++i) {\n    float xv = orc_bf16_to_f32(blk[i]);\n    float qs",
+     "  for (int i = 0; i < 15; ++i) {\n    float xv = orc_bf16_to_f32(blk[i]);\n    float qs"),
 ]
 
 # cheap pins first; each mutant stops at the first pin that fails
@@ -62,6 +71,8 @@ PINS = [
     TR.test_swiglu_is_nearest_bf16_of_fp64_silu_product, TR.test_combine_matches_numpy_gather_sum,
     TC.test_e2m1_encode_is_round_to_nearest_even_on_grid, TC.test_f64_to_bf16_matches_torch_for_binary32_values,
     TC.test_e4m3_encode_matches_torch_cast_below_448,
+    T46.test_hand_worked_four_over_six_row, T46.test_four_over_six_zero_and_sign_rows,
+    T46.test_six_candidate_is_the_standard_quantizer_at_175_amax_and_choice_minimises_error,
 ]
 
 
