@@ -64,6 +64,11 @@ extern "C" {
 #define NVFP4_HIP_ERROR 3
 #define NVFP4_WORKSPACE_TOO_SMALL 4
 
+/* Block rules of the quantizer (see nvfp4_quantize). */
+#define NVFP4_BLOCK_RULE_SIX 0
+#define NVFP4_BLOCK_RULE_4OVER6_MSE 1
+#define NVFP4_BLOCK_RULE_4OVER6_MAE 2
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* nvfp4_status_string(int status);
 
@@ -82,6 +87,15 @@ const char* nvfp4_status_string(int status);
  *                (domain 1 only; device pointer)
  *   amax_in      nullable float [rows] (domain 0) or [num_groups] (domain 1):
  *                use these amax values instead of reducing |x|
+ *   block_rule   NVFP4_BLOCK_RULE_*: 0 maps every block maximum to the E2M1
+ *                value 6 (s_g = amax / 2688); 1 and 2 are Four-Over-Six
+ *                ([4BIT] "Four-Over-Six for RL Weights and Activations"):
+ *                s_g = amax / 1536 (the FP8 maximum of this mode read as 256,
+ *                so a block mapped to 4 keeps a finite E4M3 scale), and each
+ *                block keeps the candidate with its maximum mapped to 4 only
+ *                where that lowers the block error: 1 = sum of squares, 2 =
+ *                sum of absolute values of x - q*s_b*s_g, in binary32 over
+ *                the 16 elements in order; ties keep 6.
  *   codes        out uint8 [rows, k/2];  block_scales out uint8 [rows, k/16]
  *   global_scales out float [rows] (domain 0) or [num_groups] (domain 1);
  *                in domain 1 without amax_in it also serves as the scratch
@@ -90,7 +104,7 @@ const char* nvfp4_status_string(int status);
  * ---------------------------------------------------------------------- */
 int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
                    int scale_domain, const int32_t* group_offsets, int32_t num_groups,
-                   const float* amax_in,
+                   const float* amax_in, int block_rule,
                    uint8_t* codes, uint8_t* block_scales, float* global_scales,
                    void* stream);
 
@@ -114,6 +128,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
  *   x            nullable bf16 [tokens, hidden]: NULL computes the metadata only
  *   topk_idx     int32 [tokens, topk];  topk_prob float [tokens, topk]
  *   align        power of two in [1, 256]
+ *   block_rule   the quantizer's block rule (see nvfp4_quantize)
  *   expert_offsets out int32 [num_experts + 1]
  *   dst_row      out int32 [tokens, topk]
  *   row_src, row_prob  out [moe_rows_capacity(...)]
@@ -128,7 +143,7 @@ int64_t moe_rows_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int
 size_t moe_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_experts);
 int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
                 const int32_t* topk_idx, const float* topk_prob, int32_t topk,
-                int32_t num_experts, int32_t align,
+                int32_t num_experts, int32_t align, int32_t block_rule,
                 int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
                 uint8_t* codes, uint8_t* block_scales, float* global_scales,
                 void* workspace, size_t workspace_bytes, void* stream);
@@ -223,6 +238,10 @@ int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
  *
  *   x            bf16 [tokens, hidden];  y out bf16 [tokens, hidden]
  *   w1           NVFP4 gate|up weights [E, 2*inter, hidden] (+ scales, [E])
+ *   act_block_rule  block rule of both activation quantizations (the routed
+ *                tokens and the requantized D); the weights carry whatever
+ *                rule they were quantized with ([4BIT] "Four-Over-Six ...":
+ *                weights, activations or both)
  *   w2           NVFP4 down weights    [E, hidden, inter]
  *                (each row-major or tiled, per its layout member)
  *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned
@@ -258,7 +277,7 @@ size_t moe_expert_forward_workspace_size(int64_t tokens, int64_t hidden, int64_t
                                          int32_t topk, int32_t num_experts, int32_t align);
 int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
                        const int32_t* topk_idx, const float* topk_prob, int32_t topk,
-                       int32_t num_experts, int32_t align,
+                       int32_t num_experts, int32_t align, int32_t act_block_rule,
                        const nvfp4_weights* w1, const nvfp4_weights* w2, uint16_t* y,
                        void* workspace, size_t workspace_bytes,
                        const nvfp4_moe_intermediates* debug, void* const* stage_events,

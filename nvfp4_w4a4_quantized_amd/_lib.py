@@ -47,14 +47,15 @@ def lib():
     L.nvfp4_status_string.restype = C.c_char_p
     L.nvfp4_status_string.argtypes = [C.c_int]
     L.nvfp4_quantize.restype = C.c_int
-    L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, C.c_int, _vp, _i32, _vp, _vp, _vp, _vp, _vp]
+    L.nvfp4_quantize.argtypes = [_vp, _i64, _i64, _i64, C.c_int, _vp, _i32, _vp, C.c_int, _vp, _vp,
+                                 _vp, _vp]
     L.moe_rows_capacity.restype = _i64
     L.moe_rows_capacity.argtypes = [_i64, _i32, _i32, _i32]
     L.moe_permute_workspace_size.restype = C.c_size_t
     L.moe_permute_workspace_size.argtypes = [_i64, _i32, _i32]
     L.moe_permute.restype = C.c_int
-    L.moe_permute.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
-                              _vp, _vp, _vp, _vp, C.c_size_t, _vp]
+    L.moe_permute.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
+                              _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
     L.w4a4_grouped_gemm.restype = C.c_int
     L.w4a4_grouped_gemm.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
                                     C.c_int, C.c_int, _vp, _vp]
@@ -68,7 +69,7 @@ def lib():
     L.moe_expert_forward_workspace_size.restype = C.c_size_t
     L.moe_expert_forward_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
     L.moe_expert_forward.restype = C.c_int
-    L.moe_expert_forward.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _i32,
+    L.moe_expert_forward.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
                                      C.POINTER(Weights), C.POINTER(Weights), _vp, _vp, C.c_size_t,
                                      C.POINTER(Intermediates), _vp, _vp]
     L.nvfp4_event_create.restype = C.c_int

@@ -91,7 +91,9 @@ const char* nvfp4_status_string(int status) {
 
 int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x, int scale_domain,
                    const int32_t* group_offsets, int32_t num_groups, const float* amax_in,
-                   uint8_t* codes, uint8_t* block_scales, float* global_scales, void* stream) {
+                   int block_rule, uint8_t* codes, uint8_t* block_scales, float* global_scales,
+                   void* stream) {
+  if (block_rule < 0 || block_rule > 2) return NVFP4_INVALID_ARGUMENT;
   if (rows < 0 || rows >= 0x7FFFFFFFLL || k < 16 || k % 16 != 0 || ld_x < k || ld_x % 8 != 0)
     return NVFP4_INVALID_ARGUMENT;
   if (k > kMaxK) return NVFP4_UNSUPPORTED;
@@ -100,7 +102,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x, int
     return NVFP4_INVALID_ARGUMENT;
   hipStream_t s = static_cast<hipStream_t>(stream);
   QuantRowsArgs a{x, rows, k, ld_x, 0, amax_in, group_offsets, num_groups,
-                  codes, block_scales, global_scales};
+                  codes, block_scales, global_scales, block_rule};
   if (scale_domain == 0) {
     a.amax_kind = amax_in ? 1 : 0;
     return hip_status(launch_quantize_rows(a, s));
@@ -119,7 +121,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x, int
   a.amax_in = amax_src;
   hipError_t e = launch_quantize_rows(a, s);
   if (e != hipSuccess) return NVFP4_HIP_ERROR;
-  return hip_status(launch_group_finalize(amax_src, global_scales, num_groups, s));
+  return hip_status(launch_group_finalize(amax_src, global_scales, num_groups, block_rule, s));
 }
 
 int64_t moe_rows_capacity(int64_t tokens, int32_t topk, int32_t num_experts, int32_t align) {
@@ -135,10 +137,11 @@ size_t moe_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_expe
 
 int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden, const int32_t* topk_idx,
                 const float* topk_prob, int32_t topk, int32_t num_experts, int32_t align,
-                int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
+                int32_t block_rule, int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
                 uint8_t* codes, uint8_t* block_scales, float* global_scales, void* workspace,
                 size_t workspace_bytes, void* stream) {
   if (!route_args_ok(tokens, topk, num_experts, align)) return NVFP4_INVALID_ARGUMENT;
+  if (block_rule < 0 || block_rule > 2) return NVFP4_INVALID_ARGUMENT;
   if (!expert_offsets || !row_src || !row_prob || !workspace) return NVFP4_INVALID_ARGUMENT;
   if (tokens > 0 && (!topk_idx || !topk_prob || !dst_row)) return NVFP4_INVALID_ARGUMENT;
   if (!aligned(workspace, 16)) return NVFP4_INVALID_ARGUMENT;
@@ -151,7 +154,7 @@ int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden, const int32_t
   if (workspace_bytes < route_workspace_bytes(tokens, num_experts)) return NVFP4_WORKSPACE_TOO_SMALL;
   RouteArgs a{x, tokens, x ? hidden : 0, topk_idx, topk_prob, topk, num_experts, align,
               expert_offsets, dst_row, row_src, row_prob, codes, block_scales, global_scales,
-              nullptr, workspace};
+              nullptr, workspace, block_rule};
   return hip_status(launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -233,11 +236,13 @@ size_t moe_expert_forward_workspace_size(int64_t tokens, int64_t hidden, int64_t
 
 int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
                        const int32_t* topk_idx, const float* topk_prob, int32_t topk,
-                       int32_t num_experts, int32_t align, const nvfp4_weights* w1,
+                       int32_t num_experts, int32_t align, int32_t act_block_rule,
+                       const nvfp4_weights* w1,
                        const nvfp4_weights* w2, uint16_t* y, void* workspace,
                        size_t workspace_bytes, const nvfp4_moe_intermediates* debug,
                        void* const* stage_events, void* stream) {
   if (!route_args_ok(tokens, topk, num_experts, align)) return NVFP4_INVALID_ARGUMENT;
+  if (act_block_rule < 0 || act_block_rule > 2) return NVFP4_INVALID_ARGUMENT;
   if (hidden < 128 || hidden % 128 != 0 || inter < 128 || inter % 128 != 0)
     return NVFP4_UNSUPPORTED;
   if (hidden > kMaxK || inter > kMaxK) return NVFP4_UNSUPPORTED;
@@ -289,7 +294,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   // a1 + a2: routing metadata and per-token quantize-scatter (zeroes amax_d rows)
   RouteArgs ra{x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
                L.offsets, L.dst_row, L.row_src, L.row_prob, L.a1c, L.a1s, L.a1g,
-               L.amax_d, L.route_ws_i};
+               L.amax_d, L.route_ws_i, act_block_rule};
   if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a3 + a4: FC1 with the weighted SwiGLU epilogue and D's row amax
@@ -303,7 +308,8 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   if ((e = mark(2)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a5: requantize D reusing its amax (rows up to offsets[E] live on device:
   // quantize the whole capacity; rows past the end are ignored downstream)
-  QuantRowsArgs q{L.d, cap, inter, inter, 1, L.amax_d, nullptr, 0, L.a2c, L.a2s, L.a2g};
+  QuantRowsArgs q{L.d, cap, inter, inter, 1, L.amax_d, nullptr, 0, L.a2c, L.a2s, L.a2g,
+                  act_block_rule};
   if ((e = launch_quantize_rows(q, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(3)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a6: FC2

@@ -19,6 +19,7 @@ struct QuantRowsArgs {
   const uint16_t* x; int64_t rows; int64_t k; int64_t ld_x;
   int amax_kind; const float* amax_in; const int32_t* group_offsets; int32_t num_groups;
   uint8_t* codes; uint8_t* scales; float* gscale;  // gscale written for kinds 0, 1
+  int block_rule;                                   // 0 standard, 1/2 Four-Over-Six (MSE/MAE)
 };
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
 // Group amax: zero `amax_bits[num_groups]`, then atomic max of every row's amax.
@@ -27,7 +28,7 @@ hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t
                              uint32_t* amax_bits, hipStream_t s);
 // gscale[g] = amax[g] / 2688 (in place allowed: amax may alias gscale).
 hipError_t launch_group_finalize(const float* amax, float* gscale, int32_t num_groups,
-                                 hipStream_t s);
+                                 int rule, hipStream_t s);
 
 // ---- route.hip ----
 int64_t route_num_chunks(int64_t tokens);
@@ -40,6 +41,7 @@ struct RouteArgs {
   uint8_t* codes; uint8_t* scales; float* gscale;
   float* zero_per_row;  // nullable: set to 0 for every routed and padding row
   void* workspace;
+  int32_t block_rule;   // 0 standard, 1/2 Four-Over-Six (MSE/MAE)
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 

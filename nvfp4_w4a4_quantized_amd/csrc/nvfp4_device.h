@@ -137,11 +137,58 @@ __device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
   return lo;
 }
 
+// Block rules: 0 maps every block maximum to the largest E2M1 value 6.  1 and
+// 2 are Four-Over-Six (The 4-bitter Lesson, "Four-Over-Six for RL Weights
+// and Activations"): each block is quantized with its maximum mapped to 6
+// and to 4 and keeps the candidate with the smaller block error (1: sum of
+// squares, 2: sum of absolute values, both in binary32 over the 16 elements
+// in order); ties keep 6.  The page's formula names an FP8 maximum for this
+// mode without giving it; 256 keeps the 4-candidate's scale (1.5x, at most
+// 384) inside E4M3, so the outer scale is amax / (6 * 256).
+__device__ __forceinline__ float outer_scale(float amax, int rule) {
+  return rule == 0 ? amax / 2688.0f : amax / 1536.0f;
+}
+
+// E4M3 byte of the block scale mapping bmax to `top`, and the decode step.
+__device__ __forceinline__ uint32_t block_scale(float bmax, float s_g, float top, float* d) {
+  uint32_t sb = 0u;
+  if (s_g != 0.0f) sb = e4m3_encode(bmax / (top * s_g));
+  *d = e4m3_value(sb) * s_g;
+  return sb;
+}
+
+// Block error of codes c (two dwords, element 2i in the low nibble of byte
+// i) with scale byte sb: sum over i of e^2 (rule 1) or |e| (rule 2),
+// e = x_i - fl((q_i * s_b) * s_g), accumulated in order in binary32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+template <int SEL>
+__device__ __forceinline__ f32x2_t fp4_pair_value(uint32_t w) {   // codes of byte SEL
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+__device__ __forceinline__ float block_error(const float (&x)[16], uint2 c, uint32_t sb, float s_g,
+                                             int rule) {
+  const float s_b = e4m3_value(sb);
+  f32x2_t q[8];
+  q[0] = fp4_pair_value<0>(c.x); q[1] = fp4_pair_value<1>(c.x);
+  q[2] = fp4_pair_value<2>(c.x); q[3] = fp4_pair_value<3>(c.x);
+  q[4] = fp4_pair_value<0>(c.y); q[5] = fp4_pair_value<1>(c.y);
+  q[6] = fp4_pair_value<2>(c.y); q[7] = fp4_pair_value<3>(c.y);
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float v = (q[i / 2][i % 2] * s_b) * s_g;   // q * s_b is exact
+    const float e = x[i] - v;
+    acc = acc + (rule == 1 ? e * e : __builtin_fabsf(e));
+  }
+  return acc;
+}
+
 // Quantizes one 16-element block of bf16 values (two uint4 words = 8 dwords,
-// element 2i in the low half of dword i) with outer scale s_g.  Returns the
-// 8 code bytes; *scale receives the E4M3 byte.
-//   s_b = E4M3(fl(bmax / fl(6 * s_g))) (0 when s_g == 0), d = fl(s_b * s_g).
-__device__ __forceinline__ uint2 quantize_block16(const uint32_t (&w)[8], float s_g,
+// element 2i in the low half of dword i) with outer scale s_g under a block
+// rule.  Returns the 8 code bytes; *scale receives the E4M3 byte.
+//   s_b = E4M3(fl(bmax / fl(top * s_g))) (0 when s_g == 0), d = fl(s_b * s_g).
+__device__ __forceinline__ uint2 quantize_block16(const uint32_t (&w)[8], float s_g, int rule,
                                                   uint32_t* scale) {
   float x[16];
 #pragma unroll
@@ -150,14 +197,19 @@ __device__ __forceinline__ uint2 quantize_block16(const uint32_t (&w)[8], float 
     x[2 * i + 1] = bf16_hi(w[i]);
   }
   const float bmax = __uint_as_float(bf16_absmax_bits(w) << 16);
-  uint32_t sb = 0u;
-  if (s_g != 0.0f) {
-    const float t = 6.0f * s_g;
-    sb = e4m3_encode(bmax / t);
+  float d6;
+  const uint32_t sb6 = block_scale(bmax, s_g, 6.0f, &d6);
+  const uint2 c6 = encode_block16(x, d6);
+  if (rule == 0) {
+    *scale = sb6;
+    return c6;
   }
-  *scale = sb;
-  const float d = e4m3_value(sb) * s_g;
-  return encode_block16(x, d);
+  float d4;
+  const uint32_t sb4 = block_scale(bmax, s_g, 4.0f, &d4);
+  const uint2 c4 = encode_block16(x, d4);
+  const bool four = block_error(x, c4, sb4, s_g, rule) < block_error(x, c6, sb6, s_g, rule);
+  *scale = four ? sb4 : sb6;
+  return four ? c4 : c6;
 }
 
 }  // namespace nvfp4

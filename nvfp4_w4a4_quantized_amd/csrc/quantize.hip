@@ -5,7 +5,7 @@
 // 2 KiB span (coalesced), and the row stays in registers between the amax
 // reduction and the encoding.  The row amax is a wave-wide max of the |bf16|
 // bit patterns; the per-token outer scale is s_g = amax / 2688 (miniTE
-// Technical Report §5.6).  Group (per-expert) scales take an atomic max of
+// Technical Report §5.6), or amax / 1536 under Four-Over-Six.  Group (per-expert) scales take an atomic max of
 // the row amaxes first (order independent, so deterministic).
 #include "launch.h"
 #include "nvfp4_device.h"
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
     int g = find_group(a.group_offsets, a.num_groups, row);
     amax = a.amax_in[g];
   }
-  const float s_g = amax / 2688.0f;
+  const float s_g = outer_scale(amax, a.block_rule);
   uint8_t* crow = a.codes + row * (a.k / 2);
   uint8_t* srow = a.scales + row * (a.k / 16);
 #pragma unroll
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
     const int b = lane + kWave * i;
     if (b < nblocks) {
       uint32_t sb;
-      uint2 c = quantize_block16(w[i], s_g, &sb);
+      uint2 c = quantize_block16(w[i], s_g, a.block_rule, &sb);
       *reinterpret_cast<uint2*>(crow + (int64_t)b * 8) = c;
       srow[b] = (uint8_t)sb;
     }
@@ -103,13 +103,13 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(QuantRowsArgs a) {
   const uint32_t row = (uint32_t)i / nb, b = (uint32_t)i - row * nb;
   const float amax = a.amax_kind == 1 ? a.amax_in[row]
                                       : a.amax_in[find_group(a.group_offsets, a.num_groups, row)];
-  const float s_g = amax / 2688.0f;
+  const float s_g = outer_scale(amax, a.block_rule);
   const uint16_t* p = a.x + (int64_t)row * a.ld_x + (int64_t)b * 16;
   const u32x4_t u0 = load_stream16(p);
   const u32x4_t u1 = load_stream16(p + 8);
   const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
   uint32_t sb;
-  const uint2 c = quantize_block16(w, s_g, &sb);
+  const uint2 c = quantize_block16(w, s_g, a.block_rule, &sb);
   *reinterpret_cast<uint2*>(a.codes + (int64_t)row * (a.k / 2) + (int64_t)b * 8) = c;
   a.scales[(int64_t)row * (a.k / 16) + b] = (uint8_t)sb;
   if (a.amax_kind == 1 && b == 0) a.gscale[row] = s_g;
@@ -136,9 +136,9 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
-__global__ void group_finalize_kernel(const float* amax, float* gscale, int32_t n) {
+__global__ void group_finalize_kernel(const float* amax, float* gscale, int32_t n, int rule) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) gscale[i] = amax[i] / 2688.0f;
+  if (i < n) gscale[i] = outer_scale(amax[i], rule);
 }
 
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s) {
@@ -177,8 +177,9 @@ hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_group_finalize(const float* amax, float* gscale, int32_t n, hipStream_t s) {
-  group_finalize_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, gscale, n);
+hipError_t launch_group_finalize(const float* amax, float* gscale, int32_t n, int rule,
+                                 hipStream_t s) {
+  group_finalize_kernel<<<(n + 255) / 256, 256, 0, s>>>(amax, gscale, n, rule);
   return hipGetLastError();
 }
 

@@ -292,9 +292,9 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
         m = m > mi ? m : mi;
       }
       const float amax = __uint_as_float(wave_max_u32(m) << 16);
-      s_g = amax / 2688.0f;
+      s_g = outer_scale(amax, a.block_rule);
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) codes[i] = quantize_block16(w[ti][i], s_g, &sbytes[i]);
+      for (int i = 0; i < BPL; ++i) codes[i] = quantize_block16(w[ti][i], s_g, a.block_rule, &sbytes[i]);
     }
     // the quantized token into row dst (all lanes)
     auto store_row = [&](int64_t dst) {

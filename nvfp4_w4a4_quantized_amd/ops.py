@@ -53,11 +53,13 @@ class NvFp4Weights:
         return NvFp4Weights(pc, ps, self.gscale, layout=1)
 
     @classmethod
-    def quantize(cls, w_bf16: torch.Tensor) -> "NvFp4Weights":
-        """Quantizes bf16 weights [G, N, K] with one outer scale per expert."""
+    def quantize(cls, w_bf16: torch.Tensor, block_rule: int = 0) -> "NvFp4Weights":
+        """Quantizes bf16 weights [G, N, K] with one outer scale per expert
+        (block_rule: see nvfp4_quantize)."""
         G, N, K = w_bf16.shape
         offs = (torch.arange(G + 1, dtype=torch.int32, device=w_bf16.device) * N)
         codes, scales, gscale = nvfp4_quantize(w_bf16.reshape(G * N, K), scale_domain=1,
+                                               block_rule=block_rule,
                                                group_offsets=offs)
         return cls(codes.view(G, N, K // 2), scales.view(G, N, K // 16), gscale)
 
@@ -66,9 +68,12 @@ class NvFp4Weights:
                        self.layout)
 
 
-def nvfp4_quantize(x, scale_domain: int = 0, group_offsets=None, amax_in=None):
+def nvfp4_quantize(x, scale_domain: int = 0, group_offsets=None, amax_in=None,
+                   block_rule: int = 0):
     """NVFP4 quantization of a bf16 [rows, k] matrix.  Returns (codes, scales,
-    global_scales) with global_scales per row (domain 0) or per group (1)."""
+    global_scales) with global_scales per row (domain 0) or per group (1).
+    block_rule 0: every block maximum maps to 6; 1 / 2: Four-Over-Six with the
+    block error measured as a sum of squares / of absolute values."""
     _need(x, _BF16_LIKE, "x")
     rows, k = x.shape
     dev = x.device
@@ -84,7 +89,8 @@ def nvfp4_quantize(x, scale_domain: int = 0, group_offsets=None, amax_in=None):
     if amax_in is not None:
         _need(amax_in, (torch.float32,), "amax_in")
     check(lib().nvfp4_quantize(ptr(x), rows, k, k, scale_domain, ptr(group_offsets), ng,
-                               ptr(amax_in), ptr(codes), ptr(scales), ptr(gs), stream_handle()),
+                               ptr(amax_in), block_rule, ptr(codes), ptr(scales), ptr(gs),
+                               stream_handle()),
           "nvfp4_quantize")
     return codes, scales, gs
 
@@ -93,7 +99,7 @@ def moe_rows_capacity(tokens: int, topk: int, num_experts: int, align: int = 1) 
     return int(lib().moe_rows_capacity(tokens, topk, num_experts, align))
 
 
-def moe_permute(x, topk_idx, topk_prob, num_experts: int, align: int = 1):
+def moe_permute(x, topk_idx, topk_prob, num_experts: int, align: int = 1, block_rule: int = 0):
     """Routing metadata + per-token quantize-scatter.  x may be None (metadata
     only).  Returns a dict of device tensors."""
     _need(topk_idx, (torch.int32,), "topk_idx")
@@ -116,7 +122,7 @@ def moe_permute(x, topk_idx, topk_prob, num_experts: int, align: int = 1):
     wsb = int(lib().moe_permute_workspace_size(T, k, num_experts))
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     check(lib().moe_permute(ptr(x), T, H, ptr(topk_idx), ptr(topk_prob), k, num_experts, align,
-                            ptr(out["offsets"]), ptr(out["dst_row"]), ptr(out["row_src"]),
+                            block_rule, ptr(out["offsets"]), ptr(out["dst_row"]), ptr(out["row_src"]),
                             ptr(out["row_prob"]), ptr(out.get("codes")), ptr(out.get("scales")),
                             ptr(out.get("gscale")), ptr(ws), ws.numel(), stream_handle()),
           "moe_permute")
@@ -215,7 +221,7 @@ class StageTimer:
 def moe_expert_forward(x, topk_idx, topk_prob, num_experts: int, inter: int,
                        w1: NvFp4Weights, w2: NvFp4Weights, align: int = 1, workspace=None,
                        debug: bool = False, fc1_out: bool = False, y_rows_f32: bool = False,
-                       timer: StageTimer | None = None, y=None):
+                       timer: StageTimer | None = None, y=None, act_block_rule: int = 0):
     """The whole expert layer.  Returns y (bf16 [T, H]); with debug=True also a
     dict of the intermediates (allocated here, written by the library)."""
     _need(x, _BF16_LIKE, "x")
@@ -249,7 +255,7 @@ def moe_expert_forward(x, topk_idx, topk_prob, num_experts: int, inter: int,
         dbg = Intermediates(**{n: t.data_ptr() for n, t in inter_t.items()})
     ev = timer.events if timer is not None else None
     check(lib().moe_expert_forward(ptr(x), T, H, inter, ptr(topk_idx), ptr(topk_prob), k,
-                                   num_experts, align, C.byref(w1.c_struct()),
+                                   num_experts, align, act_block_rule, C.byref(w1.c_struct()),
                                    C.byref(w2.c_struct()), ptr(y), ptr(workspace),
                                    workspace.numel(), C.byref(dbg) if dbg is not None else None,
                                    C.cast(ev, C.c_void_p) if ev is not None else None,

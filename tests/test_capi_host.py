@@ -63,22 +63,25 @@ def test_host_side_sizes(L):
 def test_invalid_arguments_rejected_before_any_device_call(L):
     fake = C.c_void_p(0x1000)   # never dereferenced: validation fails first
     # k not a multiple of 16
-    assert L.nvfp4_quantize(fake, 4, 24, 24, 0, None, 0, None, fake, fake, fake, None) == INVALID
+    assert L.nvfp4_quantize(fake, 4, 24, 24, 0, None, 0, None, 0, fake, fake, fake, None) == INVALID
     # missing output
-    assert L.nvfp4_quantize(fake, 4, 32, 32, 0, None, 0, None, None, fake, fake, None) == INVALID
+    assert L.nvfp4_quantize(fake, 4, 32, 32, 0, None, 0, None, 0, None, fake, fake, None) == INVALID
     # unknown domain / domain 1 without offsets
-    assert L.nvfp4_quantize(fake, 4, 32, 32, 1, None, 2, None, fake, fake, fake, None) == INVALID
+    assert L.nvfp4_quantize(fake, 4, 32, 32, 1, None, 2, None, 0, fake, fake, fake, None) == INVALID
     # k beyond the supported maximum
-    assert L.nvfp4_quantize(fake, 4, 32768, 32768, 0, None, 0, None, fake, fake, fake, None) == UNSUPPORTED
+    assert L.nvfp4_quantize(fake, 4, 32768, 32768, 0, None, 0, None, 0, fake, fake, fake, None) == UNSUPPORTED
+    # unknown block rule
+    assert L.nvfp4_quantize(fake, 4, 32, 32, 0, None, 0, None, 3, fake, fake, fake, None) == INVALID
     # misaligned x
-    assert L.nvfp4_quantize(C.c_void_p(0x1002), 4, 32, 32, 0, None, 0, None, fake, fake, fake, None) == INVALID
+    assert L.nvfp4_quantize(C.c_void_p(0x1002), 4, 32, 32, 0, None, 0, None, 0, fake, fake, fake, None) == INVALID
     # topk > experts, bad align, too many experts
     args = (fake, 16, 64, fake, fake)
-    assert L.moe_permute(*args, 5, 4, 1, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
-    assert L.moe_permute(*args, 2, 4, 3, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
-    assert L.moe_permute(*args, 2, 2048, 1, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
+    assert L.moe_permute(*args, 5, 4, 1, 0, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
+    assert L.moe_permute(*args, 2, 4, 3, 0, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
+    assert L.moe_permute(*args, 2, 2048, 1, 0, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
     # workspace too small
-    assert L.moe_permute(*args, 2, 4, 1, fake, fake, fake, fake, fake, fake, fake, fake, 4, None) == WS_SMALL
+    assert L.moe_permute(*args, 2, 4, 1, 0, fake, fake, fake, fake, fake, fake, fake, fake, 4, None) == WS_SMALL
+    assert L.moe_permute(*args, 2, 4, 1, 7, fake, fake, fake, fake, fake, fake, fake, fake, 1 << 20, None) == INVALID
     # GEMM: k not a multiple of 128, n not a multiple of 32, bad dtype
     g = (fake, fake, fake, 64, fake, fake, fake, fake, 2)
     assert L.w4a4_grouped_gemm(*g, 64, 96, 0, 0, fake, None) == UNSUPPORTED
@@ -102,12 +105,15 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     # expert layer: hidden not a multiple of 128, missing weights
     from nvfp4_w4a4_quantized_amd._lib import Weights
     w = Weights(0x1000, 0x1000, 0x1000)
-    assert L.moe_expert_forward(fake, 8, 200, 128, fake, fake, 2, 4, 1, C.byref(w), C.byref(w),
+    assert L.moe_expert_forward(fake, 8, 200, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(w),
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == UNSUPPORTED
-    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, None, C.byref(w),
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, None, C.byref(w),
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
-    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, C.byref(w), C.byref(w),
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(w),
                                 fake, C.c_void_p(0x10000), 16, None, None, None) == WS_SMALL
+    # unknown activation block rule
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 5, C.byref(w), C.byref(w),
+                                fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
     wbad = Weights(0x1000, 0x1000, 0x1000, 3)   # unknown layout
-    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, C.byref(w), C.byref(wbad),
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(wbad),
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID

@@ -104,7 +104,7 @@ def test_amax_in_and_leading_dimension():
     s = torch.empty((40, 16), dtype=torch.uint8, device="cuda")
     g = torch.empty(40, dtype=torch.float32, device="cuda")
     say("nvfp4_quantize ld_x=384 k=256")
-    _lib.check(_lib.lib().nvfp4_quantize(_lib.ptr(xd), 40, 256, 384, 0, None, 0, None,
+    _lib.check(_lib.lib().nvfp4_quantize(_lib.ptr(xd), 40, 256, 384, 0, None, 0, None, 0,
                                          _lib.ptr(c), _lib.ptr(s), _lib.ptr(g),
                                          _lib.stream_handle()), "quantize ld")
     torch.cuda.synchronize()
