@@ -14,6 +14,8 @@ Prints one JSON line (rank 0):
   roofline     the FC1 kernel (dominant): algorithmic FLOPs per launch over its
                average duration from HIP events recorded on the launch stream
   cpu_baseline the CPU oracle timed on a bounded token sample of the workload
+  four_over_six the same layer with Four-Over-Six (MSE) weights and activations
+               (a secondary line; the headline is the standard block rule)
 """
 from __future__ import annotations
 
@@ -48,6 +50,10 @@ def parse():
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fc1_traffic.json"),
                    help="JSON record of measured HBM bytes per FC1 launch (rocprof PMC); "
                         "ignored when the GEMM source changed since it was taken")
+    p.add_argument("--four-over-six", type=int, default=1,
+                   help="also time the layer with Four-Over-Six (MSE) weights and activations and "
+                        "report it under 'four_over_six' (0 = skip); the headline stays the "
+                        "standard rule")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run plain device copies of this many MiB (a known-size "
                         "kernel for scaling the rocprof FETCH_SIZE/WRITE_SIZE counters)")
@@ -116,25 +122,29 @@ def main():
     y = torch.empty((w.tokens, w.hidden), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def step(timer=None):
-        moe_expert_forward(x, idx, prob, w.experts, w.inter, W1, W2, workspace=ws, y=y,
-                           timer=timer)
+    def timed(W1, W2, rule):
+        def step(timer=None):
+            moe_expert_forward(x, idx, prob, w.experts, w.inter, W1, W2, workspace=ws, y=y,
+                               timer=timer, act_block_rule=rule)
 
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    timers = [StageTimer() for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(timers[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    stages = {n: float(np.mean([t.elapsed_ms()[n] for t in timers])) for n in StageTimer.NAMES}
-    for t in timers:
-        t.close()
+        log(f"warmup {args.warmup} (block rule {rule})")
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        timers = [StageTimer() for _ in range(args.steps)]
+        log(f"timing {args.steps} steps (block rule {rule})")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(timers[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        stages = {n: float(np.mean([t.elapsed_ms()[n] for t in timers])) for n in StageTimer.NAMES}
+        for t in timers:
+            t.close()
+        return wall, stages
+
+    wall, stages = timed(W1, W2, 0)
     ms = wall * 1e3 / args.steps
     tokens_per_s = w.tokens * args.steps / wall
     total_flops = fc1_flops + fc2_flops
@@ -186,6 +196,18 @@ def main():
                      "traffic": traffic,
                      "per_launch_flops": fc1_flops},
     }
+    if args.four_over_six:
+        log("Four-Over-Six (MSE): weights requantized offline, activations in the layer")
+        V1 = NvFp4Weights.quantize(bf(w.w1), block_rule=1).packed()
+        V2 = NvFp4Weights.quantize(bf(w.w2), block_rule=1).packed()
+        wall46, st46 = timed(V1, V2, 1)
+        log("stages 4/6 (ms, HIP events): " + ", ".join(f"{k}={v:.4f}" for k, v in st46.items()))
+        result["four_over_six"] = {
+            "block_rule": "4/6, block error = sum of squares",
+            "value": w.tokens * args.steps / wall46, "unit": "tokens/s",
+            "ms_per_step": wall46 * 1e3 / args.steps, "stage_ms": st46,
+            "quantize_permute_gbps": qbytes / (st46["route_quantize"] * 1e-3) / 1e9,
+        }
     if args.cpu_tokens > 0:
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.tokens))
     else:
