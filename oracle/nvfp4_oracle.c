@@ -120,12 +120,22 @@ float orc_row_amax(const uint16_t* x, int64_t k) {
 /* One block's E4M3 scale byte and its 16 codes, with the block maximum
  * mapped to the E2M1 value `top` (6 for the standard rule; 4 for the second
  * Four-Over-Six candidate). */
+static unsigned quantize_block_bmax(const uint16_t* blk, float bmax, float s_g, float top,
+                                   unsigned codes16[16]);
+
 static unsigned quantize_block(const uint16_t* blk, float s_g, float top, unsigned codes16[16]) {
   float bmax = 0.0f;
   for (int i = 0; i < 16; ++i) {
     float a = fabsf(orc_bf16_to_f32(blk[i]));
     if (a > bmax) bmax = a;
   }
+  return quantize_block_bmax(blk, bmax, s_g, top, codes16);
+}
+
+/* The same with the scaling maximum given (the 2D tile maximum for 16x16
+ * weight blocks). */
+static unsigned quantize_block_bmax(const uint16_t* blk, float bmax, float s_g, float top,
+                                   unsigned codes16[16]) {
   /* block scale: maps the block maximum to `top` */
   unsigned sb_byte = 0;
   if (s_g != 0.0f) {
@@ -224,6 +234,16 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
                            codes, scales, gscale);
 }
 
+/* max |x| over rows [r0, r1) */
+static float group_amax(const uint16_t* x, int64_t ld_x, int64_t k, int64_t r0, int64_t r1) {
+  float amax = 0.0f;
+  for (int64_t r = r0; r < r1; ++r) {
+    float a = orc_row_amax(x + r * ld_x, k);
+    if (a > amax) amax = a;
+  }
+  return amax;
+}
+
 int orc_quantize_rule(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
                       int domain, const int32_t* group_offsets, int32_t num_groups,
                       const float* amax_in, int rule,
@@ -244,20 +264,46 @@ int orc_quantize_rule(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
     for (int32_t g = 0; g < num_groups; ++g) {
       int64_t r0 = group_offsets[g], r1 = group_offsets[g + 1];
       if (r0 < 0 || r1 < r0 || r1 > rows) return 1;
-      float amax = 0.0f;
-      if (amax_in) {
-        amax = amax_in[g];
-      } else {
-        for (int64_t r = r0; r < r1; ++r) {
-          float a = orc_row_amax(x + r * ld_x, k);
-          if (a > amax) amax = a;
-        }
-      }
+      float amax = amax_in ? amax_in[g] : group_amax(x, ld_x, k, r0, r1);
 #pragma omp parallel for schedule(static)
       for (int64_t r = r0; r < r1; ++r)
         (void)orc_quantize_row_rule(x + r * ld_x, k, amax, rule, codes + r * (k / 2),
                                     scales + r * (k / 16));
       gscale[g] = orc_outer_scale(amax, rule); /* the s_g every row of the group used */
+    }
+    return 0;
+  }
+  if (domain == 2) {
+    /* per-group outer scale with 16x16 blocks: 16 consecutive rows of a group
+     * and 16 consecutive elements share one E4M3 scale, set by the tile
+     * maximum ([miniTE] §2.2 "two-dimensional block-scaled quantization";
+     * [miniTE] App. D2 "2D weight quantization").  Reading: the tile's
+     * maximum maps to 6 exactly as a 1D block's would, every element is
+     * encoded with the tile's decode step, and the scale byte is stored in
+     * each of the tile's rows so that [rows, k/16] keeps its meaning. */
+    if (!group_offsets || num_groups < 0 || rule != 0) return 1;
+    for (int32_t g = 0; g < num_groups; ++g) {
+      int64_t r0 = group_offsets[g], r1 = group_offsets[g + 1];
+      if (r0 < 0 || r1 < r0 || r1 > rows || (r1 - r0) % 16 != 0) return 1;
+      float amax = amax_in ? amax_in[g] : group_amax(x, ld_x, k, r0, r1);
+      float s_g = orc_outer_scale(amax, 0);
+      for (int64_t t0 = r0; t0 < r1; t0 += 16) {
+        for (int64_t r = t0; r < t0 + 16; ++r) memset(codes + r * (k / 2), 0, (size_t)(k / 2));
+        for (int64_t b = 0; b < k / 16; ++b) {
+          float tmax = 0.0f;
+          for (int64_t r = t0; r < t0 + 16; ++r) {
+            float a = orc_row_amax(x + r * ld_x + b * 16, 16);
+            if (a > tmax) tmax = a;
+          }
+          for (int64_t r = t0; r < t0 + 16; ++r) {
+            unsigned c[16];
+            scales[r * (k / 16) + b] =
+                (uint8_t)quantize_block_bmax(x + r * ld_x + b * 16, tmax, s_g, 6.0f, c);
+            pack_block(b, c, codes + r * (k / 2));
+          }
+        }
+      }
+      gscale[g] = s_g;
     }
     return 0;
   }

@@ -112,6 +112,10 @@ float orc_row_amax(const uint16_t* x, int64_t k);
  *             (per-expert weights: [miniTE] §2.2 "per tensor, per expert, or
  *             per row"; [4BIT] "Baseline recipe": one FP32 scale per weight
  *             tensor).
+ *   domain 2: as domain 1, with 16x16 blocks: 16 consecutive rows of a group
+ *             times 16 consecutive elements share one scale, set by the tile
+ *             maximum; every group's row count must be a multiple of 16
+ *             (2D weight quantization: [miniTE] §2.2, App. D2); rule 0 only.
  * amax_in (nullable): [rows] (domain 0) or [num_groups] (domain 1) amax values
  * used as given instead of the reduction ([miniTE] §5.3 amax reuse).
  * Outputs: codes [rows, k/2], scales [rows, k/16], gscale [rows] or

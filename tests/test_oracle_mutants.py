@@ -10,6 +10,7 @@ import pytest
 from oracle import oracle as O
 import test_oracle_codecs as TC
 import test_oracle_four_over_six as T46
+import test_oracle_scale_domains as TD
 import test_oracle_quantize as TQ
 import test_oracle_route_gemm as TR
 
@@ -34,8 +35,8 @@ MUTANTS = [
     ("reciprocal_instead_of_division", "float r = xv / d;", "float r = xv * (1.0f / d);"),
     ("amax_in_ignored", "float amax = amax_in ? amax_in[r] : orc_row_amax(xr, k);",
      "float amax = orc_row_amax(xr, k);"),
-    ("group_amax_first_row_only", "for (int64_t r = r0; r < r1; ++r) {\n          float a = orc_row_amax",
-     "for (int64_t r = r0; r < r0 + 1; ++r) {\n          float a = orc_row_amax"),
+    ("group_amax_first_row_only", "for (int64_t r = r0; r < r1; ++r) {\n    float a = orc_row_amax",
+     "for (int64_t r = r0; r < r0 + 1; ++r) {\n    float a = orc_row_amax"),
     ("dot_drops_first_term", "for (int64_t i = 0; i < k; ++i) {\n    double p = a[i] * b[i];",
      "for (int64_t i = 1; i < k; ++i) {\n    double p = a[i] * b[i];"),
     ("gemm_wrong_group_weights", "orc_dequantize_row(b_codes + ((int64_t)g * n + j) * (k / 2),\n"
@@ -51,6 +52,10 @@ MUTANTS = [
     ("combine_skips_first_slot", "for (int32_t j = 0; j < topk; ++j) {\n        int32_t r = dst_row",
      "for (int32_t j = 1; j < topk; ++j) {\n        int32_t r = dst_row"),
     ("bf16_ties_to_odd", "(dist == best_dist && (c & 1u) == 0u)", "(dist == best_dist && (c & 1u) != 0u)"),
+    ("tile_max_first_row_only", "for (int64_t r = t0; r < t0 + 16; ++r) {\n            float a = orc_row_amax",
+     "for (int64_t r = t0; r < t0 + 1; ++r) {\n            float a = orc_row_amax"),
+    ("tile_scale_from_own_row", "quantize_block_bmax(x + r * ld_x + b * 16, tmax, s_g, 6.0f, c)",
+     "quantize_block(x + r * ld_x + b * 16, s_g, 6.0f, c)"),
     ("four_six_ties_pick_four", "int four = e4 < e6;", "int four = e4 <= e6;"),
     ("four_six_outer_divisor", "float s_g = amax / 1536.0f;", "float s_g = amax / 1792.0f;"),
     ("four_six_metrics_swapped", "float term = (metric == 1) ? e * e : fabsf(e);",
@@ -73,6 +78,8 @@ PINS = [
     TC.test_e4m3_encode_matches_torch_cast_below_448,
     T46.test_hand_worked_four_over_six_row, T46.test_four_over_six_zero_and_sign_rows,
     T46.test_six_candidate_is_the_standard_quantizer_at_175_amax_and_choice_minimises_error,
+    TD.test_2d_quantization_is_transpose_consistent,
+    TD.test_2d_tile_scale_is_the_1d_scale_of_the_row_holding_the_tile_maximum,
 ]
 
 
