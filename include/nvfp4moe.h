@@ -82,7 +82,16 @@ const char* nvfp4_status_string(int status);
  *                ld_x >= k, ld_x % 8 == 0, 16-byte aligned
  *   scale_domain 0: one outer scale per row (activations);
  *                1: one outer scale per group of rows
- *                   [group_offsets[g], group_offsets[g+1]) (expert weights)
+ *                   [group_offsets[g], group_offsets[g+1]) (expert weights;
+ *                   one group over all rows is the per-tensor scale);
+ *                2: as 1, with 16x16 two-dimensional blocks ([miniTE] §2.2,
+ *                   App. D2 "2D weight quantization"): 16 consecutive rows
+ *                   of a group and 16 consecutive elements share one E4M3
+ *                   scale set by the tile maximum, stored in each of the
+ *                   tile's rows (block_scales keeps its [rows, k/16] shape,
+ *                   so the GEMM reads it unchanged).  rows % 16 == 0 and
+ *                   block_rule 0, else NVFP4_UNSUPPORTED; every group's row
+ *                   count must be a multiple of 16 (caller contract).
  *   group_offsets int32 [num_groups + 1], non-decreasing, within [0, rows]
  *                (domain 1 only; device pointer)
  *   amax_in      nullable float [rows] (domain 0) or [num_groups] (domain 1):

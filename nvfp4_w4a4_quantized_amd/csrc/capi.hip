@@ -107,8 +107,9 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x, int
     a.amax_kind = amax_in ? 1 : 0;
     return hip_status(launch_quantize_rows(a, s));
   }
-  if (scale_domain != 1) return NVFP4_INVALID_ARGUMENT;
+  if (scale_domain != 1 && scale_domain != 2) return NVFP4_INVALID_ARGUMENT;
   if (!group_offsets || num_groups < 1 || num_groups >= 0x7FFFFFFF) return NVFP4_INVALID_ARGUMENT;
+  if (scale_domain == 2 && (rows % 16 != 0 || block_rule != 0)) return NVFP4_UNSUPPORTED;
   // group amax: reduce into global_scales (as bits) unless given
   const float* amax_src = amax_in;
   if (!amax_src) {
@@ -119,7 +120,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x, int
   }
   a.amax_kind = 2;
   a.amax_in = amax_src;
-  hipError_t e = launch_quantize_rows(a, s);
+  hipError_t e = scale_domain == 2 ? launch_quantize_tiles2d(a, s) : launch_quantize_rows(a, s);
   if (e != hipSuccess) return NVFP4_HIP_ERROR;
   return hip_status(launch_group_finalize(amax_src, global_scales, num_groups, block_rule, s));
 }

@@ -22,6 +22,8 @@ struct QuantRowsArgs {
   int block_rule;                                   // 0 standard, 1/2 Four-Over-Six (MSE/MAE)
 };
 hipError_t launch_quantize_rows(const QuantRowsArgs& a, hipStream_t s);
+// 16x16 two-dimensional blocks, per-group scale from amax_in (rows % 16 == 0)
+hipError_t launch_quantize_tiles2d(const QuantRowsArgs& a, hipStream_t s);
 // Group amax: zero `amax_bits[num_groups]`, then atomic max of every row's amax.
 hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
                              const int32_t* group_offsets, int32_t num_groups,

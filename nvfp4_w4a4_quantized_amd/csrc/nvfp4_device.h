@@ -184,6 +184,21 @@ __device__ __forceinline__ float block_error(const float (&x)[16], uint2 c, uint
   return acc;
 }
 
+// One 16-element block (8 dwords of bf16 pairs) scaled by a given maximum:
+// the 16x16 tile maximum of two-dimensional weight blocks (standard rule).
+__device__ __forceinline__ uint2 quantize_block16_tile(const uint32_t (&w)[8], float tmax, float s_g,
+                                                       uint32_t* scale) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = bf16_lo(w[i]);
+    x[2 * i + 1] = bf16_hi(w[i]);
+  }
+  float d;
+  *scale = block_scale(tmax, s_g, 6.0f, &d);
+  return encode_block16(x, d);
+}
+
 // Quantizes one 16-element block of bf16 values (two uint4 words = 8 dwords,
 // element 2i in the low half of dword i) with outer scale s_g under a block
 // rule.  Returns the 8 code bytes; *scale receives the E4M3 byte.

@@ -115,6 +115,52 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(QuantRowsArgs a) {
   if (a.amax_kind == 1 && b == 0) a.gscale[row] = s_g;
 }
 
+// 16x16 two-dimensional blocks (per-group outer scale from amax_in): each
+// lane owns one tile (16 rows of a group x one 16-element block column),
+// finds its maximum, then encodes the 16 rows with it; the scale byte is
+// stored in each of the tile's rows.  Consecutive lanes take consecutive
+// block columns, so every load and store of a wave is contiguous.
+__global__ __launch_bounds__(256) void quantize_tiles2d_kernel(QuantRowsArgs a) {
+  const int64_t nb = a.k / 16;
+  const int64_t per_rt = (nb + kWave - 1) / kWave * kWave;   // lanes per 16-row tile row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rt = gid / per_rt, b = gid % per_rt;
+  if (rt >= a.rows / 16 || b >= nb) return;
+  const int64_t r0 = rt * 16;
+  const float s_g = outer_scale(a.amax_in[find_group(a.group_offsets, a.num_groups, r0)], 0);
+  auto load = [&](int r, uint32_t (&w)[8]) {
+    const uint16_t* p = a.x + (r0 + r) * a.ld_x + b * 16;
+    const u32x4_t u0 = load_stream16(p);
+    const u32x4_t u1 = load_stream16(p + 8);
+    w[0] = u0.x; w[1] = u0.y; w[2] = u0.z; w[3] = u0.w;
+    w[4] = u1.x; w[5] = u1.y; w[6] = u1.z; w[7] = u1.w;
+  };
+  uint32_t tbits = 0u;
+  for (int r = 0; r < 16; ++r) {
+    uint32_t w[8];
+    load(r, w);
+    const uint32_t m = bf16_absmax_bits(w);
+    tbits = tbits > m ? tbits : m;
+  }
+  const float tmax = __uint_as_float(tbits << 16);
+  for (int r = 0; r < 16; ++r) {
+    uint32_t w[8];
+    load(r, w);
+    uint32_t sb;
+    const uint2 c = quantize_block16_tile(w, tmax, s_g, &sb);
+    *reinterpret_cast<uint2*>(a.codes + (r0 + r) * (a.k / 2) + b * 8) = c;
+    a.scales[(r0 + r) * (a.k / 16) + b] = (uint8_t)sb;
+  }
+}
+
+hipError_t launch_quantize_tiles2d(const QuantRowsArgs& a, hipStream_t s) {
+  const int64_t nb = a.k / 16;
+  const int64_t threads = (a.rows / 16) * ((nb + kWave - 1) / kWave * kWave);
+  if (threads == 0) return hipSuccess;
+  quantize_tiles2d_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int BPL>
 __global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* x, int64_t rows, int64_t k,
                                                          int64_t ld_x, const int32_t* off,

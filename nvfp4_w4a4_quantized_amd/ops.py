@@ -53,12 +53,14 @@ class NvFp4Weights:
         return NvFp4Weights(pc, ps, self.gscale, layout=1)
 
     @classmethod
-    def quantize(cls, w_bf16: torch.Tensor, block_rule: int = 0) -> "NvFp4Weights":
+    def quantize(cls, w_bf16: torch.Tensor, block_rule: int = 0,
+                 blocks_2d: bool = False) -> "NvFp4Weights":
         """Quantizes bf16 weights [G, N, K] with one outer scale per expert
-        (block_rule: see nvfp4_quantize)."""
+        (block_rule: see nvfp4_quantize; blocks_2d: 16x16 blocks, N % 16 == 0)."""
         G, N, K = w_bf16.shape
         offs = (torch.arange(G + 1, dtype=torch.int32, device=w_bf16.device) * N)
-        codes, scales, gscale = nvfp4_quantize(w_bf16.reshape(G * N, K), scale_domain=1,
+        codes, scales, gscale = nvfp4_quantize(w_bf16.reshape(G * N, K),
+                                               scale_domain=2 if blocks_2d else 1,
                                                block_rule=block_rule,
                                                group_offsets=offs)
         return cls(codes.view(G, N, K // 2), scales.view(G, N, K // 16), gscale)
@@ -80,7 +82,7 @@ def nvfp4_quantize(x, scale_domain: int = 0, group_offsets=None, amax_in=None,
     codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
     scales = torch.empty((rows, k // 16), dtype=torch.uint8, device=dev)
     ng = 0
-    if scale_domain == 1:
+    if scale_domain in (1, 2):
         _need(group_offsets, (torch.int32,), "group_offsets")
         ng = group_offsets.numel() - 1
         gs = torch.empty(ng, dtype=torch.float32, device=dev)

@@ -70,6 +70,9 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     assert L.nvfp4_quantize(fake, 4, 32, 32, 1, None, 2, None, 0, fake, fake, fake, None) == INVALID
     # k beyond the supported maximum
     assert L.nvfp4_quantize(fake, 4, 32768, 32768, 0, None, 0, None, 0, fake, fake, fake, None) == UNSUPPORTED
+    # 16x16 blocks need rows % 16 == 0 and the standard rule
+    assert L.nvfp4_quantize(fake, 24, 32, 32, 2, fake, 1, None, 0, fake, fake, fake, None) == UNSUPPORTED
+    assert L.nvfp4_quantize(fake, 32, 32, 32, 2, fake, 1, None, 1, fake, fake, fake, None) == UNSUPPORTED
     # unknown block rule
     assert L.nvfp4_quantize(fake, 4, 32, 32, 0, None, 0, None, 3, fake, fake, fake, None) == INVALID
     # misaligned x
