@@ -208,6 +208,18 @@ def main():
             "ms_per_step": wall46 * 1e3 / args.steps, "stage_ms": st46,
             "quantize_permute_gbps": qbytes / (st46["route_quantize"] * 1e-3) / 1e9,
         }
+    # offline weight quantization (a0), once each: 1D blocks and 16x16 blocks
+    wq = {}
+    for name, kw in (("w1_1d", {}), ("w1_2d", {"blocks_2d": True})):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wb = bf(w.w1)
+        torch.cuda.synchronize()
+        e0.record()
+        NvFp4Weights.quantize(wb, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        wq[name] = e0.elapsed_time(e1)
+    result["weight_quantize_ms"] = wq
     if args.cpu_tokens > 0:
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.tokens))
     else:
