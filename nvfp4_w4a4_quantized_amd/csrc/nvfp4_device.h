@@ -73,15 +73,35 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   return __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
-// Wave-wide maximum of a non-negative value held as raw bits (monotonic for
-// non-negative floats).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
-    v = v > o ? v : o;
-  }
+// Wave-wide inclusive scans through DPP lane moves (no LDS round trips):
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the row broadcasts
+// of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).  Every
+// lane of the wave must be active.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v, Op op) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int rl = lane & 15;
+  uint32_t t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  if (rl >= 1) v = op(t, v);
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  if (rl >= 2) v = op(t, v);
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  if (rl >= 4) v = op(t, v);
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  if (rl >= 8) v = op(t, v);
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x142, 0xf, 0xf, false);   // row_bcast:15
+  if ((lane & 31) >= 16) v = op(t, v);
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x143, 0xf, 0xf, false);   // row_bcast:31
+  if (lane >= 32) v = op(t, v);
   return v;
+}
+
+// Wave-wide maximum of a non-negative value held as raw bits (monotonic for
+// non-negative floats), the same in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = wave_incl_scan_dpp(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
 // Encodes 16 consecutive elements (one block) given the block's decode step

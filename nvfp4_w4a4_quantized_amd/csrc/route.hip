@@ -61,19 +61,13 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int
     for (int e = lane; e < E; e += kWave) hist[(int64_t)e * nchunks + chunk] = h[e];
 }
 
-__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v, int lane) {
+  (void)lane;
+  return (int32_t)wave_incl_scan_dpp((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
-__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int32_t y = __shfl_up(v, o, kWave);
-    if (lane >= o) v += y;
-  }
-  return v;
+__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan_i32(v, 0), kWave - 1);
 }
 
 // Single workgroup of kScanThreads.  Wave w handles experts w + 16i, EPW of
@@ -151,7 +145,7 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* hist,
         const int e = e0 + NWAVES * i;
         const int32_t in = wave_incl_scan_i32(x[i], lane);
         if (e < E && c < nchunks) hist[(int64_t)e * nchunks + c] = carry[i] + in - x[i];
-        carry[i] += __shfl(in, kWave - 1, kWave);
+        carry[i] += __builtin_amdgcn_readlane(in, kWave - 1);
       }
     };
 #pragma unroll
