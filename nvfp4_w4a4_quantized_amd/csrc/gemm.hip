@@ -158,11 +158,12 @@ __device__ __noinline__ float swiglu_tail(float g, float u, float p) {
   return (float)(((double)g * eg / (1.0 + eg)) * (double)u * (double)p);
 }
 
-__device__ __forceinline__ float swiglu_fast(float g, float u, float p) {
-  // D is checked to one bf16 ulp; the hardware reciprocal (about 1 ulp of
-  // binary32) is far inside that.
+// silu(g) * up, with the router weight already folded into `up` (a few
+// binary32 roundings; D is checked to one bf16 ulp and the hardware
+// reciprocal, about 1 ulp of binary32, is far inside that)
+__device__ __forceinline__ float swiglu_fast(float g, float up) {
   const float silu = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-  return (silu * u) * p;
+  return silu * up;
 }
 
 // two binary32 -> two bf16 (round to nearest even) in one dword
@@ -419,35 +420,34 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
         const int64_t I = a.inter;
         const int64_t gate0 = nt * (BN / 2) + (int64_t)wave * GC;
         const float p = a.row_prob[rr];
-        uint32_t mx = 0u;
+        const float s = sga * sgb;               // C = ACC * s_ga * s_gb
+        const float sp = s * p;                  // the up half, weighted
+        u16x2_t mx2 = {0, 0};
         if (rv && gate0 < I) {
 #pragma unroll
           for (int c8 = 0; c8 < PL; c8 += 8) {
             const int c = eq * PL + c8;          // column inside the gate half
-            float gv[8], uv[8], dv[8];
+            float gv[8], dv[8];
+            float gmin = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-              gv[i] = (src[c + i] * sga) * sgb;
-              uv[i] = (src[GC + c + i] * sga) * sgb;
-            }
-            float gmin = gv[0];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              dv[i] = swiglu_fast(gv[i], uv[i], p);
+              gv[i] = src[c + i] * s;
+              dv[i] = swiglu_fast(gv[i], src[GC + c + i] * sp);
               gmin = fminf(gmin, gv[i]);
             }
             if (gmin < -80.0f) {
 #pragma unroll
               for (int i = 0; i < 8; ++i)
-                if (gv[i] < -80.0f) dv[i] = swiglu_tail(gv[i], uv[i], p);
+                if (gv[i] < -80.0f) dv[i] = swiglu_tail(gv[i], src[GC + c + i] * s, p);
             }
             uint32_t packed[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               packed[i] = pack_bf16x2(dv[2 * i], dv[2 * i + 1]);
-              const uint32_t m0 = packed[i] & 0x7FFFu, m1 = (packed[i] >> 16) & 0x7FFFu;
-              mx = mx > m0 ? mx : m0;
-              mx = mx > m1 ? mx : m1;
+              const uint32_t mag = packed[i] & 0x7FFF7FFFu;
+              u16x2_t v;
+              __builtin_memcpy(&v, &mag, 4);
+              mx2 = __builtin_elementwise_max(mx2, v);
             }
             const int64_t col = gate0 + c;
             *reinterpret_cast<uint4*>(a.d_out + rr * I + col) =
@@ -455,6 +455,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
             if (a.c_out) {
               float* cg = a.c_out + rr * 2 * I + col;
               float* cu = cg + I;
+              float uv[8];
+#pragma unroll
+              for (int i = 0; i < 8; ++i) uv[i] = src[GC + c + i] * s;
               *reinterpret_cast<float4*>(cg) = make_float4(gv[0], gv[1], gv[2], gv[3]);
               *reinterpret_cast<float4*>(cg + 4) = make_float4(gv[4], gv[5], gv[6], gv[7]);
               *reinterpret_cast<float4*>(cu) = make_float4(uv[0], uv[1], uv[2], uv[3]);
@@ -462,6 +465,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
             }
           }
         }
+        uint32_t mx = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
         // the row's maximum over the wave's four column quarters
         uint32_t other = (uint32_t)__shfl_xor((int)mx, 16, kWave);
         mx = mx > other ? mx : other;
@@ -471,6 +475,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
           atomicMax(reinterpret_cast<uint32_t*>(a.amax) + row, mx << 16);
       } else {
         constexpr int PL = 8 * WN;               // columns per lane
+        const float s = sga * sgb;               // out = ACC * s_ga * s_gb
         const int64_t col0 = nt * BN + (int64_t)wave * 32 * WN + eq * PL;
         if (rv) {
 #pragma unroll
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
             if (col >= N) break;                 // N % 32 == 0: 8-column runs are whole
             float v[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = (src[eq * PL + c8 + i] * sga) * sgb;
+            for (int i = 0; i < 8; ++i) v[i] = src[eq * PL + c8 + i] * s;
             if (EPI == EPI_F32) {
               float* o = static_cast<float*>(a.out) + rr * N + col;
               *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
