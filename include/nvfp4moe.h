@@ -192,8 +192,9 @@ int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const flo
  * w4a4_grouped_gemm_swiglu -- FC1 with the fused router-weighted SwiGLU
  * epilogue and the row amax of its output.
  * [miniTE] §5.3 (weighted SwiGLU with row amax: the statistic of exactly the
- * tensor FC2 quantizes), §5.4 ("C = gate | up", "D = act(gate, up) x prob",
- * "reduce D amax concurrently").
+ * tensor FC2 quantizes), §5.4 (the pre-activation output is the gate half
+ * followed by the up half; the activation output is weighted by the routing
+ * probability; its amax is reduced in the same epilogue).
  *
  * B holds the fused [G, 2*inter, k] gate|up weights (gate = rows [0, inter)).
  * For every routed row r and j < inter, with C the grouped GEMM above:

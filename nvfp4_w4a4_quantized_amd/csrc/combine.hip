@@ -1,7 +1,8 @@
 // combine.hip -- unpermute the expert outputs back to token order:
 // y[t, :] = bf16(sum_j Y[dst_row[t, j], :]), j ascending, fp32 accumulation.
-// The router weight was applied before FC2 (miniTE Technical Report §5.4,
-// "D = act(gate, up) x prob"), so this is a plain sum.  One workgroup per
+// The router weight was applied before FC2 (miniTE Technical Report §5.4:
+// the activated gate/up product is multiplied by the routing probability),
+// so this is a plain sum.  One workgroup per
 // token; each thread owns 8 consecutive columns (16-byte loads and stores).
 // The fixed j order makes the result bitwise reproducible.
 #include "launch.h"

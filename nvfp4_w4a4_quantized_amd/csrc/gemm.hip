@@ -9,8 +9,9 @@
 // and lies in [2^-10, 2688], so the product is exact in fp16; the f16 x f16
 // products are exact in the fp32 accumulator of v_mfma_f32_32x32x16_f16.  The
 // per-row and per-expert FP32 outer scales are applied once per output in
-// the epilogue (miniTE §5.4 "ACC x alpha_a[m] (x alpha_b[n])"; miniTE summary
-// §4.2 "FP32 epilogue rescaling").
+// the epilogue (miniTE Technical Report §5.4: the accumulator is multiplied
+// by the per-row factor and, optionally, a per-column one; miniTE summary
+// §4.2: FP32 rescaling after the block-scaled product).
 //
 // Structure: see the kernel comment below.  Group boundaries come from the
 // device offsets: every workgroup derives its (group, m-tile) from a

@@ -171,7 +171,7 @@ static void pack_block(int64_t b, const unsigned codes16[16], uint8_t* codes) {
 
 float orc_quantize_row_with_amax(const uint16_t* x, int64_t k, float amax,
                                  uint8_t* codes, uint8_t* scales) {
-  /* outer (second-level) scale: [miniTE] §5.6 "gs = gamax / 2688" */
+  /* outer (second-level) scale: [miniTE] §5.6 divides the amax by 2688 */
   float s_g = amax / 2688.0f;
   memset(codes, 0, (size_t)(k / 2));
   for (int64_t b = 0; b < k / 16; ++b) {
@@ -276,8 +276,8 @@ int orc_quantize_rule(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
   if (domain == 2) {
     /* per-group outer scale with 16x16 blocks: 16 consecutive rows of a group
      * and 16 consecutive elements share one E4M3 scale, set by the tile
-     * maximum ([miniTE] §2.2 "two-dimensional block-scaled quantization";
-     * [miniTE] App. D2 "2D weight quantization").  Reading: the tile's
+     * maximum ([miniTE] §2.2 and App. D2 compare one- and two-dimensional
+     * block scaling of weights without giving the block shape).  Reading: the tile's
      * maximum maps to 6 exactly as a 1D block's would, every element is
      * encoded with the tile's decode step, and the scale byte is stored in
      * each of the tile's rows so that [rows, k/16] keeps its meaning. */

@@ -64,7 +64,7 @@ uint16_t orc_f64_to_bf16(double v);   /* round-to-nearest-even, finite inputs */
 /* ---- O2-O4: NVFP4 quantization of one row ----------------------------- */
 
 /* Quantizes k bf16 values (k % 16 == 0) given the outer-scale amax:
- *   s_g = fl32(amax / 2688)                        [miniTE] §5.6 "gs = gamax/2688"
+ *   s_g = fl32(amax / 2688)                        [miniTE] §5.6 (outer amax over 2688)
  *   per 16-element block b (along k):
  *     bmax = max |x| over the block
  *     s_b  = 0                     if s_g == 0
@@ -82,7 +82,7 @@ float orc_quantize_row_with_amax(const uint16_t* x, int64_t k, float amax,
  * every block is quantized twice, with its maximum mapped to the E2M1 value
  * 6 and to 4, and keeps the candidate with the smaller block error; ties keep
  * 6.  rule 1 measures the error as a sum of squares, rule 2 as a sum of
- * absolute values ("MSE or MAE").  Readings of the pages (their formula
+ * absolute values (the page allows either).  Readings of the pages (their formula
  * names an FP8 maximum E4M3_4OVER6_MAXVAL without giving it):
  *   s_g   = fl32(amax / 1536), 1536 = 6 * 256: the FP8 maximum is lowered to
  *           256 so that the 4-candidate's block scale (1.5x the 6-candidate's,
@@ -91,8 +91,9 @@ float orc_quantize_row_with_amax(const uint16_t* x, int64_t k, float amax,
  *           d = fl32(s_b * s_g), codes E2M1(fl32(x / d)) as in rule 0;
  *   error = sum over the 16 elements, in order, of e^2 (rule 1) or |e|
  *           (rule 2), e = fl32(x - fl32((q * s_b) * s_g)), in binary32 (the
- *           page's "candidate = fp4_value * fp8_scale * amax / (E2M1_MAXVAL *
- *           E4M3_4OVER6_MAXVAL)" with fp32 error accumulation);
+ *           page's reference candidate: code value times block scale times
+ *           amax over E2M1_MAXVAL * E4M3_4OVER6_MAXVAL, errors summed in
+ *           FP32);
  *   the 4-candidate is kept only if its error is strictly smaller.
  * rule 0 is orc_quantize_row_with_amax.  Returns s_g. */
 float orc_quantize_row_rule(const uint16_t* x, int64_t k, float amax, int rule,
@@ -109,9 +110,9 @@ float orc_row_amax(const uint16_t* x, int64_t k);
  *   domain 0: one outer scale per row (per-token activations:
  *             [miniTE] §2.3, §5.1; [4BIT] "Baseline recipe").
  *   domain 1: one outer scale per group of rows [off[g], off[g+1])
- *             (per-expert weights: [miniTE] §2.2 "per tensor, per expert, or
- *             per row"; [4BIT] "Baseline recipe": one FP32 scale per weight
- *             tensor).
+ *             (per-expert weights: [miniTE] §2.2 lets the recipe pick a tensor,
+ *             expert or row domain; [4BIT] "Baseline recipe": one FP32 scale
+ *             per weight tensor).
  *   domain 2: as domain 1, with 16x16 blocks: 16 consecutive rows of a group
  *             times 16 consecutive elements share one scale, set by the tile
  *             maximum; every group's row count must be a multiple of 16
@@ -191,11 +192,12 @@ int orc_grouped_gemm_at(const uint8_t* a_codes, const uint8_t* a_scales, const f
 
 /* ---- O8: router-weighted SwiGLU and its row amax ---------------------- */
 
-/* C [rows, 2I] fp32 holds gate | up ([miniTE] §5.4 "C = gate | up"):
+/* C [rows, 2I] fp32 holds the gate half then the up half ([miniTE] §5.4):
  *   D[r, j] = bf16(silu(C[r, j]) * C[r, I + j] * prob[r]),  j < I,
- * evaluated in fp64 and rounded once to bf16 ([miniTE] §5.4 "D = act(gate,up)
- * x prob"; §5.3 the weighted SwiGLU output is exactly the FC2 quantizer
- * input).  amax[r] = max_j |D[r, j]| over the bf16 values. */
+ * evaluated in fp64 and rounded once to bf16 ([miniTE] §5.4: the activation
+ * output is weighted by the routing probability; §5.3 the weighted SwiGLU
+ * output is exactly the FC2 quantizer input).  amax[r] = max_j |D[r, j]|
+ * over the bf16 values. */
 void orc_swiglu(const float* c, const float* prob, int64_t rows, int64_t inter,
                 uint16_t* d, float* amax);
 
