@@ -20,8 +20,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def gemm_source_hash() -> str:
-    with open(os.path.join(HERE, "csrc", "gemm.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 of the GEMM source with comments and blank space removed: a
+    record stays valid across comment edits and goes stale on any code change."""
+    with open(os.path.join(HERE, "csrc", "gemm.hip")) as f:
+        src = f.read()
+    code = []
+    for line in src.splitlines():
+        line = line.split("//", 1)[0].strip()
+        if line:
+            code.append(" ".join(line.split()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
 def _per_kernel(path, counter):
