@@ -320,8 +320,11 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   // 32-row blocks of the tile (the others are all padding); substeps 4..7
   // also decode the next stage's A (raw registers loaded one stage earlier)
   // into buffer `nxt`.  Each part of the B registers is reloaded with stage
-  // `bnext` as soon as it has been decoded.
-  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bnext, bool more) {
+  // `bnext` as soon as it has been decoded.  The loads are unconditional
+  // (the last stage re-fetches itself): with a branch around them the
+  // compiler has to assume the short path and waits for the loads just
+  // issued before the A decode.
+  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bnext) {
     constexpr int MV = decltype(mv_c)::value;
     const uint8_t* sb = smem + buf * A_BYTES;
     half2_t bsc[WN][2];
@@ -330,7 +333,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
       bsc[n][0] = e4m3x2_to_half2(bs[n]);
       bsc[n][1] = e4m3x2_to_half2(bs[n] >> 16);
     }
-    if (more) b_load_s(bnext);
+    b_load_s(bnext);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       half8_t fa[MV], fb[WN];
@@ -343,8 +347,10 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
         const _Float16 sc = bsc[n][s / 4][(s / 2) % 2];
         fb[n] = decode8(c, half2_t{sc, sc});
       }
-      if (more && s == 3) b_load_c0(bnext);
-      if (more && s == 7) b_load_c1(bnext);
+      // the scheduler would sink these loads to the end of the stage, where
+      // the next stage waits on them at once: keep them here
+      if (s == 3) { b_load_c0(bnext); __builtin_amdgcn_sched_barrier(0); }
+      if (s == 7) { b_load_c1(bnext); __builtin_amdgcn_sched_barrier(0); }
 #pragma unroll
       for (int m = 0; m < MV; ++m)
 #pragma unroll
@@ -359,8 +365,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   // codes (in registers,
   // loaded one stage earlier) are decoded into the other buffer between the
   // MFMAs of substeps 4-7, after which the registers receive the A codes of
-  // the stage after that.  The tail stages re-fetch the last stage's A into
-  // registers that nothing reads: the loop stays branch-free.
+  // the stage after that.  The tail stages re-fetch the last stage's A and B
+  // into registers that nothing reads: the loop stays branch-free.
   const int64_t nst = K / kKS;
   auto main_loop = [&](auto mv_c) {
     a_load(0);
@@ -373,8 +379,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
     __syncthreads();
     for (int64_t it = 0; it < nst; ++it) {
       const int cur = (int)(it & 1), nxt = cur ^ 1;
+      const int64_t st1 = it + 1 < nst ? it + 1 : nst - 1;
       const int64_t st2 = it + 2 < nst ? it + 2 : nst - 1;
-      compute(mv_c, cur, nxt, it + 1, it + 1 < nst);
+      compute(mv_c, cur, nxt, st1);
       a_load(st2);
       __syncthreads();
     }
