@@ -115,9 +115,13 @@ __device__ __forceinline__ bool locate_mtile(const int32_t* off, int G, int BM, 
 // K order: inside a 128 stage, lane half h covers elements [64h, 64h+64)
 // and substep s takes [64h + 8s, 64h + 8s + 8); A and B use the same order,
 // so the dot products are unchanged.
-// The epilogue goes through LDS, 16 rows at a time, so that each lane
-// finishes contiguous columns of one output row.
+// The epilogue works on the accumulator registers in place: each lane holds
+// one column of 16 rows per 32-row block, and for the SwiGLU tile the gate and
+// up columns of one output column sit in the same lane.
 constexpr int kKS = 128;          // K per stage
+#ifndef NVFP4_VPM
+#define NVFP4_VPM 4
+#endif
 
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2 };
 
@@ -154,7 +158,7 @@ __device__ __forceinline__ bool xcd_remap(int64_t bid, int64_t n, int64_t* logic
 // SwiGLU weighted by the router probability, in binary32; below g = -80
 // binary32 exp(-g) overflows while g e^g u p may still be a normal bf16, so
 // that rare tail is evaluated in binary64.
-__device__ __noinline__ float swiglu_tail(float g, float u, float p) {
+__device__ __forceinline__ float swiglu_tail(float g, float u, float p) {
   const double eg = exp((double)g);
   return (float)(((double)g * eg / (1.0 + eg)) * (double)u * (double)p);
 }
@@ -191,10 +195,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   constexpr int A_BYTES = WM * 8 * 64 * 16;         // fp16 A stage (fragment order)
   constexpr int A_UNITS = BM * 4;                   // quarter rows of 32 elements
   constexpr int APT = A_UNITS / NT;                 // A units per thread
-  constexpr int LD = 32 * WN + 4;                   // fp32 words per epilogue LDS row
   static_assert(A_UNITS % NT == 0, "A stage split across threads");
   static_assert(EPI != EPI_SWIGLU || WN % 2 == 0, "SwiGLU pairs gate and up blocks");
-  static_assert(LD % 64 == 4, "epilogue rows on rotating banks");
+  static_assert(3 * BM * 4 <= 2 * A_BYTES, "epilogue row factors fit the A buffers");
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -316,47 +319,87 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][n][i] = 0.0f;
 
-  // multiplies stage buffer `buf` with the B registers for the first MV
-  // 32-row blocks of the tile (the others are all padding); substeps 4..7
-  // also decode the next stage's A (raw registers loaded one stage earlier)
-  // into buffer `nxt`.  Each part of the B registers is reloaded with stage
-  // `bnext` as soon as it has been decoded.  The loads are unconditional
-  // (the last stage re-fetches itself): with a branch around them the
-  // compiler has to assume the short path and waits for the loads just
-  // issued before the A decode.
-  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bnext) {
-    constexpr int MV = decltype(mv_c)::value;
-    const uint8_t* sb = smem + buf * A_BYTES;
-    half2_t bsc[WN][2];
+  // decoded B operands of the substep about to be multiplied (filled one
+  // substep ahead, across the stage boundary too)
+  half8_t fbc[WN];
+  // the lane's B operands of substep s from the code registers and scales
+  auto b_decode = [&](int s, const half2_t (&bsc)[WN][2], half8_t (&fb)[WN]) {
+#pragma unroll
+    for (int n = 0; n < WN; ++n) {
+      const uint32_t c = s < 4 ? bc0[n][s] : bc1[n][s - 4];
+      const _Float16 sc = bsc[n][s / 4][(s / 2) % 2];
+      fb[n] = decode8(c, half2_t{sc, sc});
+    }
+  };
+  auto b_scales = [&](half2_t (&bsc)[WN][2]) {
 #pragma unroll
     for (int n = 0; n < WN; ++n) {
       bsc[n][0] = e4m3x2_to_half2(bs[n]);
       bsc[n][1] = e4m3x2_to_half2(bs[n] >> 16);
     }
+  };
+
+  // multiplies stage buffer `buf` with the B operands for the first MV
+  // 32-row blocks of the tile (the others are all padding).  Software
+  // pipelined by substep: while the MFMAs of substep s run, the lane reads
+  // the A fragments and decodes the B operands of substep s+1 (at s = 7:
+  // substep 0 of the next stage), and substeps 4..7 decode the next
+  // stage's A (raw registers loaded one stage earlier) into buffer `nxt`.
+  // The B code registers of substeps 0-3 / 4-7 and the scales are reloaded
+  // with stage `bnext` right after their last decode.  The loads are
+  // unconditional (the last stage re-fetches itself): with a branch around
+  // them the compiler has to assume the short path and waits for the loads
+  // just issued before the A decode.
+  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bnext) {
+    constexpr int MV = decltype(mv_c)::value;
+    constexpr int VPM = NVFP4_VPM;                 // VALU per MFMA slot
+    const uint8_t* sb = smem + buf * A_BYTES;
+    auto a_frag = [&](int m, int s) {
+      return *reinterpret_cast<const half8_t*>(sb + ((m * 8 + s) * 64 + aslot(lane, s / 4)) * 16);
+    };
+    half2_t bsc[WN][2];
+    b_scales(bsc);
     b_load_s(bnext);
+    half8_t fa[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) fa[m] = a_frag(m, 0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      half8_t fa[MV], fb[WN];
-#pragma unroll
-      for (int m = 0; m < MV; ++m)
-        fa[m] = *reinterpret_cast<const half8_t*>(sb + ((m * 8 + s) * 64 + aslot(lane, s / 4)) * 16);
-#pragma unroll
-      for (int n = 0; n < WN; ++n) {
-        const uint32_t c = s < 4 ? bc0[n][s] : bc1[n][s - 4];
-        const _Float16 sc = bsc[n][s / 4][(s / 2) % 2];
-        fb[n] = decode8(c, half2_t{sc, sc});
+      half8_t fbn[WN];
+      if (s < 7) {
+        b_decode(s + 1, bsc, fbn);
+      } else {                       // substep 0 of the next stage
+        half2_t bsn[WN][2];
+        b_scales(bsn);
+        b_decode(0, bsn, fbn);
       }
-      // the scheduler would sink these loads to the end of the stage, where
-      // the next stage waits on them at once: keep them here
-      if (s == 3) { b_load_c0(bnext); __builtin_amdgcn_sched_barrier(0); }
-      if (s == 7) { b_load_c1(bnext); __builtin_amdgcn_sched_barrier(0); }
+      // fragment m's registers take fragment m of the next substep as soon
+      // as its MFMAs are issued
 #pragma unroll
-      for (int m = 0; m < MV; ++m)
+      for (int m = 0; m < MV; ++m) {
 #pragma unroll
         for (int n = 0; n < WN; ++n)
-          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[m], fb[n], acc[m][n], 0, 0, 0);
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[m], fbc[n], acc[m][n], 0, 0, 0);
+        if (s < 7) fa[m] = a_frag(m, s + 1);
+      }
       if (s >= 4) a_decode(s - 4, nxt);
+      if (s == 2) b_load_c0(bnext);  // substeps 0-3 decoded
+      if (s == 6) b_load_c1(bnext);  // substeps 4-7 decoded
+#pragma unroll
+      for (int n = 0; n < WN; ++n) fbc[n] = fbn[n];
+      // issue order: each MFMA followed by a share of the decode arithmetic,
+      // which runs in the MFMA's shadow, and the fragment reads in between
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+#pragma unroll
+        for (int n = 0; n < WN; ++n) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+        }
+        if (s < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -373,6 +416,11 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
     b_load_s(0);
     b_load_c0(0);
     b_load_c1(0);
+    {
+      half2_t bsc[WN][2];
+      b_scales(bsc);
+      b_decode(0, bsc, fbc);
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) a_decode(c, 0);
     a_load(nst > 1 ? 1 : 0);
@@ -397,115 +445,152 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
     default: main_loop(std::integral_constant<int, WM>{}); break;
   }
 
-  // ---- epilogue through LDS, 16 rows at a time (each wave its own region,
-  // after the loop's last barrier nothing reads the A buffers).
-  // acc[m][n][r] is C[32m + 8(r/4) + 4(lane/32) + r%4][32n + lane%32] of
-  // this wave's tile; rows 16hh.. 16hh+15 come from r in [8hh, 8hh+8).
-  float* ep = reinterpret_cast<float*>(smem) + wave * 16 * LD;
+  // ---- epilogue straight from the accumulators: acc[m][n][r] holds
+  // C[32m + 8(r/4) + 4h + r%4][32n + l32] of this wave's tile (h = lane/32,
+  // l32 = lane%32).  The per-row factors go through LDS once (after the
+  // loop's last barrier nothing reads the A buffers).  For 16-bit outputs
+  // neighbouring lanes swap one value per row pair, so that each lane
+  // stores two adjacent columns of one row as one dword.
+  float* rfac = reinterpret_cast<float*>(smem);  // [BM] s_ga*s_gb, [BM] times p, [BM] p
   const float sgb = a.b_gscale[g];
-  const int er = lane & 15;                     // row of the 16 this lane finishes
-  const int eq = lane >> 4;                     // which quarter of the columns
+  if (tid < BM) {
+    const int64_t row = row0 + tid;
+    const int64_t rr = row < row1 ? row : row1 - 1;
+    const float s = a.a_gscale[rr] * sgb;         // C = ACC * s_ga * s_gb
+    rfac[tid] = s;
+    if (EPI == EPI_SWIGLU) {
+      const float p = a.row_prob[rr];
+      rfac[BM + tid] = s * p;                     // the up half, weighted
+      rfac[2 * BM + tid] = p;
+    }
+  }
+  __syncthreads();
+  const bool odd = (lane & 1) != 0;
+  // the row (inside the tile) of accumulator element r of 32-row block m
+  auto trow = [&](int m, int r) { return 32 * m + 8 * (r / 4) + 4 * half + (r % 4); };
+  // pairs lanes 2i and 2i+1: of the rows of elements (r0, r0 + 1) the even
+  // lane keeps the first and the odd lane the second, both as the bf16 pair
+  // (column 2i, column 2i+1)
+  auto pair_bf16 = [&](float v0, float v1) {
+    const float give = odd ? v0 : v1;
+    const float got = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, give), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    return odd ? pack_bf16x2(got, v1) : pack_bf16x2(v0, got);
+  };
 #pragma unroll
   for (int m = 0; m < WM; ++m) {
+    if (m >= mv) continue;
+    float sv[16];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      if (m < mv) {
+    for (int q = 0; q < 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4*>(rfac + 32 * m + 8 * q + 4 * half);
+      sv[4 * q] = t.x; sv[4 * q + 1] = t.y; sv[4 * q + 2] = t.z; sv[4 * q + 3] = t.w;
+    }
+    if (EPI == EPI_SWIGLU) {
+      constexpr int HALF = WN / 2;
+      const int64_t I = a.inter;
+      const int64_t gate0 = nt * (BN / 2) + (int64_t)wave * 32 * HALF;
+      float spv[16];
 #pragma unroll
-        for (int n = 0; n < WN; ++n)
-#pragma unroll
-          for (int r = 8 * hh; r < 8 * hh + 8; ++r)
-            ep[(8 * (r / 4 - 2 * hh) + 4 * half + (r % 4)) * LD + 32 * n + l32] = acc[m][n][r];
+      for (int q = 0; q < 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(rfac + BM + 32 * m + 8 * q + 4 * half);
+        spv[4 * q] = t.x; spv[4 * q + 1] = t.y; spv[4 * q + 2] = t.z; spv[4 * q + 3] = t.w;
       }
-      __syncthreads();                           // the rows are in LDS
-      const int64_t row = row0 + 32 * m + 16 * hh + er;
-      const bool rv = row < row1;
-      const int64_t rr = rv ? row : row1 - 1;
-      const float sga = a.a_gscale[rr];
-      const float* src = ep + er * LD;
-      if (EPI == EPI_SWIGLU) {
-        constexpr int GC = 16 * WN;              // gate columns of this wave
-        constexpr int PL = GC / 4;               // gate columns per lane
-        const int64_t I = a.inter;
-        const int64_t gate0 = nt * (BN / 2) + (int64_t)wave * GC;
-        const float p = a.row_prob[rr];
-        const float s = sga * sgb;               // C = ACC * s_ga * s_gb
-        const float sp = s * p;                  // the up half, weighted
-        u16x2_t mx2 = {0, 0};
-        if (rv && gate0 < I) {
+      uint32_t rmax[8];                          // |D| maxima of this lane's rows (bf16 bits)
 #pragma unroll
-          for (int c8 = 0; c8 < PL; c8 += 8) {
-            const int c = eq * PL + c8;          // column inside the gate half
-            float gv[8], dv[8];
-            float gmin = 0.0f;
+      for (int t = 0; t < 8; ++t) rmax[t] = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              gv[i] = src[c + i] * s;
-              dv[i] = swiglu_fast(gv[i], src[GC + c + i] * sp);
-              gmin = fminf(gmin, gv[i]);
-            }
-            if (gmin < -80.0f) {
+      for (int n = 0; n < HALF; ++n) {
+        if (gate0 + 32 * n >= I) break;          // inter % 64 == 0: 32-column blocks are whole
+        float dv[16];
+        float gmin = 0.0f;
 #pragma unroll
-              for (int i = 0; i < 8; ++i)
-                if (gv[i] < -80.0f) dv[i] = swiglu_tail(gv[i], src[GC + c + i] * s, p);
-            }
-            uint32_t packed[4];
+        for (int r = 0; r < 16; ++r) {
+          const float gv = acc[m][n][r] * sv[r];
+          dv[r] = swiglu_fast(gv, acc[m][HALF + n][r] * spv[r]);
+          gmin = fminf(gmin, gv);
+        }
+        if (gmin < -80.0f) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              packed[i] = pack_bf16x2(dv[2 * i], dv[2 * i + 1]);
-              const uint32_t mag = packed[i] & 0x7FFF7FFFu;
-              u16x2_t v;
-              __builtin_memcpy(&v, &mag, 4);
-              mx2 = __builtin_elementwise_max(mx2, v);
-            }
-            const int64_t col = gate0 + c;
-            *reinterpret_cast<uint4*>(a.d_out + rr * I + col) =
-                make_uint4(packed[0], packed[1], packed[2], packed[3]);
-            if (a.c_out) {
-              float* cg = a.c_out + rr * 2 * I + col;
-              float* cu = cg + I;
-              float uv[8];
-#pragma unroll
-              for (int i = 0; i < 8; ++i) uv[i] = src[GC + c + i] * s;
-              *reinterpret_cast<float4*>(cg) = make_float4(gv[0], gv[1], gv[2], gv[3]);
-              *reinterpret_cast<float4*>(cg + 4) = make_float4(gv[4], gv[5], gv[6], gv[7]);
-              *reinterpret_cast<float4*>(cu) = make_float4(uv[0], uv[1], uv[2], uv[3]);
-              *reinterpret_cast<float4*>(cu + 4) = make_float4(uv[4], uv[5], uv[6], uv[7]);
-            }
+          for (int r = 0; r < 16; ++r) {
+            const float gv = acc[m][n][r] * sv[r];
+            if (gv < -80.0f) dv[r] = swiglu_tail(gv, acc[m][HALF + n][r] * sv[r], rfac[2 * BM + trow(m, r)]);
           }
         }
-        uint32_t mx = mx2[0] > mx2[1] ? mx2[0] : mx2[1];
-        // the row's maximum over the wave's four column quarters
-        uint32_t other = (uint32_t)__shfl_xor((int)mx, 16, kWave);
-        mx = mx > other ? mx : other;
-        other = (uint32_t)__shfl_xor((int)mx, 32, kWave);
-        mx = mx > other ? mx : other;
-        if (rv && eq == 0 && mx != 0u)
-          atomicMax(reinterpret_cast<uint32_t*>(a.amax) + row, mx << 16);
-      } else {
-        constexpr int PL = 8 * WN;               // columns per lane
-        const float s = sga * sgb;               // out = ACC * s_ga * s_gb
-        const int64_t col0 = nt * BN + (int64_t)wave * 32 * WN + eq * PL;
-        if (rv) {
+        const int64_t colp = gate0 + 32 * n + (l32 & ~1);
 #pragma unroll
-          for (int c8 = 0; c8 < PL; c8 += 8) {
-            const int64_t col = col0 + c8;
-            if (col >= N) break;                 // N % 32 == 0: 8-column runs are whole
-            float v[8];
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t pk = pair_bf16(dv[2 * t], dv[2 * t + 1]);
+          const int64_t row = row0 + trow(m, 2 * t) + (odd ? 1 : 0);
+          if (row < row1) *reinterpret_cast<uint32_t*>(a.d_out + row * I + colp) = pk;
+          const uint32_t mag = pk & 0x7FFF7FFFu;
+          const uint32_t m16 = (mag & 0xFFFFu) > (mag >> 16) ? (mag & 0xFFFFu) : (mag >> 16);
+          rmax[t] = rmax[t] > m16 ? rmax[t] : m16;
+        }
+        if (a.c_out) {
+          const int64_t cg = gate0 + 32 * n + l32;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = src[eq * PL + c8 + i] * s;
-            if (EPI == EPI_F32) {
-              float* o = static_cast<float*>(a.out) + rr * N + col;
-              *reinterpret_cast<float4*>(o) = make_float4(v[0], v[1], v[2], v[3]);
-              *reinterpret_cast<float4*>(o + 4) = make_float4(v[4], v[5], v[6], v[7]);
-            } else {
-              uint16_t* o = static_cast<uint16_t*>(a.out) + rr * N + col;
-              *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = row0 + trow(m, r);
+            if (row < row1) {
+              a.c_out[row * 2 * I + cg] = acc[m][n][r] * sv[r];
+              a.c_out[row * 2 * I + I + cg] = acc[m][HALF + n][r] * sv[r];
             }
           }
         }
       }
-      __syncthreads();                           // rows consumed before they are overwritten
+      // row maxima over the wave's columns: the 16 lanes of one parity in a
+      // lane half share rows; three halving exchanges (lane bits 4, 3, 2)
+      // leave lane bits (4,3,2) = t's bits, a last one over bit 1 completes it
+      const int b4 = (lane >> 4) & 1, b3 = (lane >> 3) & 1, b2 = (lane >> 2) & 1;
+      auto umax = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+      uint32_t v4[4], v2[2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t give = b4 ? rmax[j] : rmax[4 + j];
+        const uint32_t got = (uint32_t)__builtin_amdgcn_ds_swizzle((int)give, 0x401F);   // lane ^ 16
+        v4[j] = umax(b4 ? rmax[4 + j] : rmax[j], got);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t give = b3 ? v4[j] : v4[2 + j];
+        const uint32_t got = (uint32_t)__builtin_amdgcn_ds_swizzle((int)give, 0x201F);   // lane ^ 8
+        v2[j] = umax(b3 ? v4[2 + j] : v4[j], got);
+      }
+      uint32_t mx;
+      {
+        const uint32_t give = b2 ? v2[0] : v2[1];
+        const uint32_t got = (uint32_t)__builtin_amdgcn_ds_swizzle((int)give, 0x101F);     // lane ^ 4
+        mx = umax(b2 ? v2[1] : v2[0], got);
+      }
+      mx = umax(mx, (uint32_t)__builtin_amdgcn_ds_swizzle((int)mx, 0x081F));               // lane ^ 2
+      const int t = 4 * b4 + 2 * b3 + b2;
+      const int rr = 2 * t + (odd ? 1 : 0);
+      const int64_t row = row0 + 32 * m + 8 * (rr / 4) + 4 * half + (rr % 4);
+      if (((lane >> 1) & 1) == 0 && row < row1 && mx != 0u)
+        atomicMax(reinterpret_cast<uint32_t*>(a.amax) + row, mx << 16);
+    } else {
+#pragma unroll
+      for (int n = 0; n < WN; ++n) {
+        const int64_t col0 = nt * BN + (int64_t)wave * 32 * WN + 32 * n;
+        if (col0 >= N) break;                    // N % 32 == 0: 32-column blocks are whole
+        if (EPI == EPI_F32) {
+          float* o = static_cast<float*>(a.out) + col0 + l32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t row = row0 + trow(m, r);
+            if (row < row1) o[row * N] = acc[m][n][r] * sv[r];
+          }
+        } else {
+          uint16_t* o = static_cast<uint16_t*>(a.out) + col0 + (l32 & ~1);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const uint32_t pk = pair_bf16(acc[m][n][2 * t] * sv[2 * t], acc[m][n][2 * t + 1] * sv[2 * t + 1]);
+            const int64_t row = row0 + trow(m, 2 * t) + (odd ? 1 : 0);
+            if (row < row1) *reinterpret_cast<uint32_t*>(o + row * N) = pk;
+          }
+        }
+      }
     }
   }
 }
@@ -557,9 +642,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.n * a.k / 2 > 0xFFFFFFFFll) return hipErrorInvalidValue;   // 32-bit lane offsets into a group
-  size_t lds = (size_t)2 * WM * 8 * 64 * 16;
-  const size_t epi = (size_t)NW * 16 * (32 * WN + 4) * 4;
-  if (epi > lds) lds = epi;
+  const size_t lds = (size_t)2 * WM * 8 * 64 * 16;   // A double buffer (the epilogue's row factors fit)
   gemm_w4a4_kernel<WM, WN, NW, EPI><<<(unsigned)blocks, 64 * NW, lds, s>>>(a);
   return hipGetLastError();
 }
