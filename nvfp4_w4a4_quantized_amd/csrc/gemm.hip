@@ -53,45 +53,6 @@ __device__ __forceinline__ half8_t decode8(uint32_t c, half2_t sb) {
   return r;
 }
 
-// ---- tile -> group map ---------------------------------------------------
-
-// Finds the group owning global m-tile `mt` (m-tiles are numbered group by
-// group, ceil(rows_g / BM) per group).  Returns false if mt is past the end.
-__device__ __forceinline__ bool locate_mtile(const int32_t* off, int G, int BM, int64_t mt,
-                                             int* g_out, int64_t* row0, int64_t* row1) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int64_t carry = 0;
-  for (int base = 0; base < G; base += kWave) {
-    const int g = base + lane;
-    int64_t cnt = 0;
-    if (g < G) {
-      const int64_t n = (int64_t)off[g + 1] - (int64_t)off[g];
-      cnt = n > 0 ? (n + BM - 1) / BM : 0;
-    }
-    int64_t incl = cnt;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      int64_t y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
-    const int64_t start = carry + incl - cnt;
-    const bool mine = (g < G) && (mt >= start) && (mt < start + cnt);
-    const uint64_t hit = __ballot(mine);
-    if (hit) {
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      const int gg = __shfl(g, src, kWave);
-      const int64_t st = __shfl(start, src, kWave);
-      *g_out = gg;
-      *row0 = (int64_t)off[gg] + (mt - st) * BM;
-      const int64_t end = off[gg + 1];
-      *row1 = (*row0 + BM < end) ? *row0 + BM : end;
-      return true;
-    }
-    carry += __shfl(incl, kWave - 1, kWave);
-  }
-  return false;
-}
-
 // ---- kernel --------------------------------------------------------------
 //
 // Workgroup = NW waves side by side along N, sized so that two workgroups
@@ -125,34 +86,204 @@ constexpr int kKS = 128;          // K per stage
 
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2 };
 
-// Number of BM-row tiles over all groups (the same value in every lane).
-__device__ __forceinline__ int64_t count_mtiles(const int32_t* off, int G, int BM) {
-  const int lane = threadIdx.x & (kWave - 1);
-  int64_t total = 0;
-  for (int base = 0; base < G; base += kWave) {
-    const int g = base + lane;
-    int64_t cnt = 0;
-    if (g < G) {
-      const int64_t n = (int64_t)off[g + 1] - (int64_t)off[g];
-      cnt = n > 0 ? (n + BM - 1) / BM : 0;
-    }
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) cnt += __shfl_xor(cnt, o, kWave);
-    total += cnt;
-  }
-  return total;
+// ---- tile schedule ---------------------------------------------------------
+//
+// Tiles are numbered m-tile major with the n-tiles inner, m-tiles group by
+// group (ceil(rows_g / BM) per group).  Workgroups are dealt to the 8 XCDs
+// round robin (workgroup b runs on XCD b % 8), and the tiles are cut into 8
+// contiguous ranges of about equal estimated cost, one per XCD, at m-tile
+// boundaries: consecutive tiles share A rows and, inside a group, B rows,
+// which then stay in that XCD's L2, and no XCD runs dry long before the
+// others.  Workgroup b takes tile b / 8 of its XCD's range.  A tile with v
+// valid 32-row blocks and S K-stages costs kCostFixed + S (kCostStage + v)
+// units: its prologue and epilogue, and the B decode and loads of every
+// stage, do not shrink with its rows.  Counts and costs come from the device
+// offsets (the host never reads them), read once per workgroup for up to
+// 256 groups; the grid is an upper bound and surplus workgroups exit.
+constexpr uint32_t kCostFixed = 24, kCostStage = 2;
+constexpr uint32_t kCostMaxStages = 16;     // keeps the total cost inside 32 bits
+
+__device__ __forceinline__ uint32_t tile_cost(uint32_t v, uint32_t stages) {
+  return kCostFixed + stages * (kCostStage + v);
 }
 
-// Workgroups are dealt to the 8 XCDs round robin (workgroup b runs on XCD
-// b % 8).  Of the n real tiles (counted on the device; the grid is an upper
-// bound), XCD x takes an equal contiguous range: consecutive tiles share A
-// rows and, inside an expert, B rows, which then stay in that XCD's L2.
-// Returns false for the surplus workgroups.
-__device__ __forceinline__ bool xcd_remap(int64_t bid, int64_t n, int64_t* logical) {
-  const int64_t x = bid % 8, pos = bid / 8, q = n / 8, r = n % 8;
-  if (pos >= ((x < r) ? q + 1 : q)) return false;
-  *logical = (x < r) ? x * (q + 1) + pos : r * (q + 1) + (x - r) * q + pos;
-  return true;
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v = wave_incl_scan_dpp(v, [](uint32_t x, uint32_t y) { return x + y; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t v) {
+  return wave_incl_scan_dpp(v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+
+// 256 consecutive groups, four per lane (group base + 64 i + lane)
+struct GroupChunk {
+  uint32_t cnt[4], cost[4], full[4];   // m-tiles, their cost, whole m-tiles
+  int32_t start[4], end[4];            // row range of the group
+};
+
+template <int BM>
+__device__ __forceinline__ void load_chunk(const int32_t* off, int G, uint32_t stages, int base,
+                                           GroupChunk& c) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = base + 64 * i + lane;
+    c.start[i] = g < G ? off[g] : 0;
+    c.end[i] = g < G ? off[g + 1] : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n = (int64_t)c.end[i] - (int64_t)c.start[i];
+    c.cnt[i] = 0; c.cost[i] = 0; c.full[i] = 0;
+    if (n > 0) {
+      const uint32_t f = (uint32_t)(n / BM), rem = (uint32_t)(n % BM);
+      c.full[i] = f;
+      c.cnt[i] = f + (rem ? 1u : 0u);
+      c.cost[i] = f * tile_cost(BM / 32, stages) + (rem ? tile_cost((rem + 31) / 32, stages) : 0u);
+    }
+  }
+}
+
+// Finds workgroup bid's tile: its group *g, rows [*row0, *row1) and n-tile
+// *nt (the same in every lane).  Returns false for a surplus workgroup.
+// Up to 256 groups the offsets are read once and every step works on the
+// lane-resident scans; beyond that each step streams the groups again.
+template <int BM>
+__device__ bool schedule_tile(const int32_t* off, int G, int64_t K, int64_t ntn, int64_t bid,
+                              int* g_out, int64_t* row0, int64_t* row1, int64_t* nt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint32_t stages = (uint32_t)std::min<int64_t>(K / kKS, kCostMaxStages);
+  const uint32_t full_cost = tile_cost(BM / 32, stages);
+  const int x = (int)(bid % 8);
+  const uint32_t pos = (uint32_t)(bid / 8);
+  const uint32_t un = (uint32_t)ntn;
+  // first m-tile of the group seen by this lane whose preceding cost reaches
+  // t, given the group's scans (t <= ik)
+  auto at = [&](uint32_t t, uint32_t ic, uint32_t ik, uint32_t cnt, uint32_t cost, uint32_t full) {
+    const uint32_t ec = ic - cnt, ek = ik - cost;
+    uint32_t j = t > ek ? (t - ek + full_cost - 1) / full_cost : 0u;
+    if (j > full) j = cnt;                       // inside the partial tile: take the next one
+    return ec + j;
+  };
+  auto first_lane = [](uint64_t hit) { return __ffsll((unsigned long long)hit) - 1; };
+  uint32_t f0, f1, mt;
+  if (G <= 256) {
+    GroupChunk c;
+    load_chunk<BM>(off, G, stages, 0, c);
+    const int cols = (G + kWave - 1) / kWave;
+    uint32_t ic[4], ik[4], cc = 0, ck = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < cols) {
+        ic[i] = wave_incl_sum_u32(c.cnt[i]) + cc;
+        ik[i] = wave_incl_sum_u32(c.cost[i]) + ck;
+        cc = (uint32_t)__builtin_amdgcn_readlane((int)ic[i], kWave - 1);
+        ck = (uint32_t)__builtin_amdgcn_readlane((int)ik[i], kWave - 1);
+      } else {
+        ic[i] = cc; ik[i] = ck;
+      }
+    }
+    const uint32_t tiles = cc, total = ck;
+    // XCD x's m-tiles [f0, f1): the first m-tiles whose preceding tiles
+    // cost at least x/8 and (x+1)/8 of the total
+    auto find = [&](uint32_t t) {
+      uint32_t r = tiles;
+      bool got = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t hit = __ballot(i < cols && 64 * i + lane < G && ik[i] >= t);
+        if (!got && hit) {
+          r = (uint32_t)__shfl((int)at(t, ic[i], ik[i], c.cnt[i], c.cost[i], c.full[i]),
+                               first_lane(hit), kWave);
+          got = true;
+        }
+      }
+      return r;
+    };
+    f0 = find((uint32_t)((uint64_t)total * x / 8));
+    f1 = x == 7 ? tiles : find((uint32_t)((uint64_t)total * (x + 1) / 8));
+    const uint32_t logical = f0 * un + pos;
+    if (logical >= f1 * un) return false;
+    mt = logical / un;
+    *nt = logical - mt * un;
+    bool got = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t hit = __ballot(i < cols && 64 * i + lane < G && ic[i] > mt);
+      if (!got && hit) {
+        const int src = first_lane(hit);
+        const int32_t r0 = c.start[i] + (int32_t)(mt - (ic[i] - c.cnt[i])) * BM;
+        const int32_t r1 = std::min<int32_t>(r0 + BM, c.end[i]);
+        *g_out = 64 * i + src;
+        *row0 = __shfl(r0, src, kWave);
+        *row1 = __shfl(r1, src, kWave);
+        got = true;
+      }
+    }
+    return got;
+  }
+  // many groups: stream them for the totals, the range and the tile's group
+  GroupChunk c;
+  uint32_t tiles = 0, total = 0;
+  for (int base = 0; base < G; base += 256) {
+    load_chunk<BM>(off, G, stages, base, c);
+    tiles += wave_sum_u32(c.cnt[0] + c.cnt[1] + c.cnt[2] + c.cnt[3]);
+    total += wave_sum_u32(c.cost[0] + c.cost[1] + c.cost[2] + c.cost[3]);
+  }
+  const uint32_t t0 = (uint32_t)((uint64_t)total * x / 8), t1 = (uint32_t)((uint64_t)total * (x + 1) / 8);
+  bool have0 = false, have1 = (x == 7);
+  f0 = tiles; f1 = tiles;
+  uint32_t carry_c = 0, carry_k = 0;
+  for (int base = 0; base < G && !(have0 && have1); base += 256) {
+    load_chunk<BM>(off, G, stages, base, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = base + 64 * i + lane < G;
+      const uint32_t ic = wave_incl_sum_u32(c.cnt[i]) + carry_c;
+      const uint32_t ik = wave_incl_sum_u32(c.cost[i]) + carry_k;
+      if (!have0) {
+        const uint64_t hit = __ballot(valid && ik >= t0);
+        if (hit) {
+          f0 = (uint32_t)__shfl((int)at(t0, ic, ik, c.cnt[i], c.cost[i], c.full[i]), first_lane(hit), kWave);
+          have0 = true;
+        }
+      }
+      if (!have1) {
+        const uint64_t hit = __ballot(valid && ik >= t1);
+        if (hit) {
+          f1 = (uint32_t)__shfl((int)at(t1, ic, ik, c.cnt[i], c.cost[i], c.full[i]), first_lane(hit), kWave);
+          have1 = true;
+        }
+      }
+      carry_c = (uint32_t)__builtin_amdgcn_readlane((int)ic, kWave - 1);
+      carry_k = (uint32_t)__builtin_amdgcn_readlane((int)ik, kWave - 1);
+    }
+  }
+  const uint32_t logical = f0 * un + pos;
+  if (logical >= f1 * un) return false;
+  mt = logical / un;
+  *nt = logical - mt * un;
+  carry_c = 0;
+  for (int base = 0; base < G; base += 256) {
+    load_chunk<BM>(off, G, stages, base, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ic = wave_incl_sum_u32(c.cnt[i]) + carry_c;
+      const uint64_t hit = __ballot(base + 64 * i + lane < G && ic > mt);
+      if (hit) {
+        const int src = first_lane(hit);
+        const int32_t r0 = c.start[i] + (int32_t)(mt - (ic - c.cnt[i])) * BM;
+        const int32_t r1 = std::min<int32_t>(r0 + BM, c.end[i]);
+        *g_out = base + 64 * i + src;
+        *row0 = __shfl(r0, src, kWave);
+        *row1 = __shfl(r1, src, kWave);
+        return true;
+      }
+      carry_c = (uint32_t)__builtin_amdgcn_readlane((int)ic, kWave - 1);
+    }
+  }
+  return false;
 }
 
 // SwiGLU weighted by the router probability, in binary32; below g = -80
@@ -197,7 +328,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   constexpr int APT = A_UNITS / NT;                 // A units per thread
   static_assert(A_UNITS % NT == 0, "A stage split across threads");
   static_assert(EPI != EPI_SWIGLU || WN % 2 == 0, "SwiGLU pairs gate and up blocks");
-  static_assert(3 * BM * 4 <= 2 * A_BYTES, "epilogue row factors fit the A buffers");
+  static_assert((4 * BM + NW * 2048) * 4 <= 2 * A_BYTES, "epilogue row factors and tail staging fit the A buffers");
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -207,13 +338,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   const int64_t N = a.n;
 
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  int64_t logical;
-  if (!xcd_remap(blockIdx.x, count_mtiles(a.offsets, a.num_groups, BM) * ntn, &logical)) return;
-  const int64_t mt = logical / ntn;
-  const int64_t nt = logical % ntn;
   int g;
-  int64_t row0, row1;
-  if (!locate_mtile(a.offsets, a.num_groups, BM, mt, &g, &row0, &row1)) return;
+  int64_t row0, row1, nt;
+  if (!schedule_tile<BM>(a.offsets, a.num_groups, K, ntn, blockIdx.x, &g, &row0, &row1, &nt)) return;
   g = __builtin_amdgcn_readfirstlane(g);       // wave-uniform: scalar bases below
   row0 = uniform64(row0);
   row1 = uniform64(row1);
@@ -468,6 +595,25 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   const bool odd = (lane & 1) != 0;
   // the row (inside the tile) of accumulator element r of 32-row block m
   auto trow = [&](int m, int r) { return 32 * m + 8 * (r / 4) + 4 * half + (r % 4); };
+  // Stores address rows from a per-lane base row plus a compile-time offset
+  // times a uniform row pitch.  Paired 16-bit stores: lane row
+  // row0 + 4h + (lane & 1), offset 32m + 8(t/2) + 2(t%2) for pair t of
+  // block m; single-column stores: lane row row0 + 4h, offset trow - 4h.
+  const int64_t prow = row0 + 4 * half + (odd ? 1 : 0);
+  const int plim = (int)(row1 - prow);           // pair offsets below this are real rows
+  auto poff = [](int m, int t) { return 32 * m + 8 * (t / 2) + 2 * (t % 2); };
+  // stores dwords v[t] at p + poff(m, t) * pitch, all of them when block m
+  // is whole, else those on real rows
+  auto store_pairs = [&](uint32_t* p, int64_t pitch, int m, const uint32_t (&v)[8]) {
+    if (row0 + 32 * (m + 1) <= row1) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) p[poff(m, t) * pitch] = v[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (poff(m, t) < plim) p[poff(m, t) * pitch] = v[t];
+    }
+  };
   // pairs lanes 2i and 2i+1: of the rows of elements (r0, r0 + 1) the even
   // lane keeps the first and the odd lane the second, both as the bf16 pair
   // (column 2i, column 2i+1)
@@ -511,22 +657,33 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
           gmin = fminf(gmin, gv);
         }
         if (gmin < -80.0f) {
+          // rare: the binary64 tail, in one copy (a loop over the 16
+          // elements staged in this wave's part of the free A buffers)
+          float* tg = rfac + 4 * BM + wave * 2048;  // [16][64] gate, then [16][64] result
 #pragma unroll
+          for (int r = 0; r < 16; ++r) tg[r * 64 + lane] = acc[m][n][r] * sv[r];
+          float* tu = tg + 1024;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tu[r * 64 + lane] = acc[m][HALF + n][r] * sv[r];
+#pragma unroll 1
           for (int r = 0; r < 16; ++r) {
-            const float gv = acc[m][n][r] * sv[r];
-            if (gv < -80.0f) dv[r] = swiglu_tail(gv, acc[m][HALF + n][r] * sv[r], rfac[2 * BM + trow(m, r)]);
+            const float gv = tg[r * 64 + lane];
+            if (gv < -80.0f) tu[r * 64 + lane] = swiglu_tail(gv, tu[r * 64 + lane], rfac[2 * BM + trow(m, r)]);
           }
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (tg[r * 64 + lane] < -80.0f) dv[r] = tu[r * 64 + lane];
         }
         const int64_t colp = gate0 + 32 * n + (l32 & ~1);
+        uint32_t pk[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const uint32_t pk = pair_bf16(dv[2 * t], dv[2 * t + 1]);
-          const int64_t row = row0 + trow(m, 2 * t) + (odd ? 1 : 0);
-          if (row < row1) *reinterpret_cast<uint32_t*>(a.d_out + row * I + colp) = pk;
-          const uint32_t mag = pk & 0x7FFF7FFFu;
+          pk[t] = pair_bf16(dv[2 * t], dv[2 * t + 1]);
+          const uint32_t mag = pk[t] & 0x7FFF7FFFu;
           const uint32_t m16 = (mag & 0xFFFFu) > (mag >> 16) ? (mag & 0xFFFFu) : (mag >> 16);
           rmax[t] = rmax[t] > m16 ? rmax[t] : m16;
         }
+        store_pairs(reinterpret_cast<uint32_t*>(a.d_out + prow * I + colp), I / 2, m, pk);
         if (a.c_out) {
           const int64_t cg = gate0 + 32 * n + l32;
 #pragma unroll
@@ -575,20 +732,22 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
         const int64_t col0 = nt * BN + (int64_t)wave * 32 * WN + 32 * n;
         if (col0 >= N) break;                    // N % 32 == 0: 32-column blocks are whole
         if (EPI == EPI_F32) {
-          float* o = static_cast<float*>(a.out) + col0 + l32;
+          const int64_t srow = row0 + 4 * half;
+          float* o = static_cast<float*>(a.out) + srow * N + col0 + l32;
+          const int slim = (int)(row1 - srow);
+          const bool whole = row0 + 32 * (m + 1) <= row1;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t row = row0 + trow(m, r);
-            if (row < row1) o[row * N] = acc[m][n][r] * sv[r];
+            const int off = trow(m, r) - 4 * half;
+            if (whole || off < slim) o[off * N] = acc[m][n][r] * sv[r];
           }
         } else {
-          uint16_t* o = static_cast<uint16_t*>(a.out) + col0 + (l32 & ~1);
+          uint32_t pk[8];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const uint32_t pk = pair_bf16(acc[m][n][2 * t] * sv[2 * t], acc[m][n][2 * t + 1] * sv[2 * t + 1]);
-            const int64_t row = row0 + trow(m, 2 * t) + (odd ? 1 : 0);
-            if (row < row1) *reinterpret_cast<uint32_t*>(o + row * N) = pk;
-          }
+          for (int t = 0; t < 8; ++t)
+            pk[t] = pair_bf16(acc[m][n][2 * t] * sv[2 * t], acc[m][n][2 * t + 1] * sv[2 * t + 1]);
+          store_pairs(reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + prow * N + col0 + (l32 & ~1)),
+                      N / 2, m, pk);
         }
       }
     }
@@ -636,9 +795,15 @@ template <int WM, int WN, int NW, int EPI>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   constexpr int BM = 32 * WM, BN = 32 * WN * NW;
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (a.n + BN - 1) / BN;
-  // upper bound on the m-tiles of all groups: sum ceil(n_g/BM) <= cap/BM + G
+  // upper bound on the m-tiles of all groups: sum ceil(n_g/BM) <= cap/BM + G.
+  // An XCD's range costs at most a 1/8 share of the total plus one m-tile,
+  // and an m-tile costs between tile_cost(1) and tile_cost(WM), which bounds
+  // its m-tiles; the grid gives every XCD that many positions.
   const int64_t mtiles = (a.rows_cap + BM - 1) / BM + a.num_groups;
-  const int64_t blocks = mtiles * ntn;
+  const int64_t st = std::min<int64_t>(a.k / kKS, kCostMaxStages);
+  const int64_t cmax = kCostFixed + st * (kCostStage + WM), cmin = kCostFixed + st * (kCostStage + 1);
+  const int64_t per_xcd = (cmax * (mtiles + 8) + 8 * cmin - 1) / (8 * cmin) + 1;
+  const int64_t blocks = 8 * per_xcd * ntn;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.n * a.k / 2 > 0xFFFFFFFFll) return hipErrorInvalidValue;   // 32-bit lane offsets into a group

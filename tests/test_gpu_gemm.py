@@ -60,6 +60,22 @@ def test_plain_fp32_full_compare(shape):
     assert np.array_equal(gpu_t[r0:r1].view(np.uint32), gpu[r0:r1].view(np.uint32))
 
 
+def test_many_groups_full_compare():
+    """More groups than one 256-group chunk of the tile schedule, with empty,
+    tiny and multi-tile groups (every tile assigned once)."""
+    rng = np.random.default_rng(17)
+    G, n, k = 300, 64, 128
+    sizes = rng.integers(0, 12, G)
+    sizes[rng.integers(0, G, 5)] = [0, 129, 300, 1, 255]
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(offs[-1])
+    A, W = _operands(rng, rows, G, n, k)
+    say("gemm many groups", G, rows, n, k)
+    gpu = _run_plain(A, W, offs)
+    ref, bound = O.grouped_gemm(*A, *W, offs, with_bound=True)
+    assert_gemm_close(gpu, ref, bound, "many groups")
+
+
 def test_pack_weights_is_the_documented_permutation():
     """nvfp4_pack_weights against the byte map stated in the header, written
     out here with numpy index arithmetic."""
