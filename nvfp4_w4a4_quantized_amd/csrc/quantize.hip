@@ -99,10 +99,18 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
 __global__ __launch_bounds__(256) void quantize_blocks_kernel(QuantRowsArgs a) {
   const uint32_t nb = (uint32_t)(a.k / 16);
   const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  if (i >= (uint64_t)a.rows * nb) return;
-  const uint32_t row = (uint32_t)i / nb, b = (uint32_t)i - row * nb;
-  const float amax = a.amax_kind == 1 ? a.amax_in[row]
-                                      : a.amax_in[find_group(a.group_offsets, a.num_groups, row)];
+  const uint64_t total = (uint64_t)a.rows * nb;
+  const uint32_t row = (uint32_t)(i < total ? i : total - 1) / nb;
+  int g = 0;
+  if (a.amax_kind != 1) {
+    // a wave's rows are consecutive: one uniform search from its first row,
+    // then lanes past a group boundary step forward
+    g = find_group(a.group_offsets, a.num_groups, (int64_t)__builtin_amdgcn_readfirstlane(row));
+    while (g + 1 < a.num_groups && (int64_t)a.group_offsets[g + 1] <= (int64_t)row) ++g;
+  }
+  if (i >= total) return;
+  const uint32_t b = (uint32_t)i - row * nb;
+  const float amax = a.amax_kind == 1 ? a.amax_in[row] : a.amax_in[g];
   const float s_g = outer_scale(amax, a.block_rule);
   const uint16_t* p = a.x + (int64_t)row * a.ld_x + (int64_t)b * 16;
   const u32x4_t u0 = load_stream16(p);
@@ -161,20 +169,42 @@ hipError_t launch_quantize_tiles2d(const QuantRowsArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Group amax: each wave takes kAmaxRows consecutive rows, keeps a per-lane
+// running maximum while the rows stay in one group, and publishes it with one
+// atomic max when the group changes or its rows end.  (One atomic per row
+// serialised on the group's single word: about 0.6 us each.)
+constexpr int kAmaxRows = 64;
+
 template <int BPL>
-__global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* x, int64_t rows, int64_t k,
-                                                         int64_t ld_x, const int32_t* off,
-                                                         int32_t num_groups, uint32_t* amax_bits) {
+__global__ __launch_bounds__(256) void group_amax_kernel(const uint16_t* x, int64_t k, int64_t ld_x,
+                                                         const int32_t* off, int32_t num_groups,
+                                                         uint32_t* amax_bits) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (row >= rows) return;
-  if (row < off[0] || row >= off[num_groups]) return;
-  uint32_t w[BPL][8];
-  uint32_t m = wave_max_u32(load_row_blocks<BPL>(x + row * ld_x, (int)(k / 16), lane, w));
-  if (lane == 0) {
-    int g = find_group(off, num_groups, row);
-    atomicMax(amax_bits + g, m << 16);
+  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  const int64_t last = off[num_groups];
+  const int64_t r0 = (int64_t)off[0] + wid * kAmaxRows;
+  if (r0 >= last) return;
+  const int64_t r1 = r0 + kAmaxRows < last ? r0 + kAmaxRows : last;
+  const int nblocks = (int)(k / 16);
+  int g = find_group(off, num_groups, r0);
+  int64_t gend = off[g + 1];
+  uint32_t m = 0u;
+  auto flush = [&]() {
+    const uint32_t mx = wave_max_u32(m);
+    if (lane == 0 && mx != 0u) atomicMax(amax_bits + g, mx << 16);
+    m = 0u;
+  };
+  for (int64_t r = r0; r < r1; ++r) {
+    while (r >= gend) {                          // next non-empty group (uniform)
+      flush();
+      ++g;
+      gend = off[g + 1];
+    }
+    uint32_t w[BPL][8];
+    const uint32_t mi = load_row_blocks<BPL>(x + r * ld_x, nblocks, lane, w);
+    m = m > mi ? m : mi;
   }
+  flush();
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
@@ -211,13 +241,15 @@ hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t
                              hipStream_t s) {
   fill_u32_kernel<<<(num_groups + 255) / 256, 256, 0, s>>>(amax_bits, num_groups, 0u);
   if (rows == 0) return hipGetLastError();
-  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  // the group rows lie inside [0, rows): an upper bound on the waves needed
+  const int64_t waves = (rows + kAmaxRows - 1) / kAmaxRows;
+  dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   switch (blocks_per_lane(k)) {
-    case 1: group_amax_kernel<1><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
-    case 2: group_amax_kernel<2><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
-    case 4: group_amax_kernel<4><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
-    case 8: group_amax_kernel<8><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
-    case 16: group_amax_kernel<16><<<grid, block, 0, s>>>(x, rows, k, ld_x, off, num_groups, amax_bits); break;
+    case 1: group_amax_kernel<1><<<grid, block, 0, s>>>(x, k, ld_x, off, num_groups, amax_bits); break;
+    case 2: group_amax_kernel<2><<<grid, block, 0, s>>>(x, k, ld_x, off, num_groups, amax_bits); break;
+    case 4: group_amax_kernel<4><<<grid, block, 0, s>>>(x, k, ld_x, off, num_groups, amax_bits); break;
+    case 8: group_amax_kernel<8><<<grid, block, 0, s>>>(x, k, ld_x, off, num_groups, amax_bits); break;
+    case 16: group_amax_kernel<16><<<grid, block, 0, s>>>(x, k, ld_x, off, num_groups, amax_bits); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
