@@ -143,19 +143,22 @@ __global__ __launch_bounds__(256) void quantize_tiles2d_kernel(QuantRowsArgs a) 
     w[0] = u0.x; w[1] = u0.y; w[2] = u0.z; w[3] = u0.w;
     w[4] = u1.x; w[5] = u1.y; w[6] = u1.z; w[7] = u1.w;
   };
+  // the whole tile stays in registers (one pass over HBM): a second read of
+  // the rows no longer hits L2 once the other waves' tiles have gone through
+  uint32_t w[16][8];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) load(r, w[r]);
   uint32_t tbits = 0u;
+#pragma unroll
   for (int r = 0; r < 16; ++r) {
-    uint32_t w[8];
-    load(r, w);
-    const uint32_t m = bf16_absmax_bits(w);
+    const uint32_t m = bf16_absmax_bits(w[r]);
     tbits = tbits > m ? tbits : m;
   }
   const float tmax = __uint_as_float(tbits << 16);
+#pragma unroll
   for (int r = 0; r < 16; ++r) {
-    uint32_t w[8];
-    load(r, w);
     uint32_t sb;
-    const uint2 c = quantize_block16_tile(w, tmax, s_g, &sb);
+    const uint2 c = quantize_block16_tile(w[r], tmax, s_g, &sb);
     *reinterpret_cast<uint2*>(a.codes + (r0 + r) * (a.k / 2) + b * 8) = c;
     a.scales[(r0 + r) * (a.k / 16) + b] = (uint8_t)sb;
   }
