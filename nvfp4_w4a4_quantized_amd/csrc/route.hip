@@ -7,11 +7,12 @@
 // Three launches, no host synchronisation:
 //   1. hist:    one wave per chunk of 64 tokens counts its entries per expert
 //               (LDS histogram) -> hist[e][chunk] (expert-major).
-//   2. scan:    one workgroup; each wave takes whole experts: the expert's
-//               total is a wave sum over its chunk counts, offsets[] are the
-//               exclusive scan of the totals rounded up to `align`, and
-//               base[e][chunk] = offsets[e] + #entries of e in earlier chunks
-//               is a wave scan along the expert's contiguous row.
+//   2. scan:    one workgroup per 8 experts; each derives every expert's
+//               total (a thread per expert sums its contiguous row of chunk
+//               counts) and offsets[] (exclusive scan of the totals rounded
+//               up to `align`), then writes base[e][chunk] = offsets[e] +
+//               #entries of e in earlier chunks for its own experts with
+//               wave scans along their rows.
 //   3. scatter: each wave takes TPW consecutive tokens of one chunk.  It
 //               quantizes a token once (row amax, block scales, codes in
 //               registers) while the next token's row is already loading, and
@@ -26,16 +27,20 @@
 namespace nvfp4 {
 
 constexpr int kChunk = 64;          // tokens per chunk = lanes of one wave
-constexpr int kScanThreads = 1024;
+constexpr int kScanThreads = 256;
 
 int64_t route_num_chunks(int64_t tokens) { return (tokens + kChunk - 1) / kChunk; }
 
-// workspace: base[E][nchunks] int32, counts[E] int32 (each 256-byte aligned)
+// workspace: hist[E][nchunks] int32, base[E][nchunks] int32, counts[E]
+// int32 (each 256-byte aligned)
+static size_t route_matrix_bytes(int64_t tokens, int32_t num_experts) {
+  const size_t m = (size_t)route_num_chunks(tokens) * (size_t)num_experts * 4u;
+  return (m + 255u) & ~(size_t)255u;
+}
+
 size_t route_workspace_bytes(int64_t tokens, int32_t num_experts) {
-  size_t base = (size_t)route_num_chunks(tokens) * (size_t)num_experts * 4u;
-  base = (base + 255u) & ~(size_t)255u;
   size_t counts = ((size_t)num_experts * 4u + 255u) & ~(size_t)255u;
-  return base + counts;
+  return 2 * route_matrix_bytes(tokens, num_experts) + counts;
 }
 
 __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int64_t tokens,
@@ -70,97 +75,88 @@ __device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
   return __builtin_amdgcn_readlane(wave_incl_scan_i32(v, 0), kWave - 1);
 }
 
-// Single workgroup of kScanThreads.  Wave w handles experts w + 16i, EPW of
-// them at a time so that their loads are in flight together; the counts of
-// the first EPW experts' first CPL*64 chunks stay in registers between the
-// totals pass and the base pass (the whole matrix for E <= 128, T <= 8192).
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(int32_t* hist, int64_t nchunks,
-                                                                  int32_t E, int32_t align,
-                                                                  int32_t* counts,
+// Scan: one workgroup per kScanExperts experts.  Every workgroup derives all
+// experts' offsets itself (thread e sums expert e's contiguous row of chunk
+// counts, then a block scan of the padded totals), then writes the chunk
+// bases of its own experts with wave scans along their rows; workgroup 0
+// also publishes offsets[] and counts[].  Many small workgroups instead of
+// one: the per-expert chains run in parallel.
+constexpr int kScanExperts = 8;     // experts whose bases one workgroup writes
+constexpr int kScanMaxE = 1024;     // experts per layer (4 per thread)
+
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t* hist, int32_t* base,
+                                                                  int64_t nchunks, int32_t E,
+                                                                  int32_t align, int32_t* counts,
                                                                   int32_t* offsets) {
   constexpr int NWAVES = kScanThreads / kWave;
-  constexpr int EPW = 8, CPL = 2;
-  __shared__ int32_t cnt[1024];
-  __shared__ int32_t off[1024];
+  constexpr int PER = kScanMaxE / kScanThreads;   // experts per thread in the totals
+  __shared__ int32_t off[kScanMaxE + 1];
   __shared__ int32_t wsum[NWAVES];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  int32_t xv[EPW][CPL];                        // cached counts of the first expert group
-  auto cnt_at = [&](int e, int64_t c) -> int32_t {
-    return (e < E && c < nchunks) ? hist[(int64_t)e * nchunks + c] : 0;
-  };
-  // expert totals
-  for (int e0 = w; e0 < E; e0 += NWAVES * EPW) {
-    const bool first = e0 == w;
-    int32_t s[EPW];
+  // expert totals: expert e = tid + kScanThreads*i, summed over its row
+  int32_t tot[PER], pad[PER];
 #pragma unroll
-    for (int i = 0; i < EPW; ++i) s[i] = 0;
-#pragma unroll
-    for (int cb = 0; cb < CPL; ++cb)
-#pragma unroll
-      for (int i = 0; i < EPW; ++i) {
-        const int32_t v = cnt_at(e0 + NWAVES * i, (int64_t)cb * kWave + lane);
-        if (first) xv[i][cb] = v;
-        s[i] += v;
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid + kScanThreads * i;
+    int32_t t = 0;
+    if (e < E) {
+      const int32_t* row = hist + (int64_t)e * nchunks;
+      int64_t c = 0;
+      if ((nchunks & 3) == 0) {                    // rows are 16-byte aligned
+        for (; c < nchunks; c += 4) {
+          const int4 q = *reinterpret_cast<const int4*>(row + c);
+          t += q.x + q.y + q.z + q.w;
+        }
       }
-    for (int64_t c = (int64_t)CPL * kWave + lane; c < nchunks; c += kWave)
+      for (; c < nchunks; ++c) t += row[c];
+    }
+    tot[i] = t;
+    pad[i] = (t + align - 1) / align * align;
+  }
+  // exclusive scan of the padded totals in expert order: thread-major blocks
+  // (expert tid + 256 i) scanned per i across the workgroup, i in order
+  int32_t carry = 0;
 #pragma unroll
-      for (int i = 0; i < EPW; ++i) s[i] += cnt_at(e0 + NWAVES * i, c);
+  for (int i = 0; i < PER; ++i) {
+    if (kScanThreads * i >= E) break;
+    const int32_t incl = wave_incl_scan_i32(pad[i], lane);
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    int32_t before = carry, all = 0;
 #pragma unroll
-    for (int i = 0; i < EPW; ++i) {
-      const int e = e0 + NWAVES * i;
-      const int32_t t = wave_sum_i32(s[i]);
-      if (e < E && lane == 0) cnt[e] = t;
+    for (int j = 0; j < NWAVES; ++j) {
+      const int32_t v = wsum[j];
+      if (j < w) before += v;
+      all += v;
+    }
+    const int e = tid + kScanThreads * i;
+    if (e < E) off[e] = before + incl - pad[i];
+    carry += all;
+    __syncthreads();                               // wsum is rewritten next round
+  }
+  if (tid == 0) off[E] = carry;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += kScanThreads) offsets[e] = off[e];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + kScanThreads * i;
+      if (e < E) counts[e] = tot[i];
     }
   }
-  __syncthreads();
-  // exclusive scan of padded counts over experts (E <= 1024 = block size)
-  const int32_t v = (tid < E) ? (cnt[tid] + align - 1) / align * align : 0;
-  const int32_t incl = wave_incl_scan_i32(v, lane);
-  if (lane == kWave - 1) wsum[w] = incl;
-  __syncthreads();
-  if (w == 0) {
-    const int32_t ws = (lane < NWAVES) ? wsum[lane] : 0;
-    const int32_t wi = wave_incl_scan_i32(ws, lane);
-    if (lane < NWAVES) wsum[lane] = wi - ws;    // exclusive
-  }
-  __syncthreads();
-  const int32_t excl = incl - v + wsum[w];
-  if (tid < E) {
-    off[tid] = excl;
-    offsets[tid] = excl;
-    counts[tid] = cnt[tid];
-    if (tid == E - 1) offsets[E] = excl + v;
-  }
-  __syncthreads();
-  // base[e][c] = offsets[e] + entries of e in chunks before c
-  for (int e0 = w; e0 < E; e0 += NWAVES * EPW) {
-    const bool first = e0 == w;
-    int32_t carry[EPW];
-#pragma unroll
-    for (int i = 0; i < EPW; ++i) carry[i] = (e0 + NWAVES * i < E) ? off[e0 + NWAVES * i] : 0;
-    auto scan_block = [&](int64_t c0, const int32_t (&x)[EPW]) {
+  // base[e][c] = offsets[e] + entries of e in chunks before c, for this
+  // workgroup's experts (wave w takes experts e0 + w, e0 + w + NWAVES, ...)
+  const int e0 = blockIdx.x * kScanExperts;
+  for (int e = e0 + w; e < e0 + kScanExperts && e < E; e += NWAVES) {
+    const int32_t* row = hist + (int64_t)e * nchunks;
+    int32_t* brow = base + (int64_t)e * nchunks;
+    int32_t run = off[e];
+    for (int64_t c0 = 0; c0 < nchunks; c0 += kWave) {
       const int64_t c = c0 + lane;
-#pragma unroll
-      for (int i = 0; i < EPW; ++i) {
-        const int e = e0 + NWAVES * i;
-        const int32_t in = wave_incl_scan_i32(x[i], lane);
-        if (e < E && c < nchunks) hist[(int64_t)e * nchunks + c] = carry[i] + in - x[i];
-        carry[i] += __builtin_amdgcn_readlane(in, kWave - 1);
-      }
-    };
-#pragma unroll
-    for (int cb = 0; cb < CPL; ++cb) {
-      int32_t x[EPW];
-#pragma unroll
-      for (int i = 0; i < EPW; ++i)
-        x[i] = first ? xv[i][cb] : cnt_at(e0 + NWAVES * i, (int64_t)cb * kWave + lane);
-      scan_block((int64_t)cb * kWave, x);
-    }
-    for (int64_t c0 = (int64_t)CPL * kWave; c0 < nchunks; c0 += kWave) {
-      int32_t x[EPW];
-#pragma unroll
-      for (int i = 0; i < EPW; ++i) x[i] = cnt_at(e0 + NWAVES * i, c0 + lane);
-      scan_block(c0, x);
+      const int32_t x = c < nchunks ? row[c] : 0;
+      const int32_t in = wave_incl_scan_i32(x, lane);
+      if (c < nchunks) brow[c] = run + in - x;
+      run += __builtin_amdgcn_readlane(in, kWave - 1);
     }
   }
 }
@@ -341,14 +337,16 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int64_t nchunks = route_num_chunks(a.tokens);
   const int E = a.num_experts;
-  int32_t* base = static_cast<int32_t*>(a.workspace);
-  size_t base_bytes = ((size_t)nchunks * (size_t)E * 4u + 255u) & ~(size_t)255u;
-  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + base_bytes);
+  const size_t mbytes = route_matrix_bytes(a.tokens, E);
+  int32_t* hist = static_cast<int32_t*>(a.workspace);
+  int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + mbytes);
+  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + 2 * mbytes);
   if (nchunks > 0) {
     route_hist_kernel<<<(unsigned)((nchunks + 3) / 4), 256, 4 * E * sizeof(int32_t), s>>>(
-        a.topk_idx, a.tokens, a.topk, E, nchunks, base);
+        a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
   }
-  route_scan_kernel<<<1, kScanThreads, 0, s>>>(base, nchunks, E, a.align, counts, a.offsets);
+  route_scan_kernel<<<(unsigned)((E + kScanExperts - 1) / kScanExperts), kScanThreads, 0, s>>>(
+      hist, base, nchunks, E, a.align, counts, a.offsets);
   const int bpl = a.x ? blocks_per_lane(a.hidden) : 1;
   if (bpl == 0) return hipErrorInvalidValue;
   const int tpw = tokens_per_wave(bpl);
