@@ -178,7 +178,8 @@ int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
  *                group_offsets[0] >= 0, group_offsets[G] <= rows_cap; empty
  *                groups are legal; the host never reads it
  *   out_dtype    0: float32, 1: bf16 (round-to-nearest-even)
- *   out          [rows_cap, n]; rows outside [off[0], off[G]) are not written
+ *   out          [rows_cap, n], 16-byte aligned; rows outside [off[0], off[G])
+ *                are not written
  * Limits: k % 128 == 0, k <= 16384; n % 32 == 0; 1 <= num_groups <= 1024;
  * one group's B codes (n * k / 2 bytes) below 4 GiB (NVFP4_UNSUPPORTED).
  * ---------------------------------------------------------------------- */

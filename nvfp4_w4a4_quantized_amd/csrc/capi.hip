@@ -183,7 +183,7 @@ int w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const flo
   int st = gemm_args_ok(a_codes, a_scales, a_gscale, rows_cap, b_codes, b_scales, b_gscale,
                         group_offsets, num_groups, k);
   if (st != NVFP4_OK) return st;
-  if (!out || (out_dtype != 0 && out_dtype != 1)) return NVFP4_INVALID_ARGUMENT;
+  if (!out || (out_dtype != 0 && out_dtype != 1) || !aligned(out, 16)) return NVFP4_INVALID_ARGUMENT;
   if (b_layout != 0 && b_layout != 1) return NVFP4_INVALID_ARGUMENT;
   if (n < 32 || n % 32 != 0) return NVFP4_UNSUPPORTED;
   if ((int64_t)num_groups * n >= 0x7FFFFFFFLL) return NVFP4_INVALID_ARGUMENT;

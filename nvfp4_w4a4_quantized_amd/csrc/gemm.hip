@@ -329,6 +329,7 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   static_assert(A_UNITS % NT == 0, "A stage split across threads");
   static_assert(EPI != EPI_SWIGLU || WN % 2 == 0, "SwiGLU pairs gate and up blocks");
   static_assert((4 * BM + NW * 2048) * 4 <= 2 * A_BYTES, "epilogue row factors and tail staging fit the A buffers");
+  static_assert((2 * BM + NW * 32 * 36) * 4 <= 2 * A_BYTES, "bf16 output staging fits the A buffers");
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -727,6 +728,9 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
       if (((lane >> 1) & 1) == 0 && row < row1 && mx != 0u)
         atomicMax(reinterpret_cast<uint32_t*>(a.amax) + row, mx << 16);
     } else {
+      // bf16: the wave's 32 x 32*WN block is staged in LDS (one dword per
+      // column pair) and stored as 16-byte pieces, 8 lanes per row
+      uint32_t* stage = reinterpret_cast<uint32_t*>(smem) + 2 * BM + wave * (32 * 36);
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
         const int64_t col0 = nt * BN + (int64_t)wave * 32 * WN + 32 * n;
@@ -746,8 +750,25 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
 #pragma unroll
           for (int t = 0; t < 8; ++t)
             pk[t] = pair_bf16(acc[m][n][2 * t] * sv[2 * t], acc[m][n][2 * t + 1] * sv[2 * t + 1]);
-          store_pairs(reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.out) + prow * N + col0 + (l32 & ~1)),
-                      N / 2, m, pk);
+          // the pairs go to this wave's [32][72] bf16 staging block (row
+          // pitch 144 bytes), to leave as 16-byte row pieces below
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            stage[(poff(0, t) + 4 * half + (odd ? 1 : 0)) * 36 + 16 * n + (l32 >> 1)] = pk[t];
+        }
+      }
+      if (EPI == EPI_BF16) {
+        static_assert(WN == 2, "the staged block is 64 columns wide");
+        const int64_t colw = nt * BN + (int64_t)wave * 32 * WN;   // the wave's first column
+        if (colw < N) {
+          const int sr = lane >> 3, sc = lane & 7;               // 8 rows x 8 pieces of 16 bytes
+          uint16_t* o = static_cast<uint16_t*>(a.out) + (row0 + 32 * m) * N + colw + 8 * sc;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 8 * q + sr;
+            const uint4 v = *reinterpret_cast<const uint4*>(stage + r * 36 + 4 * sc);
+            if (row0 + 32 * m + r < row1) *reinterpret_cast<uint4*>(o + (int64_t)r * N) = v;
+          }
         }
       }
     }

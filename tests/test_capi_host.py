@@ -90,6 +90,7 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     assert L.w4a4_grouped_gemm(*g, 64, 96, 0, 0, fake, None) == UNSUPPORTED
     assert L.w4a4_grouped_gemm(*g, 48, 128, 0, 0, fake, None) == UNSUPPORTED
     assert L.w4a4_grouped_gemm(*g, 64, 128, 0, 7, fake, None) == INVALID
+    assert L.w4a4_grouped_gemm(*g, 64, 128, 0, 1, C.c_void_p(0x1008), None) == INVALID   # out not 16-byte aligned
     assert L.w4a4_grouped_gemm(*g, 64, 120, 0, 0, fake, None) == INVALID
     # unknown B layout
     assert L.w4a4_grouped_gemm(*g, 64, 128, 2, 0, fake, None) == INVALID
