@@ -124,6 +124,27 @@ def test_group_domain_with_empty_groups():
     assert np.array_equal(host(g), rg)
 
 
+@pytest.mark.parametrize("k", [256, 2048])
+def test_group_domain_across_waves(k):
+    """Groups spanning several 64-row waves of the group-amax reduction and
+    boundaries inside the encoder's waves, with each group's maximum planted
+    in a different wave (the per-wave partial maxima must combine)."""
+    rng = np.random.default_rng(k)
+    rows = 700
+    x = (rng.standard_normal((rows, k)) * 0.5).astype(np.float32)
+    offs = np.array([0, 100, 100, 333, 334, 700], np.int32)
+    for g, r in enumerate([90, 0, 150, 333, 650]):
+        if offs[g] <= r < offs[g + 1]:
+            x[r, (7 * g) % k] = 40.0 + g          # the group's maximum
+    xb = to_bf16_bits(x)
+    say("nvfp4_quantize groups across waves", k)
+    c, s, gsc = _ops().nvfp4_quantize(dev_bf16(xb), scale_domain=1, group_offsets=dev(offs))
+    torch.cuda.synchronize()
+    rc, rs, rg = O.quantize(xb, domain=1, group_offsets=offs)
+    assert np.array_equal(host(gsc), rg)
+    assert np.array_equal(host(s), rs) and np.array_equal(host(c), rc)
+
+
 @pytest.mark.parametrize("wid", [0, 2])
 def test_expert_weights(wid):
     """a0: per-expert weight quantization of the gate|up and down matrices."""
