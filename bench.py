@@ -20,6 +20,20 @@ Prints one JSON line (rank 0):
   cpu_baseline the CPU oracle timed on a bounded token sample of the workload
   four_over_six the same layer with Four-Over-Six (MSE) weights and activations
                (a secondary line; the headline is the standard block rule)
+  secondary    the other measured shapes, each timed the same way:
+               dense_t8192   W4A4 attention projections (per-token quantize +
+                             G=1 GEMM for QKV, then for O-proj), tokens/s and
+                             fraction of the dense fp16 MFMA peak
+               decode_t256   the expert layer at 256 tokens with uniform routing,
+                             bound by streaming the weights: fraction of HBM peak
+                             (three weight copies rotated, 1 GB, so that the
+                             256 MB last-level cache cannot hold them)
+               long_t32768   the expert layer at 32768 tokens, Student-t(3)
+                             activations with outlier channels and zero rows,
+                             Zipf(1.3) routing
+               The expert layers reuse the headline's quantized weights (same
+               shapes and N(0, 0.02) distribution; the timing does not depend on
+               weight values).
 """
 from __future__ import annotations
 
@@ -58,6 +72,9 @@ def parse():
                    help="also time the layer with Four-Over-Six (MSE) weights and activations and "
                         "report it under 'four_over_six' (0 = skip); the headline stays the "
                         "standard rule")
+    p.add_argument("--secondary", type=int, default=1,
+                   help="also time the dense projections and the 256- and 32768-token layers "
+                        "and report them under 'secondary' (0 = skip)")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run plain device copies of this many MiB (a known-size "
                         "kernel for scaling the rocprof FETCH_SIZE/WRITE_SIZE counters)")
@@ -72,6 +89,174 @@ def moe_algorithmic(w):
     # quantize + permute: read x and routing, write codes/scales/s_g and maps
     qbytes = T * H * 2 + T * k * 8 + R * (H // 2 + H // 16 + 4) + R * 8 + T * k * 4
     return fc1, fc2, qbytes
+
+
+def moe_layer_bytes(w):
+    """HBM bytes the layer must move with its intermediates in HBM: the
+    quantize/permute bytes, both weight sets (codes, block scales, outer
+    scales) read once, A1 read by FC1, D written and read back, A2 written and
+    read, the expert rows written by FC2 and read by the combine, y written."""
+    R, H, I, T, E = w.routed_rows, w.hidden, w.inter, w.tokens, w.experts
+    _, _, qbytes = moe_algorithmic(w)
+    weights = E * 2 * I * (H // 2 + H // 16) + E * H * (I // 2 + I // 16) + 2 * E * 4
+    a1 = R * (H // 2 + H // 16 + 4 + 4)          # codes, scales, s_g, router weight
+    d = 2 * R * I * 2 + 2 * R * 4                 # D bf16 and its row amax, each both ways
+    a2 = 2 * R * (I // 2 + I // 16 + 4)
+    rows = 2 * R * H * 2
+    return qbytes + weights + a1 + d + a2 + rows + T * H * 2
+
+
+def run_steps(step, steps, warmup, label, timer_cls=None):
+    """Warm-up, then `steps` uninstrumented calls timed by the host clock
+    around device synchronisations; with timer_cls, the same number of steps
+    again with a fresh timer per step, whose per-stage averages are returned."""
+    import torch
+    log(f"warmup {warmup} ({label})")
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    log(f"timing {steps} steps ({label})")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stages = None
+    if timer_cls is not None:
+        timers = [timer_cls() for _ in range(steps)]
+        log(f"stage events over {steps} more steps ({label})")
+        for i in range(steps):
+            step(timers[i])
+        torch.cuda.synchronize()
+        stages = {n: float(np.mean([t.elapsed_ms()[n] for t in timers])) for n in timer_cls.NAMES}
+        for t in timers:
+            t.close()
+    return wall, stages
+
+
+class _TorchStages:
+    """Events recorded on the current stream between the dense path's calls."""
+    NAMES = ("quantize_qkv", "gemm_qkv", "quantize_o", "gemm_o")
+
+    def __init__(self):
+        import torch
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+
+    def mark(self, i):
+        self.ev[i].record()
+
+    def elapsed_ms(self):
+        return {n: self.ev[i].elapsed_time(self.ev[i + 1]) for i, n in enumerate(self.NAMES)}
+
+    def close(self):
+        pass
+
+
+def bench_dense(args, dev, bf):
+    """W4A4 attention projections, 8192 tokens: per-token NVFP4 quantize of the
+    input, then one G=1 grouped GEMM with bf16 output, for QKV (K=2048,
+    N=5120) and O-proj (K=4096, N=2048) with independent inputs."""
+    import torch
+
+    from nvfp4_w4a4_quantized_amd.ops import NvFp4Weights, nvfp4_quantize, w4a4_grouped_gemm
+    from nvfp4_w4a4_quantized_amd.workloads import make_dense
+    log("generating the dense projections workload")
+    d = make_dense()
+    T = d.tokens
+    flops = 0.0
+    qbytes = 0
+    legs = []
+    for name, xb, wb in d.projections:
+        N, K = wb.shape
+        x = bf(xb)
+        W = NvFp4Weights.quantize(bf(wb).view(1, N, K)).packed()
+        q = (torch.empty((T, K // 2), dtype=torch.uint8, device=dev),
+             torch.empty((T, K // 16), dtype=torch.uint8, device=dev),
+             torch.empty(T, dtype=torch.float32, device=dev))
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        offs = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        legs.append((x, W, q, out, offs))
+        flops += 2.0 * T * N * K
+        qbytes += T * K * 2 + T * (K // 2 + K // 16 + 4)
+    torch.cuda.synchronize()
+
+    def step(timer):
+        for i, (x, W, q, out, offs) in enumerate(legs):
+            if timer:
+                timer.mark(2 * i)
+            nvfp4_quantize(x, out=q)
+            if timer:
+                timer.mark(2 * i + 1)
+            w4a4_grouped_gemm(q[0], q[1], q[2], W, offs, out_dtype=torch.bfloat16, out=out)
+        if timer:
+            timer.mark(4)
+
+    wall, st = run_steps(step, args.steps, args.warmup, "dense projections", _TorchStages)
+    ms = wall * 1e3 / args.steps
+    gemm_ms = st["gemm_qkv"] + st["gemm_o"]
+    return {
+        "workload": d.name, "tokens": T,
+        "projections": "qkv K=2048 N=5120, o_proj K=4096 N=2048 (independent inputs)",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+        "flops_per_step": flops,
+        "effective_tflops": flops / (ms * 1e-3) / 1e12,
+        "frac_of_f16_peak": flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "stage_ms": st,
+        "gemm_only_tflops": flops / (gemm_ms * 1e-3) / 1e12,
+        "gemm_only_frac_of_f16_peak": flops / (gemm_ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "quantize_gbps": qbytes / ((st["quantize_qkv"] + st["quantize_o"]) * 1e-3) / 1e9,
+    }
+
+
+def bench_moe_secondary(args, dev, bf, wid, W1, W2, weight_copies, label):
+    """The expert layer on another token count / routing, with the headline's
+    weights (rotated over `weight_copies` copies)."""
+    import torch
+
+    from nvfp4_w4a4_quantized_amd.ops import (NvFp4Weights, StageTimer, moe_expert_forward,
+                                              moe_expert_forward_workspace_size)
+    from nvfp4_w4a4_quantized_amd.workloads import make_moe
+    log(f"generating workload {label} (routing and activations)")
+    w = make_moe(wid, with_weights=False)
+    x = bf(w.x)
+    idx = torch.from_numpy(w.topk_idx).to(dev)
+    prob = torch.from_numpy(w.topk_prob).to(dev)
+    sets = [(W1, W2)]
+    for _ in range(weight_copies - 1):
+        sets.append(tuple(NvFp4Weights(V.codes.clone(), V.scales.clone(), V.gscale.clone(),
+                                       V.layout) for V in (W1, W2)))
+    ws = torch.empty(moe_expert_forward_workspace_size(w.tokens, w.hidden, w.inter, w.topk,
+                                                       w.experts), dtype=torch.uint8, device=dev)
+    y = torch.empty((w.tokens, w.hidden), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    it = [0]
+
+    def step(timer):
+        V1, V2 = sets[it[0] % len(sets)]
+        it[0] += 1
+        moe_expert_forward(x, idx, prob, w.experts, w.inter, V1, V2, workspace=ws, y=y,
+                           timer=timer)
+
+    wall, st = run_steps(step, args.steps, args.warmup, label, StageTimer)
+    ms = wall * 1e3 / args.steps
+    fc1, fc2, qbytes = moe_algorithmic(w)
+    lbytes = moe_layer_bytes(w)
+    rec = {
+        "workload": w.name, "tokens": w.tokens, "routed_rows": w.routed_rows,
+        "active_experts": w.meta["active_experts"],
+        "cv_rows_per_expert": round(w.meta["cv_rows_per_expert"], 3),
+        "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+        "effective_tflops": (fc1 + fc2) / (ms * 1e-3) / 1e12,
+        "frac_of_f16_peak": (fc1 + fc2) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "layer_bytes": lbytes,
+        "hbm_gbps": lbytes / (ms * 1e-3) / 1e9,
+        "frac_of_hbm_peak": lbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "weight_copies_rotated": weight_copies,
+        "stage_ms": st,
+        "quantize_permute_gbps": qbytes / (st["route_quantize"] * 1e-3) / 1e9,
+    }
+    del ws, y, sets
+    return rec
 
 
 def cpu_baseline(w, n_tokens):
@@ -127,34 +312,14 @@ def main():
     torch.cuda.synchronize()
 
     def timed(W1, W2, rule):
-        def step(timer=None):
+        def step(timer):
             moe_expert_forward(x, idx, prob, w.experts, w.inter, W1, W2, workspace=ws, y=y,
                                timer=timer, act_block_rule=rule)
-
-        log(f"warmup {args.warmup} (block rule {rule})")
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        # throughput: the steps exactly as a caller runs them (no events
-        # between the stages: each recorded event idles the GPU ~5 us)
-        log(f"timing {args.steps} steps (block rule {rule})")
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        # per-stage breakdown (and the FC1 roofline): the same number of steps
-        # again with HIP events recorded on the launch stream between stages
-        timers = [StageTimer() for _ in range(args.steps)]
-        log(f"stage events over {args.steps} more steps (block rule {rule})")
-        for i in range(args.steps):
-            step(timers[i])
-        torch.cuda.synchronize()
-        stages = {n: float(np.mean([t.elapsed_ms()[n] for t in timers])) for n in StageTimer.NAMES}
-        for t in timers:
-            t.close()
-        return wall, stages
+        # throughput from the steps exactly as a caller runs them (no events
+        # between the stages: each recorded event idles the GPU ~5 us); the
+        # per-stage breakdown and the FC1 roofline from the same number of
+        # steps again with HIP events recorded on the launch stream
+        return run_steps(step, args.steps, args.warmup, f"block rule {rule}", StageTimer)
 
     wall, stages = timed(W1, W2, 0)
     ms = wall * 1e3 / args.steps
@@ -221,6 +386,15 @@ def main():
             "ms_per_step": wall46 * 1e3 / args.steps, "stage_ms": st46,
             "quantize_permute_gbps": qbytes / (st46["route_quantize"] * 1e-3) / 1e9,
         }
+    if args.secondary:
+        sec = {"dense_t8192": bench_dense(args, dev, bf)}
+        sec["decode_t256"] = bench_moe_secondary(args, dev, bf, "decode_moe_t256", W1, W2, 3,
+                                                 "decode_t256")
+        sec["long_t32768"] = bench_moe_secondary(args, dev, bf, "long_heavytail_moe_t32768",
+                                                 W1, W2, 1, "long_t32768")
+        for k, v in sec.items():
+            log(f"{k}: {v['value']:.4g} tokens/s, {v['ms_per_step']:.4f} ms/step")
+        result["secondary"] = sec
     # offline weight quantization (a0) of W1: 1D blocks and 16x16 blocks.  Five
     # calls back to back after a warm-up call, so that the launches queue
     # ahead of the GPU and the figure is the GPU time per call (group amax,

@@ -318,18 +318,36 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// LDS of one workgroup: the double-buffered fp16 A stage, which the epilogue
+// reuses for its row factors ([BM] floats for a plain output; three for
+// SwiGLU, plus a [16][64] gate and result staging per wave for the rare
+// binary64 tail) and, for bf16 output, a [32][36]-dword block per wave.
+template <int WM, int NW, int EPI>
+constexpr int gemm_lds_bytes() {
+  constexpr int a_buf = 2 * WM * 8 * 64 * 16;
+  constexpr int epi = EPI == EPI_SWIGLU ? (4 * 32 * WM + NW * 2048) * 4
+                    : EPI == EPI_BF16   ? (2 * 32 * WM + NW * 32 * 36) * 4
+                                        : 32 * WM * 4;
+  return a_buf > epi ? a_buf : epi;
+}
+
+// Waves per SIMD the register budget is sized for: the 128-row tile's 128
+// accumulator registers need the 256-register budget of two waves; the
+// 32-row tile fits 128 registers and runs four.
+template <int WM>
+constexpr int gemm_waves_per_simd() { return WM == 1 ? 4 : 2; }
+
 template <int WM, int WN, int NW, int EPI>
-__global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_kernel(GemmArgs a) {
   constexpr int BM = 32 * WM;
   constexpr int BN = 32 * WN * NW;
   constexpr int NT = 64 * NW;                       // threads
   constexpr int A_BYTES = WM * 8 * 64 * 16;         // fp16 A stage (fragment order)
   constexpr int A_UNITS = BM * 4;                   // quarter rows of 32 elements
   constexpr int APT = A_UNITS / NT;                 // A units per thread
-  static_assert(A_UNITS % NT == 0, "A stage split across threads");
+  static_assert(APT >= 1 && A_UNITS % NT == 0, "A stage split across threads");
   static_assert(EPI != EPI_SWIGLU || WN % 2 == 0, "SwiGLU pairs gate and up blocks");
-  static_assert((4 * BM + NW * 2048) * 4 <= 2 * A_BYTES, "epilogue row factors and tail staging fit the A buffers");
-  static_assert((2 * BM + NW * 32 * 36) * 4 <= 2 * A_BYTES, "bf16 output staging fits the A buffers");
+  static_assert(gemm_lds_bytes<WM, NW, EPI>() <= 160 * 1024, "LDS of one workgroup");
   extern __shared__ __align__(16) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -384,20 +402,24 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
     }
   }
   // one stage of the lane's B columns, reloaded in place a part at a time:
-  // codes of substeps 0-3 (bc0), 4-7 (bc1) and the four block scales (bs)
-  u32x4_t bc0[WN], bc1[WN];
-  uint32_t bs[WN];
-  auto b_load_c0 = [&](int64_t st) {
-#pragma unroll
-    for (int n = 0; n < WN; ++n) bc0[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * b_cstage + bco[n]);
+  // codes of substeps 0-3 (c0), 4-7 (c1) and the four block scales (s).  The
+  // 128-row tile holds one such set; the 32-row tile, whose stages are short,
+  // holds two and keeps the loads of the next two stages in flight.
+  struct BSet {
+    u32x4_t c0[WN], c1[WN];
+    uint32_t s[WN];
   };
-  auto b_load_c1 = [&](int64_t st) {
+  auto b_load_c0 = [&](BSet& b, int64_t st) {
 #pragma unroll
-    for (int n = 0; n < WN; ++n) bc1[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * b_cstage + b_c1 + bco[n]);
+    for (int n = 0; n < WN; ++n) b.c0[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * b_cstage + bco[n]);
   };
-  auto b_load_s = [&](int64_t st) {
+  auto b_load_c1 = [&](BSet& b, int64_t st) {
 #pragma unroll
-    for (int n = 0; n < WN; ++n) bs[n] = *reinterpret_cast<const uint32_t*>(b_sbase + st * b_sstage + bso[n]);
+    for (int n = 0; n < WN; ++n) b.c1[n] = *reinterpret_cast<const u32x4_t*>(b_cbase + st * b_cstage + b_c1 + bco[n]);
+  };
+  auto b_load_s = [&](BSet& b, int64_t st) {
+#pragma unroll
+    for (int n = 0; n < WN; ++n) b.s[n] = *reinterpret_cast<const uint32_t*>(b_sbase + st * b_sstage + bso[n]);
   };
 
   // 16-byte slot of MFMA lane l in an A fragment block of substeps 4sq..4sq+3:
@@ -451,34 +473,36 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   // substep ahead, across the stage boundary too)
   half8_t fbc[WN];
   // the lane's B operands of substep s from the code registers and scales
-  auto b_decode = [&](int s, const half2_t (&bsc)[WN][2], half8_t (&fb)[WN]) {
+  auto b_decode = [&](const BSet& b, int s, const half2_t (&bsc)[WN][2], half8_t (&fb)[WN]) {
 #pragma unroll
     for (int n = 0; n < WN; ++n) {
-      const uint32_t c = s < 4 ? bc0[n][s] : bc1[n][s - 4];
+      const uint32_t c = s < 4 ? b.c0[n][s] : b.c1[n][s - 4];
       const _Float16 sc = bsc[n][s / 4][(s / 2) % 2];
       fb[n] = decode8(c, half2_t{sc, sc});
     }
   };
-  auto b_scales = [&](half2_t (&bsc)[WN][2]) {
+  auto b_scales = [&](const BSet& b, half2_t (&bsc)[WN][2]) {
 #pragma unroll
     for (int n = 0; n < WN; ++n) {
-      bsc[n][0] = e4m3x2_to_half2(bs[n]);
-      bsc[n][1] = e4m3x2_to_half2(bs[n] >> 16);
+      bsc[n][0] = e4m3x2_to_half2(b.s[n]);
+      bsc[n][1] = e4m3x2_to_half2(b.s[n] >> 16);
     }
   };
 
-  // multiplies stage buffer `buf` with the B operands for the first MV
-  // 32-row blocks of the tile (the others are all padding).  Software
-  // pipelined by substep: while the MFMAs of substep s run, the lane reads
-  // the A fragments and decodes the B operands of substep s+1 (at s = 7:
-  // substep 0 of the next stage), and substeps 4..7 decode the next
-  // stage's A (raw registers loaded one stage earlier) into buffer `nxt`.
-  // The B code registers of substeps 0-3 / 4-7 and the scales are reloaded
-  // with stage `bnext` right after their last decode.  The loads are
-  // unconditional (the last stage re-fetches itself): with a branch around
-  // them the compiler has to assume the short path and waits for the loads
-  // just issued before the A decode.
-  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bnext) {
+  // multiplies stage buffer `buf` with the B operands of set `cb` for the
+  // first MV 32-row blocks of the tile (the others are all padding).
+  // Software pipelined by substep: while the MFMAs of substep s run, the
+  // lane reads the A fragments and decodes the B operands of substep s+1 (at
+  // s = 7: substep 0 of the next stage, from set `nb`), and substeps 4..7
+  // decode the next stage's A (raw registers loaded one stage earlier) into
+  // buffer `nxt`.  Set cb's code registers of substeps 0-3 / 4-7 and its
+  // scales are reloaded with stage `bload` right after their last decode
+  // (one set: nb is cb and bload the next stage; two sets: nb holds the next
+  // stage and bload is the one after).  The loads are unconditional (the
+  // last stages re-fetch the last one): with a branch around them the
+  // compiler has to assume the short path and waits for the loads just
+  // issued before the A decode.
+  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bload, BSet& cb, BSet& nb) {
     constexpr int MV = decltype(mv_c)::value;
     constexpr int VPM = NVFP4_VPM;                 // VALU per MFMA slot
     const uint8_t* sb = smem + buf * A_BYTES;
@@ -486,8 +510,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
       return *reinterpret_cast<const half8_t*>(sb + ((m * 8 + s) * 64 + aslot(lane, s / 4)) * 16);
     };
     half2_t bsc[WN][2];
-    b_scales(bsc);
-    b_load_s(bnext);
+    b_scales(cb, bsc);
+    b_load_s(cb, bload);
     half8_t fa[MV];
 #pragma unroll
     for (int m = 0; m < MV; ++m) fa[m] = a_frag(m, 0);
@@ -496,11 +520,11 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
     for (int s = 0; s < 8; ++s) {
       half8_t fbn[WN];
       if (s < 7) {
-        b_decode(s + 1, bsc, fbn);
+        b_decode(cb, s + 1, bsc, fbn);
       } else {                       // substep 0 of the next stage
         half2_t bsn[WN][2];
-        b_scales(bsn);
-        b_decode(0, bsn, fbn);
+        b_scales(nb, bsn);
+        b_decode(nb, 0, bsn, fbn);
       }
       // fragment m's registers take fragment m of the next substep as soon
       // as its MFMAs are issued
@@ -512,8 +536,8 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
         if (s < 7) fa[m] = a_frag(m, s + 1);
       }
       if (s >= 4) a_decode(s - 4, nxt);
-      if (s == 2) b_load_c0(bnext);  // substeps 0-3 decoded
-      if (s == 6) b_load_c1(bnext);  // substeps 4-7 decoded
+      if (s == 2) b_load_c0(cb, bload);  // substeps 0-3 decoded
+      if (s == 6) b_load_c1(cb, bload);  // substeps 4-7 decoded
 #pragma unroll
       for (int n = 0; n < WN; ++n) fbc[n] = fbn[n];
       // issue order: each MFMA followed by a share of the decode arithmetic,
@@ -539,26 +563,45 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   // the stage after that.  The tail stages re-fetch the last stage's A and B
   // into registers that nothing reads: the loop stays branch-free.
   const int64_t nst = K / kKS;
-  auto main_loop = [&](auto mv_c) {
+  BSet bx, by;
+  auto prologue = [&]() {
     a_load(0);
-    b_load_s(0);
-    b_load_c0(0);
-    b_load_c1(0);
+    b_load_s(bx, 0);
+    b_load_c0(bx, 0);
+    b_load_c1(bx, 0);
     {
       half2_t bsc[WN][2];
-      b_scales(bsc);
-      b_decode(0, bsc, fbc);
+      b_scales(bx, bsc);
+      b_decode(bx, 0, bsc, fbc);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) a_decode(c, 0);
     a_load(nst > 1 ? 1 : 0);
     __syncthreads();
+  };
+  auto clamp_st = [&](int64_t st) { return st < nst ? st : nst - 1; };
+  auto main_loop = [&](auto mv_c) {
+    prologue();
     for (int64_t it = 0; it < nst; ++it) {
       const int cur = (int)(it & 1), nxt = cur ^ 1;
-      const int64_t st1 = it + 1 < nst ? it + 1 : nst - 1;
-      const int64_t st2 = it + 2 < nst ? it + 2 : nst - 1;
-      compute(mv_c, cur, nxt, st1);
-      a_load(st2);
+      compute(mv_c, cur, nxt, clamp_st(it + 1), bx, bx);
+      a_load(clamp_st(it + 2));
+      __syncthreads();
+    }
+  };
+  // two B sets, an even number of stages: stages it (set x) and it+1 (set y)
+  // per iteration, each set reloaded two stages ahead
+  auto main_loop2 = [&](auto mv_c) {
+    prologue();
+    b_load_s(by, clamp_st(1));
+    b_load_c0(by, clamp_st(1));
+    b_load_c1(by, clamp_st(1));
+    for (int64_t it = 0; it < nst; it += 2) {
+      compute(mv_c, 0, 1, clamp_st(it + 2), bx, by);
+      a_load(clamp_st(it + 2));
+      __syncthreads();
+      compute(mv_c, 1, 0, clamp_st(it + 3), by, bx);
+      a_load(clamp_st(it + 3));
       __syncthreads();
     }
   };
@@ -566,7 +609,10 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
   // last rows are padding when the group ends inside it.
   const int mv = __builtin_amdgcn_readfirstlane((int)std::min<int64_t>(WM, (row1 - row0 + 31) / 32));
   static_assert(WM <= 4, "main loop instances");
-  switch (mv) {
+  if constexpr (WM == 1) {
+    if (nst % 2 == 0) main_loop2(std::integral_constant<int, 1>{});
+    else main_loop(std::integral_constant<int, 1>{});
+  } else switch (mv) {
     case 1: main_loop(std::integral_constant<int, 1>{}); break;
     case 2: if constexpr (WM >= 2) main_loop(std::integral_constant<int, 2 <= WM ? 2 : 1>{}); break;
     case 3: if constexpr (WM >= 3) main_loop(std::integral_constant<int, 3 <= WM ? 3 : 1>{}); break;
@@ -762,12 +808,15 @@ __global__ __launch_bounds__(64 * NW, 2) void gemm_w4a4_kernel(GemmArgs a) {
         const int64_t colw = nt * BN + (int64_t)wave * 32 * WN;   // the wave's first column
         if (colw < N) {
           const int sr = lane >> 3, sc = lane & 7;               // 8 rows x 8 pieces of 16 bytes
+          // N % 32 == 0: the wave's second 32-column block may lie past N
+          // (its staging was not written), a piece never straddles it
+          const bool col_ok = colw + 8 * sc < N;
           uint16_t* o = static_cast<uint16_t*>(a.out) + (row0 + 32 * m) * N + colw + 8 * sc;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int r = 8 * q + sr;
             const uint4 v = *reinterpret_cast<const uint4*>(stage + r * 36 + 4 * sc);
-            if (row0 + 32 * m + r < row1) *reinterpret_cast<uint4*>(o + (int64_t)r * N) = v;
+            if (col_ok && row0 + 32 * m + r < row1) *reinterpret_cast<uint4*>(o + (int64_t)r * N) = v;
           }
         }
       }
@@ -828,25 +877,45 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.n * a.k / 2 > 0xFFFFFFFFll) return hipErrorInvalidValue;   // 32-bit lane offsets into a group
-  const size_t lds = (size_t)2 * WM * 8 * 64 * 16;   // A double buffer (the epilogue's row factors fit)
+  constexpr size_t lds = (size_t)gemm_lds_bytes<WM, NW, EPI>();
   gemm_w4a4_kernel<WM, WN, NW, EPI><<<(unsigned)blocks, 64 * NW, lds, s>>>(a);
   return hipGetLastError();
 }
 
-// Tile: MFMA blocks per wave (M, N) and waves per workgroup (along N).
+// Tiles: MFMA blocks per wave (M, N) and waves per workgroup (along N).  The
+// 128 x 256 tile serves groups of many rows.  When the groups average at
+// most kSmallTileRows rows (decode-sized batches: a few rows per expert) the
+// 128-row tile would multiply one 32-row block and leave the weight stream
+// at two workgroups per CU; the 32 x 128 tile runs four waves per SIMD, so
+// twice as many weight loads are in flight.
 #ifndef NVFP4_GEMM_TILE
 #define NVFP4_GEMM_TILE 4, 2, 4
 #endif
 #ifndef NVFP4_GEMM_TILE_FC1
 #define NVFP4_GEMM_TILE_FC1 NVFP4_GEMM_TILE
 #endif
+#define NVFP4_GEMM_TILE_SMALL 1, 2, 2
+#ifndef NVFP4_SMALL_TILE_ROWS
+#define NVFP4_SMALL_TILE_ROWS 32
+#endif
+constexpr int64_t kSmallTileRows = NVFP4_SMALL_TILE_ROWS;
+
+bool gemm_uses_small_tile(int64_t rows_cap, int64_t num_groups) {
+  return rows_cap <= kSmallTileRows * num_groups;
+}
 
 hipError_t launch_gemm_plain(const GemmArgs& a, hipStream_t s) {
+  if (gemm_uses_small_tile(a.rows_cap, a.num_groups)) {
+    if (a.out_dtype == 0) return launch_cfg<NVFP4_GEMM_TILE_SMALL, EPI_F32>(a, s);
+    return launch_cfg<NVFP4_GEMM_TILE_SMALL, EPI_BF16>(a, s);
+  }
   if (a.out_dtype == 0) return launch_cfg<NVFP4_GEMM_TILE, EPI_F32>(a, s);
   return launch_cfg<NVFP4_GEMM_TILE, EPI_BF16>(a, s);
 }
 
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s) {
+  if (gemm_uses_small_tile(a.rows_cap, a.num_groups))
+    return launch_cfg<NVFP4_GEMM_TILE_SMALL, EPI_SWIGLU>(a, s);
   return launch_cfg<NVFP4_GEMM_TILE_FC1, EPI_SWIGLU>(a, s);
 }
 

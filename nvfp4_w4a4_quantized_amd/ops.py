@@ -71,23 +71,32 @@ class NvFp4Weights:
 
 
 def nvfp4_quantize(x, scale_domain: int = 0, group_offsets=None, amax_in=None,
-                   block_rule: int = 0):
+                   block_rule: int = 0, out=None):
     """NVFP4 quantization of a bf16 [rows, k] matrix.  Returns (codes, scales,
     global_scales) with global_scales per row (domain 0) or per group (1).
     block_rule 0: every block maximum maps to 6; 1 / 2: Four-Over-Six with the
-    block error measured as a sum of squares / of absolute values."""
+    block error measured as a sum of squares / of absolute values.  `out` may
+    supply the three output tensors (contiguous, of those shapes)."""
     _need(x, _BF16_LIKE, "x")
     rows, k = x.shape
     dev = x.device
-    codes = torch.empty((rows, k // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((rows, k // 16), dtype=torch.uint8, device=dev)
     ng = 0
     if scale_domain in (1, 2):
         _need(group_offsets, (torch.int32,), "group_offsets")
         ng = group_offsets.numel() - 1
-        gs = torch.empty(ng, dtype=torch.float32, device=dev)
+    shapes = ((rows, k // 2), (rows, k // 16), (ng if scale_domain in (1, 2) else rows,))
+    if out is None:
+        codes = torch.empty(shapes[0], dtype=torch.uint8, device=dev)
+        scales = torch.empty(shapes[1], dtype=torch.uint8, device=dev)
+        gs = torch.empty(shapes[2], dtype=torch.float32, device=dev)
     else:
-        gs = torch.empty(rows, dtype=torch.float32, device=dev)
+        codes, scales, gs = out
+        for t, n, d, shp in ((codes, "codes", torch.uint8, shapes[0]),
+                             (scales, "scales", torch.uint8, shapes[1]),
+                             (gs, "global_scales", torch.float32, shapes[2])):
+            _need(t, (d,), n)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{n}: shape {tuple(t.shape)}, expected {shp}")
     if amax_in is not None:
         _need(amax_in, (torch.float32,), "amax_in")
     check(lib().nvfp4_quantize(ptr(x), rows, k, k, scale_domain, ptr(group_offsets), ng,
@@ -147,6 +156,10 @@ def w4a4_grouped_gemm(a_codes, a_scales, a_gscale, b: NvFp4Weights, group_offset
     code = 0 if out_dtype == torch.float32 else 1
     if out is None:
         out = torch.empty((rows_cap, N), dtype=out_dtype, device=a_codes.device)
+    else:
+        _need(out, (out_dtype,), "out")
+        if tuple(out.shape) != (rows_cap, N):
+            raise ValueError(f"out: shape {tuple(out.shape)}, expected {(rows_cap, N)}")
     check(lib().w4a4_grouped_gemm(ptr(a_codes), ptr(a_scales), ptr(a_gscale), rows_cap,
                                   ptr(b.codes), ptr(b.scales), ptr(b.gscale), ptr(group_offsets),
                                   G, N, K, b.layout, code, ptr(out), stream_handle()),

@@ -239,3 +239,89 @@ def test_swiglu_workload(wid):
     rv = bf16_bits_to_f32(dref).astype(np.float64)
     assert np.all(np.abs(dv - rv) <= bf16_ulp(rv) * 1.0001 + 1e-40)
     assert np.array_equal(amax, np.abs(bf16_bits_to_f32(d)).max(axis=1))
+
+
+def _pad_rows(a: np.ndarray, rows: int) -> np.ndarray:
+    """`a` with junk rows appended up to `rows` (the kernel never reads them
+    for the groups' outputs; a larger row capacity selects the 128-row tile)."""
+    fill = 0x5A if a.dtype == np.uint8 else 0.75
+    return np.concatenate([a, np.full((rows - a.shape[0],) + a.shape[1:], fill, a.dtype)])
+
+
+@pytest.mark.parametrize("epi", ["f32", "bf16", "swiglu"])
+@pytest.mark.parametrize("tiled", [False, True])
+@pytest.mark.parametrize("K", [384, 512])
+def test_small_and_large_tiles_agree(epi, tiled, K):
+    """Groups of a few rows (at most 32 on average) run on the 32 x 128 tile;
+    the same problem with its row capacity padded past 32 rows per group runs
+    on the 128 x 256 tile.  Both match the oracle, and each other bit for bit
+    (every output element sees the same MFMA sequence).  K = 384 (3 stages)
+    takes the small tile's one-B-set loop, K = 512 (4 stages) its two-set
+    loop."""
+    rng = np.random.default_rng(31 + K)
+    G = 24
+    n = 256 if epi == "swiglu" else 160
+    sizes = rng.integers(0, 24, G)
+    sizes[[2, 7, 11]] = [0, 70, 33]            # empty, three 32-row blocks, a ragged second block
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    R = int(offs[-1])
+    assert R <= 32 * G
+    A, W = _operands(rng, R, G, n, K, 2.0)
+    prob = rng.random(R).astype(np.float32)
+    big = 32 * G + 1
+    Ab = tuple(_pad_rows(x, big) for x in A)
+    outs = []
+    for tag, AA in (("small tile", A), ("large tile", Ab)):
+        say("gemm tiles", epi, "tiled" if tiled else "row-major", tag)
+        if epi == "swiglu":
+            pp = np.concatenate([prob, np.zeros(AA[0].shape[0] - R, np.float32)])
+            c, d, amax = _swiglu_case(AA, W, offs, pp, tag, tiled)
+            outs.append((c[:R], d[:R], amax[:R]))
+        else:
+            dt = torch.float32 if epi == "f32" else torch.bfloat16
+            outs.append(_run_plain(AA, W, offs, dt, tiled)[:R])
+    ref, bound = O.grouped_gemm(*A, *W, offs, with_bound=True)
+    if epi == "swiglu":
+        (c0, d0, m0), (c1, d1, m1) = outs
+        assert_gemm_close(c0, ref, bound, "swiglu C, small tile")
+        dref, _ = O.swiglu(c0, prob)
+        dv = bf16_bits_to_f32(d0).astype(np.float64)
+        rv = bf16_bits_to_f32(dref).astype(np.float64)
+        assert np.all(np.abs(dv - rv) <= bf16_ulp(rv) * 1.0001 + 1e-40)
+        assert np.array_equal(m0, np.abs(bf16_bits_to_f32(d0)).max(axis=1))
+        assert np.array_equal(c0.view(np.uint32), c1.view(np.uint32))
+        assert np.array_equal(d0, d1) and np.array_equal(m0.view(np.uint32), m1.view(np.uint32))
+    else:
+        g0, g1 = outs
+        if epi == "f32":
+            assert_gemm_close(g0, ref, bound, f"{epi}, small tile")
+        else:
+            err = np.abs(g0.astype(np.float64) - ref)
+            assert np.all(err <= 2.0 ** -10 * bound + 1e-6 + bf16_ulp(ref) * 0.5 * 1.0001)
+        assert np.array_equal(g0.view(np.uint32), g1.view(np.uint32))
+
+
+def test_bf16_output_stays_inside_its_columns():
+    """bf16 output with N % 64 == 32 (the last wave's second 32-column block
+    lies past N) on both tiles: columns >= N of a wider output view and the
+    rows after the buffer stay untouched."""
+    from nvfp4_w4a4_quantized_amd.ops import w4a4_grouped_gemm
+    rng = np.random.default_rng(33)
+    n, K = 96, 256
+    for offs, G in ((np.array([0, 70, 150], np.int32), 2),
+                    (np.array([0, 5, 9, 30, 31, 40], np.int32), 5)):
+        R = int(offs[-1])
+        A, W = _operands(rng, R, G, n, K)
+        say("gemm bf16 guard", n, offs.tolist())
+        # rows R..R+7 of a sentinel buffer follow the output
+        buf = torch.full(((R + 8) * n,), -7.0, dtype=torch.bfloat16, device="cuda")
+        out = buf[:R * n].view(R, n)
+        w4a4_grouped_gemm(dev(A[0]), dev(A[1]), dev(A[2]), _weights(W), dev(offs),
+                          out_dtype=torch.bfloat16, out=out)
+        torch.cuda.synchronize()
+        tail = host(buf[R * n:])
+        assert np.all(bf16_bits_to_f32(tail) == -7.0)
+        ref, bound = O.grouped_gemm(*A, *W, offs, with_bound=True)
+        got = bf16_bits_to_f32(host(out))
+        err = np.abs(got.astype(np.float64) - ref)
+        assert np.all(err <= 2.0 ** -10 * bound + 1e-6 + bf16_ulp(ref) * 0.5 * 1.0001)
