@@ -319,16 +319,20 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 }
 
 // LDS of one workgroup: the double-buffered fp16 A stage, which the epilogue
-// reuses for its row factors ([BM] floats for a plain output; three for
-// SwiGLU, plus a [16][64] gate and result staging per wave for the rare
-// binary64 tail) and, for bf16 output, a [32][36]-dword block per wave.
+// reuses as staging (SwiGLU: a [16][64] gate and result block per wave for
+// the rare binary64 tail; bf16 output: a [32][36]-dword block per wave),
+// followed by the tile's per-row factors, written by the prologue ([BM]
+// floats s_ga*s_gb; SwiGLU also [BM] times the router weight and [BM] the
+// router weight).
+template <int WM, int NW, int EPI>
+constexpr int gemm_rfac_offset() {
+  constexpr int a_buf = 2 * WM * 8 * 64 * 16;
+  constexpr int stage = EPI == EPI_SWIGLU ? NW * 2048 * 4 : EPI == EPI_BF16 ? NW * 32 * 36 * 4 : 0;
+  return a_buf > stage ? a_buf : stage;
+}
 template <int WM, int NW, int EPI>
 constexpr int gemm_lds_bytes() {
-  constexpr int a_buf = 2 * WM * 8 * 64 * 16;
-  constexpr int epi = EPI == EPI_SWIGLU ? (4 * 32 * WM + NW * 2048) * 4
-                    : EPI == EPI_BF16   ? (2 * 32 * WM + NW * 32 * 36) * 4
-                                        : 32 * WM * 4;
-  return a_buf > epi ? a_buf : epi;
+  return gemm_rfac_offset<WM, NW, EPI>() + (EPI == EPI_SWIGLU ? 3 : 1) * 32 * WM * 4;
 }
 
 // Waves per SIMD the register budget is sized for: the 128-row tile's 128
@@ -564,7 +568,18 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
   // into registers that nothing reads: the loop stays branch-free.
   const int64_t nst = K / kKS;
   BSet bx, by;
+  // the tile's per-row factors: loaded with the first stage, written to LDS
+  // once its A has been decoded (the epilogue then starts without a load)
+  float* rfac = reinterpret_cast<float*>(smem + gemm_rfac_offset<WM, NW, EPI>());
+  float rf_sa = 0.0f, rf_p = 0.0f;
+  const float sgb = a.b_gscale[g];
   auto prologue = [&]() {
+    if (tid < BM) {
+      const int64_t row = row0 + tid;
+      const int64_t rr = row < row1 ? row : row1 - 1;
+      rf_sa = a.a_gscale[rr];
+      if (EPI == EPI_SWIGLU) rf_p = a.row_prob[rr];
+    }
     a_load(0);
     b_load_s(bx, 0);
     b_load_c0(bx, 0);
@@ -577,6 +592,14 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
 #pragma unroll
     for (int c = 0; c < 4; ++c) a_decode(c, 0);
     a_load(nst > 1 ? 1 : 0);
+    if (tid < BM) {
+      const float sc = rf_sa * sgb;               // C = ACC * s_ga * s_gb
+      rfac[tid] = sc;
+      if (EPI == EPI_SWIGLU) {
+        rfac[BM + tid] = sc * rf_p;               // the up half, weighted
+        rfac[2 * BM + tid] = rf_p;
+      }
+    }
     __syncthreads();
   };
   auto clamp_st = [&](int64_t st) { return st < nst ? st : nst - 1; };
@@ -625,20 +648,6 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
   // loop's last barrier nothing reads the A buffers).  For 16-bit outputs
   // neighbouring lanes swap one value per row pair, so that each lane
   // stores two adjacent columns of one row as one dword.
-  float* rfac = reinterpret_cast<float*>(smem);  // [BM] s_ga*s_gb, [BM] times p, [BM] p
-  const float sgb = a.b_gscale[g];
-  if (tid < BM) {
-    const int64_t row = row0 + tid;
-    const int64_t rr = row < row1 ? row : row1 - 1;
-    const float s = a.a_gscale[rr] * sgb;         // C = ACC * s_ga * s_gb
-    rfac[tid] = s;
-    if (EPI == EPI_SWIGLU) {
-      const float p = a.row_prob[rr];
-      rfac[BM + tid] = s * p;                     // the up half, weighted
-      rfac[2 * BM + tid] = p;
-    }
-  }
-  __syncthreads();
   const bool odd = (lane & 1) != 0;
   // the row (inside the tile) of accumulator element r of 32-row block m
   auto trow = [&](int m, int r) { return 32 * m + 8 * (r / 4) + 4 * half + (r % 4); };
@@ -706,7 +715,7 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
         if (gmin < -80.0f) {
           // rare: the binary64 tail, in one copy (a loop over the 16
           // elements staged in this wave's part of the free A buffers)
-          float* tg = rfac + 4 * BM + wave * 2048;  // [16][64] gate, then [16][64] result
+          float* tg = reinterpret_cast<float*>(smem) + wave * 2048;  // [16][64] gate, then [16][64] result
 #pragma unroll
           for (int r = 0; r < 16; ++r) tg[r * 64 + lane] = acc[m][n][r] * sv[r];
           float* tu = tg + 1024;
@@ -776,7 +785,7 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
     } else {
       // bf16: the wave's 32 x 32*WN block is staged in LDS (one dword per
       // column pair) and stored as 16-byte pieces, 8 lanes per row
-      uint32_t* stage = reinterpret_cast<uint32_t*>(smem) + 2 * BM + wave * (32 * 36);
+      uint32_t* stage = reinterpret_cast<uint32_t*>(smem) + wave * (32 * 36);
 #pragma unroll
       for (int n = 0; n < WN; ++n) {
         const int64_t col0 = nt * BN + (int64_t)wave * 32 * WN + 32 * n;

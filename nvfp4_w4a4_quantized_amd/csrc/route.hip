@@ -83,18 +83,52 @@ __device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
 // one: the per-expert chains run in parallel.
 constexpr int kScanExperts = 8;     // experts whose bases one workgroup writes
 constexpr int kScanMaxE = 1024;     // experts per layer (4 per thread)
+constexpr int kScanPer = kScanMaxE / kScanThreads;   // experts per thread in the totals
+constexpr int kScanWaves = kScanThreads / kWave;
+
+// Expert offsets from the totals tot[i] of experts tid + kScanThreads*i (a
+// kScanThreads-thread block): off[e] = exclusive scan, in expert order, of
+// the totals rounded up to `align`; off[E] = the padded row count.  The
+// thread-major blocks are scanned per i across the workgroup, i in order.
+// Ends with a barrier (off is then readable by every thread).
+__device__ void block_expert_offsets(const int32_t (&tot)[kScanPer], int32_t E, int32_t align,
+                                     int32_t* off, int32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  int32_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    if (kScanThreads * i >= E) break;
+    const int32_t pad = (tot[i] + align - 1) / align * align;
+    const int32_t incl = wave_incl_scan_i32(pad, lane);
+    if (lane == kWave - 1) wsum[w] = incl;
+    __syncthreads();
+    int32_t before = carry, all = 0;
+#pragma unroll
+    for (int j = 0; j < kScanWaves; ++j) {
+      const int32_t v = wsum[j];
+      if (j < w) before += v;
+      all += v;
+    }
+    const int e = tid + kScanThreads * i;
+    if (e < E) off[e] = before + incl - pad;
+    carry += all;
+    __syncthreads();                               // wsum is rewritten next round
+  }
+  if (tid == 0) off[E] = carry;
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t* hist, int32_t* base,
                                                                   int64_t nchunks, int32_t E,
                                                                   int32_t align, int32_t* counts,
                                                                   int32_t* offsets) {
-  constexpr int NWAVES = kScanThreads / kWave;
-  constexpr int PER = kScanMaxE / kScanThreads;   // experts per thread in the totals
+  constexpr int NWAVES = kScanWaves;
+  constexpr int PER = kScanPer;
   __shared__ int32_t off[kScanMaxE + 1];
   __shared__ int32_t wsum[NWAVES];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   // expert totals: expert e = tid + kScanThreads*i, summed over its row
-  int32_t tot[PER], pad[PER];
+  int32_t tot[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = tid + kScanThreads * i;
@@ -111,31 +145,8 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t*
       for (; c < nchunks; ++c) t += row[c];
     }
     tot[i] = t;
-    pad[i] = (t + align - 1) / align * align;
   }
-  // exclusive scan of the padded totals in expert order: thread-major blocks
-  // (expert tid + 256 i) scanned per i across the workgroup, i in order
-  int32_t carry = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    if (kScanThreads * i >= E) break;
-    const int32_t incl = wave_incl_scan_i32(pad[i], lane);
-    if (lane == kWave - 1) wsum[w] = incl;
-    __syncthreads();
-    int32_t before = carry, all = 0;
-#pragma unroll
-    for (int j = 0; j < NWAVES; ++j) {
-      const int32_t v = wsum[j];
-      if (j < w) before += v;
-      all += v;
-    }
-    const int e = tid + kScanThreads * i;
-    if (e < E) off[e] = before + incl - pad[i];
-    carry += all;
-    __syncthreads();                               // wsum is rewritten next round
-  }
-  if (tid == 0) off[E] = carry;
-  __syncthreads();
+  block_expert_offsets(tot, E, align, off, wsum);
   if (blockIdx.x == 0) {
     for (int e = tid; e <= E; e += kScanThreads) offsets[e] = off[e];
 #pragma unroll
@@ -184,21 +195,82 @@ __device__ __forceinline__ void load_token_row(const uint16_t* xr, int nblocks, 
   }
 }
 
-template <int BPL, int KMAX>
+// Small batches (SMALL: at most kSmallEntries routing entries) run the
+// whole permutation in this one launch: every workgroup histograms all the
+// expert ids in LDS, also counting those of the tokens before its own chunk
+// (a workgroup's 4*TPW tokens lie in one chunk), derives the offsets with
+// the block scan, and takes its chunk bases from LDS.  The redundant
+// histograms (a few KiB of ids per workgroup) cost less than the two extra
+// dependent launches.  Workgroup 0 publishes offsets[].
+constexpr int64_t kSmallEntries = 4096;
+
+template <int BPL, int KMAX, bool SMALL>
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const int32_t* base,
                                                             const int32_t* counts,
                                                             int64_t token_waves, int64_t nchunks) {
   constexpr int TPW = tokens_per_wave(BPL);
   static_assert(kChunk % TPW == 0, "a wave's tokens share one chunk");
+  static_assert(kChunk % (4 * TPW) == 0, "a workgroup's tokens share one chunk");
+  static_assert(!SMALL || kScanThreads == 256, "the block scan runs on the 256 threads");
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int k = a.topk, E = a.num_experts;
   const int64_t H = a.hidden;
+  const int64_t t0 = wid * TPW;                      // TPW consecutive tokens of one chunk
+  const int nt = wid < token_waves ? (int)(a.tokens - t0 < TPW ? a.tokens - t0 : TPW) : 0;
+  const int nblocks = (int)(H / 16);
+
+  // Phase 1: every load of the wave is issued before any store (a store may
+  // alias a later load as far as the compiler knows): the tokens' rows, the
+  // chunk's expert ids, and the destinations with their base counters.
+  uint32_t w[TPW][BPL][8];
+  if (a.x) {
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti)
+      if (ti < nt) load_token_row<BPL>(a.x + (t0 + ti) * H, nblocks, lane, w[ti]);
+  }
+
+  // SMALL: per-expert entries (s_cnt), those before the chunk (s_bef, then
+  // the chunk bases) and the offsets (s_off), all in LDS
+  __shared__ int32_t s_cnt[SMALL ? kScanMaxE : 1], s_bef[SMALL ? kScanMaxE : 1];
+  __shared__ int32_t s_off[SMALL ? kScanMaxE + 1 : 1], s_wsum[kScanWaves];
+  if constexpr (SMALL) {
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += 256) { s_cnt[e] = 0; s_bef[e] = 0; }
+    __syncthreads();
+    const int64_t c0 = ((int64_t)blockIdx.x * 4 * TPW) / kChunk * kChunk;   // the chunk's first token
+    const int64_t nent = a.tokens * k, nbef = (c0 < a.tokens ? c0 : a.tokens) * k;
+    for (int64_t i = tid; i < nent; i += 256) {
+      const int e = a.topk_idx[i];
+      if (e >= 0 && e < E) {
+        atomicAdd(s_cnt + e, 1);
+        if (i < nbef) atomicAdd(s_bef + e, 1);
+      }
+    }
+    __syncthreads();
+    int32_t tot[kScanPer];
+#pragma unroll
+    for (int i = 0; i < kScanPer; ++i) {
+      const int e = tid + 256 * i;
+      tot[i] = e < E ? s_cnt[e] : 0;
+    }
+    block_expert_offsets(tot, E, a.align, s_off, s_wsum);
+    for (int e = tid; e < E; e += 256) s_bef[e] += s_off[e];
+    if (blockIdx.x == 0)
+      for (int e = tid; e <= E; e += 256) a.offsets[e] = s_off[e];
+    __syncthreads();
+  }
+  auto chunk_base = [&](int e, int64_t chunk) -> int64_t {
+    if constexpr (SMALL) return s_bef[e];
+    else return base[(int64_t)e * nchunks + chunk];
+  };
+
   if (wid >= token_waves) {
     // padding rows of expert e: [offsets[e] + counts[e], offsets[e+1])
     const int64_t e = wid - token_waves;
     if (e >= E) return;
-    const int64_t r0 = (int64_t)a.offsets[e] + counts[e], r1 = a.offsets[e + 1];
+    const int64_t r0 = SMALL ? (int64_t)s_off[e] + s_cnt[e] : (int64_t)a.offsets[e] + counts[e];
+    const int64_t r1 = SMALL ? s_off[e + 1] : a.offsets[e + 1];
     for (int64_t r = r0; r < r1; ++r) {
       if (lane == 0) {
         a.row_src[r] = -1;
@@ -216,22 +288,9 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     }
     return;
   }
-  const int64_t t0 = wid * TPW;                      // TPW consecutive tokens of one chunk
-  const int nt = (int)(a.tokens - t0 < TPW ? a.tokens - t0 : TPW);
   const int64_t chunk = t0 / kChunk;
   const int64_t tl = chunk * kChunk + lane;          // token of this lane in the chunk
   const bool lane_valid = tl < a.tokens;
-  const int nblocks = (int)(H / 16);
-
-  // Phase 1: every load of the wave is issued before any store (a store may
-  // alias a later load as far as the compiler knows): the tokens' rows, the
-  // chunk's expert ids, and the destinations with their base counters.
-  uint32_t w[TPW][BPL][8];
-  if (a.x) {
-#pragma unroll
-    for (int ti = 0; ti < TPW; ++ti)
-      if (ti < nt) load_token_row<BPL>(a.x + (t0 + ti) * H, nblocks, lane, w[ti]);
-  }
   // destination of entry j of token ti is held by lane j (lanes < k)
   int64_t dst_l[TPW];
   if constexpr (KMAX > 0) {
@@ -254,7 +313,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) hit |= (ids[i] == e);
             const uint64_t mask = __ballot(hit);
-            const int64_t d = (int64_t)base[(int64_t)e * nchunks + chunk] + __popcll(mask & below_mask);
+            const int64_t d = chunk_base(e, chunk) + __popcll(mask & below_mask);
             if (lane == j) dst_l[ti] = d;
           }
         }
@@ -325,7 +384,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
           if (lane_valid)
             for (int i = 0; i < k; ++i) hit |= (a.topk_idx[tl * k + i] == e);
           const uint64_t mask = __ballot(hit);
-          dst = (int64_t)base[(int64_t)e * nchunks + chunk] + __popcll(mask & below_mask);
+          dst = chunk_base(e, chunk) + __popcll(mask & below_mask);
         }
         if (lane == 0) store_meta(j, dst);
         store_row(dst);
@@ -341,12 +400,15 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   int32_t* hist = static_cast<int32_t*>(a.workspace);
   int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + mbytes);
   int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + 2 * mbytes);
-  if (nchunks > 0) {
-    route_hist_kernel<<<(unsigned)((nchunks + 3) / 4), 256, 4 * E * sizeof(int32_t), s>>>(
-        a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
+  const bool small = a.tokens * a.topk <= kSmallEntries;
+  if (!small) {
+    if (nchunks > 0) {
+      route_hist_kernel<<<(unsigned)((nchunks + 3) / 4), 256, 4 * E * sizeof(int32_t), s>>>(
+          a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
+    }
+    route_scan_kernel<<<(unsigned)((E + kScanExperts - 1) / kScanExperts), kScanThreads, 0, s>>>(
+        hist, base, nchunks, E, a.align, counts, a.offsets);
   }
-  route_scan_kernel<<<(unsigned)((E + kScanExperts - 1) / kScanExperts), kScanThreads, 0, s>>>(
-      hist, base, nchunks, E, a.align, counts, a.offsets);
   const int bpl = a.x ? blocks_per_lane(a.hidden) : 1;
   if (bpl == 0) return hipErrorInvalidValue;
   const int tpw = tokens_per_wave(bpl);
@@ -356,7 +418,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int kmax = a.topk <= 8 ? 8 : (a.topk <= 16 ? 16 : 0);
   switch (bpl * 100 + kmax) {
 #define NVFP4_SCATTER(B, KM) \
-    case B * 100 + KM: route_scatter_kernel<B, KM><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks); break;
+    case B * 100 + KM:                                                                              \
+      if (small) route_scatter_kernel<B, KM, true><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks); \
+      else route_scatter_kernel<B, KM, false><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks); \
+      break;
     NVFP4_SCATTER(1, 8) NVFP4_SCATTER(2, 8) NVFP4_SCATTER(4, 8) NVFP4_SCATTER(8, 8) NVFP4_SCATTER(16, 8)
     NVFP4_SCATTER(1, 16) NVFP4_SCATTER(2, 16) NVFP4_SCATTER(4, 16) NVFP4_SCATTER(8, 16) NVFP4_SCATTER(16, 16)
     NVFP4_SCATTER(1, 0) NVFP4_SCATTER(2, 0) NVFP4_SCATTER(4, 0) NVFP4_SCATTER(8, 0) NVFP4_SCATTER(16, 0)

@@ -72,9 +72,12 @@ def _fixture_routing(rng, T, k, E, kind):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 300])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 300, 1100])
 @pytest.mark.parametrize("kind", ["empty_and_tiny", "one_expert", "dropped"])
 def test_edge_routings(T, kind):
+    """Up to 4096 routing entries (T*k) the permutation runs as one launch
+    that histograms the ids in every workgroup; T = 1100 (4400 entries) takes
+    the histogram / scan / scatter launches."""
     rng = np.random.default_rng(T * 31 + len(kind))
     E, k, H = 16, 4, 256
     idx = _fixture_routing(rng, T, k, E, kind)
@@ -85,9 +88,11 @@ def test_edge_routings(T, kind):
         _permute_and_compare(x, idx, prob, E, align, f"{kind} T={T}")
 
 
-def test_metadata_only_and_many_experts():
-    rng = np.random.default_rng(3)
-    T, k, E = 1000, 8, 1024
+@pytest.mark.parametrize("T", [1000, 300])
+def test_metadata_only_and_many_experts(T):
+    """1024 experts, on both permutation paths (8000 and 2400 entries)."""
+    rng = np.random.default_rng(3 + T)
+    k, E = 8, 1024
     idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     prob = rng.random((T, k)).astype(np.float32)
     _permute_and_compare(None, idx, prob, E, 1, "metadata only E=1024")
@@ -116,10 +121,11 @@ def test_deterministic_repeat():
 
 
 @pytest.mark.parametrize("k,E", [(12, 40), (20, 64)])
-def test_wide_topk(k, E):
-    """top-k beyond 8 (16-id register path) and beyond 16 (generic path)."""
-    rng = np.random.default_rng(k)
-    T = 200
+@pytest.mark.parametrize("T", [200, 400])
+def test_wide_topk(k, E, T):
+    """top-k beyond 8 (16-id register path) and beyond 16 (generic path), on
+    the one-launch permutation (T = 200) and the three-launch one (T = 400)."""
+    rng = np.random.default_rng(k + T)
     idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
     idx[3, 2] = -1
     prob = rng.random((T, k)).astype(np.float32)
