@@ -115,9 +115,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // roundings (relative error below 3.1 * 2^-24), far inside the 2^-20 offset,
 // and fl(x/d) itself is within 2^-24 of x/d.  E2M1 rounding is monotonic, so
 // when lo and hi get the same code, every value between them, fl(x/d)
-// included, gets that code.  A block where any element's two codes differ
-// (its quotient lies near a rounding threshold), and every block with
-// d < 2^-126, recomputes all 16 quotients with the IEEE division.  d == 0
+// included, gets that code.  An element pair whose two codes differ (a
+// quotient near a rounding threshold) is recomputed with the IEEE division,
+// and every block with d < 2^-126 recomputes all 16 quotients.  d == 0
 // (s_b underflowed or s_g == 0) gives r = x * 0 = +-0: magnitude 0, sign
 // kept.  Overflowing products (huge x/d) saturate to code 7 on both sides.
 template <int SEL>
@@ -139,7 +139,10 @@ __device__ __forceinline__ uint2 pack_fp4_block(const float (&r)[16]) {
 
 __device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
   const bool full_div = (d != 0.0f) && (d < 1.17549435e-38f);
-  const float inv = (d == 0.0f) ? 0.0f : 1.0f / d;
+  // inv = 1/d within one ulp (v_rcp_f32, a normal input): with the 2^-20
+  // offsets the products still bracket fl(x/d) strictly (total relative
+  // error below 2^-23 + 3 * 2^-24 < 2^-21)
+  const float inv = (d == 0.0f) ? 0.0f : __builtin_amdgcn_rcpf(d);
   const float inv_lo = inv * 0.99999904632568359375f;   // 1 - 2^-20
   const float inv_hi = inv * 1.00000095367431640625f;   // 1 + 2^-20
   float r[16];
@@ -149,12 +152,38 @@ __device__ __forceinline__ uint2 encode_block16(const float (&x)[16], float d) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) r[i] = x[i] * inv_hi;
   const uint2 hi = pack_fp4_block(r);
-  if (full_div || lo.x != hi.x || lo.y != hi.y) {
+  if (full_div) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) r[i] = x[i] / d;
     return pack_fp4_block(r);
   }
-  return lo;
+  // Only the element pairs whose two codes differ take the IEEE division.
+  // With bf16 inputs and scales that are short binary fractions, quotients
+  // at or within an ulp of a rounding threshold are not rare (a few per
+  // thousand elements, most of them exact ties), so a per-block fallback
+  // would run in most waves; per pair it runs where a lane needs it.
+  uint2 out = lo;
+  const uint32_t dx = lo.x ^ hi.x, dy = lo.y ^ hi.y;
+  if ((dx | dy) != 0u) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t dw = j < 4 ? dx : dy;
+      if ((dw >> (8 * (j % 4))) & 0xFFu) {
+        const float r0 = x[2 * j] / d, r1 = x[2 * j + 1] / d;
+        switch (j) {
+          case 0: out.x = pack_fp4_pair<0>(out.x, r0, r1); break;
+          case 1: out.x = pack_fp4_pair<1>(out.x, r0, r1); break;
+          case 2: out.x = pack_fp4_pair<2>(out.x, r0, r1); break;
+          case 3: out.x = pack_fp4_pair<3>(out.x, r0, r1); break;
+          case 4: out.y = pack_fp4_pair<0>(out.y, r0, r1); break;
+          case 5: out.y = pack_fp4_pair<1>(out.y, r0, r1); break;
+          case 6: out.y = pack_fp4_pair<2>(out.y, r0, r1); break;
+          default: out.y = pack_fp4_pair<3>(out.y, r0, r1); break;
+        }
+      }
+    }
+  }
+  return out;
 }
 
 // Block rules: 0 maps every block maximum to the largest E2M1 value 6.  1 and
@@ -169,10 +198,27 @@ __device__ __forceinline__ float outer_scale(float amax, int rule) {
   return rule == 0 ? amax / 2688.0f : amax / 1536.0f;
 }
 
+// e4m3_encode(fl(num / den)) for num >= 0 (or NaN/inf), den > 0, without the
+// IEEE division in the common case.  q = fl(num * rcp(den)) lies within a
+// few ulp of fl(num / den) when den is normal.  Above 2^-6 the E4M3 byte is
+// the round-to-nearest-even of q's top 3 mantissa bits (values from 432 up
+// all give 0x7E), so two quotients a few ulp apart can only get different
+// bytes when a midpoint between E4M3 neighbours (dropped 20 bits = 0x80000)
+// lies between them; within 16 ulp of one, in the E4M3 subnormal range, or
+// for a subnormal den, the IEEE quotient decides.
+__device__ __forceinline__ uint32_t e4m3_of_quotient(float num, float den) {
+  if (num == 0.0f) return 0u;
+  const float q = num * __builtin_amdgcn_rcpf(den);
+  const uint32_t dropped = __float_as_uint(q) & 0xFFFFFu;
+  const bool near_mid = dropped - 0x7FFF0u <= 0x20u;
+  if (near_mid || q < 0.0157f || den < 1.17549435e-38f) return e4m3_encode(num / den);
+  return e4m3_encode(q);
+}
+
 // E4M3 byte of the block scale mapping bmax to `top`, and the decode step.
 __device__ __forceinline__ uint32_t block_scale(float bmax, float s_g, float top, float* d) {
   uint32_t sb = 0u;
-  if (s_g != 0.0f) sb = e4m3_encode(bmax / (top * s_g));
+  if (s_g != 0.0f) sb = e4m3_of_quotient(bmax, top * s_g);
   *d = e4m3_value(sb) * s_g;
   return sb;
 }

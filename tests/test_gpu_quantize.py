@@ -167,3 +167,71 @@ def test_deterministic_repeat():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+def _e4m3_midpoint_rows(amax):
+    """Rows whose block-scale quotients fl(bmax / fl(6 s_g)) sit exactly on
+    E4M3 rounding midpoints, and on the bf16 neighbours of those bmax values.
+    amax = 2688 (1536 under Four-Over-Six) makes s_g = 1 and the divisor
+    exactly 6; bmax = 6 mu for a midpoint mu needs at most 7 significant
+    bits, so it is a bf16 value."""
+    mids = []
+    for e in range(1, 16):                       # normal binades 2^-6 .. 2^8
+        base = 2.0 ** (e - 7)
+        for m in range(8):                       # between (e, m) and its successor
+            mu = base * (1 + (2 * m + 1) / 16)
+            if 6 * mu < 0.98 * amax:
+                mids.append(mu)
+    mids += [(n + 0.5) / 512 for n in range(8)]  # E4M3 subnormal range ties
+    bm = []
+    for mu in mids:
+        v = np.float32(6 * mu)
+        b = int(to_bf16_bits(np.array([v]))[0])
+        assert float(np.array([b << 16], np.uint32).view(np.float32)[0]) == v
+        bm += [b, b - 1, b + 1]                  # the tie and the neighbouring bf16 values
+    rng = np.random.default_rng(41)
+    nb = 128
+    rows = []
+    for r0 in range(0, len(bm), nb - 1):
+        chunk = bm[r0:r0 + nb - 1]
+        row = np.zeros(16 * nb, np.uint16)
+        row[0] = int(to_bf16_bits(np.array([amax], np.float32))[0])
+        for i, b in enumerate(chunk):
+            blk = 16 * (i + 1)
+            bmax = float(np.array([b << 16], np.uint32).view(np.float32)[0])
+            # the block maximum in a random slot, smaller random values around it
+            vals = rng.uniform(-1, 1, 16).astype(np.float32) * np.float32(bmax * 0.9)
+            vals[rng.integers(16)] = bmax * (1 if rng.random() < 0.5 else -1)
+            row[blk:blk + 16] = to_bf16_bits(vals)
+            row[blk + int(np.argmax(np.abs(vals)))] = b | (0x8000 if vals[np.argmax(np.abs(vals))] < 0 else 0)
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_block_scale_quotient_midpoints(rule):
+    """The block scale's E4M3 rounding at exact midpoints (ties to even) and
+    next to them, through the per-token quantizer, the given-amax block
+    quantizer and the routing scatter."""
+    amax = 2688.0 if rule == 0 else 1536.0
+    xb = _e4m3_midpoint_rows(amax)
+    T = xb.shape[0]
+    ops = _ops()
+    say("block-scale midpoints", rule, xb.shape)
+    c, s, g = ops.nvfp4_quantize(dev_bf16(xb), block_rule=rule)
+    am = np.full(T, amax, np.float32)
+    c2, s2, g2 = ops.nvfp4_quantize(dev_bf16(xb), amax_in=dev(am), block_rule=rule)
+    idx = np.zeros((T, 1), np.int32)
+    prob = np.ones((T, 1), np.float32)
+    p = ops.moe_permute(dev_bf16(xb), dev(idx), dev(prob), 1, block_rule=rule)
+    torch.cuda.synchronize()
+    rc, rs, rg = O.quantize(xb, rule=rule)
+    for what, (hc, hs, hg) in (("per token", (c, s, g)), ("amax_in", (c2, s2, g2)),
+                               ("scatter", (p["codes"], p["scales"], p["gscale"]))):
+        assert np.array_equal(host(hg).view(np.uint32), rg.view(np.uint32)), what
+        hs = host(hs)
+        if not np.array_equal(hs, rs):
+            r, b = np.argwhere(hs != rs)[0]
+            raise AssertionError(f"{what}: scale of row {r} block {b}: gpu {hs[r, b]:02x} "
+                                 f"oracle {rs[r, b]:02x}")
+        assert np.array_equal(host(hc), rc), what
