@@ -72,9 +72,13 @@ def parse():
                    help="also time the layer with Four-Over-Six (MSE) weights and activations and "
                         "report it under 'four_over_six' (0 = skip); the headline stays the "
                         "standard rule")
-    p.add_argument("--secondary", type=int, default=1,
-                   help="also time the dense projections and the 256- and 32768-token layers "
-                        "and report them under 'secondary' (0 = skip)")
+    p.add_argument("--secondary", default="dense,decode,long",
+                   help="comma list of the secondary workloads to time and report under "
+                        "'secondary' (dense: the attention projections; decode: the 256-token "
+                        "layer; long: the 32768-token layer); empty or 0 = none")
+    p.add_argument("--skip-headline", action="store_true",
+                   help="profiling aid: quantize the headline workload's weights but time only "
+                        "the secondary workloads (the headline fields are then null)")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run plain device copies of this many MiB (a known-size "
                         "kernel for scaling the rocprof FETCH_SIZE/WRITE_SIZE counters)")
@@ -259,6 +263,25 @@ def bench_moe_secondary(args, dev, bf, wid, W1, W2, weight_copies, label):
     return rec
 
 
+def run_secondary(args, dev, bf, W1, W2):
+    names = [n for n in str(args.secondary).replace(" ", "").split(",") if n and n != "0"]
+    unknown = set(names) - {"dense", "decode", "long"}
+    if unknown:
+        raise SystemExit(f"bench.py: unknown secondary workload(s) {sorted(unknown)}")
+    sec = {}
+    if "dense" in names:
+        sec["dense_t8192"] = bench_dense(args, dev, bf)
+    if "decode" in names:
+        sec["decode_t256"] = bench_moe_secondary(args, dev, bf, "decode_moe_t256", W1, W2, 3,
+                                                 "decode_t256")
+    if "long" in names:
+        sec["long_t32768"] = bench_moe_secondary(args, dev, bf, "long_heavytail_moe_t32768",
+                                                 W1, W2, 1, "long_t32768")
+    for k, v in sec.items():
+        log(f"{k}: {v['value']:.4g} tokens/s, {v['ms_per_step']:.4f} ms/step")
+    return sec
+
+
 def cpu_baseline(w, n_tokens):
     from oracle import oracle as O
     E, I, H = w.experts, w.inter, w.hidden
@@ -321,6 +344,13 @@ def main():
         # steps again with HIP events recorded on the launch stream
         return run_steps(step, args.steps, args.warmup, f"block rule {rule}", StageTimer)
 
+    if args.skip_headline:
+        secondary = run_secondary(args, dev, bf, W1, W2)
+        print(json.dumps({"metric": "MoE W4A4 expert-layer tokens/s", "value": None,
+                          "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "note": "headline skipped (profiling aid)",
+                          "secondary": secondary}), flush=True)
+        return
     wall, stages = timed(W1, W2, 0)
     ms = wall * 1e3 / args.steps
     tokens_per_s = w.tokens * args.steps / wall
@@ -386,14 +416,8 @@ def main():
             "ms_per_step": wall46 * 1e3 / args.steps, "stage_ms": st46,
             "quantize_permute_gbps": qbytes / (st46["route_quantize"] * 1e-3) / 1e9,
         }
-    if args.secondary:
-        sec = {"dense_t8192": bench_dense(args, dev, bf)}
-        sec["decode_t256"] = bench_moe_secondary(args, dev, bf, "decode_moe_t256", W1, W2, 3,
-                                                 "decode_t256")
-        sec["long_t32768"] = bench_moe_secondary(args, dev, bf, "long_heavytail_moe_t32768",
-                                                 W1, W2, 1, "long_t32768")
-        for k, v in sec.items():
-            log(f"{k}: {v['value']:.4g} tokens/s, {v['ms_per_step']:.4f} ms/step")
+    sec = run_secondary(args, dev, bf, W1, W2)
+    if sec:
         result["secondary"] = sec
     # offline weight quantization (a0) of W1: 1D blocks and 16x16 blocks.  Five
     # calls back to back after a warm-up call, so that the launches queue
