@@ -257,9 +257,10 @@ int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
  *                (each row-major or tiled, per its layout member)
  *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned
  *   debug        nullable: every non-NULL member receives that intermediate
- *                (in place of the workspace copy); fc1_out and y_rows_f32
- *                are only produced when requested (y_rows_f32 switches the
- *                FC2 output to fp32)
+ *                (in place of the workspace copy); fc1_out, y_rows_f32 and
+ *                row_src are only produced when requested (y_rows_f32
+ *                switches the FC2 output to fp32; nothing in the layer reads
+ *                the row-to-token map, so it is not written otherwise)
  *   stage_events nullable array of 6 hipEvent_t (as void*), recorded on
  *                `stream` before route, FC1, requantize, FC2, combine and
  *                after combine (profiling; see nvfp4_event_*).

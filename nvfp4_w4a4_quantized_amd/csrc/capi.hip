@@ -155,7 +155,7 @@ int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden, const int32_t
   if (workspace_bytes < route_workspace_bytes(tokens, num_experts)) return NVFP4_WORKSPACE_TOO_SMALL;
   RouteArgs a{x, tokens, x ? hidden : 0, topk_idx, topk_prob, topk, num_experts, align,
               expert_offsets, dst_row, row_src, row_prob, codes, block_scales, global_scales,
-              nullptr, workspace, block_rule};
+              nullptr, 0, workspace, block_rule};
   return hip_status(launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -292,10 +292,13 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   };
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return NVFP4_HIP_ERROR;
-  // a1 + a2: routing metadata and per-token quantize-scatter (zeroes amax_d rows)
+  // a1 + a2: routing metadata and per-token quantize-scatter; amax_d is
+  // zeroed over the whole capacity (FC1 takes atomic maxima into it).  The
+  // row-to-token map is only written when the caller asks for it (nothing
+  // downstream reads it).
   RouteArgs ra{x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
-               L.offsets, L.dst_row, L.row_src, L.row_prob, L.a1c, L.a1s, L.a1g,
-               L.amax_d, L.route_ws_i, act_block_rule};
+               L.offsets, L.dst_row, (debug && debug->row_src) ? debug->row_src : nullptr,
+               L.row_prob, L.a1c, L.a1s, L.a1g, L.amax_d, cap, L.route_ws_i, act_block_rule};
   if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a3 + a4: FC1 with the weighted SwiGLU epilogue and D's row amax

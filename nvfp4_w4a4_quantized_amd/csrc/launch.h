@@ -41,7 +41,8 @@ struct RouteArgs {
   int32_t align;
   int32_t* offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
   uint8_t* codes; uint8_t* scales; float* gscale;
-  float* zero_per_row;  // nullable: set to 0 for every routed and padding row
+  float* zero_per_row;  // nullable: rows [0, zero_rows) set to 0 (one coalesced fill)
+  int64_t zero_rows;
   void* workspace;
   int32_t block_rule;   // 0 standard, 1/2 Four-Over-Six (MSE/MAE)
 };

@@ -118,15 +118,27 @@ __device__ void block_expert_offsets(const int32_t (&tot)[kScanPer], int32_t E, 
   __syncthreads();
 }
 
+// zero[0, n) = 0 by the whole grid (grid-stride, 16-byte stores where aligned)
+__device__ __forceinline__ void grid_zero_fill(float* zero, int64_t n) {
+  if (!zero) return;
+  const int64_t nt = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n4 = (reinterpret_cast<uintptr_t>(zero) & 15u) == 0 ? n / 4 : 0;
+  for (int64_t i = i0; i < n4; i += nt) reinterpret_cast<float4*>(zero)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t i = 4 * n4 + i0; i < n; i += nt) zero[i] = 0.0f;
+}
+
 __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t* hist, int32_t* base,
                                                                   int64_t nchunks, int32_t E,
                                                                   int32_t align, int32_t* counts,
-                                                                  int32_t* offsets) {
+                                                                  int32_t* offsets, float* zero,
+                                                                  int64_t nzero) {
   constexpr int NWAVES = kScanWaves;
   constexpr int PER = kScanPer;
   __shared__ int32_t off[kScanMaxE + 1];
   __shared__ int32_t wsum[NWAVES];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  grid_zero_fill(zero, nzero);
   // expert totals: expert e = tid + kScanThreads*i, summed over its row
   int32_t tot[PER];
 #pragma unroll
@@ -260,6 +272,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
       for (int e = tid; e <= E; e += 256) a.offsets[e] = s_off[e];
     __syncthreads();
   }
+  if constexpr (SMALL) grid_zero_fill(a.zero_per_row, a.zero_rows);
   auto chunk_base = [&](int e, int64_t chunk) -> int64_t {
     if constexpr (SMALL) return s_bef[e];
     else return base[(int64_t)e * nchunks + chunk];
@@ -273,9 +286,8 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     const int64_t r1 = SMALL ? s_off[e + 1] : a.offsets[e + 1];
     for (int64_t r = r0; r < r1; ++r) {
       if (lane == 0) {
-        a.row_src[r] = -1;
+        if (a.row_src) a.row_src[r] = -1;
         a.row_prob[r] = 0.0f;
-        if (a.zero_per_row) a.zero_per_row[r] = 0.0f;
         if (a.x) a.gscale[r] = 0.0f;
       }
       if (a.x) {
@@ -363,9 +375,8 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     auto store_meta = [&](int j, int64_t dst) {
       a.dst_row[t * k + j] = (int32_t)dst;
       if (dst < 0) return;
-      a.row_src[dst] = (int32_t)t;
+      if (a.row_src) a.row_src[dst] = (int32_t)t;
       a.row_prob[dst] = a.topk_prob[t * k + j];
-      if (a.zero_per_row) a.zero_per_row[dst] = 0.0f;
       if (a.x) a.gscale[dst] = s_g;
     };
     if constexpr (KMAX > 0) {
@@ -407,7 +418,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
           a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
     }
     route_scan_kernel<<<(unsigned)((E + kScanExperts - 1) / kScanExperts), kScanThreads, 0, s>>>(
-        hist, base, nchunks, E, a.align, counts, a.offsets);
+        hist, base, nchunks, E, a.align, counts, a.offsets, a.zero_per_row, a.zero_rows);
   }
   const int bpl = a.x ? blocks_per_lane(a.hidden) : 1;
   if (bpl == 0) return hipErrorInvalidValue;
