@@ -4,7 +4,8 @@
 // §5.3: the row amax is collected while the token is being permuted and the
 // quantizer reuses it).
 //
-// Three launches, no host synchronisation:
+// Three launches, no host synchronisation (one for small batches: see
+// kSmallEntries below):
 //   1. hist:    one wave per chunk of 64 tokens counts its entries per expert
 //               (LDS histogram) -> hist[e][chunk] (expert-major).
 //   2. scan:    one workgroup per 8 experts; each derives every expert's
@@ -12,7 +13,8 @@
 //               counts) and offsets[] (exclusive scan of the totals rounded
 //               up to `align`), then writes base[e][chunk] = offsets[e] +
 //               #entries of e in earlier chunks for its own experts with
-//               wave scans along their rows.
+//               wave scans along their rows.  It also clears the rows'
+//               amax cells that FC1 accumulates into (one coalesced fill).
 //   3. scatter: each wave takes TPW consecutive tokens of one chunk.  It
 //               quantizes a token once (row amax, block scales, codes in
 //               registers) while the next token's row is already loading, and
