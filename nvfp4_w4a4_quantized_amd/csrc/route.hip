@@ -45,6 +45,9 @@ size_t route_workspace_bytes(int64_t tokens, int32_t num_experts) {
   return 2 * route_matrix_bytes(tokens, num_experts) + counts;
 }
 
+// KMAX > 0 (topk <= KMAX): a lane's k expert ids are all requested before
+// the first LDS add (a loop over a run-time count would wait for each load).
+template <int KMAX>
 __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int64_t tokens,
                                                           int32_t topk, int32_t E,
                                                           int64_t nchunks, int32_t* hist) {
@@ -57,9 +60,18 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int
   if (chunk < nchunks) {
     const int64_t t = chunk * kChunk + lane;
     if (t < tokens) {
-      for (int j = 0; j < topk; ++j) {
-        int e = idx[t * topk + j];
-        if (e >= 0 && e < E) atomicAdd(h + e, 1);
+      if constexpr (KMAX > 0) {
+        int ids[KMAX];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) ids[j] = j < topk ? idx[t * topk + j] : -1;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j)
+          if (ids[j] >= 0 && ids[j] < E) atomicAdd(h + ids[j], 1);
+      } else {
+        for (int j = 0; j < topk; ++j) {
+          int e = idx[t * topk + j];
+          if (e >= 0 && e < E) atomicAdd(h + e, 1);
+        }
       }
     }
   }
@@ -151,6 +163,14 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t*
       const int32_t* row = hist + (int64_t)e * nchunks;
       int64_t c = 0;
       if ((nchunks & 3) == 0) {                    // rows are 16-byte aligned
+        // eight 16-byte loads in flight per step, not one load per wait
+        for (; c + 32 <= nchunks; c += 32) {
+          int4 q[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) q[u] = *reinterpret_cast<const int4*>(row + c + 4 * u);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) t += q[u].x + q[u].y + q[u].z + q[u].w;
+        }
         for (; c < nchunks; c += 4) {
           const int4 q = *reinterpret_cast<const int4*>(row + c);
           t += q.x + q.y + q.z + q.w;
@@ -416,8 +436,14 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const bool small = a.tokens * a.topk <= kSmallEntries;
   if (!small) {
     if (nchunks > 0) {
-      route_hist_kernel<<<(unsigned)((nchunks + 3) / 4), 256, 4 * E * sizeof(int32_t), s>>>(
-          a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
+      const unsigned hg = (unsigned)((nchunks + 3) / 4);
+      const size_t hl = 4 * E * sizeof(int32_t);
+      if (a.topk <= 8)
+        route_hist_kernel<8><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
+      else if (a.topk <= 16)
+        route_hist_kernel<16><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
+      else
+        route_hist_kernel<0><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
     }
     route_scan_kernel<<<(unsigned)((E + kScanExperts - 1) / kScanExperts), kScanThreads, 0, s>>>(
         hist, base, nchunks, E, a.align, counts, a.offsets, a.zero_per_row, a.zero_rows);
