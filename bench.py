@@ -63,7 +63,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="qwen3_30b_a3b_moe_t8192")
-    p.add_argument("--cpu-tokens", type=int, default=2048,
+    p.add_argument("--cpu-tokens", type=int, default=4096,
                    help="tokens of the oracle's CPU-baseline sample (0 = skip)")
     p.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "fc1_traffic.json"),
                    help="JSON record of measured HBM bytes per FC1 launch (rocprof PMC); "
