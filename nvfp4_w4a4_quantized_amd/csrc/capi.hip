@@ -42,8 +42,17 @@ struct MoeLayout {
   uint16_t* d; float* amax_d;
   uint8_t* a2c; uint8_t* a2s; float* a2g;
   uint16_t* y_rows;
+  int4* tab1; int4* tab2;   // FC1 / FC2 tile tables
   size_t bytes;
 };
+
+// The FC1 / FC2 launch arguments that fix the grids (sizes only).
+GemmArgs moe_gemm_shape(int64_t cap, int64_t H, int64_t I, int32_t E, bool fc1) {
+  GemmArgs g{};
+  g.num_groups = E; g.rows_cap = cap;
+  g.n = fc1 ? 2 * I : H; g.k = fc1 ? H : I; g.inter = fc1 ? I : 0;
+  return g;
+}
 
 MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_t E, int32_t align) {
   const int64_t cap = moe_rows_capacity(T, k, E, align);
@@ -63,6 +72,8 @@ MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_
   L.a2s = c.take<uint8_t>((size_t)(cap * I / 16));
   L.a2g = c.take<float>((size_t)cap);
   L.y_rows = c.take<uint16_t>((size_t)(cap * H));
+  L.tab1 = c.take<int4>((size_t)gemm_grid_blocks(moe_gemm_shape(cap, H, I, E, true), true));
+  L.tab2 = c.take<int4>((size_t)gemm_grid_blocks(moe_gemm_shape(cap, H, I, E, false), false));
   L.bytes = c.used;
   return L;
 }
@@ -153,9 +164,13 @@ int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden, const int32_t
     if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_INVALID_ARGUMENT;
   }
   if (workspace_bytes < route_workspace_bytes(tokens, num_experts)) return NVFP4_WORKSPACE_TOO_SMALL;
-  RouteArgs a{x, tokens, x ? hidden : 0, topk_idx, topk_prob, topk, num_experts, align,
-              expert_offsets, dst_row, row_src, row_prob, codes, block_scales, global_scales,
-              nullptr, 0, workspace, block_rule};
+  RouteArgs a{};
+  a.x = x; a.tokens = tokens; a.hidden = x ? hidden : 0;
+  a.topk_idx = topk_idx; a.topk_prob = topk_prob; a.topk = topk;
+  a.num_experts = num_experts; a.align = align;
+  a.offsets = expert_offsets; a.dst_row = dst_row; a.row_src = row_src; a.row_prob = row_prob;
+  a.codes = codes; a.scales = block_scales; a.gscale = global_scales;
+  a.workspace = workspace; a.block_rule = block_rule;
   return hip_status(launch_route(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -292,22 +307,41 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   };
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return NVFP4_HIP_ERROR;
-  // a1 + a2: routing metadata and per-token quantize-scatter; amax_d is
-  // zeroed over the whole capacity (FC1 takes atomic maxima into it).  The
-  // row-to-token map is only written when the caller asks for it (nothing
-  // downstream reads it).
-  RouteArgs ra{x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
-               L.offsets, L.dst_row, (debug && debug->row_src) ? debug->row_src : nullptr,
-               L.row_prob, L.a1c, L.a1s, L.a1g, L.amax_d, cap, L.route_ws_i, act_block_rule};
-  if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
-  if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
-  // a3 + a4: FC1 with the weighted SwiGLU epilogue and D's row amax
   GemmArgs g1{};
   g1.a_codes = L.a1c; g1.a_scales = L.a1s; g1.a_gscale = L.a1g;
   g1.b_codes = w1->codes; g1.b_scales = w1->scales; g1.b_gscale = w1->gscale;
   g1.offsets = L.offsets; g1.num_groups = num_experts; g1.rows_cap = cap;
   g1.n = 2 * inter; g1.k = hidden; g1.inter = inter; g1.b_layout = w1->layout;
   g1.row_prob = L.row_prob; g1.d_out = L.d; g1.amax = L.amax_d; g1.c_out = c_out;
+  g1.tile_table = L.tab1;
+  GemmArgs g2{};
+  g2.a_codes = L.a2c; g2.a_scales = L.a2s; g2.a_gscale = L.a2g;
+  g2.b_codes = w2->codes; g2.b_scales = w2->scales; g2.b_gscale = w2->gscale;
+  g2.offsets = L.offsets; g2.num_groups = num_experts; g2.rows_cap = cap;
+  g2.n = hidden; g2.k = inter; g2.b_layout = w2->layout;
+  g2.out_dtype = y_f32 ? 0 : 1;
+  g2.out = y_f32 ? static_cast<void*>(y_f32) : static_cast<void*>(L.y_rows);
+  g2.tile_table = L.tab2;
+  // a1 + a2: routing metadata and per-token quantize-scatter.  The same
+  // launches clear amax_d over the whole capacity (FC1 takes atomic maxima
+  // into it) and, while they hold the offsets, write both GEMMs' tile
+  // tables.  The row-to-token map is only written when the caller asks for
+  // it (nothing downstream reads it).
+  RouteArgs ra{};
+  ra.x = x; ra.tokens = tokens; ra.hidden = hidden;
+  ra.topk_idx = topk_idx; ra.topk_prob = topk_prob; ra.topk = topk;
+  ra.num_experts = num_experts; ra.align = align;
+  ra.offsets = L.offsets; ra.dst_row = L.dst_row;
+  ra.row_src = (debug && debug->row_src) ? debug->row_src : nullptr;
+  ra.row_prob = L.row_prob; ra.codes = L.a1c; ra.scales = L.a1s; ra.gscale = L.a1g;
+  ra.zero_per_row = L.amax_d; ra.zero_rows = cap;
+  ra.tables[0] = gemm_tile_table_spec(g1, true, L.tab1);
+  ra.tables[1] = gemm_tile_table_spec(g2, false, L.tab2);
+  ra.num_tables = 2;
+  ra.workspace = L.route_ws_i; ra.block_rule = act_block_rule;
+  if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
+  // a3 + a4: FC1 with the weighted SwiGLU epilogue and D's row amax
   if ((e = launch_gemm_swiglu(g1, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(2)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a5: requantize D reusing its amax (rows up to offsets[E] live on device:
@@ -317,13 +351,6 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   if ((e = launch_quantize_rows(q, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(3)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a6: FC2
-  GemmArgs g2{};
-  g2.a_codes = L.a2c; g2.a_scales = L.a2s; g2.a_gscale = L.a2g;
-  g2.b_codes = w2->codes; g2.b_scales = w2->scales; g2.b_gscale = w2->gscale;
-  g2.offsets = L.offsets; g2.num_groups = num_experts; g2.rows_cap = cap;
-  g2.n = hidden; g2.k = inter; g2.b_layout = w2->layout;
-  g2.out_dtype = y_f32 ? 0 : 1;
-  g2.out = y_f32 ? static_cast<void*>(y_f32) : static_cast<void*>(L.y_rows);
   if ((e = launch_gemm_plain(g2, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(4)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a7: combine

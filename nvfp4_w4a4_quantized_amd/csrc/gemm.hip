@@ -22,6 +22,7 @@
 
 #include "launch.h"
 #include "nvfp4_device.h"
+#include "tile_schedule.h"
 
 namespace nvfp4 {
 
@@ -79,42 +80,18 @@ __device__ __forceinline__ half8_t decode8(uint32_t c, half2_t sb) {
 // The epilogue works on the accumulator registers in place: each lane holds
 // one column of 16 rows per 32-row block, and for the SwiGLU tile the gate and
 // up columns of one output column sit in the same lane.
-constexpr int kKS = 128;          // K per stage
 #ifndef NVFP4_VPM
 #define NVFP4_VPM 4
 #endif
 
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_SWIGLU = 2 };
 
-// ---- tile schedule ---------------------------------------------------------
+// ---- tile schedule (cost model, tables: tile_schedule.h) -------------------
 //
-// Tiles are numbered m-tile major with the n-tiles inner, m-tiles group by
-// group (ceil(rows_g / BM) per group).  Workgroups are dealt to the 8 XCDs
-// round robin (workgroup b runs on XCD b % 8), and the tiles are cut into 8
-// contiguous ranges of about equal estimated cost, one per XCD, at m-tile
-// boundaries: consecutive tiles share A rows and, inside a group, B rows,
-// which then stay in that XCD's L2, and no XCD runs dry long before the
-// others.  Workgroup b takes tile b / 8 of its XCD's range.  A tile with v
-// valid 32-row blocks and S K-stages costs kCostFixed + S (kCostStage + v)
-// units: its prologue and epilogue, and the B decode and loads of every
-// stage, do not shrink with its rows.  Counts and costs come from the device
-// offsets (the host never reads them), read once per workgroup for up to
-// 256 groups; the grid is an upper bound and surplus workgroups exit.
-constexpr uint32_t kCostFixed = 24, kCostStage = 2;
-constexpr uint32_t kCostMaxStages = 16;     // keeps the total cost inside 32 bits
-
-__device__ __forceinline__ uint32_t tile_cost(uint32_t v, uint32_t stages) {
-  return kCostFixed + stages * (kCostStage + v);
-}
-
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  v = wave_incl_scan_dpp(v, [](uint32_t x, uint32_t y) { return x + y; });
-  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
-}
-
-__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t v) {
-  return wave_incl_scan_dpp(v, [](uint32_t x, uint32_t y) { return x + y; });
-}
+// Workgroups derive their tile from the device offsets (schedule_tile below)
+// unless the launch carries a precomputed table.  Up to 256 groups the
+// offsets are read once per workgroup; the grid is an upper bound and
+// surplus workgroups exit.
 
 // 256 consecutive groups, four per lane (group base + 64 i + lane)
 struct GroupChunk {
@@ -363,7 +340,13 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
   int g;
   int64_t row0, row1, nt;
-  if (!schedule_tile<BM>(a.offsets, a.num_groups, K, ntn, blockIdx.x, &g, &row0, &row1, &nt)) return;
+  if (a.tile_table) {                           // precomputed schedule: one 16-byte entry
+    const int4 te = a.tile_table[blockIdx.x];
+    if (te.x < 0) return;
+    g = te.x; row0 = te.y; row1 = te.z; nt = te.w;
+  } else if (!schedule_tile<BM>(a.offsets, a.num_groups, K, ntn, blockIdx.x, &g, &row0, &row1, &nt)) {
+    return;
+  }
   g = __builtin_amdgcn_readfirstlane(g);       // wave-uniform: scalar bases below
   row0 = uniform64(row0);
   row1 = uniform64(row1);
@@ -870,8 +853,15 @@ hipError_t launch_pack_b(const uint8_t* codes, const uint8_t* scales, int64_t ro
 
 // ---- launchers -------------------------------------------------------------
 
+// Grid of one launch: BM-row tiles, ntn n-tiles per m-tile, and the
+// workgroup positions the XCD ranges need.
+struct TileCfg {
+  int bm;
+  int64_t ntn, blocks;
+};
+
 template <int WM, int WN, int NW, int EPI>
-static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+static TileCfg tile_cfg(const GemmArgs& a) {
   constexpr int BM = 32 * WM, BN = 32 * WN * NW;
   const int64_t ntn = (EPI == EPI_SWIGLU) ? (a.inter + BN / 2 - 1) / (BN / 2) : (a.n + BN - 1) / BN;
   // upper bound on the m-tiles of all groups: sum ceil(n_g/BM) <= cap/BM + G.
@@ -882,7 +872,12 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   const int64_t st = std::min<int64_t>(a.k / kKS, kCostMaxStages);
   const int64_t cmax = kCostFixed + st * (kCostStage + WM), cmin = kCostFixed + st * (kCostStage + 1);
   const int64_t per_xcd = (cmax * (mtiles + 8) + 8 * cmin - 1) / (8 * cmin) + 1;
-  const int64_t blocks = 8 * per_xcd * ntn;
+  return TileCfg{BM, ntn, 8 * per_xcd * ntn};
+}
+
+template <int WM, int WN, int NW, int EPI>
+static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  const int64_t blocks = tile_cfg<WM, WN, NW, EPI>(a).blocks;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.n * a.k / 2 > 0xFFFFFFFFll) return hipErrorInvalidValue;   // 32-bit lane offsets into a group
@@ -926,6 +921,26 @@ hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s) {
   if (gemm_uses_small_tile(a.rows_cap, a.num_groups))
     return launch_cfg<NVFP4_GEMM_TILE_SMALL, EPI_SWIGLU>(a, s);
   return launch_cfg<NVFP4_GEMM_TILE_FC1, EPI_SWIGLU>(a, s);
+}
+
+// the configuration launch_gemm_plain / launch_gemm_swiglu pick
+static TileCfg launch_tile_cfg(const GemmArgs& a, bool swiglu) {
+  const bool small = gemm_uses_small_tile(a.rows_cap, a.num_groups);
+  if (swiglu)
+    return small ? tile_cfg<NVFP4_GEMM_TILE_SMALL, EPI_SWIGLU>(a) : tile_cfg<NVFP4_GEMM_TILE_FC1, EPI_SWIGLU>(a);
+  return small ? tile_cfg<NVFP4_GEMM_TILE_SMALL, EPI_BF16>(a) : tile_cfg<NVFP4_GEMM_TILE, EPI_BF16>(a);
+}
+
+int64_t gemm_grid_blocks(const GemmArgs& a, bool swiglu) {
+  const int64_t b = launch_tile_cfg(a, swiglu).blocks;
+  return b > 0 ? b : 0;
+}
+
+TileTableSpec gemm_tile_table_spec(const GemmArgs& a, bool swiglu, int4* table) {
+  const TileCfg c = launch_tile_cfg(a, swiglu);
+  TileTableSpec t{};
+  t.table = table; t.bm = c.bm; t.k = a.k; t.ntn = c.ntn; t.blocks = c.blocks > 0 ? c.blocks : 0;
+  return t;
 }
 
 }  // namespace nvfp4

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "tile_schedule.h"
 
 namespace nvfp4 {
 
@@ -43,6 +44,8 @@ struct RouteArgs {
   uint8_t* codes; uint8_t* scales; float* gscale;
   float* zero_per_row;  // nullable: rows [0, zero_rows) set to 0 (one coalesced fill)
   int64_t zero_rows;
+  TileTableSpec tables[2];  // GEMM tile tables written from the offsets (num_tables of them)
+  int32_t num_tables;
   void* workspace;
   int32_t block_rule;   // 0 standard, 1/2 Four-Over-Six (MSE/MAE)
 };
@@ -61,9 +64,18 @@ struct GemmArgs {
   int out_dtype; void* out;
   // SwiGLU epilogue
   const float* row_prob; uint16_t* d_out; float* amax; float* c_out; int64_t inter;
+  // nullable: the launch's tile schedule, written beforehand by a kernel that
+  // holds the offsets (one {group, row0, row1, n-tile} entry per workgroup,
+  // group < 0 = none; see tile_schedule.h)
+  const int4* tile_table;
 };
 hipError_t launch_gemm_plain(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);
+// Workgroups of the launch that launch_gemm_plain / launch_gemm_swiglu make
+// for these arguments (the entries of its tile table).
+int64_t gemm_grid_blocks(const GemmArgs& a, bool swiglu);
+// What a table builder needs to write that launch's table into `table`.
+TileTableSpec gemm_tile_table_spec(const GemmArgs& a, bool swiglu, int4* table);
 // Row-major B (rows % 32 == 0, k % 128 == 0) -> the tiled layout.
 hipError_t launch_pack_b(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                          uint8_t* pcodes, uint8_t* pscales, hipStream_t s);

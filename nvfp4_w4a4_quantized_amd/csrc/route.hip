@@ -238,10 +238,16 @@ __device__ __forceinline__ void load_token_row(const uint16_t* xr, int nblocks, 
 // dependent launches.  Workgroup 0 publishes offsets[].
 constexpr int64_t kSmallEntries = 4096;
 
+// Workgroups appended to the scatter grid that write the GEMMs' tile tables
+// (RouteArgs::tables) from the offsets, while the other workgroups permute:
+// the tables cost no launch and no time on the routing's critical path.
+constexpr int kTableWorkgroups = 16;
+
 template <int BPL, int KMAX, bool SMALL>
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const int32_t* base,
                                                             const int32_t* counts,
-                                                            int64_t token_waves, int64_t nchunks) {
+                                                            int64_t token_waves, int64_t nchunks,
+                                                            int64_t table_wg0) {
   constexpr int TPW = tokens_per_wave(BPL);
   static_assert(kChunk % TPW == 0, "a wave's tokens share one chunk");
   static_assert(kChunk % (4 * TPW) == 0, "a workgroup's tokens share one chunk");
@@ -250,8 +256,18 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
   const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int k = a.topk, E = a.num_experts;
   const int64_t H = a.hidden;
+  const bool table_wg = (int64_t)blockIdx.x >= table_wg0;   // uniform per workgroup
+  __shared__ TileTableLds tls;
+  if constexpr (!SMALL) {
+    if (table_wg) {                      // offsets come from the scan launch
+      const int64_t wg = (int64_t)blockIdx.x - table_wg0;
+      build_tile_tables(a.offsets, E, a.tables[0], a.tables[1], a.num_tables, wg * 256 + threadIdx.x,
+                        (int64_t)kTableWorkgroups * 256, tls);
+      return;
+    }
+  }
   const int64_t t0 = wid * TPW;                      // TPW consecutive tokens of one chunk
-  const int nt = wid < token_waves ? (int)(a.tokens - t0 < TPW ? a.tokens - t0 : TPW) : 0;
+  const int nt = (wid < token_waves && !table_wg) ? (int)(a.tokens - t0 < TPW ? a.tokens - t0 : TPW) : 0;
   const int nblocks = (int)(H / 16);
 
   // Phase 1: every load of the wave is issued before any store (a store may
@@ -294,7 +310,15 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
       for (int e = tid; e <= E; e += 256) a.offsets[e] = s_off[e];
     __syncthreads();
   }
-  if constexpr (SMALL) grid_zero_fill(a.zero_per_row, a.zero_rows);
+  if constexpr (SMALL) {
+    grid_zero_fill(a.zero_per_row, a.zero_rows);
+    if (table_wg) {                      // offsets from this workgroup's own histogram
+      const int64_t wg = (int64_t)blockIdx.x - table_wg0;
+      build_tile_tables(s_off, E, a.tables[0], a.tables[1], a.num_tables, wg * 256 + threadIdx.x,
+                        (int64_t)kTableWorkgroups * 256, tls);
+      return;
+    }
+  }
   auto chunk_base = [&](int e, int64_t chunk) -> int64_t {
     if constexpr (SMALL) return s_bef[e];
     else return base[(int64_t)e * nchunks + chunk];
@@ -453,13 +477,15 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int tpw = tokens_per_wave(bpl);
   const int64_t token_waves = (a.tokens + tpw - 1) / tpw;
   const int64_t waves = token_waves + E;
-  dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  const int64_t table_wg0 = (waves + 3) / 4;
+  const int64_t twg = a.num_tables > 0 ? kTableWorkgroups : 0;
+  dim3 grid((unsigned)(table_wg0 + twg)), block(256);
   const int kmax = a.topk <= 8 ? 8 : (a.topk <= 16 ? 16 : 0);
   switch (bpl * 100 + kmax) {
 #define NVFP4_SCATTER(B, KM) \
     case B * 100 + KM:                                                                              \
-      if (small) route_scatter_kernel<B, KM, true><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks); \
-      else route_scatter_kernel<B, KM, false><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks); \
+      if (small) route_scatter_kernel<B, KM, true><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks, table_wg0); \
+      else route_scatter_kernel<B, KM, false><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks, table_wg0); \
       break;
     NVFP4_SCATTER(1, 8) NVFP4_SCATTER(2, 8) NVFP4_SCATTER(4, 8) NVFP4_SCATTER(8, 8) NVFP4_SCATTER(16, 8)
     NVFP4_SCATTER(1, 16) NVFP4_SCATTER(2, 16) NVFP4_SCATTER(4, 16) NVFP4_SCATTER(8, 16) NVFP4_SCATTER(16, 16)

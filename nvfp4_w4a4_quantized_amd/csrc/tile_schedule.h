@@ -1,0 +1,160 @@
+// tile_schedule.h -- the grouped GEMM's tile schedule, shared by the GEMM
+// (which derives its own tile without a table) and the routing kernels
+// (which write the FC1 and FC2 tables of the expert layer while they hold
+// the expert offsets).
+//
+// Tiles are numbered m-tile major with the n-tiles inner, m-tiles group by
+// group (ceil(rows_g / BM) per group).  Workgroups are dealt to the 8 XCDs
+// round robin (workgroup b runs on XCD b % 8), and the tiles are cut into 8
+// contiguous ranges of about equal estimated cost, one per XCD, at m-tile
+// boundaries: consecutive tiles share A rows and, inside a group, B rows,
+// which then stay in that XCD's L2, and no XCD runs dry long before the
+// others.  Workgroup b takes tile b / 8 of its XCD's range.  A tile with v
+// valid 32-row blocks and S K-stages costs kCostFixed + S (kCostStage + v)
+// units: its prologue and epilogue, and the B decode and loads of every
+// stage, do not shrink with its rows.
+#pragma once
+
+#include <algorithm>
+#include <cstdint>
+
+#include "nvfp4_device.h"
+
+namespace nvfp4 {
+
+constexpr int kKS = 128;                    // K per stage
+constexpr uint32_t kCostFixed = 24, kCostStage = 2;
+constexpr uint32_t kCostMaxStages = 16;     // keeps the total cost inside 32 bits
+
+__device__ __forceinline__ uint32_t tile_cost(uint32_t v, uint32_t stages) {
+  return kCostFixed + stages * (kCostStage + v);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v = wave_incl_scan_dpp(v, [](uint32_t x, uint32_t y) { return x + y; });
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+__device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t v) {
+  return wave_incl_scan_dpp(v, [](uint32_t x, uint32_t y) { return x + y; });
+}
+
+// One GEMM launch's tile table: one {group, row0, row1, n-tile} entry per
+// workgroup position (group < 0: no tile), for bm-row tiles, ntn n-tiles per
+// m-tile, K (the cost model's stages) and the launch's `blocks` positions.
+struct TileTableSpec {
+  int4* table;
+  int32_t bm;
+  int64_t k, ntn, blocks;
+};
+
+constexpr int kMaxTableGroups = 1024;
+
+// LDS of the table builder (the calling kernel declares one).
+struct TileTableLds {
+  uint32_t cnt[kMaxTableGroups], cost[kMaxTableGroups], full[kMaxTableGroups];
+  uint32_t ic[kMaxTableGroups], ik[kMaxTableGroups];   // inclusive prefix sums
+  uint32_t wc[4], wk[4], f0[8], f1[8];
+};
+
+// Writes entries first, first + stride, ... of the table from the offsets
+// off[0..G] (global or LDS), exactly as the GEMM's own lookup derives each
+// workgroup's tile: per-group m-tile counts and costs with their inclusive
+// prefix sums over the groups, the 8 XCD cut points (the first m-tiles whose
+// preceding cost reaches x/8 of the total), then for every position b its
+// XCD range position, m-tile, n-tile, group and rows.  A 256-thread
+// workgroup calls it (it synchronises the workgroup), G <= kMaxTableGroups.
+template <int BM>
+__device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec& t, int64_t first,
+                                 int64_t stride, TileTableLds& s) {
+  constexpr int PER = kMaxTableGroups / 256;    // groups per thread, contiguous
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const uint32_t stages = (uint32_t)std::min<int64_t>(t.k / kKS, kCostMaxStages);
+  const uint32_t full_cost = tile_cost(BM / 32, stages);
+  uint32_t lc = 0, lk = 0;
+  uint32_t pc[PER], pk[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int gi = PER * tid + i;
+    uint32_t cnt = 0, cost = 0, full = 0;
+    if (gi < G) {
+      const int64_t n = (int64_t)off[gi + 1] - (int64_t)off[gi];
+      if (n > 0) {
+        const uint32_t f = (uint32_t)(n / BM), rem = (uint32_t)(n % BM);
+        full = f;
+        cnt = f + (rem ? 1u : 0u);
+        cost = f * full_cost + (rem ? tile_cost((rem + 31) / 32, stages) : 0u);
+      }
+      s.cnt[gi] = cnt; s.cost[gi] = cost; s.full[gi] = full;
+    }
+    lc += cnt; lk += cost;
+    pc[i] = lc; pk[i] = lk;                        // inclusive within the thread
+  }
+  const uint32_t ic = wave_incl_sum_u32(lc), ik = wave_incl_sum_u32(lk);
+  if (lane == kWave - 1) { s.wc[w] = ic; s.wk[w] = ik; }
+  __syncthreads();
+  uint32_t bc = ic - lc, bk = ik - lk;             // exclusive over the workgroup
+  for (int j = 0; j < w; ++j) { bc += s.wc[j]; bk += s.wk[j]; }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int gi = PER * tid + i;
+    if (gi < G) { s.ic[gi] = bc + pc[i]; s.ik[gi] = bk + pk[i]; }
+  }
+  __syncthreads();
+  const uint32_t tiles = s.ic[G - 1], total = s.ik[G - 1];
+  // XCD x's m-tile range [f0, f1): the first m-tile of the first group whose
+  // inclusive cost reaches the cut, as in the GEMM's lookup
+  auto find = [&](uint32_t c) -> uint32_t {
+    int lo = 0, hi = G;                            // first group with ik >= c
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s.ik[mid] >= c) hi = mid; else lo = mid + 1;
+    }
+    if (lo >= G) return tiles;
+    const uint32_t cnt = s.cnt[lo], ec = s.ic[lo] - cnt, ek = s.ik[lo] - s.cost[lo];
+    uint32_t j = c > ek ? (c - ek + full_cost - 1) / full_cost : 0u;
+    if (j > s.full[lo]) j = cnt;                   // inside the partial tile: take the next one
+    return ec + j;
+  };
+  if (tid < 8) {
+    const int x = tid;
+    s.f0[x] = find((uint32_t)((uint64_t)total * x / 8));
+    s.f1[x] = x == 7 ? tiles : find((uint32_t)((uint64_t)total * (x + 1) / 8));
+  }
+  __syncthreads();
+  const uint32_t un = (uint32_t)t.ntn;
+  for (int64_t b = first; b < t.blocks; b += stride) {
+    const int x = (int)(b % 8);
+    const uint32_t pos = (uint32_t)(b / 8);
+    const uint32_t logical = s.f0[x] * un + pos;
+    int4 e = make_int4(-1, 0, 0, 0);
+    if (logical < s.f1[x] * un) {
+      const uint32_t mt = logical / un;
+      int lo = 0, hi = G - 1;                      // first group with ic > mt
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (s.ic[mid] > mt) hi = mid; else lo = mid + 1;
+      }
+      const int32_t r0 = off[lo] + (int32_t)(mt - (s.ic[lo] - s.cnt[lo])) * BM;
+      const int32_t r1 = std::min<int32_t>(r0 + BM, off[lo + 1]);
+      e = make_int4(lo, r0, r1, (int)(logical - mt * un));
+    }
+    t.table[b] = e;
+  }
+  __syncthreads();                                 // the LDS arrays may be reused next
+}
+
+// The first n (0-2) of the tables t0, t1: this thread's entries first,
+// first + stride, ... of each (256-thread workgroups).
+__device__ __forceinline__ void build_tile_tables(const int32_t* off, int G, const TileTableSpec& t0,
+                                                  const TileTableSpec& t1, int n, int64_t first,
+                                                  int64_t stride, TileTableLds& s) {
+  auto one = [&](const TileTableSpec& t) {
+    if (t.bm == 32) build_tile_table<32>(off, G, t, first, stride, s);
+    else build_tile_table<128>(off, G, t, first, stride, s);
+  };
+  if (n > 0) one(t0);
+  if (n > 1) one(t1);
+}
+
+}  // namespace nvfp4

@@ -150,3 +150,28 @@ def test_perf_path_bf16_rows_and_determinism():
     yref, yb = O.grouped_gemm_at(*A2, *W2, it["expert_offsets"], rows, cols)
     got = bf16_bits_to_f32(it["y_rows"][rows, cols]).astype(np.float64)
     assert np.all(np.abs(got - yref) <= 2.0 ** -10 * yb + 1e-6 + bf16_ulp(yref) * 0.5001)
+
+
+@pytest.mark.parametrize("tokens,experts,zipf", [(160, 300, 0.0), (2000, 300, 1.2)])
+def test_many_experts_replay_chain(tokens, experts, zipf):
+    """300 experts: the layer's precomputed tile schedules span groups held by
+    several waves of their builder, on the 32-row tile (about 3 rows per
+    expert) and on the 128-row tile with skewed routing (empty, tiny and
+    multi-tile experts); every step of the chain is checked in full."""
+    from nvfp4_w4a4_quantized_amd.workloads import MoeWorkload, random_bf16, route_topk
+    rng = np.random.default_rng(tokens + experts)
+    H, I, k = 256, 128, 6
+    logits = rng.standard_normal((tokens, experts)).astype(np.float32)
+    if zipf:
+        logits += (-zipf * np.log(np.arange(1, experts + 1))).astype(np.float32)
+    idx, prob = route_topk(logits, k)
+    w = MoeWorkload(f"many_experts_t{tokens}", -1, tokens, H, I, experts, k,
+                    random_bf16(rng, (tokens, H)), idx, prob, None, None, {})
+    from gpu_util import oracle_weights
+    W1 = oracle_weights(random_bf16(rng, (experts, 2 * I, H), 0.02))
+    W2 = oracle_weights(random_bf16(rng, (experts, H, I), 0.02))
+    y, it, _ = _replay_chain(w, W1, W2, 1, True, rng)
+    yo, _ = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2)
+    a = bf16_bits_to_f32(y).astype(np.float64)
+    b = bf16_bits_to_f32(yo).astype(np.float64)
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-2
