@@ -14,9 +14,10 @@
 // §4.2: FP32 rescaling after the block-scaled product).
 //
 // Structure: see the kernel comment below.  Group boundaries come from the
-// device offsets: every workgroup derives its (group, m-tile) from a
-// wave-wide scan of the per-group tile counts, so the host never reads them;
-// surplus workgroups exit.
+// device offsets, so the host never reads them: every workgroup derives its
+// (group, m-tile) from a wave-wide scan of the per-group tile counts, or
+// reads it from a tile table that a kernel holding the offsets wrote
+// beforehand (tile_schedule.h); surplus workgroups exit.
 #include <type_traits>
 #include <algorithm>
 
