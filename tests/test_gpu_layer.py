@@ -175,3 +175,24 @@ def test_many_experts_replay_chain(tokens, experts, zipf):
     a = bf16_bits_to_f32(y).astype(np.float64)
     b = bf16_bits_to_f32(yo).astype(np.float64)
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-2
+
+
+@pytest.mark.parametrize("tokens,align", [(0, 1), (0, 16), (1, 1), (1, 16)])
+def test_empty_and_single_token_layer(tokens, align):
+    """No tokens: the tile tables are empty and every GEMM workgroup exits;
+    y is empty.  One token: k rows in k experts (padded rows with align > 1),
+    checked against the oracle layer."""
+    from nvfp4_w4a4_quantized_amd.ops import moe_expert_forward
+    w, W1, W2 = moe_case(0)
+    x, idx, prob = w.x[:tokens], w.topk_idx[:tokens], w.topk_prob[:tokens]
+    say("moe_expert_forward tokens", tokens, "align", align)
+    y = moe_expert_forward(dev_bf16(x.reshape(tokens, w.hidden)), dev(idx.reshape(tokens, w.topk)),
+                           dev(prob.reshape(tokens, w.topk)), w.experts, w.inter, _weights(W1),
+                           _weights(W2), align=align)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (tokens, w.hidden)
+    if tokens:
+        yo, _ = O.moe_forward(x, idx, prob, w.experts, w.inter, W1, W2, align=align)
+        a = bf16_bits_to_f32(host(y)).astype(np.float64)
+        b = bf16_bits_to_f32(yo).astype(np.float64)
+        assert np.linalg.norm(a - b) <= 2e-2 * np.linalg.norm(b) + 1e-6
