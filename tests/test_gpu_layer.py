@@ -196,3 +196,26 @@ def test_empty_and_single_token_layer(tokens, align):
         a = bf16_bits_to_f32(host(y)).astype(np.float64)
         b = bf16_bits_to_f32(yo).astype(np.float64)
         assert np.linalg.norm(a - b) <= 2e-2 * np.linalg.norm(b) + 1e-6
+
+
+@pytest.mark.parametrize("wid", [0, 2, 3])
+def test_forward_equals_composed_calls(wid):
+    """moe_expert_forward (GEMM tiles from the tables its routing launch
+    writes) against the same layer composed from the public calls (GEMM tiles
+    from each workgroup's own lookup): every kernel is deterministic and an
+    output element sees the same arithmetic whichever workgroup computes it,
+    so y matches bit for bit."""
+    from nvfp4_w4a4_quantized_amd import ops
+    w, W1, W2 = moe_case(wid)
+    x, idx, prob = dev_bf16(w.x), dev(w.topk_idx), dev(w.topk_prob)
+    w1, w2 = _weights(W1), _weights(W2)
+    say("forward vs composed calls", wid)
+    y = ops.moe_expert_forward(x, idx, prob, w.experts, w.inter, w1, w2)
+    p = ops.moe_permute(x, idx, prob, w.experts)
+    d, amax, _ = ops.w4a4_grouped_gemm_swiglu(p["codes"], p["scales"], p["gscale"], w1,
+                                             p["offsets"], p["row_prob"])
+    a2c, a2s, a2g = ops.nvfp4_quantize(d, amax_in=amax)
+    rows = ops.w4a4_grouped_gemm(a2c, a2s, a2g, w2, p["offsets"], out_dtype=torch.bfloat16)
+    yc = ops.moe_combine(rows, p["dst_row"])
+    torch.cuda.synchronize()
+    assert torch.equal(y, yc)
