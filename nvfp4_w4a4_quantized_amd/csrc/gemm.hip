@@ -431,23 +431,31 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
   }
   u32x4_t araw[APT];
   uint32_t asc[APT];
+  auto a_load_unit = [&](int j, int64_t st) {
+    araw[j] = *reinterpret_cast<const u32x4_t*>(a_cbase + st * 64 + a_src[j]);
+    asc[j] = *reinterpret_cast<const uint16_t*>(a_sbase + st * 8 + a_ssrc[j]);
+  };
   auto a_load = [&](int64_t st) {
 #pragma unroll
-    for (int j = 0; j < APT; ++j) {
-      araw[j] = *reinterpret_cast<const u32x4_t*>(a_cbase + st * 64 + a_src[j]);
-      asc[j] = *reinterpret_cast<const uint16_t*>(a_sbase + st * 8 + a_ssrc[j]);
-    }
+    for (int j = 0; j < APT; ++j) a_load_unit(j, st);
   };
-  // decode chunk c (8 elements) of the thread's quarter rows into buffer buf
-  auto a_decode = [&](int c, int buf) {
+  // decode chunk c (8 elements) of quarter row j into buffer buf
+  auto a_decode_unit = [&](int j, int c, int buf) {
     uint8_t* sb = smem + buf * A_BYTES;
-#pragma unroll
-    for (int j = 0; j < APT; ++j) {
-      const half2_t s2 = e4m3x2_to_half2(asc[j]);
-      const _Float16 sc = (c < 2) ? s2[0] : s2[1];
-      *reinterpret_cast<half8_t*>(sb + a_dst[j] + c * 1024) = decode8(araw[j][c], half2_t{sc, sc});
-    }
+    const half2_t s2 = e4m3x2_to_half2(asc[j]);
+    const _Float16 sc = (c < 2) ? s2[0] : s2[1];
+    *reinterpret_cast<half8_t*>(sb + a_dst[j] + c * 1024) = decode8(araw[j][c], half2_t{sc, sc});
   };
+  auto a_decode = [&](int c, int buf) {
+#pragma unroll
+    for (int j = 0; j < APT; ++j) a_decode_unit(j, c, buf);
+  };
+  // With two quarter rows per thread, the next stage's A is decoded one
+  // chunk per substep (row 0 in substeps 0-3, row 1 in 4-7) and each row's
+  // registers take the stage after that as soon as its last chunk is decoded;
+  // otherwise all rows are decoded in substeps 4-7 and reloaded after the
+  // stage.  Spreading keeps the decode arithmetic even across the substeps.
+  constexpr bool A_SPREAD = APT == 2;
 
   float16_t acc[WM][WN];
 #pragma unroll
@@ -490,7 +498,7 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
   // last stages re-fetch the last one): with a branch around them the
   // compiler has to assume the short path and waits for the loads just
   // issued before the A decode.
-  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bload, BSet& cb, BSet& nb) {
+  auto compute = [&](auto mv_c, int buf, int nxt, int64_t bload, int64_t aload, BSet& cb, BSet& nb) {
     constexpr int MV = decltype(mv_c)::value;
     constexpr int VPM = NVFP4_VPM;                 // VALU per MFMA slot
     const uint8_t* sb = smem + buf * A_BYTES;
@@ -523,7 +531,12 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
           acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[m], fbc[n], acc[m][n], 0, 0, 0);
         if (s < 7) fa[m] = a_frag(m, s + 1);
       }
-      if (s >= 4) a_decode(s - 4, nxt);
+      if constexpr (A_SPREAD) {
+        a_decode_unit(s / 4, s % 4, nxt);
+        if (s % 4 == 3) a_load_unit(s / 4, aload);
+      } else if (s >= 4) {
+        a_decode(s - 4, nxt);
+      }
       if (s == 2) b_load_c0(cb, bload);  // substeps 0-3 decoded
       if (s == 6) b_load_c1(cb, bload);  // substeps 4-7 decoded
 #pragma unroll
@@ -591,8 +604,8 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
     prologue();
     for (int64_t it = 0; it < nst; ++it) {
       const int cur = (int)(it & 1), nxt = cur ^ 1;
-      compute(mv_c, cur, nxt, clamp_st(it + 1), bx, bx);
-      a_load(clamp_st(it + 2));
+      compute(mv_c, cur, nxt, clamp_st(it + 1), clamp_st(it + 2), bx, bx);
+      if constexpr (!A_SPREAD) a_load(clamp_st(it + 2));
       __syncthreads();
     }
   };
@@ -604,11 +617,11 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
     b_load_c0(by, clamp_st(1));
     b_load_c1(by, clamp_st(1));
     for (int64_t it = 0; it < nst; it += 2) {
-      compute(mv_c, 0, 1, clamp_st(it + 2), bx, by);
-      a_load(clamp_st(it + 2));
+      compute(mv_c, 0, 1, clamp_st(it + 2), clamp_st(it + 2), bx, by);
+      if constexpr (!A_SPREAD) a_load(clamp_st(it + 2));
       __syncthreads();
-      compute(mv_c, 1, 0, clamp_st(it + 3), by, bx);
-      a_load(clamp_st(it + 3));
+      compute(mv_c, 1, 0, clamp_st(it + 3), clamp_st(it + 3), by, bx);
+      if constexpr (!A_SPREAD) a_load(clamp_st(it + 3));
       __syncthreads();
     }
   };

@@ -1,0 +1,67 @@
+"""Host checks of the profile summarisers (counter files are synthetic here)."""
+import csv
+import json
+
+from nvfp4_w4a4_quantized_amd import mfma_counters, traffic
+
+COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+        "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+        "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+        "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+FC1 = "void nvfp4::gemm_w4a4_kernel<4, 2, 4, 2>(nvfp4::GemmArgs)"
+FC2 = "void nvfp4::gemm_w4a4_kernel<4, 2, 4, 1>(nvfp4::GemmArgs)"
+COPY = "void at::native::vectorized_elementwise_kernel<4, bitwise_not>(int)"
+
+
+def _write(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COLS)
+        w.writeheader()
+        for i, (did, name, grid, counter, value, t0, t1) in enumerate(rows):
+            w.writerow({c: 0 for c in COLS} | {
+                "Correlation_Id": i, "Dispatch_Id": did, "Kernel_Name": name,
+                "Grid_Size": grid, "Counter_Name": counter, "Counter_Value": value,
+                "Start_Timestamp": t0, "End_Timestamp": t1})
+
+
+def test_mfma_counters_groups_by_launch_and_drops_warmup(tmp_path):
+    p = tmp_path / "m.csv"
+    rows = []
+    # FC1: a slow warm-up dispatch, then two at 400 us with 450 GFLOP of MOPS
+    for did, ns, util in ((1, 900_000, 10.0), (3, 400_000, 50.0), (5, 400_000, 60.0)):
+        rows.append((did, FC1, 1000, "MfmaUtil", util, 0, ns))
+        rows.append((did, FC1, 1000, "SQ_INSTS_VALU_MFMA_MOPS_F16", 450e9 / 512, 0, ns))
+    # the same kernel at two grid sizes (two dense GEMMs) stays apart
+    for did, grid in ((7, 2000), (8, 3000), (9, 2000), (10, 3000)):
+        rows.append((did, FC2, grid, "MfmaUtil", 40.0, 0, 100_000))
+        rows.append((did, FC2, grid, "SQ_INSTS_VALU_MFMA_MOPS_F16", 100e9 / 512, 0, 100_000))
+    _write(p, rows)
+    per = mfma_counters.per_dispatch(str(p))
+    assert [len(v) for v in per.values()] == [3, 2, 2]
+    text = mfma_counters.table(str(p), {"4, 2, 4, 2>": 412.3, "/3000": 90.0})
+    lines = [l for l in text.splitlines() if l.startswith("| `")]
+    assert len(lines) == 3
+    fc1 = lines[0].split("|")
+    # warm-up dropped: 400 us, 55% mean utilisation, 450 GFLOP -> 1125 TFLOP/s
+    assert fc1[3].strip() == "2" and fc1[4].strip() == "400.0" and fc1[5].strip() == "55.0%"
+    assert fc1[6].strip() == "450.0" and fc1[7].strip() == "412.3" and fc1[8].strip() == "1125"
+    assert lines[1].split("|")[7].strip() == "-" and lines[2].split("|")[7].strip() == "90.0"
+
+
+def test_traffic_scales_by_copy_calibration(tmp_path):
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    mib = 64
+    known = mib << 20
+    # the copy reads half its bytes by FETCH_SIZE (KiB) and all of them by WRITE_SIZE
+    _write(f, [(1, COPY, 1, "FETCH_SIZE", known / 2 / 1024, 0, 1),
+               (2, FC1, 1, "FETCH_SIZE", 100_000.0, 0, 1),
+               (3, FC1, 1, "FETCH_SIZE", 300_000.0, 0, 1)])
+    _write(w, [(1, COPY, 1, "WRITE_SIZE", known / 1024, 0, 1),
+               (2, FC1, 1, "WRITE_SIZE", 50_000.0, 0, 1),
+               (3, FC1, 1, "WRITE_SIZE", 50_000.0, 0, 1)])
+    out = tmp_path / "t.json"
+    traffic.main(["traffic", str(f), str(w), str(mib), str(out)])
+    rec = json.load(open(out))
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["fc1_hbm_bytes_per_launch"] == 2.0 * 200_000 * 1024 + 50_000 * 1024
+    assert rec["gemm_source_sha256"] == traffic.gemm_source_hash()
