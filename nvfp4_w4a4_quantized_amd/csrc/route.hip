@@ -271,13 +271,37 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
   const int nblocks = (int)(H / 16);
 
   // Phase 1: every load of the wave is issued before any store (a store may
-  // alias a later load as far as the compiler knows): the tokens' rows, the
-  // chunk's expert ids, and the destinations with their base counters.
+  // alias a later load as far as the compiler knows) and before the first
+  // barrier (loads do not move across one): the tokens' rows, the chunk's
+  // expert ids, the router weights of the lane's entries and, for small
+  // batches, all the routing entries for the histogram.  The kernel then
+  // waits for memory once.
   uint32_t w[TPW][BPL][8];
   if (a.x) {
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti)
       if (ti < nt) load_token_row<BPL>(a.x + (t0 + ti) * H, nblocks, lane, w[ti]);
+  }
+  const int64_t chunk = t0 / kChunk;
+  const int64_t tl = chunk * kChunk + lane;          // token of this lane in the chunk
+  const bool lane_valid = tl < a.tokens && nt > 0;
+  int ids[KMAX > 0 ? KMAX : 1];                      // the expert ids of the lane's chunk token
+  float prob_l[TPW];                                 // router weight of entry `lane` of token ti
+  if constexpr (KMAX > 0) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) ids[i] = (lane_valid && i < k) ? a.topk_idx[tl * k + i] : -1;
+#pragma unroll
+    for (int ti = 0; ti < TPW; ++ti) prob_l[ti] = (ti < nt && lane < k) ? a.topk_prob[(t0 + ti) * k + lane] : 0.0f;
+  }
+  constexpr int kHistPer = SMALL ? (int)(kSmallEntries / 256) : 1;   // entries per thread
+  int hist_ids[kHistPer];
+  if constexpr (SMALL) {
+    const int64_t nent = a.tokens * k;
+#pragma unroll
+    for (int u = 0; u < kHistPer; ++u) {
+      const int64_t i = threadIdx.x + 256 * u;
+      hist_ids[u] = i < nent ? a.topk_idx[i] : -1;
+    }
   }
 
   // SMALL: per-expert entries (s_cnt), those before the chunk (s_bef, then
@@ -289,9 +313,11 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     for (int e = tid; e < E; e += 256) { s_cnt[e] = 0; s_bef[e] = 0; }
     __syncthreads();
     const int64_t c0 = ((int64_t)blockIdx.x * 4 * TPW) / kChunk * kChunk;   // the chunk's first token
-    const int64_t nent = a.tokens * k, nbef = (c0 < a.tokens ? c0 : a.tokens) * k;
-    for (int64_t i = tid; i < nent; i += 256) {
-      const int e = a.topk_idx[i];
+    const int64_t nbef = (c0 < a.tokens ? c0 : a.tokens) * k;
+#pragma unroll
+    for (int u = 0; u < kHistPer; ++u) {
+      const int64_t i = tid + 256 * u;
+      const int e = hist_ids[u];
       if (e >= 0 && e < E) {
         atomicAdd(s_cnt + e, 1);
         if (i < nbef) atomicAdd(s_bef + e, 1);
@@ -346,17 +372,11 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     }
     return;
   }
-  const int64_t chunk = t0 / kChunk;
-  const int64_t tl = chunk * kChunk + lane;          // token of this lane in the chunk
-  const bool lane_valid = tl < a.tokens;
   // destination of entry j of token ti is held by lane j (lanes < k)
   int64_t dst_l[TPW];
   if constexpr (KMAX > 0) {
     // every lane holds the k expert ids of its own chunk token, so the
     // ballots need no memory traffic; a token's ids come from its lane
-    int ids[KMAX];
-#pragma unroll
-    for (int i = 0; i < KMAX; ++i) ids[i] = (lane_valid && i < k) ? a.topk_idx[tl * k + i] : -1;
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti) {
       dst_l[ti] = -1;
@@ -417,16 +437,16 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
         }
       }
     };
-    // the maps of entry j, by the lane that holds it
-    auto store_meta = [&](int j, int64_t dst) {
+    // the maps of entry j (router weight p), by the lane that holds it
+    auto store_meta = [&](int j, int64_t dst, float p) {
       a.dst_row[t * k + j] = (int32_t)dst;
       if (dst < 0) return;
       if (a.row_src) a.row_src[dst] = (int32_t)t;
-      a.row_prob[dst] = a.topk_prob[t * k + j];
+      a.row_prob[dst] = p;
       if (a.x) a.gscale[dst] = s_g;
     };
     if constexpr (KMAX > 0) {
-      if (lane < k) store_meta(lane, dst_l[ti]);
+      if (lane < k) store_meta(lane, dst_l[ti], prob_l[ti]);
 #pragma unroll
       for (int j = 0; j < KMAX; ++j)
         if (j < k) store_row(__shfl(dst_l[ti], j, kWave));
@@ -443,7 +463,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
           const uint64_t mask = __ballot(hit);
           dst = chunk_base(e, chunk) + __popcll(mask & below_mask);
         }
-        if (lane == 0) store_meta(j, dst);
+        if (lane == 0) store_meta(j, dst, a.topk_prob[t * k + j]);
         store_row(dst);
       }
     }
