@@ -580,15 +580,33 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
     a_load(0);
     b_load_s(bx, 0);
     b_load_c0(bx, 0);
-    b_load_c1(bx, 0);
-    {
-      half2_t bsc[WN][2];
-      b_scales(bx, bsc);
-      b_decode(bx, 0, bsc, fbc);
-    }
+    if constexpr (A_SPREAD) {
+      // the loads left in flight end in the loop's own order (A row 0 of
+      // stage 1, B codes of substeps 4-7, A row 1), so the wait counts the
+      // compiler derives at the loop head hold for both ways in
+      {
+        half2_t bsc[WN][2];
+        b_scales(bx, bsc);
+        b_decode(bx, 0, bsc, fbc);
+      }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a_decode(c, 0);
-    a_load(nst > 1 ? 1 : 0);
+      for (int c = 0; c < 4; ++c) a_decode_unit(0, c, 0);
+      a_load_unit(0, nst > 1 ? 1 : 0);
+      b_load_c1(bx, 0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a_decode_unit(1, c, 0);
+      a_load_unit(1, nst > 1 ? 1 : 0);
+    } else {
+      b_load_c1(bx, 0);
+      {
+        half2_t bsc[WN][2];
+        b_scales(bx, bsc);
+        b_decode(bx, 0, bsc, fbc);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a_decode(c, 0);
+      a_load(nst > 1 ? 1 : 0);
+    }
     if (tid < BM) {
       const float sc = rf_sa * sgb;               // C = ACC * s_ga * s_gb
       rfac[tid] = sc;
