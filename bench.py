@@ -305,8 +305,8 @@ def cpu_baseline(w, n_tokens):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the sharded path is described in DESIGN.md, not built)", file=sys.stderr)
+        print(f"bench.py: the expert layer runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is designed, not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
 

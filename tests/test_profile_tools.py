@@ -65,3 +65,14 @@ def test_traffic_scales_by_copy_calibration(tmp_path):
     assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
     assert rec["fc1_hbm_bytes_per_launch"] == 2.0 * 200_000 * 1024 + 50_000 * 1024
     assert rec["gemm_source_sha256"] == traffic.gemm_source_hash()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
