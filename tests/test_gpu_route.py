@@ -72,12 +72,13 @@ def _fixture_routing(rng, T, k, E, kind):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 300, 1100])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 300, 1024, 1025, 1100])
 @pytest.mark.parametrize("kind", ["empty_and_tiny", "one_expert", "dropped"])
 def test_edge_routings(T, kind):
     """Up to 4096 routing entries (T*k) the permutation runs as one launch
-    that histograms the ids in every workgroup; T = 1100 (4400 entries) takes
-    the histogram / scan / scatter launches."""
+    that histograms the ids in every workgroup (T = 1024: exactly 4096, every
+    thread holding 16 of them); from T = 1025 (4100 entries) it takes the
+    histogram / scan / scatter launches."""
     rng = np.random.default_rng(T * 31 + len(kind))
     E, k, H = 16, 4, 256
     idx = _fixture_routing(rng, T, k, E, kind)
