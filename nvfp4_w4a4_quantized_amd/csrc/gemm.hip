@@ -57,10 +57,12 @@ __device__ __forceinline__ half8_t decode8(uint32_t c, half2_t sb) {
 
 // ---- kernel --------------------------------------------------------------
 //
-// Workgroup = NW waves side by side along N, sized so that two workgroups
-// share a compute unit (one wave of each per SIMD): while one workgroup sits
-// in its prologue, a barrier or its VALU-heavy epilogue, the other keeps the
-// matrix cores busy.  The workgroup owns a BM x BN output tile of one group
+// Workgroup = NW waves side by side along N, each with the register budget
+// of two waves per SIMD.  With four waves two workgroups share a compute unit
+// (one wave of each per SIMD): while one workgroup sits in its prologue, a
+// barrier or its VALU-heavy epilogue, the other keeps the matrix cores busy.
+// With eight waves one workgroup fills the unit and each decoded A stage
+// serves twice the columns.  The workgroup owns a BM x BN output tile of one group
 // (BM = 32*WM rows, BN = NW*32*WN columns); each wave a BM x (32*WN) sub-tile
 // held in accumulator registers (WM x WN v_mfma_f32_32x32x16_f16 tiles).
 // K advances in stages of 128.
@@ -919,7 +921,12 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 }
 
 // Tiles: MFMA blocks per wave (M, N) and waves per workgroup (along N).  The
-// 128 x 256 tile serves groups of many rows.  When the groups average at
+// 128 x 256 tile serves groups of many rows, two workgroups per CU.  FC1
+// (the SwiGLU epilogue) takes the 128 x 512 tile, one workgroup per CU: its
+// 16-stage K loop gains more from decoding each A stage for twice the
+// columns than it loses without a second workgroup to cover prologue and
+// epilogue; FC2's 6-stage loop and the plain GEMMs lose more than they
+// gain, so they keep 128 x 256.  When the groups average at
 // most kSmallTileRows rows (decode-sized batches: a few rows per expert) the
 // 128-row tile would multiply one 32-row block and leave the weight stream
 // at two workgroups per CU; the 32 x 128 tile runs four waves per SIMD, so
@@ -928,7 +935,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 #define NVFP4_GEMM_TILE 4, 2, 4
 #endif
 #ifndef NVFP4_GEMM_TILE_FC1
-#define NVFP4_GEMM_TILE_FC1 NVFP4_GEMM_TILE
+#define NVFP4_GEMM_TILE_FC1 4, 2, 8
 #endif
 #define NVFP4_GEMM_TILE_SMALL 1, 2, 2
 #ifndef NVFP4_SMALL_TILE_ROWS

@@ -254,7 +254,8 @@ def _pad_rows(a: np.ndarray, rows: int) -> np.ndarray:
 def test_small_and_large_tiles_agree(epi, tiled, K):
     """Groups of a few rows (at most 32 on average) run on the 32 x 128 tile;
     the same problem with its row capacity padded past 32 rows per group runs
-    on the 128 x 256 tile.  Both match the oracle, and each other bit for bit
+    on the 128-row tile (128 x 256; 128 x 512 with the SwiGLU epilogue).  Both
+    match the oracle, and each other bit for bit
     (every output element sees the same MFMA sequence).  K = 384 (3 stages)
     takes the small tile's one-B-set loop, K = 512 (4 stages) its two-set
     loop."""

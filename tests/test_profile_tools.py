@@ -8,7 +8,7 @@ COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "
         "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
         "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
         "Counter_Value", "Start_Timestamp", "End_Timestamp"]
-FC1 = "void nvfp4::gemm_w4a4_kernel<4, 2, 4, 2>(nvfp4::GemmArgs)"
+FC1 = "void nvfp4::gemm_w4a4_kernel<4, 2, 8, 2>(nvfp4::GemmArgs)"
 FC2 = "void nvfp4::gemm_w4a4_kernel<4, 2, 4, 1>(nvfp4::GemmArgs)"
 COPY = "void at::native::vectorized_elementwise_kernel<4, bitwise_not>(int)"
 
@@ -38,7 +38,7 @@ def test_mfma_counters_groups_by_launch_and_drops_warmup(tmp_path):
     _write(p, rows)
     per = mfma_counters.per_dispatch(str(p))
     assert [len(v) for v in per.values()] == [3, 2, 2]
-    text = mfma_counters.table(str(p), {"4, 2, 4, 2>": 412.3, "/3000": 90.0})
+    text = mfma_counters.table(str(p), {"4, 2, 8, 2>": 412.3, "/3000": 90.0})
     lines = [l for l in text.splitlines() if l.startswith("| `")]
     assert len(lines) == 3
     fc1 = lines[0].split("|")
