@@ -922,11 +922,13 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 
 // Tiles: MFMA blocks per wave (M, N) and waves per workgroup (along N).  The
 // 128 x 256 tile serves groups of many rows, two workgroups per CU.  FC1
-// (the SwiGLU epilogue) takes the 128 x 512 tile, one workgroup per CU: its
-// 16-stage K loop gains more from decoding each A stage for twice the
-// columns than it loses without a second workgroup to cover prologue and
-// epilogue; FC2's 6-stage loop and the plain GEMMs lose more than they
-// gain, so they keep 128 x 256.  When the groups average at
+// (the SwiGLU epilogue; K = hidden size, 16 stages at 2048) takes the
+// 128 x 512 tile, one workgroup per CU: it gains more from decoding each A
+// stage for twice the columns than it loses without a second workgroup to
+// cover prologue and epilogue.  The plain GEMMs keep 128 x 256: FC2's short
+// K (the intermediate size, 6 stages at 768) loses on the wider tile, and
+// for dense shapes the outcome depends on how the tiles fill the last round
+// of the grid.  When the groups average at
 // most kSmallTileRows rows (decode-sized batches: a few rows per expert) the
 // 128-row tile would multiply one 32-row block and leave the weight stream
 // at two workgroups per CU; the 32 x 128 tile runs four waves per SIMD, so
