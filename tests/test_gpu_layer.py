@@ -91,17 +91,30 @@ def _replay_chain(w, W1, W2, align, full, rng):
     return y, it, ybound
 
 
+def _requant_flip_rate(it, ref, rows):
+    """Fraction of FC2-input E2M1 codes (nibbles of the routed rows) that differ
+    between the GPU layer and a pure oracle run.  They differ only where the
+    two FC1 accumulations round a D value differently, which moves a code
+    across a threshold or changes the row's amax."""
+    g = it["a2_codes"][:rows].view(np.uint8)
+    o = ref["a2_codes"][:rows].view(np.uint8)
+    diff = ((g & 0xF) != (o & 0xF)).sum() + ((g >> 4) != (o >> 4)).sum()
+    return diff / (2.0 * g.size)
+
+
 @pytest.mark.parametrize("align", [1, 16])
 def test_tiny_layer_replay_chain_and_end_to_end(align):
     w, W1, W2 = moe_case(0)
     rng = np.random.default_rng(1)
     y, it, _ = _replay_chain(w, W1, W2, align, True, rng)
-    yo, _ = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2, align=align)
+    yo, ref = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2, align=align)
     a = bf16_bits_to_f32(y).astype(np.float64)
     b = bf16_bits_to_f32(yo).astype(np.float64)
     rel = np.linalg.norm(a - b) / np.linalg.norm(b)
-    print(f"tiny layer end-to-end rel L2 vs pure oracle: {rel:.3e}")
+    flips = _requant_flip_rate(it, ref, int(it["expert_offsets"][-1]))
+    print(f"tiny layer end-to-end rel L2 vs pure oracle: {rel:.3e}, requant code flips {flips:.2e}")
     assert rel < 1e-2
+    assert flips < 1e-2
 
 
 @pytest.mark.parametrize("wid", [2, 3, 4])
@@ -113,13 +126,15 @@ def test_workload_layer_replay_chain(wid):
 
 def test_decode_layer_end_to_end():
     w, W1, W2 = moe_case(3)
-    y, _ = _forward(w, W1, W2)
-    yo, _ = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2)
+    y, it = _forward(w, W1, W2)
+    yo, ref = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2)
     a = bf16_bits_to_f32(y).astype(np.float64)
     b = bf16_bits_to_f32(yo).astype(np.float64)
     rel = np.linalg.norm(a - b) / np.linalg.norm(b)
-    print(f"decode layer end-to-end rel L2 vs pure oracle: {rel:.3e}")
+    flips = _requant_flip_rate(it, ref, int(it["expert_offsets"][-1]))
+    print(f"decode layer end-to-end rel L2 vs pure oracle: {rel:.3e}, requant code flips {flips:.2e}")
     assert rel < 1e-2
+    assert flips < 1e-2
 
 
 def test_perf_path_bf16_rows_and_determinism():
