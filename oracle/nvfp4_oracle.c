@@ -440,6 +440,7 @@ int orc_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const floa
     /* decode the group's B once: q_b * s_b (outer scale applied at the end) */
     double* bdec = (double*)malloc(sizeof(double) * (size_t)(n * k));
     if (!bdec) return 1;
+#pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < n; ++j)
       orc_dequantize_row(b_codes + ((int64_t)g * n + j) * (k / 2),
                          b_scales + ((int64_t)g * n + j) * (k / 16), 1.0f, k, bdec + j * k);

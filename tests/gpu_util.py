@@ -59,6 +59,53 @@ def assert_gemm_close(gpu: np.ndarray, ref: np.ndarray, bound: np.ndarray, what:
                            f"{ref.reshape(-1)[bad[:4]]}, tol {tol.reshape(-1)[bad[:4]]}")
 
 
+def _row_slice(A, r0, r1):
+    return tuple(np.ascontiguousarray(a[r0:r1]) for a in A)
+
+
+def oracle_gemm_chunks(A, W, offs, chunk_rows=None):
+    """The oracle grouped GEMM with its bound over rows [offs[0], offs[-1]),
+    yielded as (r0, r1, ref, bound) slices of at most `chunk_rows` rows, so
+    the host holds one slice of the fp32 result and its fp64 bound at a time.
+    A slice is the same definition on the rows it covers: its group offsets
+    are the full ones clipped to [r0, r1)."""
+    offs = np.asarray(offs, np.int64)
+    n = W[0].shape[1]
+    if chunk_rows is None:
+        chunk_rows = max(1024, (256 << 20) // (12 * n))      # ~256 MB of result + bound
+    start, end = int(offs[0]), int(offs[-1])
+    for r0 in range(start, end, chunk_rows):
+        r1 = min(end, r0 + chunk_rows)
+        lo = (np.clip(offs, r0, r1) - r0).astype(np.int32)
+        ref, bound = O.grouped_gemm(*_row_slice(A, r0, r1), *W, lo, with_bound=True)
+        yield r0, r1, ref, bound
+
+
+def assert_gemm_full(gpu: np.ndarray, A, W, offs, what: str, bf16_out: bool = False,
+                     chunks=None):
+    """Every output element of the rows [offs[0], offs[-1]) against the oracle:
+    fp32 output within 2^-10 * sum|a_k b_k| + 1e-6; bf16 output (uint16 bit
+    patterns) the round-to-nearest-even of a value within that tolerance,
+    i.e. within it plus half a bf16 ulp of the oracle value.  `chunks` may be
+    a list of precomputed oracle_gemm_chunks slices of the same problem.
+    Returns the number of elements compared."""
+    count = 0
+    for r0, r1, ref, bound in (chunks if chunks is not None else oracle_gemm_chunks(A, W, offs)):
+        g = gpu[r0:r1]
+        if bf16_out:
+            got = bf16_bits_to_f32(g).astype(np.float64)
+            err = np.abs(got - ref.astype(np.float64))
+            tol = gemm_tol(bound) + bf16_ulp(ref) * 0.5 * 1.0001
+            bad = np.flatnonzero(~(err <= tol))
+            assert bad.size == 0, (f"{what} rows [{r0},{r1}): {bad.size} of {err.size} "
+                                   f"outside tolerance; first flat idx {bad[:4]}")
+        else:
+            assert_gemm_close(g, ref, bound, f"{what} rows [{r0},{r1})")
+        count += ref.size
+        say(f"{what}: rows [{r0}, {r1}) of [{int(offs[0])}, {int(offs[-1])}) within tolerance")
+    return count
+
+
 @functools.lru_cache(maxsize=None)
 def moe_case(wid, with_weights=True):
     """Workload + oracle-quantized weights (cached for the session)."""
@@ -75,3 +122,23 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     v = np.abs(np.asarray(v, np.float64))
     e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
     return 2.0 ** (e - 7)
+
+
+@functools.lru_cache(maxsize=None)
+def moe_permute_ref(wid):
+    """The oracle's routing + quantize-scatter of workload `wid` (cached)."""
+    w, _, _ = moe_case(wid)
+    return O.moe_permute(w.x, w.topk_idx, w.topk_prob, w.experts)
+
+
+@functools.lru_cache(maxsize=None)
+def fc1_oracle_chunks(wid):
+    """The oracle FC1 (pre-activation C and its bound) of workload `wid` on
+    the oracle's own A1, as a list of row slices.  Several tests compare GPU
+    FC1 outputs on A1 bit-identical to the oracle's against it; the slices
+    are computed once per session."""
+    w, W1, _ = moe_case(wid)
+    p = moe_permute_ref(wid)
+    A1 = (p["codes"], p["scales"], p["gscale"])
+    return list(oracle_gemm_chunks(A1, W1, p["offsets"]))
+
