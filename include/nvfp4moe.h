@@ -46,7 +46,11 @@
  * kernels do not handle) and enqueues nothing.  Launch failures return
  * NVFP4_HIP_ERROR.  Data-dependent preconditions (finite inputs, expert ids
  * of one token distinct) are the caller's contract; expert ids outside
- * [0, num_experts) are legal and mean "not routed".
+ * [0, num_experts) are legal and mean "not routed".  A library built with
+ * NVFP4_DEBUG_CHECKS defined (libnvfp4moe_debug.so) checks them on the device
+ * in moe_permute and moe_expert_forward and reports what it found in the
+ * precondition word (below); a violated precondition never faults, in either
+ * build, it only makes the affected outputs meaningless.
  */
 #ifndef NVFP4MOE_H
 #define NVFP4MOE_H
@@ -71,6 +75,28 @@ extern "C" {
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* nvfp4_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Precondition word (debug build).  [miniTE] §4.5 (strict layout checks and
+ * a deterministic mode to make failures attributable).
+ * The first uint32 (byte offset 0) of the workspace of moe_permute and of
+ * moe_expert_forward is reserved in every build.  In a build with
+ * NVFP4_DEBUG_CHECKS, each call clears it on its stream before its first
+ * kernel and its routing kernels OR into it:
+ *   NVFP4_PRECONDITION_DUPLICATE_EXPERT  a token names one expert id in
+ *                                        [0, num_experts) more than once
+ *   NVFP4_PRECONDITION_NONFINITE_INPUT   an activation x is Inf or NaN
+ *   NVFP4_PRECONDITION_NONFINITE_PROB    a router weight is Inf or NaN
+ * The word is valid once the call's work on the stream has completed; the
+ * caller reads it with an ordinary device-to-host copy.  Outputs for clean
+ * inputs are bit-identical to the release build's.  In the release build the
+ * word is left untouched.
+ * nvfp4_debug_checks() returns 1 in a build with NVFP4_DEBUG_CHECKS, else 0.
+ * ---------------------------------------------------------------------- */
+#define NVFP4_PRECONDITION_DUPLICATE_EXPERT 0x1u
+#define NVFP4_PRECONDITION_NONFINITE_INPUT 0x2u
+#define NVFP4_PRECONDITION_NONFINITE_PROB 0x4u
+int nvfp4_debug_checks(void);
 
 /* ------------------------------------------------------------------------
  * nvfp4_quantize -- NVFP4 quantization of a bf16 matrix.
@@ -144,7 +170,7 @@ int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
  *   codes, block_scales, global_scales  out [capacity, hidden/2],
  *                [capacity, hidden/16], [capacity] (unused when x is NULL)
  *   workspace    device scratch of moe_permute_workspace_size() bytes,
- *                16-byte aligned
+ *                16-byte aligned; its first uint32 is the precondition word
  * Limits: 1 <= topk <= num_experts <= 1024; hidden % 16 == 0,
  * hidden <= 16384; tokens * topk + num_experts * align < 2^31.
  * ---------------------------------------------------------------------- */
@@ -255,7 +281,8 @@ int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
  *                weights, activations or both)
  *   w2           NVFP4 down weights    [E, hidden, inter]
  *                (each row-major or tiled, per its layout member)
- *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned
+ *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned;
+ *                its first uint32 is the precondition word
  *   debug        nullable: every non-NULL member receives that intermediate
  *                (in place of the workspace copy); fc1_out, y_rows_f32 and
  *                row_src are only produced when requested (y_rows_f32

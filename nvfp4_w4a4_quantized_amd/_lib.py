@@ -13,6 +13,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnvfp4moe.so")
+# the same library built with NVFP4_DEBUG_CHECKS (device-side precondition
+# checks reported in the workspace's precondition word)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libnvfp4moe_debug.so")
 
 _vp = C.c_void_p
 _i64 = C.c_int64
@@ -34,16 +37,32 @@ class Intermediates(C.Structure):
 
 
 _lib = None
+_debug_lib = None
 
 
 def lib():
+    """The release library (loaded once)."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise NvFp4Error(f"{LIB_PATH} is missing: build it with `python -m "
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def debug_lib():
+    """The NVFP4_DEBUG_CHECKS build of the same interface (loaded once)."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(DEBUG_LIB_PATH)
+    return _debug_lib
+
+
+def _load(path):
+    if not os.path.exists(path):
+        raise NvFp4Error(f"{path} is missing: build it with `python -m "
                          "nvfp4_w4a4_quantized_amd.build` (there is no fallback path)")
-    L = C.CDLL(LIB_PATH)
+    L = C.CDLL(path)
+    L.nvfp4_debug_checks.restype = C.c_int
+    L.nvfp4_debug_checks.argtypes = []
     L.nvfp4_status_string.restype = C.c_char_p
     L.nvfp4_status_string.argtypes = [C.c_int]
     L.nvfp4_quantize.restype = C.c_int
@@ -80,7 +99,6 @@ def lib():
     L.nvfp4_event_elapsed_ms.argtypes = [_vp, _vp, C.POINTER(C.c_float)]
     L.nvfp4_event_destroy.restype = C.c_int
     L.nvfp4_event_destroy.argtypes = [_vp]
-    _lib = L
     return L
 
 

@@ -1,4 +1,8 @@
-"""Builds the gfx950 HIP library libnvfp4moe.so in-tree (package directory).
+"""Builds the gfx950 HIP library libnvfp4moe.so in-tree (package directory),
+and its debug twin libnvfp4moe_debug.so (NVFP4_DEBUG_CHECKS: the routing
+kernels check the data preconditions on the device and report them in the
+workspace's precondition word; only the sources that read the flag are
+compiled twice).
 
 Every kernel is compiled for gfx950 only, with -ffp-contract=off and correctly
 rounded fp32 division (the quantizer's bit-exact contract), and with packed
@@ -16,7 +20,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4moe.so")
+DEBUG_LIB = os.path.join(HERE, "libnvfp4moe_debug.so")
 SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "combine.hip", "capi.hip"]
+DEBUG_SOURCES = ["route.hip", "capi.hip"]      # the sources that read NVFP4_DEBUG_CHECKS
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -28,9 +34,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, ("debug_" if debug else "") + src.replace(".hip", ".o"))
+    extra = ["-DNVFP4_DEBUG_CHECKS"] if debug else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -43,19 +50,27 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8")))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    units = [(s, False) for s in SOURCES] + [(s, True) for s in DEBUG_SOURCES]
+    jobs = min(len(units), int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda u: _compile(u[0], verbose, u[1]), units))
+    release = objs[:len(SOURCES)]
+    debug_objs = dict(zip(DEBUG_SOURCES, objs[len(SOURCES):]))
+    _link(release, LIB, verbose)
+    _link([debug_objs.get(s, o) for s, o in zip(SOURCES, release)], DEBUG_LIB, verbose)
     return LIB
 
 

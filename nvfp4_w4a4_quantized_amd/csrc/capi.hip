@@ -100,6 +100,14 @@ const char* nvfp4_status_string(int status) {
   }
 }
 
+int nvfp4_debug_checks(void) {
+#ifdef NVFP4_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 int nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x, int scale_domain,
                    const int32_t* group_offsets, int32_t num_groups, const float* amax_in,
                    int block_rule, uint8_t* codes, uint8_t* block_scales, float* global_scales,

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include "nvfp4moe.h"
 #include "tile_schedule.h"
 
 namespace nvfp4 {
@@ -46,8 +47,9 @@ struct RouteArgs {
   int64_t zero_rows;
   TileTableSpec tables[2];  // GEMM tile tables written from the offsets (num_tables of them)
   int32_t num_tables;
-  void* workspace;
+  void* workspace;      // route_workspace_bytes(); its first uint32 is the precondition word
   int32_t block_rule;   // 0 standard, 1/2 Four-Over-Six (MSE/MAE)
+  uint32_t* error_word; // set by launch_route in a build with NVFP4_DEBUG_CHECKS
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 

@@ -33,8 +33,10 @@ constexpr int kScanThreads = 256;
 
 int64_t route_num_chunks(int64_t tokens) { return (tokens + kChunk - 1) / kChunk; }
 
-// workspace: hist[E][nchunks] int32, base[E][nchunks] int32, counts[E]
-// int32 (each 256-byte aligned)
+// workspace: the precondition word (uint32, in a 256-byte slot of its own),
+// hist[E][nchunks] int32, base[E][nchunks] int32, counts[E] int32 (each
+// 256-byte aligned)
+constexpr size_t kErrorSlot = 256;
 static size_t route_matrix_bytes(int64_t tokens, int32_t num_experts) {
   const size_t m = (size_t)route_num_chunks(tokens) * (size_t)num_experts * 4u;
   return (m + 255u) & ~(size_t)255u;
@@ -42,8 +44,28 @@ static size_t route_matrix_bytes(int64_t tokens, int32_t num_experts) {
 
 size_t route_workspace_bytes(int64_t tokens, int32_t num_experts) {
   size_t counts = ((size_t)num_experts * 4u + 255u) & ~(size_t)255u;
-  return 2 * route_matrix_bytes(tokens, num_experts) + counts;
+  return kErrorSlot + 2 * route_matrix_bytes(tokens, num_experts) + counts;
 }
+
+#ifdef NVFP4_DEBUG_CHECKS
+// Debug build: data preconditions checked on the device.  Each wave ORs the
+// bits of what it found into the workspace's error word (cleared by the
+// launch sequence first); nothing else changes, and a violated precondition
+// stays fault-free (ranks of duplicated ids stay within the expert's counted
+// rows, the quantizer has no value-dependent control flow).
+__global__ void clear_word_kernel(uint32_t* word) {
+  if (threadIdx.x == 0) *word = 0u;
+}
+
+__device__ __forceinline__ void report_bits(uint32_t* word, bool hit, uint32_t bit) {
+  if (__ballot(hit) != 0ull && (threadIdx.x & (kWave - 1)) == 0) atomicOr(word, bit);
+}
+
+// bf16 pair with an exponent field of all ones (Inf or NaN)
+__device__ __forceinline__ bool bf16_pair_nonfinite(uint32_t u) {
+  return (u & 0x7F80u) == 0x7F80u || (u & 0x7F800000u) == 0x7F800000u;
+}
+#endif
 
 // KMAX > 0 (topk <= KMAX): a lane's k expert ids are all requested before
 // the first LDS add (a loop over a run-time count would wait for each load).
@@ -403,6 +425,46 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     for (int ti = 0; ti < TPW; ++ti) dst_l[ti] = -1;
   }
 
+#ifdef NVFP4_DEBUG_CHECKS
+  {
+    // one token naming an expert twice; a non-finite router weight; a
+    // non-finite activation (all of the wave's tokens)
+    bool dup = false, badp = false, badx = false;
+    if constexpr (KMAX > 0) {
+      if (lane_valid && tl >= t0 && tl < t0 + nt) {
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i)
+#pragma unroll
+          for (int j = i + 1; j < KMAX; ++j)
+            dup |= (j < k && ids[i] >= 0 && ids[i] < E && ids[i] == ids[j]);
+      }
+#pragma unroll
+      for (int ti = 0; ti < TPW; ++ti) badp |= (ti < nt && lane < k && !__builtin_isfinite(prob_l[ti]));
+    } else {
+      for (int ti = 0; ti < nt; ++ti) {
+        const int32_t* row = a.topk_idx + (t0 + ti) * k;
+        for (int j = lane; j < k; j += kWave) {
+          const int e = row[j];
+          badp |= !__builtin_isfinite(a.topk_prob[(t0 + ti) * k + j]);
+          if (e < 0 || e >= E) continue;
+          for (int i = 0; i < j; ++i) dup |= (row[i] == e);
+        }
+      }
+    }
+    if (a.x) {
+#pragma unroll
+      for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+        for (int i = 0; i < BPL; ++i)
+#pragma unroll
+          for (int u = 0; u < 8; ++u) badx |= (ti < nt && bf16_pair_nonfinite(w[ti][i][u]));
+    }
+    report_bits(a.error_word, dup, NVFP4_PRECONDITION_DUPLICATE_EXPERT);
+    report_bits(a.error_word, badp, NVFP4_PRECONDITION_NONFINITE_PROB);
+    report_bits(a.error_word, badx, NVFP4_PRECONDITION_NONFINITE_INPUT);
+  }
+#endif
+
   // Phase 2: quantize each token once, then write its k rows and maps
 #pragma unroll
   for (int ti = 0; ti < TPW; ++ti) {
@@ -470,13 +532,19 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
   }
 }
 
-hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
+  RouteArgs a = args;
   const int64_t nchunks = route_num_chunks(a.tokens);
   const int E = a.num_experts;
   const size_t mbytes = route_matrix_bytes(a.tokens, E);
-  int32_t* hist = static_cast<int32_t*>(a.workspace);
-  int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + mbytes);
-  int32_t* counts = reinterpret_cast<int32_t*>(static_cast<char*>(a.workspace) + 2 * mbytes);
+  char* ws = static_cast<char*>(a.workspace);
+  int32_t* hist = reinterpret_cast<int32_t*>(ws + kErrorSlot);
+  int32_t* base = reinterpret_cast<int32_t*>(ws + kErrorSlot + mbytes);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + kErrorSlot + 2 * mbytes);
+#ifdef NVFP4_DEBUG_CHECKS
+  a.error_word = reinterpret_cast<uint32_t*>(ws);
+  clear_word_kernel<<<1, 64, 0, s>>>(a.error_word);
+#endif
   const bool small = a.tokens * a.topk <= kSmallEntries;
   if (!small) {
     if (nchunks > 0) {

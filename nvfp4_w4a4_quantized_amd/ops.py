@@ -110,9 +110,14 @@ def moe_rows_capacity(tokens: int, topk: int, num_experts: int, align: int = 1) 
     return int(lib().moe_rows_capacity(tokens, topk, num_experts, align))
 
 
-def moe_permute(x, topk_idx, topk_prob, num_experts: int, align: int = 1, block_rule: int = 0):
+def moe_permute(x, topk_idx, topk_prob, num_experts: int, align: int = 1, block_rule: int = 0,
+                workspace=None, library=None):
     """Routing metadata + per-token quantize-scatter.  x may be None (metadata
-    only).  Returns a dict of device tensors."""
+    only).  Returns a dict of device tensors.  `workspace`: a uint8 device
+    tensor of at least moe_permute_workspace_size bytes (allocated here when
+    None); `library`: the loaded library to call (the release build by
+    default, _lib.debug_lib() for the precondition-checking build)."""
+    L = library if library is not None else lib()
     _need(topk_idx, (torch.int32,), "topk_idx")
     _need(topk_prob, (torch.float32,), "topk_prob")
     T, k = topk_idx.shape
@@ -130,9 +135,11 @@ def moe_permute(x, topk_idx, topk_prob, num_experts: int, align: int = 1, block_
         out["codes"] = torch.empty((cap, H // 2), dtype=torch.uint8, device=dev)
         out["scales"] = torch.empty((cap, H // 16), dtype=torch.uint8, device=dev)
         out["gscale"] = torch.empty(cap, dtype=torch.float32, device=dev)
-    wsb = int(lib().moe_permute_workspace_size(T, k, num_experts))
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
-    check(lib().moe_permute(ptr(x), T, H, ptr(topk_idx), ptr(topk_prob), k, num_experts, align,
+    wsb = int(L.moe_permute_workspace_size(T, k, num_experts))
+    ws = workspace if workspace is not None else torch.empty(max(wsb, 256), dtype=torch.uint8,
+                                                             device=dev)
+    _need(ws, (torch.uint8,), "workspace")
+    check(L.moe_permute(ptr(x), T, H, ptr(topk_idx), ptr(topk_prob), k, num_experts, align,
                             block_rule, ptr(out["offsets"]), ptr(out["dst_row"]), ptr(out["row_src"]),
                             ptr(out["row_prob"]), ptr(out.get("codes")), ptr(out.get("scales")),
                             ptr(out.get("gscale")), ptr(ws), ws.numel(), stream_handle()),
@@ -236,16 +243,19 @@ class StageTimer:
 def moe_expert_forward(x, topk_idx, topk_prob, num_experts: int, inter: int,
                        w1: NvFp4Weights, w2: NvFp4Weights, align: int = 1, workspace=None,
                        debug: bool = False, fc1_out: bool = False, y_rows_f32: bool = False,
-                       timer: StageTimer | None = None, y=None, act_block_rule: int = 0):
+                       timer: StageTimer | None = None, y=None, act_block_rule: int = 0,
+                       library=None):
     """The whole expert layer.  Returns y (bf16 [T, H]); with debug=True also a
-    dict of the intermediates (allocated here, written by the library)."""
+    dict of the intermediates (allocated here, written by the library).
+    `library`: the loaded library to call (release build by default)."""
+    L = library if library is not None else lib()
     _need(x, _BF16_LIKE, "x")
     _need(topk_idx, (torch.int32,), "topk_idx")
     _need(topk_prob, (torch.float32,), "topk_prob")
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
-    wsb = moe_expert_forward_workspace_size(T, H, inter, k, num_experts, align)
+    wsb = int(L.moe_expert_forward_workspace_size(T, H, inter, k, num_experts, align))
     if workspace is None:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
     if y is None:
@@ -269,7 +279,7 @@ def moe_expert_forward(x, topk_idx, topk_prob, num_experts: int, inter: int,
             inter_t["y_rows_f32"] = e((cap, H), torch.float32)
         dbg = Intermediates(**{n: t.data_ptr() for n, t in inter_t.items()})
     ev = timer.events if timer is not None else None
-    check(lib().moe_expert_forward(ptr(x), T, H, inter, ptr(topk_idx), ptr(topk_prob), k,
+    check(L.moe_expert_forward(ptr(x), T, H, inter, ptr(topk_idx), ptr(topk_prob), k,
                                    num_experts, align, act_block_rule, C.byref(w1.c_struct()),
                                    C.byref(w2.c_struct()), ptr(y), ptr(workspace),
                                    workspace.numel(), C.byref(dbg) if dbg is not None else None,

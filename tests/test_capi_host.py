@@ -11,6 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
 LIB = os.path.join(ROOT, "nvfp4_w4a4_quantized_amd", "libnvfp4moe.so")
+DEBUG_LIB = os.path.join(ROOT, "nvfp4_w4a4_quantized_amd", "libnvfp4moe_debug.so")
 
 INVALID, UNSUPPORTED, WS_SMALL = 1, 2, 4
 
@@ -39,14 +40,28 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
-def test_library_exports_every_declared_symbol(L):
-    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+@pytest.mark.parametrize("path", [LIB, DEBUG_LIB], ids=["release", "debug"])
+def test_library_exports_every_declared_symbol(path):
+    if not os.path.exists(path):
+        pytest.fail(f"{path} not built (run __graft_entry__.build())")
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
                          check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
     missing = [n for n in _declared_functions() if n not in exported]
     assert not missing, missing
+    lib = C.CDLL(path)
     for n in _declared_functions():
-        getattr(L, n)   # resolvable through ctypes
+        getattr(lib, n)   # resolvable through ctypes
+
+
+def test_debug_build_reports_itself(L):
+    """The precondition checks exist only in the NVFP4_DEBUG_CHECKS build."""
+    from nvfp4_w4a4_quantized_amd import _lib
+    assert L.nvfp4_debug_checks() == 0
+    assert _lib.debug_lib().nvfp4_debug_checks() == 1
+    # both builds reserve the same workspace (the word's slot included)
+    for args in ((8192, 8, 128), (1, 1, 1), (32768, 8, 1024)):
+        assert L.moe_permute_workspace_size(*args) == _lib.debug_lib().moe_permute_workspace_size(*args)
 
 
 def test_host_side_sizes(L):
@@ -121,3 +136,4 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     wbad = Weights(0x1000, 0x1000, 0x1000, 3)   # unknown layout
     assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(wbad),
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
+
