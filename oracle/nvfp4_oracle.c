@@ -594,6 +594,125 @@ int orc_moe_forward_rule(const uint16_t* x, int64_t tokens, int64_t hidden, int6
   return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* O12: single-pass FC1 -> SwiGLU -> quantize -> FC2 ([miniTE] §5.6)         */
+/* ------------------------------------------------------------------------ */
+
+int orc_online_quantize(const uint16_t* p, int64_t rows, int64_t inter, int64_t tile,
+                        uint8_t* codes, uint8_t* scales, float* gs) {
+  if (rows < 0 || inter < 16 || inter % 16 != 0 || tile < 16 || tile % 16 != 0) return 1;
+  const int64_t ntiles = (inter + tile - 1) / tile;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* pr = p + r * inter;
+    uint8_t* cr = codes + r * (inter / 2);
+    memset(cr, 0, (size_t)(inter / 2));
+    float gamax = 0.0f;                               /* running row amax */
+    for (int64_t i = 0; i < ntiles; ++i) {
+      const int64_t c0 = i * tile, c1 = (c0 + tile < inter) ? c0 + tile : inter;
+      float rowmax = orc_row_amax(pr + c0, c1 - c0);  /* max |P_i| */
+      if (rowmax > gamax) gamax = rowmax;
+      float s = gamax / 2688.0f;                      /* gs = gamax / 2688 */
+      for (int64_t b = c0 / 16; b < c1 / 16; ++b) {
+        unsigned c[16];
+        scales[r * (inter / 16) + b] = (uint8_t)quantize_block(pr + b * 16, s, 6.0f, c);
+        pack_block(b, c, cr);
+      }
+      gs[r * ntiles + i] = s;
+    }
+  }
+  return 0;
+}
+
+int orc_single_pass_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gs,
+                         int64_t tile, const uint8_t* b_codes, const uint8_t* b_scales,
+                         const float* b_gscale, const int32_t* offsets, int32_t num_groups,
+                         int64_t n, int64_t k, float* out, double* bound) {
+  if (num_groups < 0 || n < 0 || k < 16 || k % 16 != 0 || tile < 16 || tile % 16 != 0) return 1;
+  const int64_t ntiles = (k + tile - 1) / tile;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    int64_t r0 = offsets[g], r1 = offsets[g + 1];
+    if (r1 < r0) return 1;
+    if (r1 == r0) continue;
+    /* q_b * s_b of the group's rows (its outer scale applied at the end) */
+    double* bdec = (double*)malloc(sizeof(double) * (size_t)(n * k));
+    if (!bdec) return 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < n; ++j)
+      orc_dequantize_row(b_codes + ((int64_t)g * n + j) * (k / 2),
+                         b_scales + ((int64_t)g * n + j) * (k / 16), 1.0f, k, bdec + j * k);
+    const double sgw = (double)b_gscale[g];
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t r = r0; r < r1; ++r) {
+      /* q_a * s_a: block scales included, the tiles' gs excluded */
+      double* adec = (double*)malloc(sizeof(double) * (size_t)k);
+      orc_dequantize_row(a_codes + r * (k / 2), a_scales + r * (k / 16), 1.0f, k, adec);
+      const float* gsr = gs + r * ntiles;
+      for (int64_t j = 0; j < n; ++j) {
+        const double* bj = bdec + j * k;
+        double o = 0.0, gs_prev = 0.0, babs = 0.0;
+        for (int64_t i = 0; i < ntiles; ++i) {
+          const int64_t c0 = i * tile, c1 = (c0 + tile < k) ? c0 + tile : k;
+          const double gsi = (double)gsr[i];
+          if (gsi == 0.0) continue;                   /* gamax = 0: contributes zero */
+          double d_o = 0.0, d_abs = 0.0;
+          for (int64_t kk = c0; kk < c1; ++kk) {
+            double prod = adec[kk] * bj[kk];          /* exact: <= 6 significant bits each */
+            d_o += prod;
+            d_abs += fabs(prod);
+          }
+          o = o * (gs_prev / gsi) + d_o;              /* O = O * (gs_prev / gs) + dO_i */
+          gs_prev = gsi;
+          babs += d_abs * gsi;
+        }
+        out[r * n + j] = (float)(o * gs_prev * sgw);  /* Y = O * gs_prev * gs_W2 */
+        if (bound) bound[r * n + j] = babs * fabs(sgw);
+      }
+      free(adec);
+    }
+    free(bdec);
+  }
+  return 0;
+}
+
+int orc_moe_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
+                                const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                                int32_t num_experts, int32_t align, int64_t tile,
+                                const uint8_t* w1_codes, const uint8_t* w1_scales,
+                                const float* w1_gscale, const uint8_t* w2_codes,
+                                const uint8_t* w2_scales, const float* w2_gscale,
+                                const orc_moe_buffers* b, float* gs_tiles, uint16_t* y,
+                                double* stage_seconds) {
+  if (!b || !gs_tiles || hidden % 16 != 0 || inter % 16 != 0) return 1;
+  double t0 = now_seconds();
+  int st = orc_moe_permute_rule(x, tokens, hidden, topk_idx, topk_prob, topk, num_experts, align,
+                                0, b->offsets, b->dst_row, b->row_src, b->row_prob,
+                                b->a1_codes, b->a1_scales, b->a1_gscale);
+  if (st) return st;
+  int64_t rows = b->offsets[num_experts];
+  double t1 = now_seconds();
+  st = orc_grouped_gemm(b->a1_codes, b->a1_scales, b->a1_gscale, w1_codes, w1_scales, w1_gscale,
+                        b->offsets, num_experts, 2 * inter, hidden, b->c_fc1, NULL);
+  if (st) return st;
+  double t2 = now_seconds();
+  orc_swiglu(b->c_fc1, b->row_prob, rows, inter, b->d, b->amax_d);   /* P = D */
+  double t3 = now_seconds();
+  st = orc_online_quantize(b->d, rows, inter, tile, b->a2_codes, b->a2_scales, gs_tiles);
+  if (st) return st;
+  double t4 = now_seconds();
+  st = orc_single_pass_gemm(b->a2_codes, b->a2_scales, gs_tiles, tile, w2_codes, w2_scales,
+                            w2_gscale, b->offsets, num_experts, hidden, inter, b->y_rows, NULL);
+  if (st) return st;
+  double t5 = now_seconds();
+  orc_combine(b->y_rows, b->dst_row, tokens, topk, hidden, y);
+  double t6 = now_seconds();
+  if (stage_seconds) {
+    stage_seconds[0] = t1 - t0; stage_seconds[1] = t2 - t1; stage_seconds[2] = t3 - t2;
+    stage_seconds[3] = t4 - t3; stage_seconds[4] = t5 - t4; stage_seconds[5] = t6 - t5;
+  }
+  return 0;
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

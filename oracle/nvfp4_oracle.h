@@ -242,6 +242,60 @@ int orc_moe_forward_rule(const uint16_t* x, int64_t tokens, int64_t hidden, int6
                          const uint8_t* w2_codes, const uint8_t* w2_scales, const float* w2_gscale,
                          const orc_moe_buffers* buf, uint16_t* y, double* stage_seconds);
 
+/* ---- O12: single-pass FC1 -> SwiGLU -> quantize -> FC2 ---------------- */
+/* [miniTE] §5.6 "Exploring Single-Pass Fusion": FC2 consumes the activation
+ * in K-tiles before the row's full amax is known.  A running row amax over
+ * the tiles seen so far sets each tile's outer scale, and the FC2 partial
+ * sum is converted to the new scale whenever that scale grows.  The codes
+ * therefore differ from the two-pass quantization by design.
+ *
+ * Readings (the page gives the steps, not the sizes):
+ *   - the activation tile P_i is the weighted SwiGLU of O8 rounded to bf16,
+ *     i.e. columns [i*tile, min((i+1)*tile, inter)) of the two-pass D, so
+ *     that a row whose maximum lies in its first tile quantizes exactly as
+ *     in the two-pass path;
+ *   - gs_i = fl32(gamax_i / 2688) with gamax_i = max(|P_0..P_i|), and the
+ *     tile's blocks are encoded by O3/O4 with s_g = gs_i;
+ *   - "If gamax = 0 ... skip": a tile with gs_i == 0 adds nothing (its
+ *     scales are 0 and its codes carry only the sign, as O4 gives);
+ *   - tile (the K-tile width) is a parameter, a multiple of 16; the last
+ *     tile may be narrower. */
+
+/* O12a: per row of P (bf16 [rows, inter]), tile by tile in ascending order:
+ * gamax = max(gamax, max|P_i|), gs_i = gamax / 2688, then E4M3 scales and
+ * E2M1 codes of the tile's 16-blocks with s_g = gs_i.  codes [rows,
+ * inter/2], scales [rows, inter/16], gs [rows, ntiles] with ntiles =
+ * ceil(inter / tile).  Status 1 on bad sizes. */
+int orc_online_quantize(const uint16_t* p, int64_t rows, int64_t inter, int64_t tile,
+                        uint8_t* codes, uint8_t* scales, float* gs);
+
+/* O12b: the FC2 of online-quantized rows.  For row r of group g and column
+ * n, with O = 0 and gs_prev = 0, for every tile i with gs_i > 0 in order:
+ *   dO_i = sum over the tile's k of (q_a s_a)[r, k] (q_b s_b)[g, n, k]
+ *          (exact fp64: block scales included, gs excluded),
+ *   O = O * (gs_prev / gs_i) + dO_i,  gs_prev = gs_i;
+ * then out[r, n] = fl32(O * gs_prev * s_gb[g]) (0 when every gs_i is 0).
+ * bound (nullable) = sum_k |a_k b_k| over the fully dequantized operands
+ * (a_k scaled by the gs of its tile).  Rows outside the groups untouched. */
+int orc_single_pass_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* gs,
+                         int64_t tile, const uint8_t* b_codes, const uint8_t* b_scales,
+                         const float* b_gscale, const int32_t* offsets, int32_t num_groups,
+                         int64_t n, int64_t k, float* out, double* bound);
+
+/* The whole layer with O12 in place of O9 + O10: route + quantize-permute,
+ * FC1, SwiGLU (D = P), online quantize, single-pass FC2, combine.  Buffers
+ * as orc_moe_forward (a2_gscale and amax_d unused) plus gs_tiles
+ * [R_cap, ceil(inter / tile)]; stage_seconds as orc_moe_forward (the
+ * requantize stage is the online quantize). */
+int orc_moe_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
+                                const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                                int32_t num_experts, int32_t align, int64_t tile,
+                                const uint8_t* w1_codes, const uint8_t* w1_scales,
+                                const float* w1_gscale, const uint8_t* w2_codes,
+                                const uint8_t* w2_scales, const float* w2_gscale,
+                                const orc_moe_buffers* buf, float* gs_tiles, uint16_t* y,
+                                double* stage_seconds);
+
 /* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */
 int orc_num_threads(void);
 

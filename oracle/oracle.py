@@ -106,6 +106,16 @@ def lib():
                                        C.c_int32, C.c_int32, C.c_int32, C.c_int,
                                        _u8p, _u8p, _f32p, _u8p, _u8p, _f32p,
                                        C.POINTER(_MoeBuffers), _u16p, C.c_void_p]
+    L.orc_online_quantize.restype = C.c_int
+    L.orc_online_quantize.argtypes = [_u16p, C.c_int64, C.c_int64, C.c_int64, _u8p, _u8p, _f32p]
+    L.orc_single_pass_gemm.restype = C.c_int
+    L.orc_single_pass_gemm.argtypes = [_u8p, _u8p, _f32p, C.c_int64, _u8p, _u8p, _f32p, _i32p,
+                                       C.c_int32, C.c_int64, C.c_int64, _f32p, C.c_void_p]
+    L.orc_moe_forward_single_pass.restype = C.c_int
+    L.orc_moe_forward_single_pass.argtypes = [_u16p, C.c_int64, C.c_int64, C.c_int64, _i32p,
+                                              _f32p, C.c_int32, C.c_int32, C.c_int32, C.c_int64,
+                                              _u8p, _u8p, _f32p, _u8p, _u8p, _f32p,
+                                              C.POINTER(_MoeBuffers), _f32p, _u16p, C.c_void_p]
     L.orc_num_threads.restype = C.c_int
     L.orc_num_threads.argtypes = []
     _libs[path] = L
@@ -343,3 +353,79 @@ def moe_forward(x_bf16, topk_idx, topk_prob, num_experts, inter, w1, w2, align: 
     if stage_times:
         return y, b, secs
     return y, b
+
+
+# ---- O12: single-pass FC1 -> SwiGLU -> quantize -> FC2 ------------------
+
+def num_tiles(inter: int, tile: int) -> int:
+    return (inter + tile - 1) // tile
+
+
+def online_quantize(p_bf16, tile: int):
+    """O12a: tile-by-tile quantization of bf16 rows [rows, inter] with a
+    running row amax.  Returns (codes, scales, gs [rows, ntiles])."""
+    p = np.ascontiguousarray(p_bf16, np.uint16)
+    rows, inter = p.shape
+    codes = np.zeros((rows, inter // 2), np.uint8)
+    scales = np.zeros((rows, inter // 16), np.uint8)
+    gs = np.zeros((rows, num_tiles(inter, tile)), np.float32)
+    _check(lib().orc_online_quantize(p, rows, inter, tile, codes, scales, gs), "online_quantize")
+    return codes, scales, gs
+
+
+def single_pass_gemm(a_codes, a_scales, gs, tile: int, b_codes, b_scales, b_gscale, offsets,
+                     with_bound: bool = False):
+    """O12b: the FC2 of online-quantized rows with the rescale of the
+    partial sums at every tile (fp32 result, fp64 bound)."""
+    a_codes = np.ascontiguousarray(a_codes, np.uint8)
+    rows, kh = a_codes.shape
+    G, n, _ = b_codes.shape
+    out = np.zeros((rows, n), np.float32)
+    bound = np.zeros((rows, n), np.float64) if with_bound else None
+    _check(lib().orc_single_pass_gemm(a_codes, np.ascontiguousarray(a_scales, np.uint8),
+                                      np.ascontiguousarray(gs, np.float32), tile,
+                                      np.ascontiguousarray(b_codes, np.uint8),
+                                      np.ascontiguousarray(b_scales, np.uint8),
+                                      np.ascontiguousarray(b_gscale, np.float32),
+                                      np.ascontiguousarray(offsets, np.int32), G, n, kh * 2, out,
+                                      _ptr(bound)), "single_pass_gemm")
+    return (out, bound) if with_bound else out
+
+
+def moe_forward_single_pass(x_bf16, topk_idx, topk_prob, num_experts, inter, w1, w2, tile: int,
+                            align: int = 1, stage_times: bool = False):
+    """Whole expert layer with O12 (online quantize + single-pass FC2) in
+    place of the two-pass requantize and FC2.  Returns (y, intermediates
+    [, stage seconds]); intermediates["gs_tiles"] holds the per-tile scales."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    idx = np.ascontiguousarray(topk_idx, np.int32)
+    prob = np.ascontiguousarray(topk_prob, np.float32)
+    T, H = x.shape
+    k = idx.shape[1]
+    I = inter
+    cap = rows_capacity(T, k, num_experts, align)
+    b = dict(
+        a1_codes=np.zeros((cap, H // 2), np.uint8), a1_scales=np.zeros((cap, H // 16), np.uint8),
+        a1_gscale=np.zeros(cap, np.float32), c_fc1=np.zeros((cap, 2 * I), np.float32),
+        d=np.zeros((cap, I), np.uint16), amax_d=np.zeros(cap, np.float32),
+        a2_codes=np.zeros((cap, I // 2), np.uint8), a2_scales=np.zeros((cap, I // 16), np.uint8),
+        a2_gscale=np.zeros(cap, np.float32), y_rows=np.zeros((cap, H), np.float32),
+        offsets=np.zeros(num_experts + 1, np.int32), dst_row=np.zeros((T, k), np.int32),
+        row_src=np.zeros(cap, np.int32), row_prob=np.zeros(cap, np.float32))
+    st = _MoeBuffers(**{n: b[n].ctypes.data for n in b})
+    gs = np.zeros((cap, num_tiles(I, tile)), np.float32)
+    y = np.zeros((T, H), np.uint16)
+    secs = np.zeros(6, np.float64)
+    w1c, w1s, w1g = (np.ascontiguousarray(a) for a in w1)
+    w2c, w2s, w2g = (np.ascontiguousarray(a) for a in w2)
+    _check(lib().orc_moe_forward_single_pass(
+        x, T, H, I, idx, prob, k, num_experts, align, tile,
+        w1c.astype(np.uint8, copy=False), w1s.astype(np.uint8, copy=False),
+        w1g.astype(np.float32, copy=False), w2c.astype(np.uint8, copy=False),
+        w2s.astype(np.uint8, copy=False), w2g.astype(np.float32, copy=False),
+        C.byref(st), gs, y, secs.ctypes.data_as(C.c_void_p)), "moe_forward_single_pass")
+    b["gs_tiles"] = gs
+    if stage_times:
+        return y, b, secs
+    return y, b
+

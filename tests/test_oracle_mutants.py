@@ -11,6 +11,7 @@ from oracle import oracle as O
 import test_oracle_codecs as TC
 import test_oracle_four_over_six as T46
 import test_oracle_scale_domains as TD
+import test_oracle_single_pass as TS
 import test_oracle_quantize as TQ
 import test_oracle_route_gemm as TR
 
@@ -40,9 +41,11 @@ MUTANTS = [
     ("dot_drops_first_term", "for (int64_t i = 0; i < k; ++i) {\n    double p = a[i] * b[i];",
      "for (int64_t i = 1; i < k; ++i) {\n    double p = a[i] * b[i];"),
     ("gemm_wrong_group_weights", "orc_dequantize_row(b_codes + ((int64_t)g * n + j) * (k / 2),\n"
-     "                         b_scales + ((int64_t)g * n + j) * (k / 16), 1.0f, k, bdec + j * k);",
+     "                         b_scales + ((int64_t)g * n + j) * (k / 16), 1.0f, k, bdec + j * k);\n"
+     "    double sgb",
      "orc_dequantize_row(b_codes + ((int64_t)j) * (k / 2),\n"
-     "                         b_scales + ((int64_t)j) * (k / 16), 1.0f, k, bdec + j * k);"),
+     "                         b_scales + ((int64_t)j) * (k / 16), 1.0f, k, bdec + j * k);\n"
+     "    double sgb"),
     ("gemm_drops_weight_scale", "out[r * n + j] = (float)(s * sga * sgb);", "out[r * n + j] = (float)(s * sga);"),
     ("route_unstable_order", "int64_t r = offsets[e] + fill[e];", "int64_t r = offsets[e] + counts[e] - 1 - fill[e];"),
     ("route_ignores_align", "int64_t padded = (counts[e] + align - 1) / align * align;", "int64_t padded = counts[e];"),
@@ -62,6 +65,16 @@ MUTANTS = [
      "float term = (metric == 1) ? fabsf(e) : e * e;"),
     ("four_six_second_top", "quantize_block(blk, s_g, 4.0f, c4)", "quantize_block(blk, s_g, 3.0f, c4)"),
     ("four_six_error_without_outer_scale", "float v = qs * s_g;", "float v = qs;"),
+    ("online_amax_not_running", "if (rowmax > gamax) gamax = rowmax;", "gamax = rowmax;"),
+    ("online_scale_before_tile_max", "if (rowmax > gamax) gamax = rowmax;\n      float s = gamax / 2688.0f;",
+     "float s = gamax / 2688.0f;\n      if (rowmax > gamax) gamax = rowmax;"),
+    ("online_rescale_dropped", "o = o * (gs_prev / gsi) + d_o;", "o = o + d_o;"),
+    ("online_rescale_inverted", "o = o * (gs_prev / gsi) + d_o;", "o = o * (gsi / (gs_prev + 1e-30)) + d_o;"),
+    ("online_final_scale_first_tile", "out[r * n + j] = (float)(o * gs_prev * sgw);",
+     "out[r * n + j] = (float)(o * (double)gsr[0] * sgw);"),
+    ("online_tile_end_off_by_one", "const int64_t c0 = i * tile, c1 = (c0 + tile < inter) ? c0 + tile : inter;\n      float rowmax",
+     "const int64_t c0 = i * tile, c1 = (c0 + tile < inter) ? c0 + tile - 16 : inter;\n      float rowmax"),
+    ("online_zero_tile_not_skipped", "if (gsi == 0.0) continue;", "if (gsi < 0.0) continue;"),
     ("four_six_last_element_dropped", "  for (int i = 0; i < 16; ++i) {\n    float xv = orc_bf16_to_f32(blk[i]);\n    float qs",
      "  for (int i = 0; i < 15; ++i) {\n    float xv = orc_bf16_to_f32(blk[i]);\n    float qs"),
 ]
@@ -80,6 +93,8 @@ PINS = [
     T46.test_six_candidate_is_the_standard_quantizer_at_175_amax_and_choice_minimises_error,
     TD.test_2d_quantization_is_transpose_consistent,
     TD.test_2d_tile_scale_is_the_1d_scale_of_the_row_holding_the_tile_maximum,
+    TS.test_hand_worked_three_tile_row, TS.test_zero_rows_give_zero,
+    TS.test_tile_scales_are_the_running_maximum,
 ]
 
 
