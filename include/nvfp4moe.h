@@ -67,6 +67,7 @@ extern "C" {
 #define NVFP4_UNSUPPORTED 2
 #define NVFP4_HIP_ERROR 3
 #define NVFP4_WORKSPACE_TOO_SMALL 4
+#define NVFP4_SCRATCH_LIMIT 5
 
 /* Block rules of the quantizer (see nvfp4_quantize). */
 #define NVFP4_BLOCK_RULE_SIX 0
@@ -182,6 +183,33 @@ int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden,
                 int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
                 uint8_t* codes, uint8_t* block_scales, float* global_scales,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs and results as moe_permute,
+ * without the workspace: the routing scratch is a static device array of
+ * NVFP4_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up on the first call on a
+ * device).  The call allocates nothing, host or device.  The caller still
+ * passes every input and output buffer.
+ *   Limit: moe_permute_workspace_size(tokens, topk, num_experts) <=
+ *   NVFP4_NOALLOC_SCRATCH_BYTES (e.g. 128 experts up to 261,000 tokens, 1024
+ *   experts up to 32,700 tokens), else NVFP4_SCRATCH_LIMIT before any HIP
+ *   call.
+ *   All calls on one GPU share that GPU's array: calls that overlap on one
+ *   GPU (different streams, or threads without ordering) race and give
+ *   undefined results.  Calls ordered on one stream are safe; nothing from
+ *   an earlier call is read.  In a build with NVFP4_DEBUG_CHECKS the
+ *   precondition word is written to the array, out of the caller's reach.
+ * ---------------------------------------------------------------------- */
+#define NVFP4_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int moe_permute_noalloc(const uint16_t* x, int64_t tokens, int64_t hidden,
+                        const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                        int32_t num_experts, int32_t align, int32_t block_rule,
+                        int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src,
+                        float* row_prob, uint8_t* codes, uint8_t* block_scales,
+                        float* global_scales, void* stream);
 
 /* ------------------------------------------------------------------------
  * w4a4_grouped_gemm -- one grouped call over all experts.

@@ -75,6 +75,9 @@ def _load(path):
     L.moe_permute.restype = C.c_int
     L.moe_permute.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp,
                               _vp, _vp, _vp, _vp, _vp, C.c_size_t, _vp]
+    L.moe_permute_noalloc.restype = C.c_int
+    L.moe_permute_noalloc.argtypes = [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp]
     L.w4a4_grouped_gemm.restype = C.c_int
     L.w4a4_grouped_gemm.argtypes = [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i64, _i64,
                                     C.c_int, C.c_int, _vp, _vp]

@@ -96,6 +96,7 @@ const char* nvfp4_status_string(int status) {
     case NVFP4_UNSUPPORTED: return "unsupported shape";
     case NVFP4_HIP_ERROR: return "HIP launch/runtime error";
     case NVFP4_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case NVFP4_SCRATCH_LIMIT: return "exceeds the static scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -155,22 +156,40 @@ size_t moe_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_expe
   return route_workspace_bytes(tokens, num_experts);
 }
 
-int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden, const int32_t* topk_idx,
-                const float* topk_prob, int32_t topk, int32_t num_experts, int32_t align,
-                int32_t block_rule, int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
-                uint8_t* codes, uint8_t* block_scales, float* global_scales, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// moe_permute's host-side checks of everything but the workspace.
+int nvfp4::permute_args_status(const uint16_t* x, int64_t tokens, int64_t hidden,
+                               const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                               int32_t num_experts, int32_t align, int32_t block_rule,
+                               const int32_t* expert_offsets, const int32_t* dst_row,
+                               const int32_t* row_src, const float* row_prob, const uint8_t* codes,
+                               const uint8_t* block_scales, const float* global_scales) {
   if (!route_args_ok(tokens, topk, num_experts, align)) return NVFP4_INVALID_ARGUMENT;
   if (block_rule < 0 || block_rule > 2) return NVFP4_INVALID_ARGUMENT;
-  if (!expert_offsets || !row_src || !row_prob || !workspace) return NVFP4_INVALID_ARGUMENT;
+  if (!expert_offsets || !row_src || !row_prob) return NVFP4_INVALID_ARGUMENT;
   if (tokens > 0 && (!topk_idx || !topk_prob || !dst_row)) return NVFP4_INVALID_ARGUMENT;
-  if (!aligned(workspace, 16)) return NVFP4_INVALID_ARGUMENT;
   if (x) {
     if (hidden < 16 || hidden % 16 != 0) return NVFP4_INVALID_ARGUMENT;
     if (hidden > kMaxK) return NVFP4_UNSUPPORTED;
     if (!codes || !block_scales || !global_scales) return NVFP4_INVALID_ARGUMENT;
     if (!aligned(x, 16) || !aligned(codes, 8)) return NVFP4_INVALID_ARGUMENT;
   }
+  return NVFP4_OK;
+}
+
+extern "C" {
+
+int moe_permute(const uint16_t* x, int64_t tokens, int64_t hidden, const int32_t* topk_idx,
+                const float* topk_prob, int32_t topk, int32_t num_experts, int32_t align,
+                int32_t block_rule, int32_t* expert_offsets, int32_t* dst_row, int32_t* row_src, float* row_prob,
+                uint8_t* codes, uint8_t* block_scales, float* global_scales, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const int st = permute_args_status(x, tokens, hidden, topk_idx, topk_prob, topk, num_experts,
+                                     align, block_rule, expert_offsets, dst_row, row_src, row_prob,
+                                     codes, block_scales, global_scales);
+  if (st != NVFP4_OK) return st;
+  if (!workspace || !aligned(workspace, 16)) return NVFP4_INVALID_ARGUMENT;
   if (workspace_bytes < route_workspace_bytes(tokens, num_experts)) return NVFP4_WORKSPACE_TOO_SMALL;
   RouteArgs a{};
   a.x = x; a.tokens = tokens; a.hidden = x ? hidden : 0;

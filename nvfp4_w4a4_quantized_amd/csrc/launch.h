@@ -52,6 +52,14 @@ struct RouteArgs {
   uint32_t* error_word; // set by launch_route in a build with NVFP4_DEBUG_CHECKS
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// moe_permute's host-side argument checks (all but the workspace): an
+// NVFP4_* status, NVFP4_OK when the call may proceed.  No HIP call.
+int permute_args_status(const uint16_t* x, int64_t tokens, int64_t hidden,
+                        const int32_t* topk_idx, const float* topk_prob, int32_t topk,
+                        int32_t num_experts, int32_t align, int32_t block_rule,
+                        const int32_t* expert_offsets, const int32_t* dst_row,
+                        const int32_t* row_src, const float* row_prob, const uint8_t* codes,
+                        const uint8_t* block_scales, const float* global_scales);
 
 // ---- gemm.hip ----
 struct GemmArgs {

@@ -13,7 +13,8 @@ import torch
 
 from ._lib import Intermediates, NvFp4Error, Weights, check, lib, ptr, stream_handle
 
-__all__ = ["nvfp4_quantize", "moe_rows_capacity", "moe_permute", "w4a4_grouped_gemm",
+__all__ = ["nvfp4_quantize", "moe_rows_capacity", "moe_permute", "moe_permute_noalloc",
+           "w4a4_grouped_gemm",
            "w4a4_grouped_gemm_swiglu", "moe_combine", "moe_expert_forward",
            "moe_expert_forward_workspace_size", "NvFp4Weights", "StageTimer"]
 
@@ -144,6 +145,40 @@ def moe_permute(x, topk_idx, topk_prob, num_experts: int, align: int = 1, block_
                             ptr(out["row_prob"]), ptr(out.get("codes")), ptr(out.get("scales")),
                             ptr(out.get("gscale")), ptr(ws), ws.numel(), stream_handle()),
           "moe_permute")
+    return out
+
+
+def moe_permute_noalloc(x, topk_idx, topk_prob, num_experts: int, align: int = 1,
+                        block_rule: int = 0, out=None):
+    """moe_permute through the entry point that allocates nothing: the routing
+    scratch is the library's static device array.  `out`: a dict of output
+    tensors shaped as moe_permute returns them (allocated here when None;
+    the library call itself allocates nothing).  Returns that dict."""
+    _need(topk_idx, (torch.int32,), "topk_idx")
+    _need(topk_prob, (torch.float32,), "topk_prob")
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    cap = moe_rows_capacity(T, k, num_experts, align)
+    H = 0
+    if x is not None:
+        _need(x, _BF16_LIKE, "x")
+        H = x.shape[1]
+    if out is None:
+        out = dict(
+            offsets=torch.empty(num_experts + 1, dtype=torch.int32, device=dev),
+            dst_row=torch.empty((T, k), dtype=torch.int32, device=dev),
+            row_src=torch.empty(cap, dtype=torch.int32, device=dev),
+            row_prob=torch.empty(cap, dtype=torch.float32, device=dev))
+        if x is not None:
+            out["codes"] = torch.empty((cap, H // 2), dtype=torch.uint8, device=dev)
+            out["scales"] = torch.empty((cap, H // 16), dtype=torch.uint8, device=dev)
+            out["gscale"] = torch.empty(cap, dtype=torch.float32, device=dev)
+    check(lib().moe_permute_noalloc(ptr(x), T, H, ptr(topk_idx), ptr(topk_prob), k, num_experts,
+                                    align, block_rule, ptr(out["offsets"]), ptr(out["dst_row"]),
+                                    ptr(out["row_src"]), ptr(out["row_prob"]),
+                                    ptr(out.get("codes")), ptr(out.get("scales")),
+                                    ptr(out.get("gscale")), stream_handle()),
+          "moe_permute_noalloc")
     return out
 
 

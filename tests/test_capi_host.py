@@ -137,3 +137,24 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(wbad),
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
 
+
+def test_noalloc_permute_rejects_before_any_device_call(L):
+    """moe_permute_noalloc checks its arguments and the scratch limit on the
+    host, before its first HIP call (so these run without a GPU)."""
+    SCRATCH_LIMIT = 5
+    assert L.nvfp4_status_string(SCRATCH_LIMIT).startswith(b"exceeds the static scratch")
+    limit = 4 << 20
+    fake = C.c_void_p(0x1000)
+    args = (fake, fake, fake, fake, fake, fake, fake, None)
+    # the largest token counts that fit, and the first that do not
+    for E, T_ok in ((128, 261_000), (1024, 32_700)):
+        assert L.moe_permute_workspace_size(T_ok, 8, E) <= limit
+        T_bad = T_ok
+        while L.moe_permute_workspace_size(T_bad, 8, E) <= limit:
+            T_bad += 64
+        assert L.moe_permute_noalloc(fake, T_bad, 256, fake, fake, 8, E, 1, 0, *args) == SCRATCH_LIMIT
+    # argument errors take precedence over the size
+    assert L.moe_permute_noalloc(fake, 1 << 20, 256, fake, fake, 8, 1024, 3, 0, *args) == INVALID
+    assert L.moe_permute_noalloc(fake, 16, 64, fake, fake, 5, 4, 1, 0, *args) == INVALID
+    assert L.moe_permute_noalloc(fake, 16, 64, fake, fake, 2, 4, 1, 7, *args) == INVALID
+    assert L.moe_permute_noalloc(fake, 16, 32768, fake, fake, 2, 4, 1, 0, *args) == UNSUPPORTED
