@@ -297,9 +297,13 @@ int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
 
 /* ------------------------------------------------------------------------
  * moe_expert_forward -- the whole expert layer in one call:
- *   moe_permute -> FC1 grouped GEMM + SwiGLU + amax -> requantize D with that
- *   amax -> FC2 grouped GEMM -> moe_combine.
+ *   routing + per-token quantization -> FC1 grouped GEMM + SwiGLU + amax ->
+ *   requantize D with that amax -> FC2 grouped GEMM -> moe_combine.
  * [miniTE] §5.2-§5.4 (the fused FC1 and FC2 flows).
+ * The routed rows equal moe_permute's bit for bit, but the layer does not
+ * write them: each token is quantized once into a token-major row and FC1
+ * reads routed row r from token row_src[r] (the permutation is applied by
+ * the GEMM's operand loads).
  *
  *   x            bf16 [tokens, hidden];  y out bf16 [tokens, hidden]
  *   w1           NVFP4 gate|up weights [E, 2*inter, hidden] (+ scales, [E])
@@ -312,15 +316,16 @@ int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
  *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned;
  *                its first uint32 is the precondition word
  *   debug        nullable: every non-NULL member receives that intermediate
- *                (in place of the workspace copy); fc1_out, y_rows_f32 and
- *                row_src are only produced when requested (y_rows_f32
- *                switches the FC2 output to fp32; nothing in the layer reads
- *                the row-to-token map, so it is not written otherwise)
+ *                (in place of the workspace copy); fc1_out, y_rows_f32,
+ *                a1_codes and a1_scales are only produced when requested
+ *                (y_rows_f32 switches the FC2 output to fp32; a1_codes and
+ *                a1_scales, given together, receive the permuted routed
+ *                rows of moe_permute's layout, copied from the token rows)
  *   stage_events nullable array of 6 hipEvent_t (as void*), recorded on
  *                `stream` before route, FC1, requantize, FC2, combine and
  *                after combine (profiling; see nvfp4_event_*).
- * Limits: hidden % 128 == 0, inter % 128 == 0, hidden, inter <= 16384, plus
- * the limits of moe_permute.
+ * Limits: hidden % 128 == 0, inter % 128 == 0, hidden, inter <= 16384,
+ * (tokens + 1) * hidden / 2 < 2^32, plus the limits of moe_permute.
  * ---------------------------------------------------------------------- */
 typedef struct {
   const uint8_t* codes;

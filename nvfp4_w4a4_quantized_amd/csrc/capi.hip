@@ -38,7 +38,9 @@ struct Carver {
 
 struct MoeLayout {
   int32_t* route_ws_i; int32_t* offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
-  uint8_t* a1c; uint8_t* a1s; float* a1g;
+  uint8_t* tokc; uint8_t* toks; float* tokg;   // token-major quantized activations
+  float* a1g;                                  // outer scale of each routed row
+  uint8_t* rank;                               // routing entries' ranks inside their chunk
   uint16_t* d; float* amax_d;
   uint8_t* a2c; uint8_t* a2s; float* a2g;
   uint16_t* y_rows;
@@ -63,9 +65,11 @@ MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_
   L.dst_row = c.take<int32_t>((size_t)(T * k));
   L.row_src = c.take<int32_t>((size_t)cap);
   L.row_prob = c.take<float>((size_t)cap);
-  L.a1c = c.take<uint8_t>((size_t)(cap * H / 2));
-  L.a1s = c.take<uint8_t>((size_t)(cap * H / 16));
+  L.tokc = c.take<uint8_t>((size_t)((T + 1) * H / 2));   // + the zero row padding rows read
+  L.toks = c.take<uint8_t>((size_t)((T + 1) * H / 16));
+  L.tokg = c.take<float>((size_t)T);
   L.a1g = c.take<float>((size_t)cap);
+  L.rank = c.take<uint8_t>((size_t)(T * k));
   L.d = c.take<uint16_t>((size_t)(cap * I));
   L.amax_d = c.take<float>((size_t)cap);
   L.a2c = c.take<uint8_t>((size_t)(cap * I / 2));
@@ -302,6 +306,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   if ((int64_t)num_experts * 2 * inter >= 0x7FFFFFFFLL ||
       (int64_t)num_experts * hidden >= 0x7FFFFFFFLL)
     return NVFP4_INVALID_ARGUMENT;
+  if ((tokens + 1) * (hidden / 2) > 0xFFFFFFFFLL) return NVFP4_UNSUPPORTED;   // 32-bit row offsets
   MoeLayout L = carve_moe(workspace, tokens, hidden, inter, topk, num_experts, align);
   if (workspace_bytes < L.bytes) return NVFP4_WORKSPACE_TOO_SMALL;
   float* c_out = nullptr;
@@ -311,8 +316,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
     if (debug->dst_row) L.dst_row = debug->dst_row;
     if (debug->row_src) L.row_src = debug->row_src;
     if (debug->row_prob) L.row_prob = debug->row_prob;
-    if (debug->a1_codes) L.a1c = debug->a1_codes;
-    if (debug->a1_scales) L.a1s = debug->a1_scales;
+    if ((debug->a1_codes != nullptr) != (debug->a1_scales != nullptr)) return NVFP4_INVALID_ARGUMENT;
     if (debug->a1_gscale) L.a1g = debug->a1_gscale;
     if (debug->d) L.d = debug->d;
     if (debug->amax_d) L.amax_d = debug->amax_d;
@@ -322,7 +326,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
     if (debug->y_rows) L.y_rows = debug->y_rows;
     c_out = debug->fc1_out;
     y_f32 = debug->y_rows_f32;
-    const void* ptrs16[] = {L.a1c, L.a2c, L.d, L.y_rows, y_f32};
+    const void* ptrs16[] = {debug->a1_codes, L.a2c, L.d, L.y_rows, y_f32};
     for (const void* p : ptrs16)
       if (p && !aligned(p, 16)) return NVFP4_INVALID_ARGUMENT;
   }
@@ -335,7 +339,8 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return NVFP4_HIP_ERROR;
   GemmArgs g1{};
-  g1.a_codes = L.a1c; g1.a_scales = L.a1s; g1.a_gscale = L.a1g;
+  g1.a_codes = L.tokc; g1.a_scales = L.toks; g1.a_gscale = L.a1g; g1.a_row_src = L.row_src;
+  g1.a_pad_row = tokens;
   g1.b_codes = w1->codes; g1.b_scales = w1->scales; g1.b_gscale = w1->gscale;
   g1.offsets = L.offsets; g1.num_groups = num_experts; g1.rows_cap = cap;
   g1.n = 2 * inter; g1.k = hidden; g1.inter = inter; g1.b_layout = w1->layout;
@@ -349,24 +354,31 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   g2.out_dtype = y_f32 ? 0 : 1;
   g2.out = y_f32 ? static_cast<void*>(y_f32) : static_cast<void*>(L.y_rows);
   g2.tile_table = L.tab2;
-  // a1 + a2: routing metadata and per-token quantize-scatter.  The same
-  // launches clear amax_d over the whole capacity (FC1 takes atomic maxima
-  // into it) and, while they hold the offsets, write both GEMMs' tile
-  // tables.  The row-to-token map is only written when the caller asks for
-  // it (nothing downstream reads it).
+  // a1 + a2: routing metadata and per-token quantization.  Each token is
+  // quantized once into a token-major row; FC1 reads routed row r from token
+  // row_src[r] (the permutation is applied by the GEMM's A loads, so no
+  // routed copies are written).  The same launches clear amax_d over the
+  // whole capacity (FC1 takes atomic maxima into it) and, while they hold
+  // the offsets, write both GEMMs' tile tables.
   RouteArgs ra{};
   ra.x = x; ra.tokens = tokens; ra.hidden = hidden;
   ra.topk_idx = topk_idx; ra.topk_prob = topk_prob; ra.topk = topk;
   ra.num_experts = num_experts; ra.align = align;
   ra.offsets = L.offsets; ra.dst_row = L.dst_row;
-  ra.row_src = (debug && debug->row_src) ? debug->row_src : nullptr;
-  ra.row_prob = L.row_prob; ra.codes = L.a1c; ra.scales = L.a1s; ra.gscale = L.a1g;
+  ra.row_src = L.row_src;
+  ra.row_prob = L.row_prob; ra.gscale = L.a1g;
+  ra.tok_codes = L.tokc; ra.tok_scales = L.toks; ra.tok_gscale = L.tokg; ra.entry_rank = L.rank;
   ra.zero_per_row = L.amax_d; ra.zero_rows = cap;
   ra.tables[0] = gemm_tile_table_spec(g1, true, L.tab1);
   ra.tables[1] = gemm_tile_table_spec(g2, false, L.tab2);
   ra.num_tables = 2;
   ra.workspace = L.route_ws_i; ra.block_rule = act_block_rule;
   if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if (debug && (debug->a1_codes || debug->a1_scales)) {   // the permuted rows, for inspection
+    if ((e = launch_gather_rows(L.tokc, L.toks, L.row_src, L.offsets + num_experts, cap, hidden,
+                                debug->a1_codes, debug->a1_scales, s)) != hipSuccess)
+      return NVFP4_HIP_ERROR;
+  }
   if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a3 + a4: FC1 with the weighted SwiGLU epilogue and D's row amax
   if ((e = launch_gemm_swiglu(g1, s)) != hipSuccess) return NVFP4_HIP_ERROR;

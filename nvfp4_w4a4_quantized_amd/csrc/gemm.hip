@@ -416,16 +416,24 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
   // flipping bits 2-3 keeps the slot inside its group of 16 (reads stay
   // conflict free) and spreads the writers of one row over four bank groups
   auto aslot = [](int l, int sq) { return l ^ (4 * (sq + 2 * (l >> 5))); };
-  // ---- A: thread-owned quarter rows (32 elements = 16 code bytes + 2 scales)
-  const uint8_t* a_cbase = a.a_codes + row0 * (K / 2);
-  const uint8_t* a_sbase = a.a_scales + row0 * (K / 16);
+  // ---- A: thread-owned quarter rows (32 elements = 16 code bytes + 2 scales).
+  // Row r of the tile is A row row0 + r, or, gathering (a_row_src), token
+  // row a_row_src[row0 + r] of the token-major quantized activations (a
+  // padding row's -1 reads the all-zero row a_pad_row).
+  const bool gather = a.a_row_src != nullptr;
+  const uint8_t* a_cbase = gather ? a.a_codes : a.a_codes + row0 * (K / 2);
+  const uint8_t* a_sbase = gather ? a.a_scales : a.a_scales + row0 * (K / 16);
   uint32_t a_src[APT], a_ssrc[APT];
   int a_dst[APT];
 #pragma unroll
   for (int j = 0; j < APT; ++j) {
     const int u = tid + NT * j;
     const int r = u / 4, q = u % 4, h = q / 2;
-    const int64_t ar = r < row1 - row0 ? r : row1 - row0 - 1;   // row inside the tile
+    int64_t ar = r < row1 - row0 ? r : row1 - row0 - 1;   // row inside the tile
+    if (gather) {
+      const int32_t t = a.a_row_src[row0 + ar];
+      ar = t >= 0 ? (int64_t)t : a.a_pad_row;
+    }
     a_src[j] = (uint32_t)(ar * (K / 2) + 16 * q);
     a_ssrc[j] = (uint32_t)(ar * (K / 16) + 2 * q);
     // fragment r/32, lane (r%32) + 32h, substeps 4(q%2) .. 4(q%2)+3

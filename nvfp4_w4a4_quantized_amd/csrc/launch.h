@@ -50,8 +50,22 @@ struct RouteArgs {
   void* workspace;      // route_workspace_bytes(); its first uint32 is the precondition word
   int32_t block_rule;   // 0 standard, 1/2 Four-Over-Six (MSE/MAE)
   uint32_t* error_word; // set by launch_route in a build with NVFP4_DEBUG_CHECKS
+  // Gather mode (tok_codes non-NULL, with x): each token is quantized once
+  // into token-major rows tok_codes [tokens + 1, hidden/2], tok_scales
+  // [tokens + 1, hidden/16], tok_gscale [tokens]; row `tokens` is set to
+  // zero codes and scales (the row padding rows read).  No routed-row copies
+  // are written (codes / scales unused), gscale[r] receives the outer scale
+  // of row r's token, and row_src must be given (the GEMM reads row r from
+  // token row_src[r]).
+  uint8_t* tok_codes; uint8_t* tok_scales; float* tok_gscale;
+  uint8_t* entry_rank;  // gather mode: [tokens * topk] scratch (rank inside the chunk)
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+// Permuted rows r < *rows_end (device) copied from the token-major rows of
+// gather mode; padding rows (row_src < 0) get zeros.
+hipError_t launch_gather_rows(const uint8_t* tok_codes, const uint8_t* tok_scales,
+                              const int32_t* row_src, const int32_t* rows_end, int64_t cap,
+                              int64_t hidden, uint8_t* codes, uint8_t* scales, hipStream_t s);
 // moe_permute's host-side argument checks (all but the workspace): an
 // NVFP4_* status, NVFP4_OK when the call may proceed.  No HIP call.
 int permute_args_status(const uint16_t* x, int64_t tokens, int64_t hidden,
@@ -78,6 +92,12 @@ struct GemmArgs {
   // holds the offsets (one {group, row0, row1, n-tile} entry per workgroup,
   // group < 0 = none; see tile_schedule.h)
   const int4* tile_table;
+  // nullable: A rows gathered from token-major codes / scales (row r reads
+  // token a_row_src[r]; -1, a padding row, reads row a_pad_row, all zero, so
+  // its products are +0 as in the permuted layout).  a_gscale stays per
+  // routed row.  (a_pad_row + 1) * k / 2 < 2^32.
+  const int32_t* a_row_src;
+  int64_t a_pad_row;
 };
 hipError_t launch_gemm_plain(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GemmArgs& a, hipStream_t s);

@@ -69,16 +69,17 @@ __device__ __forceinline__ bool bf16_pair_nonfinite(uint32_t u) {
 
 // KMAX > 0 (topk <= KMAX): a lane's k expert ids are all requested before
 // the first LDS add (a loop over a run-time count would wait for each load).
+// Workgroup `wg` (256 threads) counts chunks 4*wg .. 4*wg+3, one per wave;
+// lds holds 4*E counters.
 template <int KMAX>
-__global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int64_t tokens,
-                                                          int32_t topk, int32_t E,
-                                                          int64_t nchunks, int32_t* hist) {
-  extern __shared__ int32_t lds[];   // [4 waves][E]
+__device__ __forceinline__ void hist_chunks(const int32_t* idx, int64_t tokens, int32_t topk,
+                                            int32_t E, int64_t nchunks, int32_t* hist,
+                                            int64_t wg, int32_t* lds) {
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   int32_t* h = lds + wave * E;
   for (int e = lane; e < E; e += kWave) h[e] = 0;
   __syncthreads();
-  const int64_t chunk = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t chunk = wg * 4 + wave;
   if (chunk < nchunks) {
     const int64_t t = chunk * kChunk + lane;
     if (t < tokens) {
@@ -100,6 +101,80 @@ __global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int
   __syncthreads();
   if (chunk < nchunks)
     for (int e = lane; e < E; e += kWave) hist[(int64_t)e * nchunks + chunk] = h[e];
+}
+
+// Gather mode's histogram: per chunk (one wave, lane = token) a 64-bit mask
+// per expert of the chunk's tokens that chose it, built with LDS ORs.  The
+// chunk's count for an expert is the mask's popcount, and an entry's stable
+// rank among the chunk's entries of its expert (ascending token) is the
+// popcount of the mask below its lane, written to rank[t*topk + j].  A token
+// naming an expert twice counts once (both entries get one rank: a violated
+// precondition stays inside the counted rows).  lds holds 4*E masks.
+template <int KMAX>
+__device__ __forceinline__ void hist_rank_chunks(const RouteArgs& a, int64_t nchunks,
+                                                 int32_t* hist, uint8_t* rank, int64_t wg,
+                                                 unsigned long long* lds) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int E = a.num_experts, k = a.topk;
+  unsigned long long* m = lds + (size_t)wave * E;
+  for (int e = lane; e < E; e += kWave) m[e] = 0ull;
+  __syncthreads();
+  const int64_t chunk = wg * 4 + wave;
+  const int64_t t = chunk * kChunk + lane;
+  const bool valid = chunk < nchunks && t < a.tokens;
+  const unsigned long long bit = 1ull << lane, below = bit - 1ull;
+  auto routed = [&](int e) { return e >= 0 && e < E; };
+  if constexpr (KMAX > 0) {
+    int ids[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) ids[j] = (valid && j < k) ? a.topk_idx[t * k + j] : -1;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (routed(ids[j])) atomicOr(m + ids[j], bit);
+#ifdef NVFP4_DEBUG_CHECKS
+    bool dup = false;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i)
+#pragma unroll
+      for (int j = i + 1; j < KMAX; ++j) dup |= (routed(ids[i]) && ids[i] == ids[j]);
+    report_bits(a.error_word, dup, NVFP4_PRECONDITION_DUPLICATE_EXPERT);
+#endif
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+      if (valid && j < k) rank[t * k + j] = routed(ids[j]) ? (uint8_t)__popcll(m[ids[j]] & below) : 0;
+  } else {
+    bool dup = false;
+    if (valid)
+      for (int j = 0; j < k; ++j) {
+        const int e = a.topk_idx[t * k + j];
+        if (!routed(e)) continue;
+        atomicOr(m + e, bit);
+#ifdef NVFP4_DEBUG_CHECKS
+        for (int i = 0; i < j; ++i) dup |= (a.topk_idx[t * k + i] == e);
+#endif
+      }
+#ifdef NVFP4_DEBUG_CHECKS
+    report_bits(a.error_word, dup, NVFP4_PRECONDITION_DUPLICATE_EXPERT);
+#endif
+    (void)dup;
+    __syncthreads();
+    if (valid)
+      for (int j = 0; j < k; ++j) {
+        const int e = a.topk_idx[t * k + j];
+        rank[t * k + j] = routed(e) ? (uint8_t)__popcll(m[e] & below) : 0;
+      }
+  }
+  if (chunk < nchunks)
+    for (int e = lane; e < E; e += kWave) hist[(int64_t)e * nchunks + chunk] = __popcll(m[e]);
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(256) void route_hist_kernel(const int32_t* idx, int64_t tokens,
+                                                          int32_t topk, int32_t E,
+                                                          int64_t nchunks, int32_t* hist) {
+  extern __shared__ int32_t lds[];   // [4 waves][E]
+  hist_chunks<KMAX>(idx, tokens, topk, E, nchunks, hist, blockIdx.x, lds);
 }
 
 __device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v, int lane) {
@@ -154,27 +229,27 @@ __device__ void block_expert_offsets(const int32_t (&tot)[kScanPer], int32_t E, 
   __syncthreads();
 }
 
-// zero[0, n) = 0 by the whole grid (grid-stride, 16-byte stores where aligned)
-__device__ __forceinline__ void grid_zero_fill(float* zero, int64_t n) {
-  if (!zero) return;
-  const int64_t nt = (int64_t)gridDim.x * blockDim.x;
+// zero[0, n) = 0 by workgroups [0, nblocks) of the grid (grid-stride,
+// 16-byte stores where aligned)
+__device__ __forceinline__ void grid_zero_fill(float* zero, int64_t n, int64_t nblocks) {
+  if (!zero || (int64_t)blockIdx.x >= nblocks) return;
+  const int64_t nt = nblocks * blockDim.x;
   const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t n4 = (reinterpret_cast<uintptr_t>(zero) & 15u) == 0 ? n / 4 : 0;
   for (int64_t i = i0; i < n4; i += nt) reinterpret_cast<float4*>(zero)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int64_t i = 4 * n4 + i0; i < n; i += nt) zero[i] = 0.0f;
 }
 
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t* hist, int32_t* base,
-                                                                  int64_t nchunks, int32_t E,
-                                                                  int32_t align, int32_t* counts,
-                                                                  int32_t* offsets, float* zero,
-                                                                  int64_t nzero) {
+// The scan of workgroup blockIdx.x of scan_wgs (the kernels below).
+__device__ void route_scan_body(const int32_t* hist, int32_t* base, int64_t nchunks, int32_t E,
+                                int32_t align, int32_t* counts, int32_t* offsets, float* zero,
+                                int64_t nzero, int64_t scan_wgs) {
   constexpr int NWAVES = kScanWaves;
   constexpr int PER = kScanPer;
   __shared__ int32_t off[kScanMaxE + 1];
   __shared__ int32_t wsum[NWAVES];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  grid_zero_fill(zero, nzero);
+  grid_zero_fill(zero, nzero, scan_wgs);
   // expert totals: expert e = tid + kScanThreads*i, summed over its row
   int32_t tot[PER];
 #pragma unroll
@@ -228,6 +303,14 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t*
   }
 }
 
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(const int32_t* hist, int32_t* base,
+                                                                  int64_t nchunks, int32_t E,
+                                                                  int32_t align, int32_t* counts,
+                                                                  int32_t* offsets, float* zero,
+                                                                  int64_t nzero) {
+  route_scan_body(hist, base, nchunks, E, align, counts, offsets, zero, nzero, gridDim.x);
+}
+
 // tokens per scatter wave (a divisor of kChunk): two while the double-buffered
 // row fits the register budget, one for the longest rows
 constexpr int tokens_per_wave(int bpl) { return bpl <= 4 ? 2 : 1; }
@@ -251,6 +334,112 @@ __device__ __forceinline__ void load_token_row(const uint16_t* xr, int nblocks, 
   }
 }
 
+// One token of the wave's TPW, quantized in registers (row amax, block
+// scales, codes): the lane's blocks lane + 64 i.
+template <int BPL>
+__device__ __forceinline__ float quantize_token_regs(const uint32_t (&w)[BPL][8], int rule,
+                                                     uint2 (&codes)[BPL], uint32_t (&sbytes)[BPL]) {
+  uint32_t m = 0u;
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const uint32_t mi = bf16_absmax_bits(w[i]);
+    m = m > mi ? m : mi;
+  }
+  const float amax = __uint_as_float(wave_max_u32(m) << 16);
+  const float s_g = outer_scale(amax, rule);
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) codes[i] = quantize_block16(w[i], s_g, rule, &sbytes[i]);
+  return s_g;
+}
+
+// The quantized token into a row of `codes` / `scales` (all lanes).
+template <int BPL>
+__device__ __forceinline__ void store_token_row(uint8_t* cr, uint8_t* sr, int nblocks, int lane,
+                                                const uint2 (&codes)[BPL],
+                                                const uint32_t (&sbytes)[BPL]) {
+#pragma unroll
+  for (int i = 0; i < BPL; ++i) {
+    const int b = lane + kWave * i;
+    if (b < nblocks) {
+      *reinterpret_cast<uint2*>(cr + (int64_t)b * 8) = codes[i];
+      sr[b] = (uint8_t)sbytes[i];
+    }
+  }
+}
+
+// Gather mode: row `tokens` of the token-major rows, which padding rows
+// read, set to zero codes and scales (by the wave of the last token).
+__device__ __forceinline__ void zero_pad_row(const RouteArgs& a, int lane) {
+  const int64_t H = a.hidden;
+  uint8_t* cr = a.tok_codes + a.tokens * (H / 2);
+  uint8_t* sr = a.tok_scales + a.tokens * (H / 16);
+  for (int64_t i = 8 * lane; i < H / 2; i += 8 * kWave)
+    *reinterpret_cast<uint2*>(cr + i) = make_uint2(0u, 0u);
+  for (int64_t i = lane; i < H / 16; i += kWave) sr[i] = 0;
+}
+
+// Gather mode: token t quantized by one wave into its token-major row.
+template <int BPL>
+__device__ __forceinline__ void quantize_token_wave(const RouteArgs& a, int64_t t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t H = a.hidden;
+  const int nblocks = (int)(H / 16);
+  uint32_t w[1][BPL][8];
+  load_token_row<BPL>(a.x + t * H, nblocks, lane, w[0]);
+#ifdef NVFP4_DEBUG_CHECKS
+  {
+    bool badx = false;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) badx |= bf16_pair_nonfinite(w[0][i][u]);
+    report_bits(a.error_word, badx, NVFP4_PRECONDITION_NONFINITE_INPUT);
+  }
+#endif
+  uint2 codes[BPL];
+  uint32_t sbytes[BPL];
+  const float s_g = quantize_token_regs<BPL>(w[0], a.block_rule, codes, sbytes);
+  store_token_row<BPL>(a.tok_codes + t * (H / 2), a.tok_scales + t * (H / 16), nblocks, lane,
+                       codes, sbytes);
+  if (lane == 0) a.tok_gscale[t] = s_g;
+  if (t == a.tokens - 1) zero_pad_row(a, lane);
+}
+
+// Gather mode, first launch of the three-launch path: workgroups
+// [0, hist_wgs) count the chunks' entries and rank them inside their chunk
+// (hist_rank_chunks); the others quantize tokens [0, tq_end), one per wave.
+// Neither part depends on the routing offsets, so the quantization runs
+// beside the routing instead of after it.
+template <int KMAX, int BPL>
+__global__ __launch_bounds__(256) void route_hist_quant_kernel(RouteArgs a, int64_t nchunks,
+                                                               int32_t* hist, int64_t hist_wgs,
+                                                               int64_t tq_end) {
+  extern __shared__ unsigned long long lds64[];   // [4 waves][E] (histogram workgroups)
+  if ((int64_t)blockIdx.x < hist_wgs) {
+    hist_rank_chunks<KMAX>(a, nchunks, hist, a.entry_rank, blockIdx.x, lds64);
+    return;
+  }
+  const int64_t t = ((int64_t)blockIdx.x - hist_wgs) * 4 + threadIdx.x / kWave;
+  if (t < tq_end) quantize_token_wave<BPL>(a, t);
+}
+
+// Gather mode, second launch: workgroups [0, scan_wgs) run the scan; the
+// others quantize tokens [tq_begin, tokens), one per wave (the scan is a
+// short latency-bound chain on a few workgroups).
+template <int BPL>
+__global__ __launch_bounds__(256) void route_scan_quant_kernel(RouteArgs a, const int32_t* hist,
+                                                               int32_t* base, int32_t* counts,
+                                                               int64_t nchunks, int64_t scan_wgs,
+                                                               int64_t tq_begin) {
+  if ((int64_t)blockIdx.x < scan_wgs) {
+    route_scan_body(hist, base, nchunks, a.num_experts, a.align, counts, a.offsets,
+                    a.zero_per_row, a.zero_rows, scan_wgs);
+    return;
+  }
+  const int64_t t = tq_begin + ((int64_t)blockIdx.x - scan_wgs) * 4 + threadIdx.x / kWave;
+  if (t < a.tokens) quantize_token_wave<BPL>(a, t);
+}
+
 // Small batches (SMALL: at most kSmallEntries routing entries) run the
 // whole permutation in this one launch: every workgroup histograms all the
 // expert ids in LDS, also counting those of the tokens before its own chunk
@@ -260,31 +449,33 @@ __device__ __forceinline__ void load_token_row(const uint16_t* xr, int nblocks, 
 // dependent launches.  Workgroup 0 publishes offsets[].
 constexpr int64_t kSmallEntries = 4096;
 
-// Workgroups appended to the scatter grid that write the GEMMs' tile tables
-// (RouteArgs::tables) from the offsets, while the other workgroups permute:
-// the tables cost no launch and no time on the routing's critical path.
+// Workgroups at the front of the scatter grid that write the GEMMs' tile
+// tables (RouteArgs::tables) from the offsets, while the other workgroups
+// permute: the tables cost no launch.  First in the grid, they are
+// dispatched first.
 constexpr int kTableWorkgroups = 16;
 
 template <int BPL, int KMAX, bool SMALL>
 __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const int32_t* base,
                                                             const int32_t* counts,
                                                             int64_t token_waves, int64_t nchunks,
-                                                            int64_t table_wg0) {
+                                                            int64_t twg) {
   constexpr int TPW = tokens_per_wave(BPL);
   static_assert(kChunk % TPW == 0, "a wave's tokens share one chunk");
   static_assert(kChunk % (4 * TPW) == 0, "a workgroup's tokens share one chunk");
   static_assert(!SMALL || kScanThreads == 256, "the block scan runs on the 256 threads");
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  // workgroups [0, twg) write the tile tables, the others permute
+  const bool table_wg = (int64_t)blockIdx.x < twg;        // uniform per workgroup
+  const int64_t bx = table_wg ? 0 : (int64_t)blockIdx.x - twg;
+  const int64_t wid = bx * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int k = a.topk, E = a.num_experts;
   const int64_t H = a.hidden;
-  const bool table_wg = (int64_t)blockIdx.x >= table_wg0;   // uniform per workgroup
   __shared__ TileTableLds tls;
   if constexpr (!SMALL) {
     if (table_wg) {                      // offsets come from the scan launch
-      const int64_t wg = (int64_t)blockIdx.x - table_wg0;
-      build_tile_tables(a.offsets, E, a.tables[0], a.tables[1], a.num_tables, wg * 256 + threadIdx.x,
-                        (int64_t)kTableWorkgroups * 256, tls);
+      build_tile_tables(a.offsets, E, a.tables[0], a.tables[1], a.num_tables,
+                        (int64_t)blockIdx.x * 256 + threadIdx.x, twg * 256, tls);
       return;
     }
   }
@@ -309,12 +500,21 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
   const bool lane_valid = tl < a.tokens && nt > 0;
   int ids[KMAX > 0 ? KMAX : 1];                      // the expert ids of the lane's chunk token
   float prob_l[TPW];                                 // router weight of entry `lane` of token ti
+  // the expert id of entry (lane / k, lane % k) of the wave's tokens
+  int ent_e = -1;
   if constexpr (KMAX > 0) {
+    if (lane < TPW * k && lane / k < nt) ent_e = a.topk_idx[t0 * k + lane];
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) ids[i] = (lane_valid && i < k) ? a.topk_idx[tl * k + i] : -1;
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti) prob_l[ti] = (ti < nt && lane < k) ? a.topk_prob[(t0 + ti) * k + lane] : 0.0f;
   }
+  // gather mode after the first launch quantized the tokens: their outer
+  // scales become the rows' (x is NULL here)
+  float tok_sg[TPW];
+#pragma unroll
+  for (int ti = 0; ti < TPW; ++ti)
+    tok_sg[ti] = (!a.x && a.tok_gscale && ti < nt) ? a.tok_gscale[t0 + ti] : 0.0f;
   constexpr int kHistPer = SMALL ? (int)(kSmallEntries / 256) : 1;   // entries per thread
   int hist_ids[kHistPer];
   if constexpr (SMALL) {
@@ -334,7 +534,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 256) { s_cnt[e] = 0; s_bef[e] = 0; }
     __syncthreads();
-    const int64_t c0 = ((int64_t)blockIdx.x * 4 * TPW) / kChunk * kChunk;   // the chunk's first token
+    const int64_t c0 = (bx * 4 * TPW) / kChunk * kChunk;   // the chunk's first token
     const int64_t nbef = (c0 < a.tokens ? c0 : a.tokens) * k;
 #pragma unroll
     for (int u = 0; u < kHistPer; ++u) {
@@ -359,11 +559,10 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     __syncthreads();
   }
   if constexpr (SMALL) {
-    grid_zero_fill(a.zero_per_row, a.zero_rows);
+    grid_zero_fill(a.zero_per_row, a.zero_rows, gridDim.x);
     if (table_wg) {                      // offsets from this workgroup's own histogram
-      const int64_t wg = (int64_t)blockIdx.x - table_wg0;
-      build_tile_tables(s_off, E, a.tables[0], a.tables[1], a.num_tables, wg * 256 + threadIdx.x,
-                        (int64_t)kTableWorkgroups * 256, tls);
+      build_tile_tables(s_off, E, a.tables[0], a.tables[1], a.num_tables,
+                        (int64_t)blockIdx.x * 256 + threadIdx.x, twg * 256, tls);
       return;
     }
   }
@@ -382,9 +581,9 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
       if (lane == 0) {
         if (a.row_src) a.row_src[r] = -1;
         a.row_prob[r] = 0.0f;
-        if (a.x) a.gscale[r] = 0.0f;
+        if (a.x || a.tok_gscale) a.gscale[r] = 0.0f;
       }
-      if (a.x) {
+      if (a.x && !a.tok_codes) {
         uint8_t* cr = a.codes + r * (H / 2);
         for (int64_t i = lane * 8; i < H / 2; i += kWave * 8)
           *reinterpret_cast<uint2*>(cr + i) = make_uint2(0u, 0u);
@@ -397,8 +596,12 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
   // destination of entry j of token ti is held by lane j (lanes < k)
   int64_t dst_l[TPW];
   if constexpr (KMAX > 0) {
-    // every lane holds the k expert ids of its own chunk token, so the
-    // ballots need no memory traffic; a token's ids come from its lane
+    // Lane L < TPW*k holds entry (L / k, L % k) of the wave's tokens: its
+    // expert id (loaded in phase 1) and that expert's chunk base, one load
+    // instruction for the whole wave.  The ballots then need no memory
+    // traffic: every lane holds the k expert ids of its own chunk token.
+    int64_t base_l = 0;
+    if (ent_e >= 0 && ent_e < E) base_l = chunk_base(ent_e, chunk);
 #pragma unroll
     for (int ti = 0; ti < TPW; ++ti) {
       dst_l[ti] = -1;
@@ -407,13 +610,15 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
 #pragma unroll
       for (int j = 0; j < KMAX; ++j) {
         if (j < k && ti < nt) {
-          const int e = __shfl(ids[j], pos, kWave);
+          const int src = ti * k + j;
+          const int e = __builtin_amdgcn_readlane(ent_e, src);
           if (e >= 0 && e < E) {
             bool hit = false;
 #pragma unroll
             for (int i = 0; i < KMAX; ++i) hit |= (ids[i] == e);
             const uint64_t mask = __ballot(hit);
-            const int64_t d = chunk_base(e, chunk) + __popcll(mask & below_mask);
+            const int64_t b = (int64_t)__builtin_amdgcn_readlane((int)base_l, src);
+            const int64_t d = b + __popcll(mask & below_mask);
             if (lane == j) dst_l[ti] = d;
           }
         }
@@ -472,32 +677,23 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     const int64_t t = t0 + ti;
     uint2 codes[BPL];
     uint32_t sbytes[BPL];
-    float s_g = 0.0f;
+    float s_g = tok_sg[ti];
     if (a.x) {
-      uint32_t m = 0u;
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        const uint32_t mi = bf16_absmax_bits(w[ti][i]);
-        m = m > mi ? m : mi;
+      s_g = quantize_token_regs<BPL>(w[ti], a.block_rule, codes, sbytes);
+      // gather mode: the token's one quantized row (the GEMM reads it through
+      // row_src); otherwise a copy per destination row below
+      if (a.tok_codes) {
+        store_token_row<BPL>(a.tok_codes + t * (H / 2), a.tok_scales + t * (H / 16), nblocks,
+                             lane, codes, sbytes);
+        if (lane == 0) a.tok_gscale[t] = s_g;
+        if (t == a.tokens - 1) zero_pad_row(a, lane);
       }
-      const float amax = __uint_as_float(wave_max_u32(m) << 16);
-      s_g = outer_scale(amax, a.block_rule);
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) codes[i] = quantize_block16(w[ti][i], s_g, a.block_rule, &sbytes[i]);
     }
     // the quantized token into row dst (all lanes)
     auto store_row = [&](int64_t dst) {
-      if (dst < 0 || !a.x) return;
-      uint8_t* cr = a.codes + dst * (H / 2);
-      uint8_t* sr = a.scales + dst * (H / 16);
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        const int b = lane + kWave * i;
-        if (b < nblocks) {
-          *reinterpret_cast<uint2*>(cr + (int64_t)b * 8) = codes[i];
-          sr[b] = (uint8_t)sbytes[i];
-        }
-      }
+      if (dst < 0 || !a.x || a.tok_codes) return;
+      store_token_row<BPL>(a.codes + dst * (H / 2), a.scales + dst * (H / 16), nblocks, lane,
+                           codes, sbytes);
     };
     // the maps of entry j (router weight p), by the lane that holds it
     auto store_meta = [&](int j, int64_t dst, float p) {
@@ -505,7 +701,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
       if (dst < 0) return;
       if (a.row_src) a.row_src[dst] = (int32_t)t;
       a.row_prob[dst] = p;
-      if (a.x) a.gscale[dst] = s_g;
+      if (a.x || a.tok_gscale) a.gscale[dst] = s_g;
     };
     if constexpr (KMAX > 0) {
       if (lane < k) store_meta(lane, dst_l[ti], prob_l[ti]);
@@ -532,6 +728,94 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
   }
 }
 
+// Gather mode, third launch of the three-launch path.  Workgroups [0, twg)
+// write the tile tables.  Then one thread per routing entry i = t*topk + j:
+// its row is dst = base[e][chunk of t] + its rank inside the chunk, and it
+// writes dst_row[i], row_src[dst] = t, row_prob[dst] and gscale[dst] (its
+// token's outer scale).  The last workgroups give one wave per expert for
+// its padding rows [offsets[e] + counts[e], offsets[e+1]).
+__global__ __launch_bounds__(256) void route_entries_kernel(RouteArgs a, const int32_t* base,
+                                                            const int32_t* counts,
+                                                            int64_t nchunks, int64_t entry_wgs,
+                                                            int64_t twg) {
+  __shared__ TileTableLds tls;
+  if ((int64_t)blockIdx.x < twg) {
+    // one table per workgroup: the first third of them write table 0 (FC1),
+    // the rest table 1 (FC2, about twice the entries), side by side
+    const int64_t w0 = a.num_tables > 1 ? twg / 3 : twg;
+    const int64_t b = blockIdx.x;
+    if (b < w0)
+      build_tile_tables(a.offsets, a.num_experts, a.tables[0], a.tables[0], 1,
+                        b * 256 + threadIdx.x, w0 * 256, tls);
+    else
+      build_tile_tables(a.offsets, a.num_experts, a.tables[1], a.tables[1], 1,
+                        (b - w0) * 256 + threadIdx.x, (twg - w0) * 256, tls);
+    return;
+  }
+  const int64_t bx = (int64_t)blockIdx.x - twg;
+  const int E = a.num_experts, k = a.topk;
+  if (bx < entry_wgs) {
+    const int64_t i = bx * 256 + threadIdx.x;
+    const bool live = i < a.tokens * k;
+    const int64_t t = live ? i / k : 0;
+    const int e = live ? a.topk_idx[i] : -1;
+    const float p = live ? a.topk_prob[i] : 0.0f;
+#ifdef NVFP4_DEBUG_CHECKS
+    report_bits(a.error_word, live && !__builtin_isfinite(p), NVFP4_PRECONDITION_NONFINITE_PROB);
+#endif
+    if (!live) return;
+    int64_t d = -1;
+    if (e >= 0 && e < E) {
+      d = (int64_t)base[(int64_t)e * nchunks + t / kChunk] + a.entry_rank[i];
+      a.row_src[d] = (int32_t)t;
+      a.row_prob[d] = p;
+      a.gscale[d] = a.tok_gscale[t];
+    }
+    a.dst_row[i] = (int32_t)d;
+    return;
+  }
+  const int64_t e = (bx - entry_wgs) * 4 + threadIdx.x / kWave;
+  if (e >= E) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t r1 = a.offsets[e + 1];
+  for (int64_t r = (int64_t)a.offsets[e] + counts[e] + lane; r < r1; r += kWave) {
+    a.row_src[r] = -1;
+    a.row_prob[r] = 0.0f;
+    a.gscale[r] = 0.0f;
+  }
+}
+
+// The routed rows of the permuted layout from the token-major rows of gather
+// mode (debug intermediates): row r < *rows_end takes token row_src[r]'s
+// codes and scales, padding rows (row_src < 0) zeros.  One wave per row.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* tok_codes,
+                                                          const uint8_t* tok_scales,
+                                                          const int32_t* row_src,
+                                                          const int32_t* rows_end, int64_t cap,
+                                                          int64_t H, uint8_t* codes,
+                                                          uint8_t* scales) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (r >= cap || r >= (int64_t)*rows_end) return;
+  const int64_t t = row_src[r];
+  for (int64_t i = 8 * lane; i < H / 2; i += 8 * kWave) {
+    const uint2 v = t >= 0 ? *reinterpret_cast<const uint2*>(tok_codes + t * (H / 2) + i)
+                           : make_uint2(0u, 0u);
+    *reinterpret_cast<uint2*>(codes + r * (H / 2) + i) = v;
+  }
+  for (int64_t i = lane; i < H / 16; i += kWave)
+    scales[r * (H / 16) + i] = t >= 0 ? tok_scales[t * (H / 16) + i] : (uint8_t)0;
+}
+
+hipError_t launch_gather_rows(const uint8_t* tok_codes, const uint8_t* tok_scales,
+                              const int32_t* row_src, const int32_t* rows_end, int64_t cap,
+                              int64_t hidden, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (cap <= 0) return hipSuccess;
+  gather_rows_kernel<<<(unsigned)((cap + 3) / 4), 256, 0, s>>>(tok_codes, tok_scales, row_src,
+                                                              rows_end, cap, hidden, codes, scales);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
   RouteArgs a = args;
   const int64_t nchunks = route_num_chunks(a.tokens);
@@ -546,34 +830,79 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
   clear_word_kernel<<<1, 64, 0, s>>>(a.error_word);
 #endif
   const bool small = a.tokens * a.topk <= kSmallEntries;
+  const bool gather = a.tok_codes != nullptr && a.x != nullptr;
+  // gather mode: tokens [0, tq_split) are quantized in the first launch, the
+  // rest in the second
+  const int bpl_g = gather ? blocks_per_lane(a.hidden) : 1;
+  const int64_t tq_split = a.tokens / 2;
   if (!small) {
     if (nchunks > 0) {
       const unsigned hg = (unsigned)((nchunks + 3) / 4);
       const size_t hl = 4 * E * sizeof(int32_t);
-      if (a.topk <= 8)
+      const int kmax = a.topk <= 8 ? 8 : (a.topk <= 16 ? 16 : 0);
+      if (gather) {
+        // histogram + the first part of the token quantization in one
+        // launch, the scan + the rest in the next: the per-entry kernel then
+        // only writes the maps, the rows' outer scales and the tile tables
+        if (bpl_g == 0) return hipErrorInvalidValue;
+        const unsigned grid = hg + (unsigned)((tq_split + 3) / 4);
+        const size_t hl64 = 4 * E * sizeof(unsigned long long);
+        switch (bpl_g * 100 + kmax) {
+#define NVFP4_HISTQ(B, KM) \
+          case B * 100 + KM: \
+            route_hist_quant_kernel<KM, B><<<grid, 256, hl64, s>>>(a, nchunks, hist, (int64_t)hg, tq_split); break;
+          NVFP4_HISTQ(1, 8) NVFP4_HISTQ(2, 8) NVFP4_HISTQ(4, 8) NVFP4_HISTQ(8, 8) NVFP4_HISTQ(16, 8)
+          NVFP4_HISTQ(1, 16) NVFP4_HISTQ(2, 16) NVFP4_HISTQ(4, 16) NVFP4_HISTQ(8, 16) NVFP4_HISTQ(16, 16)
+          NVFP4_HISTQ(1, 0) NVFP4_HISTQ(2, 0) NVFP4_HISTQ(4, 0) NVFP4_HISTQ(8, 0) NVFP4_HISTQ(16, 0)
+#undef NVFP4_HISTQ
+          default: return hipErrorInvalidValue;
+        }
+      } else if (kmax == 8) {
         route_hist_kernel<8><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
-      else if (a.topk <= 16)
+      } else if (kmax == 16) {
         route_hist_kernel<16><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
-      else
+      } else {
         route_hist_kernel<0><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
+      }
     }
-    route_scan_kernel<<<(unsigned)((E + kScanExperts - 1) / kScanExperts), kScanThreads, 0, s>>>(
-        hist, base, nchunks, E, a.align, counts, a.offsets, a.zero_per_row, a.zero_rows);
+    const int64_t scan_wgs = (E + kScanExperts - 1) / kScanExperts;
+    if (gather) {
+      const unsigned grid = (unsigned)(scan_wgs + (a.tokens - tq_split + 3) / 4);
+      switch (bpl_g) {
+#define NVFP4_SCANQ(B) \
+        case B: route_scan_quant_kernel<B><<<grid, 256, 0, s>>>(a, hist, base, counts, nchunks, scan_wgs, tq_split); break;
+        NVFP4_SCANQ(1) NVFP4_SCANQ(2) NVFP4_SCANQ(4) NVFP4_SCANQ(8) NVFP4_SCANQ(16)
+#undef NVFP4_SCANQ
+        default: return hipErrorInvalidValue;
+      }
+    } else {
+      route_scan_kernel<<<(unsigned)scan_wgs, kScanThreads, 0, s>>>(
+          hist, base, nchunks, E, a.align, counts, a.offsets, a.zero_per_row, a.zero_rows);
+    }
+    if (gather) {
+      // the entries' rows from the chunk bases and ranks, the padding rows and
+      // the tile tables
+      const int64_t entry_wgs = (a.tokens * a.topk + 255) / 256;
+      const int64_t twg = a.num_tables > 0 ? 3 * kTableWorkgroups : 0;
+      const unsigned grid = (unsigned)(twg + entry_wgs + (E + 3) / 4);
+      route_entries_kernel<<<grid, 256, 0, s>>>(a, base, counts, nchunks, entry_wgs, twg);
+      return hipGetLastError();
+    }
   }
   const int bpl = a.x ? blocks_per_lane(a.hidden) : 1;
   if (bpl == 0) return hipErrorInvalidValue;
   const int tpw = tokens_per_wave(bpl);
   const int64_t token_waves = (a.tokens + tpw - 1) / tpw;
   const int64_t waves = token_waves + E;
-  const int64_t table_wg0 = (waves + 3) / 4;
+  const int64_t permute_wgs = (waves + 3) / 4;
   const int64_t twg = a.num_tables > 0 ? kTableWorkgroups : 0;
-  dim3 grid((unsigned)(table_wg0 + twg)), block(256);
+  dim3 grid((unsigned)(twg + permute_wgs)), block(256);
   const int kmax = a.topk <= 8 ? 8 : (a.topk <= 16 ? 16 : 0);
   switch (bpl * 100 + kmax) {
 #define NVFP4_SCATTER(B, KM) \
     case B * 100 + KM:                                                                              \
-      if (small) route_scatter_kernel<B, KM, true><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks, table_wg0); \
-      else route_scatter_kernel<B, KM, false><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks, table_wg0); \
+      if (small) route_scatter_kernel<B, KM, true><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks, twg); \
+      else route_scatter_kernel<B, KM, false><<<grid, block, 0, s>>>(a, base, counts, token_waves, nchunks, twg); \
       break;
     NVFP4_SCATTER(1, 8) NVFP4_SCATTER(2, 8) NVFP4_SCATTER(4, 8) NVFP4_SCATTER(8, 8) NVFP4_SCATTER(16, 8)
     NVFP4_SCATTER(1, 16) NVFP4_SCATTER(2, 16) NVFP4_SCATTER(4, 16) NVFP4_SCATTER(8, 16) NVFP4_SCATTER(16, 16)

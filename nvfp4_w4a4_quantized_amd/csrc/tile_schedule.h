@@ -50,12 +50,27 @@ struct TileTableSpec {
 
 constexpr int kMaxTableGroups = 1024;
 
-// LDS of the table builder (the calling kernel declares one).
+// LDS of the table builder (the calling kernel declares one): the offsets
+// and the inclusive prefix sums of the groups' m-tile counts and costs (a
+// group's own count and cost are recomputed from its offsets).
 struct TileTableLds {
-  uint32_t cnt[kMaxTableGroups], cost[kMaxTableGroups], full[kMaxTableGroups];
+  int32_t off[kMaxTableGroups + 1];
   uint32_t ic[kMaxTableGroups], ik[kMaxTableGroups];   // inclusive prefix sums
   uint32_t wc[4], wk[4], f0[8], f1[8];
 };
+
+// m-tiles of a group of n rows (cnt), whole ones (full) and their cost.
+template <int BM>
+__device__ __forceinline__ void group_tiles(int64_t n, uint32_t stages, uint32_t full_cost,
+                                            uint32_t* cnt, uint32_t* full, uint32_t* cost) {
+  *cnt = 0; *full = 0; *cost = 0;
+  if (n > 0) {
+    const uint32_t f = (uint32_t)(n / BM), rem = (uint32_t)(n % BM);
+    *full = f;
+    *cnt = f + (rem ? 1u : 0u);
+    *cost = f * full_cost + (rem ? tile_cost((rem + 31) / 32, stages) : 0u);
+  }
+}
 
 // Writes entries first, first + stride, ... of the table from the offsets
 // off[0..G] (global or LDS), exactly as the GEMM's own lookup derives each
@@ -64,6 +79,7 @@ struct TileTableLds {
 // preceding cost reaches x/8 of the total), then for every position b its
 // XCD range position, m-tile, n-tile, group and rows.  A 256-thread
 // workgroup calls it (it synchronises the workgroup), G <= kMaxTableGroups.
+// The offsets are read once into LDS; the entries need no memory reads.
 template <int BM>
 __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec& t, int64_t first,
                                  int64_t stride, TileTableLds& s) {
@@ -71,6 +87,12 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const uint32_t stages = (uint32_t)std::min<int64_t>(t.k / kKS, kCostMaxStages);
   const uint32_t full_cost = tile_cost(BM / 32, stages);
+  int32_t o[PER + 1];
+#pragma unroll
+  for (int i = 0; i <= PER; ++i) {
+    const int gi = PER * tid + i;
+    o[i] = gi <= G ? off[gi] : 0;
+  }
   uint32_t lc = 0, lk = 0;
   uint32_t pc[PER], pk[PER];
 #pragma unroll
@@ -78,14 +100,9 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
     const int gi = PER * tid + i;
     uint32_t cnt = 0, cost = 0, full = 0;
     if (gi < G) {
-      const int64_t n = (int64_t)off[gi + 1] - (int64_t)off[gi];
-      if (n > 0) {
-        const uint32_t f = (uint32_t)(n / BM), rem = (uint32_t)(n % BM);
-        full = f;
-        cnt = f + (rem ? 1u : 0u);
-        cost = f * full_cost + (rem ? tile_cost((rem + 31) / 32, stages) : 0u);
-      }
-      s.cnt[gi] = cnt; s.cost[gi] = cost; s.full[gi] = full;
+      group_tiles<BM>((int64_t)o[i + 1] - (int64_t)o[i], stages, full_cost, &cnt, &full, &cost);
+      s.off[gi] = o[i];
+      if (gi == G - 1) s.off[G] = o[i + 1];
     }
     lc += cnt; lk += cost;
     pc[i] = lc; pk[i] = lk;                        // inclusive within the thread
@@ -111,9 +128,12 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
       if (s.ik[mid] >= c) hi = mid; else lo = mid + 1;
     }
     if (lo >= G) return tiles;
-    const uint32_t cnt = s.cnt[lo], ec = s.ic[lo] - cnt, ek = s.ik[lo] - s.cost[lo];
+    uint32_t cnt, full, cost;
+    group_tiles<BM>((int64_t)s.off[lo + 1] - (int64_t)s.off[lo], stages, full_cost, &cnt, &full,
+                    &cost);
+    const uint32_t ec = s.ic[lo] - cnt, ek = s.ik[lo] - cost;
     uint32_t j = c > ek ? (c - ek + full_cost - 1) / full_cost : 0u;
-    if (j > s.full[lo]) j = cnt;                   // inside the partial tile: take the next one
+    if (j > full) j = cnt;                         // inside the partial tile: take the next one
     return ec + j;
   };
   if (tid < 8) {
@@ -135,8 +155,10 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
         const int mid = (lo + hi) >> 1;
         if (s.ic[mid] > mt) hi = mid; else lo = mid + 1;
       }
-      const int32_t r0 = off[lo] + (int32_t)(mt - (s.ic[lo] - s.cnt[lo])) * BM;
-      const int32_t r1 = std::min<int32_t>(r0 + BM, off[lo + 1]);
+      const int64_t n = (int64_t)s.off[lo + 1] - (int64_t)s.off[lo];
+      const uint32_t cnt = (uint32_t)((n + BM - 1) / BM);
+      const int32_t r0 = s.off[lo] + (int32_t)(mt - (s.ic[lo] - cnt)) * BM;
+      const int32_t r1 = std::min<int32_t>(r0 + BM, s.off[lo + 1]);
       e = make_int4(lo, r0, r1, (int)(logical - mt * un));
     }
     t.table[b] = e;
