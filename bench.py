@@ -72,6 +72,10 @@ def parse():
                    help="also time the layer with Four-Over-Six (MSE) weights and activations and "
                         "report it under 'four_over_six' (0 = skip); the headline stays the "
                         "standard rule")
+    p.add_argument("--single-pass", type=int, default=1,
+                   help="also time the layer with the single-pass FC1 -> SwiGLU -> quantize -> FC2 "
+                        "kernel (online amax compensation) and report it under 'single_pass' "
+                        "(0 = skip)")
     p.add_argument("--secondary", default="dense,decode,long",
                    help="comma list of the secondary workloads to time and report under "
                         "'secondary' (dense: the attention projections; decode: the 256-token "
@@ -86,39 +90,88 @@ def parse():
 
 
 def moe_algorithmic(w):
+    """FC1 and FC2 flops and the bytes of moe_permute's quantize + permute:
+    read x and the routing, write each routed row (codes, scales, s_g) and
+    the maps (row_src, row_prob per row; dst_row per entry)."""
     R = w.routed_rows
     H, I, T, k = w.hidden, w.inter, w.tokens, w.topk
     fc1 = 2.0 * R * 2 * I * H
     fc2 = 2.0 * R * H * I
-    # quantize + permute: read x and routing, write codes/scales/s_g and maps
     qbytes = T * H * 2 + T * k * 8 + R * (H // 2 + H // 16 + 4) + R * 8 + T * k * 4
     return fc1, fc2, qbytes
 
 
+def layer_route_bytes(w):
+    """Bytes of the layer's routing stage, which quantizes each token once and
+    lets FC1 gather the routed rows: read x and the routing, write each
+    token's row (codes, scales, s_g), and per routed row its token, router
+    weight and outer scale, per entry its row and chunk rank (one byte,
+    written and read)."""
+    R, H, T, k = w.routed_rows, w.hidden, w.tokens, w.topk
+    return T * H * 2 + T * k * 8 + T * (H // 2 + H // 16 + 4) + R * 12 + T * k * (4 + 2)
+
+
 def moe_layer_bytes(w):
     """HBM bytes the layer must move with its intermediates in HBM: the
-    quantize/permute bytes, both weight sets (codes, block scales, outer
-    scales) read once, A1 read by FC1, D written and read back, A2 written and
-    read, the expert rows written by FC2 and read by the combine, y written."""
+    routing stage's bytes, both weight sets (codes, block scales, outer
+    scales) read once, the token rows read by FC1 (once each) with each routed
+    row's token, outer scale and router weight, D written and read back, A2
+    written and read, the expert rows written by FC2 and read by the combine,
+    y written."""
     R, H, I, T, E = w.routed_rows, w.hidden, w.inter, w.tokens, w.experts
-    _, _, qbytes = moe_algorithmic(w)
     weights = E * 2 * I * (H // 2 + H // 16) + E * H * (I // 2 + I // 16) + 2 * E * 4
-    a1 = R * (H // 2 + H // 16 + 4 + 4)          # codes, scales, s_g, router weight
+    a1 = T * (H // 2 + H // 16) + R * 12          # token rows; row_src, s_g, router weight
     d = 2 * R * I * 2 + 2 * R * 4                 # D bf16 and its row amax, each both ways
     a2 = 2 * R * (I // 2 + I // 16 + 4)
     rows = 2 * R * H * 2
-    return qbytes + weights + a1 + d + a2 + rows + T * H * 2
+    return layer_route_bytes(w) + weights + a1 + d + a2 + rows + T * H * 2
+
+
+SETTLE_BATCH = 10            # steps per batch of the clock-settling phase
+SETTLE_MAX_STEPS = 400       # at most this many settling steps
+SETTLE_TOL = 0.01            # stable: a batch within 1% of the previous one
+
+SETTLE_LOG = {}
+
+
+def settle_clocks(step, label):
+    """The GPU raises its clocks over the first few hundred milliseconds of
+    sustained work (right after a short warm-up the layer's step time falls
+    from about 0.90 to 0.70 ms over 20 steps, and again after 2 s idle).
+    After the requested warm-up, steps run in batches of SETTLE_BATCH, each
+    timed by a pair of events, until one batch is within SETTLE_TOL of the
+    previous one (at most SETTLE_MAX_STEPS steps).  The extra steps are
+    reported in the output line ('clock_settle'), never hidden."""
+    import torch
+    batches = []
+    n = 0
+    while n < SETTLE_MAX_STEPS:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(SETTLE_BATCH):
+            step(None)
+        e1.record()
+        torch.cuda.synchronize()
+        n += SETTLE_BATCH
+        batches.append(e0.elapsed_time(e1) / SETTLE_BATCH)
+        if len(batches) >= 2 and abs(batches[-1] - batches[-2]) <= SETTLE_TOL * batches[-2]:
+            break
+    SETTLE_LOG[label] = {"extra_steps": n, "batch_ms_per_step": [round(b, 4) for b in batches]}
+    log(f"clock settle ({label}): {n} extra steps, ms/step per batch "
+        + ", ".join(f"{b:.4f}" for b in batches))
 
 
 def run_steps(step, steps, warmup, label, timer_cls=None):
-    """Warm-up, then `steps` uninstrumented calls timed by the host clock
-    around device synchronisations; with timer_cls, the same number of steps
-    again with a fresh timer per step, whose per-stage averages are returned."""
+    """Warm-up, clock settling (settle_clocks), then `steps` uninstrumented
+    calls timed by the host clock around device synchronisations; with
+    timer_cls, the same number of steps again with a fresh timer per step,
+    whose per-stage averages are returned."""
     import torch
     log(f"warmup {warmup} ({label})")
     for _ in range(warmup):
         step(None)
     torch.cuda.synchronize()
+    settle_clocks(step, label)
     log(f"timing {steps} steps ({label})")
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -136,6 +189,77 @@ def run_steps(step, steps, warmup, label, timer_cls=None):
         for t in timers:
             t.close()
     return wall, stages
+
+
+def bench_permute(args, w, x, idx, prob, qbytes):
+    """moe_permute on the headline routing: the quantize + permute entry point
+    that writes the k routed copies of every token (the permuted layout).
+    Warm-up, clock settling, then `steps` calls between two events."""
+    import torch
+
+    from nvfp4_w4a4_quantized_amd import _lib, ops
+    L = ops.lib()
+    ws = torch.empty(int(L.moe_permute_workspace_size(w.tokens, w.topk, w.experts)),
+                     dtype=torch.uint8, device=x.device)
+    out = ops.moe_permute(x, idx, prob, w.experts, workspace=ws)   # allocates the outputs once
+    p = _lib.ptr
+    args_c = (p(x), w.tokens, w.hidden, p(idx), p(prob), w.topk, w.experts, 1, 0,
+              p(out["offsets"]), p(out["dst_row"]), p(out["row_src"]), p(out["row_prob"]),
+              p(out["codes"]), p(out["scales"]), p(out["gscale"]), p(ws), ws.numel(),
+              _lib.stream_handle())
+
+    def step(_):
+        _lib.check(L.moe_permute(*args_c), "moe_permute")
+    for _ in range(args.warmup):
+        step(None)
+    settle_clocks(step, "moe_permute")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step(None)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    del out, ws
+    return {"ms": ms, "bytes": qbytes, "gbps": qbytes / (ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": qbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "note": "moe_permute (routing + per-token quantize + the k routed copies), timed "
+                    "between two events over the steps, outputs allocated once"}
+
+
+def bench_single_pass(args, w, x, idx, prob, W1, W2):
+    """The headline layer with FC1 -> SwiGLU -> quantize -> FC2 fused by online
+    amax compensation (one kernel per 128-row block; the intermediate and its
+    quantization stay on chip).  Timed like the headline."""
+    import torch
+
+    from nvfp4_w4a4_quantized_amd.ops import (SinglePassTimer, moe_expert_forward_single_pass,
+                                              moe_expert_forward_single_pass_workspace_size)
+    log("single-pass FC1 -> FC2 (online amax compensation)")
+    ws = torch.empty(moe_expert_forward_single_pass_workspace_size(w.tokens, w.hidden, w.inter,
+                                                                    w.topk, w.experts),
+                     dtype=torch.uint8, device=x.device)
+    y = torch.empty((w.tokens, w.hidden), dtype=torch.bfloat16, device=x.device)
+    torch.cuda.synchronize()
+
+    def step(timer):
+        moe_expert_forward_single_pass(x, idx, prob, w.experts, w.inter, W1, W2, workspace=ws,
+                                       y=y, timer=timer)
+    wall, st = run_steps(step, args.steps, args.warmup, "single pass", SinglePassTimer)
+    ms = wall * 1e3 / args.steps
+    fc1, fc2, _ = moe_algorithmic(w)
+    R, I = w.routed_rows, w.inter
+    log("stages single pass (ms, HIP events): " + ", ".join(f"{k}={v:.4f}" for k, v in st.items()))
+    del ws, y
+    return {
+        "kernel": "moe_expert_forward_single_pass (tiles of 256 intermediate columns)",
+        "value": w.tokens * args.steps / wall, "unit": "tokens/s", "ms_per_step": ms,
+        "effective_tflops": (fc1 + fc2) / (ms * 1e-3) / 1e12,
+        "frac_of_f16_peak": (fc1 + fc2) / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "stage_ms": st,
+        "fused_kernel_tflops": (fc1 + fc2) / (st["fused_fc1_fc2"] * 1e-3) / 1e12,
+        "hbm_bytes_not_moved": 2 * R * I * 2 + 2 * R * 4 + 2 * R * (I // 2 + I // 16 + 4),
+    }
 
 
 class _TorchStages:
@@ -245,6 +369,7 @@ def bench_moe_secondary(args, dev, bf, wid, W1, W2, weight_copies, label):
     ms = wall * 1e3 / args.steps
     fc1, fc2, qbytes = moe_algorithmic(w)
     lbytes = moe_layer_bytes(w)
+    rbytes = layer_route_bytes(w)
     rec = {
         "workload": w.name, "tokens": w.tokens, "routed_rows": w.routed_rows,
         "active_experts": w.meta["active_experts"],
@@ -257,7 +382,8 @@ def bench_moe_secondary(args, dev, bf, wid, W1, W2, weight_copies, label):
         "frac_of_hbm_peak": lbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "weight_copies_rotated": weight_copies,
         "stage_ms": st,
-        "quantize_permute_gbps": qbytes / (st["route_quantize"] * 1e-3) / 1e9,
+        "route_quantize_bytes": rbytes,
+        "route_quantize_gbps": rbytes / (st["route_quantize"] * 1e-3) / 1e9,
     }
     del ws, y, sets
     return rec
@@ -282,24 +408,72 @@ def run_secondary(args, dev, bf, W1, W2):
     return sec
 
 
+STAGE_NAMES = ("route_quantize", "fc1", "swiglu", "requantize", "fc2", "combine")
+
+
+def _oracle_layer(O, w, W1, W2, n_tokens, threads):
+    """One oracle run of the layer on the first n_tokens tokens: wall seconds
+    and the oracle's own per-stage seconds (steady clock)."""
+    O.set_num_threads(threads)
+    t0 = time.perf_counter()
+    _, _, secs = O.moe_forward(w.x[:n_tokens], w.topk_idx[:n_tokens], w.topk_prob[:n_tokens],
+                               w.experts, w.inter, W1, W2, stage_times=True)
+    dt = time.perf_counter() - t0
+    return dt, {n: round(float(v), 4) for n, v in zip(STAGE_NAMES, secs)}
+
+
 def cpu_baseline(w, n_tokens):
+    """The CPU oracle, as it stands, on bounded samples (one run each):
+      - the headline workload's first n_tokens tokens on all host threads
+        (the reported value, with the oracle's per-stage seconds);
+      - the 256-token tiny layer, all threads and one thread;
+      - the decode-shaped layer (256 tokens, Qwen3 shapes): all 256 tokens on
+        all threads and a 32-token sample on one thread.  It uses the
+        headline's oracle-quantized weights (same shapes and distribution;
+        the oracle's time does not depend on weight values)."""
     from oracle import oracle as O
+    from nvfp4_w4a4_quantized_amd.workloads import make_moe
     E, I, H = w.experts, w.inter, w.hidden
-    log(f"cpu baseline: oracle weight quantization (offline, untimed), sample {n_tokens} tokens")
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: oracle weight quantization (offline, untimed), {cores} host threads")
+    O.set_num_threads(cores)
     ow1 = O.quantize(w.w1.reshape(E * 2 * I, H), domain=1,
                      group_offsets=np.arange(E + 1, dtype=np.int32) * 2 * I)
     ow2 = O.quantize(w.w2.reshape(E * H, I), domain=1,
                      group_offsets=np.arange(E + 1, dtype=np.int32) * H)
     W1 = (ow1[0].reshape(E, 2 * I, H // 2), ow1[1].reshape(E, 2 * I, H // 16), ow1[2])
     W2 = (ow2[0].reshape(E, H, I // 2), ow2[1].reshape(E, H, I // 16), ow2[2])
-    t0 = time.perf_counter()
-    O.moe_forward(w.x[:n_tokens], w.topk_idx[:n_tokens], w.topk_prob[:n_tokens], E, I, W1, W2)
-    dt = time.perf_counter() - t0
-    log(f"cpu baseline: {n_tokens} tokens in {dt:.2f} s on {O.num_threads()} threads")
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": O.num_threads(), "kind": "oracle",
+    dt, stages = _oracle_layer(O, w, W1, W2, n_tokens, cores)
+    log(f"cpu baseline: {n_tokens} tokens in {dt:.2f} s on {O.num_threads()} threads; stages {stages}")
+    extra = {}
+    w0 = make_moe(0)
+    E0, I0, H0 = w0.experts, w0.inter, w0.hidden
+    q1 = O.quantize(w0.w1.reshape(E0 * 2 * I0, H0), domain=1,
+                    group_offsets=np.arange(E0 + 1, dtype=np.int32) * 2 * I0)
+    q2 = O.quantize(w0.w2.reshape(E0 * H0, I0), domain=1,
+                    group_offsets=np.arange(E0 + 1, dtype=np.int32) * H0)
+    V1 = (q1[0].reshape(E0, 2 * I0, H0 // 2), q1[1].reshape(E0, 2 * I0, H0 // 16), q1[2])
+    V2 = (q2[0].reshape(E0, H0, I0 // 2), q2[1].reshape(E0, H0, I0 // 16), q2[2])
+    rec = {"tokens": w0.tokens}
+    for th in (cores, 1):
+        d0, st0 = _oracle_layer(O, w0, V1, V2, w0.tokens, th)
+        rec[f"threads_{th}"] = {"value": w0.tokens / d0, "unit": "tokens/s", "wall_s": round(d0, 4),
+                                "stage_s": st0}
+    extra[w0.name] = rec
+    w3 = make_moe(3, with_weights=False)
+    rec = {"weights": "the headline workload's (same shapes and distribution)"}
+    for th, nt in ((cores, w3.tokens), (1, 32)):
+        d3, st3 = _oracle_layer(O, w3, W1, W2, nt, th)
+        rec[f"threads_{th}"] = {"tokens": nt, "value": nt / d3, "unit": "tokens/s",
+                                "wall_s": round(d3, 3), "stage_s": st3}
+    extra[w3.name] = rec
+    O.set_num_threads(cores)
+    log(f"cpu baseline: extra lines {json.dumps(extra)}")
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {n_tokens} of {w.tokens} tokens of the same workload (same routing "
                       f"and weights), whole layer: route+quantize, FC1, SwiGLU, requantize, FC2, "
-                      f"combine; {dt:.2f} s wall"}
+                      f"combine; one run, {dt:.2f} s wall on {cores} threads",
+            "runs": 1, "stage_s": stages, "extra": extra}
 
 
 def main():
@@ -397,7 +571,9 @@ def main():
         "effective_frac_of_f16_peak": total_flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
         "stage_ms": stages,
         "stage_sum_ms": float(sum(stages.values())),
-        "quantize_permute_gbps": qbytes / (stages["route_quantize"] * 1e-3) / 1e9,
+        "route_quantize_bytes": layer_route_bytes(w),
+        "route_quantize_gbps": layer_route_bytes(w) / (stages["route_quantize"] * 1e-3) / 1e9,
+        "moe_permute": bench_permute(args, w, x, idx, prob, qbytes),
         "roofline": {"kernel": "FC1 grouped GEMM + SwiGLU/amax epilogue",
                      "bound": "mfma", "achieved": fc1_tflops, "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": fc1_tflops / PEAK_F16_TFLOPS,
@@ -414,8 +590,10 @@ def main():
             "block_rule": "4/6, block error = sum of squares",
             "value": w.tokens * args.steps / wall46, "unit": "tokens/s",
             "ms_per_step": wall46 * 1e3 / args.steps, "stage_ms": st46,
-            "quantize_permute_gbps": qbytes / (st46["route_quantize"] * 1e-3) / 1e9,
+            "route_quantize_gbps": layer_route_bytes(w) / (st46["route_quantize"] * 1e-3) / 1e9,
         }
+    if args.single_pass:
+        result["single_pass"] = bench_single_pass(args, w, x, idx, prob, W1, W2)
     sec = run_secondary(args, dev, bf, W1, W2)
     if sec:
         result["secondary"] = sec
@@ -440,6 +618,12 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, min(args.cpu_tokens, w.tokens))
     else:
         result["cpu_baseline"] = None
+    result["clock_settle"] = {
+        "note": ("after the requested warm-up, extra untimed steps in batches of "
+                 f"{SETTLE_BATCH} until a batch's step time is within {SETTLE_TOL:.0%} of the "
+                 f"previous batch (at most {SETTLE_MAX_STEPS}): the GPU clock ramps over the "
+                 "first few hundred milliseconds of sustained work"),
+        **SETTLE_LOG}
     print(json.dumps(result), flush=True)
 
 

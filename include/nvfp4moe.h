@@ -356,6 +356,61 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
                        void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_expert_forward_single_pass -- the expert layer with FC1 -> weighted
+ * SwiGLU -> NVFP4 quantize -> FC2 fused into one kernel by online amax
+ * compensation ([miniTE] §5.6 "Exploring Single-Pass Fusion").  The
+ * intermediate activation and its quantization never leave the chip.
+ *
+ * Routing, the per-token quantization and FC1 are those of
+ * moe_expert_forward.  Per routed row r, the intermediate dimension is taken
+ * in tiles of 256 columns, i = 0, 1, ... (the last may be narrower):
+ *   P_i     = bf16(silu(gate) * up * row_prob[r]) of the tile's columns,
+ *   gamax_i = max(gamax_{i-1}, max |P_i|), gamax_{-1} = 0,
+ *   gs_i    = fl32(gamax_i / 2688),
+ *   the tile's 16-blocks encoded as in nvfp4_quantize with s_g = gs_i,
+ *   O       = O * (gs_{i-1} / gs_i) + sum over the tile's k of
+ *             (q_a s_a)(q_w s_w)   (tiles with gs_i = 0 add nothing),
+ *   Y[r, n] = O * gs_last * s_gw2[e], then the combine.
+ * A row whose maximum lies in its first tile quantizes exactly as in the
+ * two-pass layer; other rows' earlier tiles use smaller scales, so their
+ * codes differ from the two-pass codes by design.
+ *
+ *   arguments as moe_expert_forward (act_block_rule: the standard rule only)
+ *   debug        nullable: every non-NULL member receives that intermediate
+ *                (valid rows only); y_rows_f32 switches the FC2 rows to fp32;
+ *                a1_codes and a1_scales are given together
+ *   stage_events nullable array of 4 hipEvent_t (as void*), recorded before
+ *                the routing, before the fused kernel, before the combine and
+ *                after it
+ * Limits: as moe_expert_forward, and inter <= 1152 (the row block's
+ * quantized FC2 input, 128 rows x inter * 9/16 bytes, is held on chip beside
+ * the 64 KiB of operand stages).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t* expert_offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
+  uint8_t* a1_codes; uint8_t* a1_scales; float* a1_gscale;
+  float* fc1_out;                 /* [cap, 2*inter] fp32 FC1 pre-activation */
+  uint16_t* p;                    /* [cap, inter] bf16 weighted SwiGLU (the tiles P_i) */
+  uint8_t* a2_codes;              /* [cap, inter/2] the online-quantized FC2 input */
+  uint8_t* a2_scales;             /* [cap, inter/16] */
+  float* gs_tiles;                /* [cap, ceil(inter/256)] gs_i per row and tile */
+  uint16_t* y_rows;               /* [cap, hidden] bf16 FC2 rows */
+  float* y_rows_f32;              /* [cap, hidden] fp32 FC2 rows */
+} nvfp4_single_pass_intermediates;
+
+size_t moe_expert_forward_single_pass_workspace_size(int64_t tokens, int64_t hidden,
+                                                     int64_t inter, int32_t topk,
+                                                     int32_t num_experts, int32_t align);
+int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hidden,
+                                   int64_t inter, const int32_t* topk_idx,
+                                   const float* topk_prob, int32_t topk, int32_t num_experts,
+                                   int32_t align, const nvfp4_weights* w1,
+                                   const nvfp4_weights* w2, uint16_t* y, void* workspace,
+                                   size_t workspace_bytes,
+                                   const nvfp4_single_pass_intermediates* debug,
+                                   void* const* stage_events, void* stream);
+
+/* ------------------------------------------------------------------------
  * Profiling helpers: thin wrappers over hipEventCreate / hipEventRecord /
  * hipEventElapsedTime / hipEventDestroy so a caller without HIP headers can
  * time the stages of moe_expert_forward on its stream.  (These allocate a

@@ -36,6 +36,12 @@ class Intermediates(C.Structure):
         "fc1_out", "d", "amax_d", "a2_codes", "a2_scales", "a2_gscale", "y_rows", "y_rows_f32")]
 
 
+class SinglePassIntermediates(C.Structure):
+    _fields_ = [(n, _vp) for n in (
+        "expert_offsets", "dst_row", "row_src", "row_prob", "a1_codes", "a1_scales", "a1_gscale",
+        "fc1_out", "p", "a2_codes", "a2_scales", "gs_tiles", "y_rows", "y_rows_f32")]
+
+
 _lib = None
 _debug_lib = None
 
@@ -94,6 +100,13 @@ def _load(path):
     L.moe_expert_forward.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
                                      C.POINTER(Weights), C.POINTER(Weights), _vp, _vp, C.c_size_t,
                                      C.POINTER(Intermediates), _vp, _vp]
+    L.moe_expert_forward_single_pass_workspace_size.restype = C.c_size_t
+    L.moe_expert_forward_single_pass_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
+    L.moe_expert_forward_single_pass.restype = C.c_int
+    L.moe_expert_forward_single_pass.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32,
+                                                 _i32, C.POINTER(Weights), C.POINTER(Weights),
+                                                 _vp, _vp, C.c_size_t,
+                                                 C.POINTER(SinglePassIntermediates), _vp, _vp]
     L.nvfp4_event_create.restype = C.c_int
     L.nvfp4_event_create.argtypes = [C.POINTER(_vp)]
     L.nvfp4_event_record.restype = C.c_int

@@ -82,6 +82,39 @@ MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_
   return L;
 }
 
+// Workspace of the single-pass layer: routing, token rows, per-row maps and
+// scales, the FC2 rows and the fused kernel's tile table.
+struct SpLayout {
+  int32_t* route_ws_i; int32_t* offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
+  uint8_t* tokc; uint8_t* toks; float* tokg; float* a1g; uint8_t* rank;
+  uint16_t* y_rows;
+  int4* tab;
+  int64_t blocks;
+  size_t bytes;
+};
+
+SpLayout carve_single_pass(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_t E,
+                           int32_t align) {
+  const int64_t cap = moe_rows_capacity(T, k, E, align);
+  Carver c(ws);
+  SpLayout L;
+  L.route_ws_i = c.take<int32_t>(route_workspace_bytes(T, E) / 4);
+  L.offsets = c.take<int32_t>(E + 1);
+  L.dst_row = c.take<int32_t>((size_t)(T * k));
+  L.row_src = c.take<int32_t>((size_t)cap);
+  L.row_prob = c.take<float>((size_t)cap);
+  L.tokc = c.take<uint8_t>((size_t)((T + 1) * H / 2));
+  L.toks = c.take<uint8_t>((size_t)((T + 1) * H / 16));
+  L.tokg = c.take<float>((size_t)T);
+  L.a1g = c.take<float>((size_t)cap);
+  L.rank = c.take<uint8_t>((size_t)(T * k));
+  L.y_rows = c.take<uint16_t>((size_t)(cap * H));
+  L.blocks = single_pass_table_spec(cap, E, H, nullptr).blocks;
+  L.tab = c.take<int4>((size_t)L.blocks);
+  L.bytes = c.used;
+  return L;
+}
+
 bool route_args_ok(int64_t tokens, int32_t topk, int32_t num_experts, int32_t align) {
   if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > kMaxExperts) return false;
   if (topk > num_experts || !valid_align(align)) return false;
@@ -435,6 +468,103 @@ int nvfp4_event_elapsed_ms(void* start, void* stop, float* ms) {
 int nvfp4_event_destroy(void* event) {
   if (!event) return NVFP4_INVALID_ARGUMENT;
   return hip_status(hipEventDestroy(static_cast<hipEvent_t>(event)));
+}
+
+size_t moe_expert_forward_single_pass_workspace_size(int64_t tokens, int64_t hidden,
+                                                     int64_t inter, int32_t topk,
+                                                     int32_t num_experts, int32_t align) {
+  if (!route_args_ok(tokens, topk, num_experts, align) || hidden < 0 || inter < 0) return 0;
+  return carve_single_pass(nullptr, tokens, hidden, inter, topk, num_experts, align).bytes;
+}
+
+int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hidden,
+                                   int64_t inter, const int32_t* topk_idx,
+                                   const float* topk_prob, int32_t topk, int32_t num_experts,
+                                   int32_t align, const nvfp4_weights* w1,
+                                   const nvfp4_weights* w2, uint16_t* y, void* workspace,
+                                   size_t workspace_bytes,
+                                   const nvfp4_single_pass_intermediates* debug,
+                                   void* const* stage_events, void* stream) {
+  if (!route_args_ok(tokens, topk, num_experts, align)) return NVFP4_INVALID_ARGUMENT;
+  if (hidden < 128 || hidden % 128 != 0 || inter < 128 || inter % 128 != 0)
+    return NVFP4_UNSUPPORTED;
+  if (hidden > kMaxK || inter > 1152) return NVFP4_UNSUPPORTED;   // on-chip FC2 input (LDS)
+  if (!w1 || !w2 || !w1->codes || !w1->scales || !w1->gscale || !w2->codes || !w2->scales ||
+      !w2->gscale || !workspace)
+    return NVFP4_INVALID_ARGUMENT;
+  if ((w1->layout != 0 && w1->layout != 1) || (w2->layout != 0 && w2->layout != 1))
+    return NVFP4_INVALID_ARGUMENT;
+  if (tokens > 0 && (!x || !y || !topk_idx || !topk_prob)) return NVFP4_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256) || (x && !aligned(x, 16)) || (y && !aligned(y, 16)) ||
+      !aligned(w1->codes, 16) || !aligned(w2->codes, 16) || !aligned(w1->scales, 4) ||
+      !aligned(w2->scales, 4))
+    return NVFP4_INVALID_ARGUMENT;
+  if ((int64_t)num_experts * 2 * inter >= 0x7FFFFFFFLL ||
+      (int64_t)num_experts * hidden >= 0x7FFFFFFFLL)
+    return NVFP4_INVALID_ARGUMENT;
+  if ((tokens + 1) * (hidden / 2) > 0xFFFFFFFFLL) return NVFP4_UNSUPPORTED;
+  if (2 * inter * (hidden / 2) > 0xFFFFFFFFLL || hidden * (inter / 2) > 0xFFFFFFFFLL)
+    return NVFP4_UNSUPPORTED;
+  SpLayout L = carve_single_pass(workspace, tokens, hidden, inter, topk, num_experts, align);
+  if (workspace_bytes < L.bytes) return NVFP4_WORKSPACE_TOO_SMALL;
+  const int64_t cap = moe_rows_capacity(tokens, topk, num_experts, align);
+  float* y_f32 = nullptr;
+  SinglePassArgs sp{};
+  if (debug) {
+    if ((debug->a1_codes != nullptr) != (debug->a1_scales != nullptr)) return NVFP4_INVALID_ARGUMENT;
+    if (debug->expert_offsets) L.offsets = debug->expert_offsets;
+    if (debug->dst_row) L.dst_row = debug->dst_row;
+    if (debug->row_src) L.row_src = debug->row_src;
+    if (debug->row_prob) L.row_prob = debug->row_prob;
+    if (debug->a1_gscale) L.a1g = debug->a1_gscale;
+    if (debug->y_rows) L.y_rows = debug->y_rows;
+    y_f32 = debug->y_rows_f32;
+    sp.c_out = debug->fc1_out; sp.p_out = debug->p;
+    sp.a2c_out = debug->a2_codes; sp.a2s_out = debug->a2_scales; sp.gs_out = debug->gs_tiles;
+    const void* ptrs16[] = {debug->a1_codes, L.y_rows, y_f32};
+    for (const void* q : ptrs16)
+      if (q && !aligned(q, 16)) return NVFP4_INVALID_ARGUMENT;
+    if (debug->a2_codes && !aligned(debug->a2_codes, 8)) return NVFP4_INVALID_ARGUMENT;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) -> hipError_t {
+    if (!stage_events || !stage_events[i]) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s);
+  };
+  hipError_t e;
+  if ((e = mark(0)) != hipSuccess) return NVFP4_HIP_ERROR;
+  RouteArgs ra{};
+  ra.x = x; ra.tokens = tokens; ra.hidden = hidden;
+  ra.topk_idx = topk_idx; ra.topk_prob = topk_prob; ra.topk = topk;
+  ra.num_experts = num_experts; ra.align = align;
+  ra.offsets = L.offsets; ra.dst_row = L.dst_row; ra.row_src = L.row_src;
+  ra.row_prob = L.row_prob; ra.gscale = L.a1g;
+  ra.tok_codes = L.tokc; ra.tok_scales = L.toks; ra.tok_gscale = L.tokg; ra.entry_rank = L.rank;
+  ra.tables[0] = single_pass_table_spec(cap, num_experts, hidden, L.tab);
+  ra.num_tables = 1;
+  ra.workspace = L.route_ws_i; ra.block_rule = 0;
+  if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if (debug && debug->a1_codes) {
+    if ((e = launch_gather_rows(L.tokc, L.toks, L.row_src, L.offsets + num_experts, cap, hidden,
+                                debug->a1_codes, debug->a1_scales, s)) != hipSuccess)
+      return NVFP4_HIP_ERROR;
+  }
+  if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
+  sp.a_codes = L.tokc; sp.a_scales = L.toks; sp.a_gscale = L.a1g;
+  sp.a_row_src = L.row_src; sp.a_pad_row = tokens; sp.row_prob = L.row_prob;
+  sp.w1_codes = w1->codes; sp.w1_scales = w1->scales; sp.w1_gscale = w1->gscale;
+  sp.w1_layout = w1->layout;
+  sp.w2_codes = w2->codes; sp.w2_scales = w2->scales; sp.w2_gscale = w2->gscale;
+  sp.w2_layout = w2->layout;
+  sp.hidden = hidden; sp.inter = inter; sp.tile_table = L.tab;
+  sp.y_bf16 = L.y_rows; sp.y_f32 = y_f32;
+  if ((e = launch_single_pass(sp, L.blocks, s)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if ((e = mark(2)) != hipSuccess) return NVFP4_HIP_ERROR;
+  if ((e = launch_combine(y_f32 ? static_cast<const void*>(y_f32) : L.y_rows, y_f32 ? 0 : 1,
+                          L.dst_row, tokens, topk, hidden, y, s)) != hipSuccess)
+    return NVFP4_HIP_ERROR;
+  if ((e = mark(3)) != hipSuccess) return NVFP4_HIP_ERROR;
+  return NVFP4_OK;
 }
 
 }  // extern "C"

@@ -110,6 +110,35 @@ TileTableSpec gemm_tile_table_spec(const GemmArgs& a, bool swiglu, int4* table);
 hipError_t launch_pack_b(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k,
                          uint8_t* pcodes, uint8_t* pscales, hipStream_t s);
 
+// One table entry per 128-row m-tile (BM = 128, one column tile), cost
+// balanced over the XCDs like the GEMMs' (the single-pass kernel's grid).
+TileTableSpec gemm_mtile_table_spec(int64_t rows_cap, int32_t num_groups, int64_t k, int4* table);
+
+// ---- single_pass.hip ----
+// FC1 -> weighted SwiGLU -> online-amax NVFP4 quantization -> FC2 in one
+// kernel (one workgroup per 128-row m-tile of the tile table).
+struct SinglePassArgs {
+  const uint8_t* a_codes; const uint8_t* a_scales;   // token-major quantized activations
+  const float* a_gscale;                             // [rows_cap] outer scale of each routed row
+  const int32_t* a_row_src; int64_t a_pad_row;       // routed row -> token row; the zero row
+  const float* row_prob;
+  const uint8_t* w1_codes; const uint8_t* w1_scales; const float* w1_gscale; int w1_layout;
+  const uint8_t* w2_codes; const uint8_t* w2_scales; const float* w2_gscale; int w2_layout;
+  int64_t hidden, inter;
+  const int4* tile_table;
+  uint16_t* y_bf16;        // [rows_cap, hidden] FC2 rows (or:)
+  float* y_f32;            // nullable: fp32 FC2 rows instead
+  // nullable debug outputs (valid rows only)
+  float* c_out;            // [rows_cap, 2 inter] FC1 pre-activation
+  uint16_t* p_out;         // [rows_cap, inter] bf16 weighted SwiGLU
+  uint8_t* a2c_out; uint8_t* a2s_out;   // [rows_cap, inter/2], [rows_cap, inter/16]
+  float* gs_out;           // [rows_cap, ceil(inter / 256)] per-slice outer scales
+};
+TileTableSpec single_pass_table_spec(int64_t rows_cap, int32_t num_groups, int64_t hidden,
+                                     int4* table);
+int single_pass_lds_bytes(int64_t inter);
+hipError_t launch_single_pass(const SinglePassArgs& a, int64_t blocks, hipStream_t s);
+
 // ---- combine.hip ----
 hipError_t launch_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
                           int64_t tokens, int32_t topk, int64_t hidden, uint16_t* y,

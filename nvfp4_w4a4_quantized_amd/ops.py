@@ -11,12 +11,17 @@ import ctypes as C
 
 import torch
 
-from ._lib import Intermediates, NvFp4Error, Weights, check, lib, ptr, stream_handle
+from ._lib import (Intermediates, NvFp4Error, SinglePassIntermediates, Weights, check, lib, ptr,
+                   stream_handle)
 
 __all__ = ["nvfp4_quantize", "moe_rows_capacity", "moe_permute", "moe_permute_noalloc",
            "w4a4_grouped_gemm",
            "w4a4_grouped_gemm_swiglu", "moe_combine", "moe_expert_forward",
-           "moe_expert_forward_workspace_size", "NvFp4Weights", "StageTimer"]
+           "moe_expert_forward_workspace_size", "moe_expert_forward_single_pass",
+           "moe_expert_forward_single_pass_workspace_size", "SINGLE_PASS_TILE", "NvFp4Weights",
+           "StageTimer"]
+
+SINGLE_PASS_TILE = 256   # intermediate columns per online-scale tile of the single-pass layer
 
 _BF16_LIKE = (torch.bfloat16, torch.int16, torch.uint16)
 
@@ -323,3 +328,82 @@ def moe_expert_forward(x, topk_idx, topk_prob, num_experts: int, inter: int,
     if debug:
         return y, inter_t
     return y
+
+
+class SinglePassTimer(StageTimer):
+    """Four HIP events recorded by moe_expert_forward_single_pass: routing +
+    quantize, the fused FC1 -> SwiGLU -> quantize -> FC2 kernel, combine."""
+
+    NAMES = ("route_quantize", "fused_fc1_fc2", "combine")
+
+    def __init__(self):
+        L = lib()
+        self.events = (C.c_void_p * 4)()
+        for i in range(4):
+            h = C.c_void_p()
+            check(L.nvfp4_event_create(C.byref(h)), "nvfp4_event_create")
+            self.events[i] = h.value
+
+    def close(self):
+        for i in range(4):
+            if self.events[i]:
+                lib().nvfp4_event_destroy(self.events[i])
+                self.events[i] = None
+
+
+def moe_expert_forward_single_pass_workspace_size(tokens, hidden, inter, topk, num_experts,
+                                                  align=1) -> int:
+    return int(lib().moe_expert_forward_single_pass_workspace_size(tokens, hidden, inter, topk,
+                                                                   num_experts, align))
+
+
+def moe_expert_forward_single_pass(x, topk_idx, topk_prob, num_experts: int, inter: int,
+                                   w1: NvFp4Weights, w2: NvFp4Weights, align: int = 1,
+                                   workspace=None, debug: bool = False, fc1_out: bool = False,
+                                   y_rows_f32: bool = False, timer=None, y=None):
+    """The expert layer with the single-pass FC1 -> SwiGLU -> quantize -> FC2
+    kernel (online amax compensation, tiles of SINGLE_PASS_TILE columns).
+    Returns y (bf16 [T, H]); with debug=True also a dict of the intermediates:
+    routing maps, a1 rows, fc1_out (if asked), p (bf16 weighted SwiGLU),
+    a2_codes / a2_scales (the online quantization), gs_tiles, y_rows (bf16, or
+    y_rows_f32 if asked)."""
+    _need(x, _BF16_LIKE, "x")
+    _need(topk_idx, (torch.int32,), "topk_idx")
+    _need(topk_prob, (torch.float32,), "topk_prob")
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    wsb = moe_expert_forward_single_pass_workspace_size(T, H, inter, k, num_experts, align)
+    if workspace is None:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    dbg = None
+    inter_t = None
+    if debug:
+        cap = moe_rows_capacity(T, k, num_experts, align)
+        nt = (inter + SINGLE_PASS_TILE - 1) // SINGLE_PASS_TILE
+        e = lambda shape, dt: torch.zeros(shape, dtype=dt, device=dev)  # noqa: E731
+        inter_t = dict(
+            expert_offsets=e(num_experts + 1, torch.int32), dst_row=e((T, k), torch.int32),
+            row_src=e(cap, torch.int32), row_prob=e(cap, torch.float32),
+            a1_codes=e((cap, H // 2), torch.uint8), a1_scales=e((cap, H // 16), torch.uint8),
+            a1_gscale=e(cap, torch.float32), p=e((cap, inter), torch.bfloat16),
+            a2_codes=e((cap, inter // 2), torch.uint8), a2_scales=e((cap, inter // 16), torch.uint8),
+            gs_tiles=e((cap, nt), torch.float32), y_rows=e((cap, H), torch.bfloat16))
+        if fc1_out:
+            inter_t["fc1_out"] = e((cap, 2 * inter), torch.float32)
+        if y_rows_f32:
+            inter_t["y_rows_f32"] = e((cap, H), torch.float32)
+        dbg = SinglePassIntermediates(**{n: t.data_ptr() for n, t in inter_t.items()})
+    ev = timer.events if timer is not None else None
+    check(lib().moe_expert_forward_single_pass(
+        ptr(x), T, H, inter, ptr(topk_idx), ptr(topk_prob), k, num_experts, align,
+        C.byref(w1.c_struct()), C.byref(w2.c_struct()), ptr(y), ptr(workspace), workspace.numel(),
+        C.byref(dbg) if dbg is not None else None,
+        C.cast(ev, C.c_void_p) if ev is not None else None, stream_handle()),
+        "moe_expert_forward_single_pass")
+    if debug:
+        return y, inter_t
+    return y
+

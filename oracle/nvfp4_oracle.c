@@ -713,6 +713,14 @@ int orc_moe_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hidde
   return 0;
 }
 
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

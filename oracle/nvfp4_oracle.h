@@ -296,6 +296,10 @@ int orc_moe_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hidde
                                 const orc_moe_buffers* buf, float* gs_tiles, uint16_t* y,
                                 double* stage_seconds);
 
+/* Sets the number of OpenMP threads of the following calls (n > 0); the
+ * arithmetic and its order do not depend on it. */
+void orc_set_num_threads(int n);
+
 /* Number of OpenMP threads the oracle uses (1 when built without OpenMP). */
 int orc_num_threads(void);
 

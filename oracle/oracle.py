@@ -118,6 +118,8 @@ def lib():
                                               C.POINTER(_MoeBuffers), _f32p, _u16p, C.c_void_p]
     L.orc_num_threads.restype = C.c_int
     L.orc_num_threads.argtypes = []
+    L.orc_set_num_threads.restype = None
+    L.orc_set_num_threads.argtypes = [C.c_int]
     _libs[path] = L
     return L
 
@@ -151,6 +153,11 @@ def e4m3_encode(v: float) -> int:
 
 def f64_to_bf16(v: float) -> int:
     return lib().orc_f64_to_bf16(v)
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the following oracle calls (the results do not depend on it)."""
+    lib().orc_set_num_threads(int(n))
 
 
 def num_threads() -> int:

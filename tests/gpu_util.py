@@ -81,6 +81,23 @@ def oracle_gemm_chunks(A, W, offs, chunk_rows=None):
         yield r0, r1, ref, bound
 
 
+def oracle_single_pass_chunks(A2, gs, tile, W, offs, chunk_rows=None):
+    """The oracle's single-pass FC2 (O12b) with its bound over rows
+    [offs[0], offs[-1]), in row slices like oracle_gemm_chunks."""
+    offs = np.asarray(offs, np.int64)
+    n = W[0].shape[1]
+    if chunk_rows is None:
+        chunk_rows = max(1024, (256 << 20) // (12 * n))
+    start, end = int(offs[0]), int(offs[-1])
+    for r0 in range(start, end, chunk_rows):
+        r1 = min(end, r0 + chunk_rows)
+        lo = (np.clip(offs, r0, r1) - r0).astype(np.int32)
+        c, sc = _row_slice(A2, r0, r1)
+        ref, bound = O.single_pass_gemm(c, sc, np.ascontiguousarray(gs[r0:r1]), tile, *W, lo,
+                                        with_bound=True)
+        yield r0, r1, ref, bound
+
+
 def assert_gemm_full(gpu: np.ndarray, A, W, offs, what: str, bf16_out: bool = False,
                      chunks=None):
     """Every output element of the rows [offs[0], offs[-1]) against the oracle:
