@@ -83,6 +83,9 @@ def parse():
     p.add_argument("--skip-headline", action="store_true",
                    help="profiling aid: quantize the headline workload's weights but time only "
                         "the secondary workloads (the headline fields are then null)")
+    p.add_argument("--settle-max-steps", type=int, default=400,
+                   help="most extra untimed steps of the clock-settling phase (0: none, for "
+                        "profiler runs where only the kernels' own figures are used)")
     p.add_argument("--copy-calib-mib", type=int, default=0,
                    help="after timing, run plain device copies of this many MiB (a known-size "
                         "kernel for scaling the rocprof FETCH_SIZE/WRITE_SIZE counters)")
@@ -128,8 +131,8 @@ def moe_layer_bytes(w):
 
 
 SETTLE_BATCH = 10            # steps per batch of the clock-settling phase
-SETTLE_MAX_STEPS = 400       # at most this many settling steps
 SETTLE_TOL = 0.01            # stable: a batch within 1% of the previous one
+SETTLE = {"max_steps": 400}  # at most this many settling steps (--settle-max-steps)
 
 SETTLE_LOG = {}
 
@@ -145,7 +148,7 @@ def settle_clocks(step, label):
     import torch
     batches = []
     n = 0
-    while n < SETTLE_MAX_STEPS:
+    while n < SETTLE["max_steps"]:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(SETTLE_BATCH):
@@ -478,6 +481,7 @@ def cpu_baseline(w, n_tokens):
 
 def main():
     args = parse()
+    SETTLE["max_steps"] = max(0, args.settle_max_steps)
     if args.gpus != 1:
         print(f"bench.py: the expert layer runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is designed, not implemented)", file=sys.stderr)
@@ -621,7 +625,7 @@ def main():
     result["clock_settle"] = {
         "note": ("after the requested warm-up, extra untimed steps in batches of "
                  f"{SETTLE_BATCH} until a batch's step time is within {SETTLE_TOL:.0%} of the "
-                 f"previous batch (at most {SETTLE_MAX_STEPS}): the GPU clock ramps over the "
+                 f"previous batch (at most {SETTLE['max_steps']}): the GPU clock ramps over the "
                  "first few hundred milliseconds of sustained work"),
         **SETTLE_LOG}
     print(json.dumps(result), flush=True)

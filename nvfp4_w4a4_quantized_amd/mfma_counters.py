@@ -31,7 +31,7 @@ def per_dispatch(path: str):
     dispatch order."""
     disp = {}
     for r in csv.DictReader(open(path)):
-        if "gemm" not in r["Kernel_Name"]:
+        if "gemm" not in r["Kernel_Name"] and "single_pass" not in r["Kernel_Name"]:
             continue
         key = (r["Kernel_Name"], int(r["Grid_Size"]), int(r["Dispatch_Id"]))
         d = disp.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
