@@ -73,9 +73,11 @@ def test_2d_rejects_ragged_groups_and_other_rules():
 
 
 def test_per_tensor_scale_depends_on_the_batch_but_per_token_does_not():
-    """miniTE Technical Report §2.3: with a tensor-wide amax the same token gets
-    a different scale depending on the other tokens in its batch; per-token
-    amax removes that dependency."""
+    """miniTE Technical Report §2.3 (per-tensor against per-token outer
+    scales).  One token is quantized in two batches with different
+    neighbours.  Under one outer scale for the whole tensor, its codes and
+    scale change with the neighbours.  Under its own per-token scale, both
+    batches give it the same bits."""
     rng = np.random.default_rng(64)
     tok = random_bf16(rng, (1, 128), 1.0)
     ctx_a = random_bf16(rng, (3, 128), 1.0)
