@@ -411,6 +411,76 @@ int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hi
                                    void* const* stage_events, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_expert_backward -- gradients of the expert layer under the
+ * straight-through approximation: the forward's quantizers count as the
+ * identity and every gradient is a BF16 GEMM (bf16 operands, fp32
+ * accumulation) on BF16 operands.  [miniTE] §4.2 (the default learning path
+ * saves the original BF16 activations and weights and skips backward
+ * quantization); [4BIT] "Improving Gradient Stability" (the same GEMMs on
+ * the dequantized operands: pass bf16 DQ(Q(.)) as x, d, w1, w2).
+ *
+ * With routed row r of expert e (rows [expert_offsets[e],
+ * expert_offsets[e+1])), token t = row_src[r], p = row_prob[r], and the
+ * forward's FC1 output C[r] = [g | u] (gate columns [0, inter)):
+ *   dYr[r] = dy[t]                          (0 for padding rows, t < 0)
+ *   dD[r]  = dYr[r] . W2[e]                 fp32
+ *   dC[r]  = bf16([dD u p silu'(g) | dD silu(g) p]),  silu(g) = g sigmoid(g),
+ *            silu'(g) = s (1 + g (1 - s)), s = sigmoid(g); 0 for padding rows
+ *   dXr[r] = bf16(dC[r] . W1[e])
+ *   dx[t]  = bf16(sum over j of dXr[dst_row[t, j]])   (j ascending, fp32 sums)
+ *   dW2[e] = sum over e's rows of dYr[r]^T d[r]        fp32 [E, hidden, inter]
+ *   dW1[e] = sum over e's rows of dC[r]^T x[t]         fp32 [E, 2*inter, hidden]
+ *   dprob[t, j] = sum over i of dD[r, i] silu(g_i) u_i for r = dst_row[t, j]
+ *            (0 for entries not routed)
+ * The GEMMs accumulate in fp32 in an order of their own; dprob sums fixed
+ * per-256-column partials in a fixed order (bitwise reproducible).
+ *
+ *   dy       bf16 [tokens, hidden]   the gradient of y
+ *   x        bf16 [tokens, hidden]   FC1's input operand
+ *   rows_cap capacity of the routed-row arrays (moe_rows_capacity of the
+ *            forward's call); expert_offsets[num_experts] <= rows_cap
+ *   fc1_out  fp32 [rows_cap, 2*inter]  the forward's FC1 output C
+ *            (nvfp4_moe_intermediates.fc1_out)
+ *   d        bf16 [rows_cap, inter]  FC2's input operand (the forward's D)
+ *   expert_offsets [num_experts+1], row_src, row_prob [rows_cap],
+ *   dst_row [tokens, topk]: the forward's routing (nvfp4_moe_intermediates)
+ *   w1       bf16 [E, 2*inter, hidden];  w2 bf16 [E, hidden, inter]
+ *   dx       out bf16 [tokens, hidden];  dprob out fp32 [tokens, topk]
+ *   dw1, dw2 out fp32, every expert written (zeros for experts with no rows)
+ *   workspace moe_expert_backward_workspace_size() bytes, 256-byte aligned
+ *   debug    nullable: dd (fp32 [rows_cap, inter]), dp_rows (fp32
+ *            [rows_cap]) and dx_rows_f32 (fp32 [rows_cap, hidden]) are only
+ *            written when given; dc and dx_rows replace the workspace copies
+ *   stage_events nullable array of 7 hipEvent_t (as void*), recorded before
+ *            the tile tables, FC2 dgrad, FC2 wgrad, FC1 dgrad, FC1 wgrad, the
+ *            dx / dprob reductions and after them
+ * bf16 arrays 16-byte aligned, the others 4-byte aligned; rows are read
+ * only inside [0, expert_offsets[num_experts]).
+ * Limits: hidden % 128 == 0, inter % 128 == 0, hidden, inter <= 16384,
+ * num_experts <= 1024, rows_cap < 2^31.
+ * Errors: NVFP4_INVALID_ARGUMENT / NVFP4_UNSUPPORTED before any HIP call;
+ * NVFP4_WORKSPACE_TOO_SMALL; NVFP4_HIP_ERROR if a launch fails.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float* dd;                      /* [rows_cap, inter] fp32 FC2 dgrad */
+  uint16_t* dc;                   /* [rows_cap, 2*inter] bf16 SwiGLU input gradient */
+  float* dp_rows;                 /* [rows_cap] router-weight gradient of each row */
+  uint16_t* dx_rows;              /* [rows_cap, hidden] bf16 FC1 dgrad rows */
+  float* dx_rows_f32;             /* [rows_cap, hidden] fp32 FC1 dgrad rows */
+} nvfp4_moe_backward_intermediates;
+
+size_t moe_expert_backward_workspace_size(int64_t rows_cap, int64_t hidden, int64_t inter,
+                                          int32_t num_experts);
+int moe_expert_backward(const uint16_t* dy, const uint16_t* x, int64_t tokens, int64_t hidden,
+                        int64_t inter, int32_t topk, int32_t num_experts, int64_t rows_cap,
+                        const float* fc1_out, const uint16_t* d, const int32_t* expert_offsets,
+                        const int32_t* row_src, const float* row_prob, const int32_t* dst_row,
+                        const uint16_t* w1, const uint16_t* w2, uint16_t* dx, float* dw1,
+                        float* dw2, float* dprob, void* workspace, size_t workspace_bytes,
+                        const nvfp4_moe_backward_intermediates* debug,
+                        void* const* stage_events, void* stream);
+
+/* ------------------------------------------------------------------------
  * Profiling helpers: thin wrappers over hipEventCreate / hipEventRecord /
  * hipEventElapsedTime / hipEventDestroy so a caller without HIP headers can
  * time the stages of moe_expert_forward on its stream.  (These allocate a

@@ -42,6 +42,10 @@ class SinglePassIntermediates(C.Structure):
         "fc1_out", "p", "a2_codes", "a2_scales", "gs_tiles", "y_rows", "y_rows_f32")]
 
 
+class BackwardIntermediates(C.Structure):
+    _fields_ = [(n, _vp) for n in ("dd", "dc", "dp_rows", "dx_rows", "dx_rows_f32")]
+
+
 _lib = None
 _debug_lib = None
 
@@ -107,6 +111,12 @@ def _load(path):
                                                  _i32, C.POINTER(Weights), C.POINTER(Weights),
                                                  _vp, _vp, C.c_size_t,
                                                  C.POINTER(SinglePassIntermediates), _vp, _vp]
+    L.moe_expert_backward_workspace_size.restype = C.c_size_t
+    L.moe_expert_backward_workspace_size.argtypes = [_i64, _i64, _i64, _i32]
+    L.moe_expert_backward.restype = C.c_int
+    L.moe_expert_backward.argtypes = [_vp, _vp, _i64, _i64, _i64, _i32, _i32, _i64, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      C.c_size_t, C.POINTER(BackwardIntermediates), _vp, _vp]
     L.nvfp4_event_create.restype = C.c_int
     L.nvfp4_event_create.argtypes = [C.POINTER(_vp)]
     L.nvfp4_event_record.restype = C.c_int

@@ -21,8 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libnvfp4moe.so")
 DEBUG_LIB = os.path.join(HERE, "libnvfp4moe_debug.so")
-SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "single_pass.hip", "combine.hip", "capi.hip",
-           "noalloc.hip"]
+SOURCES = ["quantize.hip", "route.hip", "gemm.hip", "single_pass.hip", "backward.hip",
+           "combine.hip", "capi.hip", "noalloc.hip"]
 DEBUG_SOURCES = ["route.hip", "capi.hip"]      # the sources that read NVFP4_DEBUG_CHECKS
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

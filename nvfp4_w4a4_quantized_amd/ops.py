@@ -11,15 +11,16 @@ import ctypes as C
 
 import torch
 
-from ._lib import (Intermediates, NvFp4Error, SinglePassIntermediates, Weights, check, lib, ptr,
-                   stream_handle)
+from ._lib import (BackwardIntermediates, Intermediates, NvFp4Error, SinglePassIntermediates,
+                   Weights, check, lib, ptr, stream_handle)
 
 __all__ = ["nvfp4_quantize", "moe_rows_capacity", "moe_permute", "moe_permute_noalloc",
            "w4a4_grouped_gemm",
            "w4a4_grouped_gemm_swiglu", "moe_combine", "moe_expert_forward",
            "moe_expert_forward_workspace_size", "moe_expert_forward_single_pass",
-           "moe_expert_forward_single_pass_workspace_size", "SINGLE_PASS_TILE", "NvFp4Weights",
-           "StageTimer"]
+           "moe_expert_forward_single_pass_workspace_size", "moe_expert_backward",
+           "moe_expert_backward_workspace_size", "SINGLE_PASS_TILE", "NvFp4Weights",
+           "StageTimer", "BackwardTimer"]
 
 SINGLE_PASS_TILE = 256   # intermediate columns per online-scale tile of the single-pass layer
 
@@ -407,3 +408,90 @@ def moe_expert_forward_single_pass(x, topk_idx, topk_prob, num_experts: int, int
         return y, inter_t
     return y
 
+
+
+class BackwardTimer(StageTimer):
+    """Seven HIP events recorded by moe_expert_backward: the dgrad tile
+    tables, FC2 dgrad + SwiGLU backward, FC2 wgrad, FC1 dgrad, FC1 wgrad, and
+    the dx / dprob reductions."""
+
+    NAMES = ("tables", "fc2_dgrad_swiglu", "fc2_wgrad", "fc1_dgrad", "fc1_wgrad", "reduce")
+
+    def __init__(self):
+        L = lib()
+        self.events = (C.c_void_p * 7)()
+        for i in range(7):
+            h = C.c_void_p()
+            check(L.nvfp4_event_create(C.byref(h)), "nvfp4_event_create")
+            self.events[i] = h.value
+
+    def close(self):
+        for i in range(7):
+            if self.events[i]:
+                lib().nvfp4_event_destroy(self.events[i])
+                self.events[i] = None
+
+
+def moe_expert_backward_workspace_size(rows_cap, hidden, inter, num_experts) -> int:
+    return int(lib().moe_expert_backward_workspace_size(rows_cap, hidden, inter, num_experts))
+
+
+def moe_expert_backward(dy, x, fc1_out, d, expert_offsets, row_src, row_prob, dst_row,
+                        w1, w2, workspace=None, debug: bool = False, dd: bool = False,
+                        dx_rows_f32: bool = False, timer: BackwardTimer | None = None,
+                        out=None):
+    """Gradients of the expert layer (straight-through, BF16 GEMMs).
+    dy, x: bf16 [T, H]; fc1_out: fp32 [cap, 2I] and d: bf16 [cap, I], the
+    forward's FC1 output and FC2 input; the forward's routing arrays; w1 bf16
+    [E, 2I, H], w2 bf16 [E, H, I].  Returns dict(dx, dw1, dw2, dprob); with
+    debug=True a second dict of the intermediates (dc, dp_rows, dx_rows, and
+    dd / dx_rows_f32 if asked).  `out`: optional dict of preallocated
+    outputs with those four names."""
+    for t, n in ((dy, "dy"), (x, "x"), (d, "d"), (w1, "w1"), (w2, "w2")):
+        _need(t, _BF16_LIKE, n)
+    _need(fc1_out, (torch.float32,), "fc1_out")
+    _need(row_prob, (torch.float32,), "row_prob")
+    for t, n in ((expert_offsets, "expert_offsets"), (row_src, "row_src"), (dst_row, "dst_row")):
+        _need(t, (torch.int32,), n)
+    T, H = dy.shape
+    E = w1.shape[0]
+    inter = w2.shape[2]
+    k = dst_row.shape[1]
+    cap = d.shape[0]
+    if (tuple(x.shape) != (T, H) or tuple(fc1_out.shape) != (cap, 2 * inter)
+            or tuple(d.shape) != (cap, inter) or tuple(w1.shape) != (E, 2 * inter, H)
+            or tuple(w2.shape) != (E, H, inter) or expert_offsets.numel() != E + 1
+            or row_src.numel() < cap or row_prob.numel() < cap or dst_row.shape[0] != T):
+        raise NvFp4Error("moe_expert_backward: inconsistent shapes")
+    dev = dy.device
+    L = lib()
+    wsb = int(L.moe_expert_backward_workspace_size(cap, H, inter, E))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = dict(dx=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+                   dw1=torch.empty((E, 2 * inter, H), dtype=torch.float32, device=dev),
+                   dw2=torch.empty((E, H, inter), dtype=torch.float32, device=dev),
+                   dprob=torch.empty((T, k), dtype=torch.float32, device=dev))
+    dbg = None
+    inter_t = None
+    if debug:
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+        inter_t = dict(dc=e((cap, 2 * inter), torch.bfloat16), dp_rows=e(cap, torch.float32),
+                       dx_rows=e((cap, H), torch.bfloat16))
+        if dd:
+            inter_t["dd"] = e((cap, inter), torch.float32)
+        if dx_rows_f32:
+            inter_t["dx_rows_f32"] = e((cap, H), torch.float32)
+        dbg = BackwardIntermediates(**{n: t.data_ptr() for n, t in inter_t.items()})
+    ev = timer.events if timer is not None else None
+    check(L.moe_expert_backward(ptr(dy), ptr(x), T, H, inter, k, E, cap, ptr(fc1_out), ptr(d),
+                                ptr(expert_offsets), ptr(row_src), ptr(row_prob), ptr(dst_row),
+                                ptr(w1), ptr(w2), ptr(out["dx"]), ptr(out["dw1"]),
+                                ptr(out["dw2"]), ptr(out["dprob"]), ptr(workspace),
+                                workspace.numel(), C.byref(dbg) if dbg is not None else None,
+                                C.cast(ev, C.c_void_p) if ev is not None else None,
+                                stream_handle()), "moe_expert_backward")
+    if debug:
+        return out, inter_t
+    return out
