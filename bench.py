@@ -20,6 +20,10 @@ Prints one JSON line (rank 0):
   cpu_baseline the CPU oracle timed on a bounded token sample of the workload
   four_over_six the same layer with Four-Over-Six (MSE) weights and activations
                (a secondary line; the headline is the standard block rule)
+  single_pass  the same layer with FC1 -> SwiGLU -> quantize -> FC2 fused by
+               online amax compensation
+  backward     the layer's backward (straight-through, BF16 GEMMs on the saved
+               bf16 operands): tokens/s, per-GEMM TFLOP/s and bf16-peak fraction
   secondary    the other measured shapes, each timed the same way:
                dense_t8192   W4A4 attention projections (per-token quantize +
                              G=1 GEMM for QKV, then for O-proj), tokens/s and
@@ -76,6 +80,9 @@ def parse():
                    help="also time the layer with the single-pass FC1 -> SwiGLU -> quantize -> FC2 "
                         "kernel (online amax compensation) and report it under 'single_pass' "
                         "(0 = skip)")
+    p.add_argument("--backward", type=int, default=1,
+                   help="also time the expert layer's backward (moe_expert_backward) on the "
+                        "headline workload (0: skip)")
     p.add_argument("--secondary", default="dense,decode,long",
                    help="comma list of the secondary workloads to time and report under "
                         "'secondary' (dense: the attention projections; decode: the 256-token "
@@ -263,6 +270,61 @@ def bench_single_pass(args, w, x, idx, prob, W1, W2):
         "fused_kernel_tflops": (fc1 + fc2) / (st["fused_fc1_fc2"] * 1e-3) / 1e12,
         "hbm_bytes_not_moved": 2 * R * I * 2 + 2 * R * 4 + 2 * R * (I // 2 + I // 16 + 4),
     }
+
+
+def bench_backward(args, w, x, idx, prob, W1, W2, bf):
+    """The expert layer's backward (straight-through, BF16 GEMMs on the saved
+    bf16 operands): the forward runs once with its intermediates to supply
+    the routing, FC1's output and FC2's input, then moe_expert_backward is
+    timed like the headline.  Algorithmic flops: four GEMMs over the routed
+    rows (padding excluded), 2 R H I each for FC2's dgrad and wgrad and
+    2 R 2I H each for FC1's."""
+    import torch
+
+    from nvfp4_w4a4_quantized_amd.ops import (BackwardTimer, moe_expert_backward,
+                                              moe_expert_backward_workspace_size,
+                                              moe_expert_forward)
+    log("backward: forward once for the saved tensors")
+    _, it = moe_expert_forward(x, idx, prob, w.experts, w.inter, W1, W2, debug=True,
+                               fc1_out=True)
+    from nvfp4_w4a4_quantized_amd.workloads import random_bf16
+    dy = bf(random_bf16(np.random.Generator(np.random.PCG64(7)), (w.tokens, w.hidden)))
+    w1b, w2b = bf(w.w1), bf(w.w2)
+    cap = it["d"].shape[0]
+    ws = torch.empty(moe_expert_backward_workspace_size(cap, w.hidden, w.inter, w.experts),
+                     dtype=torch.uint8, device=x.device)
+    out = dict(dx=torch.empty_like(x),
+               dw1=torch.empty((w.experts, 2 * w.inter, w.hidden), dtype=torch.float32,
+                               device=x.device),
+               dw2=torch.empty((w.experts, w.hidden, w.inter), dtype=torch.float32,
+                               device=x.device),
+               dprob=torch.empty((w.tokens, w.topk), dtype=torch.float32, device=x.device))
+    torch.cuda.synchronize()
+
+    def step(timer):
+        moe_expert_backward(dy, x, it["fc1_out"], it["d"], it["expert_offsets"], it["row_src"],
+                            it["row_prob"], it["dst_row"], w1b, w2b, workspace=ws, out=out,
+                            timer=timer)
+    wall, st = run_steps(step, args.steps, args.warmup, "backward", BackwardTimer)
+    ms = wall * 1e3 / args.steps
+    R, H, I = w.routed_rows, w.hidden, w.inter
+    f2 = 2.0 * R * H * I
+    f1 = 2.0 * R * 2 * I * H
+    gemm = {"fc2_dgrad": f2, "fc2_wgrad": f2, "fc1_dgrad": f1, "fc1_wgrad": f1}
+    total = 2 * f1 + 2 * f2
+    log("stages backward (ms, HIP events): " + ", ".join(f"{k}={v:.4f}" for k, v in st.items()))
+    res = {
+        "kernel": "moe_expert_backward (bf16 MFMA, fp32 accumulate; dW fp32, dx bf16)",
+        "value": w.tokens * args.steps / wall, "unit": "tokens/s", "ms_per_step": ms,
+        "flops": total, "effective_tflops": total / (ms * 1e-3) / 1e12,
+        "frac_of_bf16_peak": total / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
+        "stage_ms": st,
+        "gemm_tflops": {k: v / (st[k] * 1e-3) / 1e12 for k, v in gemm.items()},
+        "gemm_frac_of_bf16_peak": {k: v / (st[k] * 1e-3) / 1e12 / PEAK_F16_TFLOPS
+                                   for k, v in gemm.items()},
+    }
+    del ws, out, it, w1b, w2b, dy
+    return res
 
 
 class _TorchStages:
@@ -598,6 +660,8 @@ def main():
         }
     if args.single_pass:
         result["single_pass"] = bench_single_pass(args, w, x, idx, prob, W1, W2)
+    if args.backward:
+        result["backward"] = bench_backward(args, w, x, idx, prob, W1, W2, bf)
     sec = run_secondary(args, dev, bf, W1, W2)
     if sec:
         result["secondary"] = sec

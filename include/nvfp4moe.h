@@ -423,17 +423,18 @@ int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hi
  * expert_offsets[e+1])), token t = row_src[r], p = row_prob[r], and the
  * forward's FC1 output C[r] = [g | u] (gate columns [0, inter)):
  *   dYr[r] = dy[t]                          (0 for padding rows, t < 0)
- *   dD[r]  = dYr[r] . W2[e]                 fp32
+ *   dD[r]  = bf16(dYr[r] . W2[e])
  *   dC[r]  = bf16([dD u p silu'(g) | dD silu(g) p]),  silu(g) = g sigmoid(g),
- *            silu'(g) = s (1 + g (1 - s)), s = sigmoid(g); 0 for padding rows
+ *            silu'(g) = s (1 + g (1 - s)), s = sigmoid(g), in fp32 from the
+ *            bf16 dD; 0 for padding rows
+ *   dp[r]  = sum over i of dD[r, i] silu(g_i) u_i          (fp32)
  *   dXr[r] = bf16(dC[r] . W1[e])
  *   dx[t]  = bf16(sum over j of dXr[dst_row[t, j]])   (j ascending, fp32 sums)
  *   dW2[e] = sum over e's rows of dYr[r]^T d[r]        fp32 [E, hidden, inter]
  *   dW1[e] = sum over e's rows of dC[r]^T x[t]         fp32 [E, 2*inter, hidden]
- *   dprob[t, j] = sum over i of dD[r, i] silu(g_i) u_i for r = dst_row[t, j]
- *            (0 for entries not routed)
- * The GEMMs accumulate in fp32 in an order of their own; dprob sums fixed
- * per-256-column partials in a fixed order (bitwise reproducible).
+ *   dprob[t, j] = dp[dst_row[t, j]]  (0 for entries not routed)
+ * The GEMMs accumulate in fp32 in an order of their own, the same on every
+ * call; dp sums in a fixed order (all outputs are bitwise reproducible).
  *
  *   dy       bf16 [tokens, hidden]   the gradient of y
  *   x        bf16 [tokens, hidden]   FC1's input operand
@@ -441,28 +442,30 @@ int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hi
  *            forward's call); expert_offsets[num_experts] <= rows_cap
  *   fc1_out  fp32 [rows_cap, 2*inter]  the forward's FC1 output C
  *            (nvfp4_moe_intermediates.fc1_out)
- *   d        bf16 [rows_cap, inter]  FC2's input operand (the forward's D)
+ *   d        bf16 [rows_cap, inter]  FC2's input operand (the forward's D;
+ *            its padding rows must be finite, the forward writes zeros)
  *   expert_offsets [num_experts+1], row_src, row_prob [rows_cap],
  *   dst_row [tokens, topk]: the forward's routing (nvfp4_moe_intermediates)
  *   w1       bf16 [E, 2*inter, hidden];  w2 bf16 [E, hidden, inter]
  *   dx       out bf16 [tokens, hidden];  dprob out fp32 [tokens, topk]
  *   dw1, dw2 out fp32, every expert written (zeros for experts with no rows)
  *   workspace moe_expert_backward_workspace_size() bytes, 256-byte aligned
- *   debug    nullable: dd (fp32 [rows_cap, inter]), dp_rows (fp32
- *            [rows_cap]) and dx_rows_f32 (fp32 [rows_cap, hidden]) are only
- *            written when given; dc and dx_rows replace the workspace copies
- *   stage_events nullable array of 7 hipEvent_t (as void*), recorded before
- *            the tile tables, FC2 dgrad, FC2 wgrad, FC1 dgrad, FC1 wgrad, the
- *            dx / dprob reductions and after them
- * bf16 arrays 16-byte aligned, the others 4-byte aligned; rows are read
- * only inside [0, expert_offsets[num_experts]).
+ *   debug    nullable: dd, dc, dp_rows and dx_rows replace the workspace
+ *            copies; dx_rows_f32 (fp32 [rows_cap, hidden], the FC1 dgrad
+ *            before its bf16 rounding) is only written when given
+ *   stage_events nullable array of 8 hipEvent_t (as void*), recorded before
+ *            the tile tables, FC2 dgrad, the SwiGLU backward, FC2 wgrad, FC1
+ *            dgrad, FC1 wgrad, the dx / dprob reductions and after them
+ * bf16 arrays and fc1_out 16-byte aligned, the others 4-byte aligned; rows
+ * are read only inside [0, expert_offsets[num_experts]).
  * Limits: hidden % 128 == 0, inter % 128 == 0, hidden, inter <= 16384,
- * num_experts <= 1024, rows_cap < 2^31.
+ * num_experts <= 1024, rows_cap < 2^31, and below 2^31 bytes each: dy (and
+ * x), fc1_out, one expert's w1 (NVFP4_UNSUPPORTED otherwise).
  * Errors: NVFP4_INVALID_ARGUMENT / NVFP4_UNSUPPORTED before any HIP call;
  * NVFP4_WORKSPACE_TOO_SMALL; NVFP4_HIP_ERROR if a launch fails.
  * ---------------------------------------------------------------------- */
 typedef struct {
-  float* dd;                      /* [rows_cap, inter] fp32 FC2 dgrad */
+  uint16_t* dd;                   /* [rows_cap, inter] bf16 FC2 dgrad */
   uint16_t* dc;                   /* [rows_cap, 2*inter] bf16 SwiGLU input gradient */
   float* dp_rows;                 /* [rows_cap] router-weight gradient of each row */
   uint16_t* dx_rows;              /* [rows_cap, hidden] bf16 FC1 dgrad rows */

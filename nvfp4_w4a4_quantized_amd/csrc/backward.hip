@@ -8,8 +8,8 @@
 // B operand is a row-major matrix whose rows run along K ("K-major"); A has
 // K contiguous in the dgrads and is K-major in the wgrads:
 //   FC2 dgrad  dD [R, I]  = dYr [R, H] . W2[e] [H, I]     A: dy rows via row_src
-//              with the SwiGLU backward in its epilogue -> dC [R, 2I] bf16
-//              and per-row partial sums of the router-weight gradient
+//              -> bf16 rows, then the SwiGLU backward (its own kernel below)
+//              -> dC [R, 2I] bf16 and the rows' router-weight gradients
 //   FC1 dgrad  dXr[R, H]  = dC [R, 2I] . W1[e] [2I, H]    -> bf16 rows
 //   FC2 wgrad  dW2[e] [H, I]  = sum over e's rows r of dYr[r]^T D[r]
 //   FC1 wgrad  dW1[e] [2I, H] = sum over e's rows r of dC[r]^T x[row_src[r]]
@@ -17,15 +17,25 @@
 // the 8 XCDs); the wgrads group K (the expert's rows) and write one fp32
 // matrix per expert.  Padding rows (row_src < 0) read as zeros.
 //
-// Tile 128 x 256, four waves of 64 x 128 (2 x 4 v_mfma_f32_32x32x16_bf16
-// blocks), K-stage 64, both operands double-buffered in LDS: the next
-// stage's global loads are in flight while the matrix cores run the current
-// one.  K-major operands are transposed on their way into LDS (two k-rows
-// per thread, packed into one dword per column), so every fragment read is
-// one 16-byte LDS load of 8 consecutive k.  The LDS row pitch of 72 bf16
-// (36 dwords) keeps both the transposing stores (32 lanes on consecutive
-// dwords of one row, the other 32 lanes 8 rows further, 32 banks apart) and
-// the 16-byte fragment reads free of bank conflicts.
+// Tile 256 x 256, four waves of 128 x 128 (4 x 4 v_mfma_f32_32x32x16_bf16
+// blocks, the accumulators filling the 256 AGPRs), K-stage 64, both operands
+// double-buffered in LDS; the global loads of stage s + 1 are in flight in
+// registers while the matrix cores run stage s (64 MFMAs per wave), and the
+// row indices of a gathered K-major operand are read a stage earlier still.
+// Every global load goes through a buffer resource and is unconditional:
+// masked lanes read zeros, so no branch makes the compiler drain the loads
+// in flight.
+// K-major tiles are copied into LDS as they lie in memory ([k][columns], 16
+// bytes per lane) and transposed by the read: ds_read_b64_tr_b16 hands each
+// lane of a 16-lane group one column of a 4 x 16 block read by the group, so
+// two of them give a lane the 8 consecutive k of its column that the matrix
+// core takes.  K-contiguous A tiles are [m][k] and read 16 bytes per lane.
+// Row pitches (bf16): 72 for [m][64 k]; 160 and 288 for the 128- and
+// 256-column K-major tiles (80 and 144 dwords, 16 banks apart from row to
+// row: the four rows of a transposing read hit 64 distinct banks).
+// The wgrads take their tiles heaviest expert first (an order the table
+// kernel writes), so the experts with the most rows start first and the
+// light ones fill in behind them.
 #include <algorithm>
 
 #include "gemm_common.h"
@@ -37,42 +47,81 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 256, BK = 64;
-constexpr int LDSP = BK + 8;                          // LDS row pitch (bf16)
-constexpr int A_BYTES = BM * LDSP * 2, B_BYTES = BN * LDSP * 2;
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int PA_KC = BK + 8;                 // A [m][k]
+constexpr int PKM = 256 + 32;                 // A [k][m] and B [k][n]
+constexpr int A_BYTES = BM * PA_KC * 2;       // == BK * PKM * 2
+constexpr int B_BYTES = BK * PKM * 2;
 constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;            // 110592
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;    // 147456
+static_assert(A_BYTES == BK * PKM * 2, "A stage");
 
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
 
+// The matrix-core operand of a K-major LDS tile s[k][c] (row pitch `pitch`):
+// lane l receives column c0 + l % 32, rows k0 + 8 (l / 32) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_km(const uint16_t* s, int pitch, int c0, int k0,
+                                            int lane) {
+  const uint16_t* p = s + (k0 + (lane >> 5) * 8 + ((lane & 15) >> 2)) * pitch + c0 +
+                      ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4 * pitch));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Loads go through buffer resources: an offset at or past the resource's
+// size reads as zero without a memory access, so a masked element needs no
+// branch (a branch around a load would make the compiler wait for every load
+// in flight where the paths join).  Sizes stay below 2^31 bytes (the host
+// checks), and kNone lies past every one.
+constexpr uint32_t kNone = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ u32x4_t bl16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+__device__ __forceinline__ float bl4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 }  // namespace
 
-// The kernel. BWD_DGRAD_*: workgroup b takes tile table entry b (group,
-// rows [r0, r1), n-tile); BWD_WGRAD: tile b of the XCD-contiguous order
-// over (group, m-tile, n-tile).
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
+// The kernel.  BWD_DGRAD_*: workgroup b takes tile table entry b (group,
+// rows [r0, r1), n-tile).  BWD_WGRAD: tile b of (expert in the order table,
+// m-tile, n-tile); GATHER 1 / 2: A / B rows along K are read through row_map.
+// Four waves, each a 128 x 128 quadrant (4 x 4 blocks of 32 x 32).
+template <int MODE, int GATHER, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  constexpr bool KMA = MODE == BWD_WGRAD;
+  constexpr bool WG = MODE == BWD_WGRAD;
+  constexpr int NT = 64 * NW;                 // threads
+  constexpr int PPT = BM * BK / 8 / NT;       // 16-byte pieces per thread and operand
+  constexpr int RKC = NT / 8, RKM = NT / 32;  // row steps of the K-contiguous / K-major pieces
+  constexpr int WNC = 2 * BN / NW;            // columns of a wave (2 waves along M)
+  constexpr int JB = WNC / 32;                // its 32-column blocks
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  int g;
+  int g, nt;
   int64_t m0, mlim, n0, k0, k1;
-  int nt;
-  if constexpr (MODE == BWD_WGRAD) {
+  if constexpr (WG) {
     const int64_t mtn = (a.m + BM - 1) / BM, ntn = (a.n + BN - 1) / BN;
-    const int64_t total = (int64_t)a.num_groups * mtn * ntn;
-    const int64_t per = (total + 7) / 8;
-    const int64_t logical = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
-    if (logical >= total) return;
-    g = (int)(logical / (mtn * ntn));
-    const int64_t t = logical % (mtn * ntn);
-    m0 = (t / ntn) * BM;
-    nt = (int)(t % ntn);
-    n0 = (int64_t)nt * BN;
+    const int64_t per = mtn * ntn;
+    const int64_t t = blockIdx.x;
+    if (t >= (int64_t)a.num_groups * per) return;
+    g = a.order[t / per];
+    const int64_t q = t % per;
+    m0 = (q / ntn) * BM;
+    nt = (int)(q % ntn);
     mlim = a.m;
     k0 = a.offsets[g];
     k1 = a.offsets[g + 1];
@@ -83,29 +132,28 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
     m0 = e.y;
     mlim = e.z;
     nt = e.w;
-    n0 = (int64_t)nt * BN;
     k0 = 0;
     k1 = a.k;
   }
+  n0 = (int64_t)nt * BN;
   g = __builtin_amdgcn_readfirstlane(g);
   const uint16_t* Ab = a.a.p;
-  const uint16_t* Bb = a.b.p + (MODE == BWD_WGRAD ? 0 : (int64_t)g * a.b.group_stride);
-  const int64_t nlim = a.n;
+  const uint16_t* Bb = a.b.p + (WG ? 0 : (int64_t)g * a.b.group_stride);
 
   auto sA = [&](int buf) { return reinterpret_cast<uint16_t*>(smem + buf * STAGE_BYTES); };
   auto sB = [&](int buf) {
     return reinterpret_cast<uint16_t*>(smem + buf * STAGE_BYTES + A_BYTES);
   };
+  const __amdgpu_buffer_rsrc_t ar = rsrc(Ab, a.a.bytes);
+  const __amdgpu_buffer_rsrc_t br = rsrc(Bb, a.b.bytes);
 
-  // ---- K-contiguous A (dgrads): piece i = tid + 256 j (j < 4) is row i / 8,
-  // k (i % 8) * 8 of the stage; the rows (and their gather) are fixed.
-  int64_t arow[4];
-  bool aok[4];
-  if constexpr (!KMA) {
+  // K-contiguous A (dgrads): piece j of a thread is row tid / 8 + RKC j, k
+  // (tid % 8) * 8 of the stage; the rows (and their gather) are fixed.
+  uint32_t aoff[PPT];
+  if constexpr (!WG) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + 256 * j;
-      const int64_t r = m0 + i / 8;
+    for (int j = 0; j < PPT; ++j) {
+      const int64_t r = m0 + tid / 8 + RKC * j;
       bool ok = r < mlim;
       int64_t src = r;
       if (ok && a.a.row_map) {
@@ -113,135 +161,126 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
         ok = t >= 0;
         if (a.a.gather) src = t;
       }
-      aok[j] = ok;
-      arow[j] = src * a.a.ld + (i % 8) * 8;
+      aoff[j] = ok ? (uint32_t)((src * a.a.ld + (tid % 8) * 8) * 2) : kNone;
     }
   }
-  // ---- K-major operand: pair piece i = tid + 256 j is k-rows 2 (i % 32) and
-  // 2 (i % 32) + 1 of the stage, columns c0 + (i / 32) * 8 .. + 7.
-  auto load_km = [&](const BwdOperand& op, const uint16_t* base, int64_t c0, int64_t clim,
-                     int64_t kk, u32x4_t* v, int np) {
-    for (int j = 0; j < np; ++j) {
-      const int i = tid + 256 * j;
-      const int64_t c = c0 + (i / 32) * 8;
+  // K-major pieces (A in the wgrads, B always): rows tid / 32 + RKM j of the
+  // stage, 8 columns at (tid % 32) * 8.
+  const int64_t acol = m0 + (tid % 32) * 8;
+  const int64_t bcol = n0 + (tid % 32) * 8;
+  const bool acol_ok = acol < mlim, bcol_ok = bcol < a.n;
+
+  // the gathered rows of a stage (clamped to the group's last row; rows past
+  // it are masked where the data loads use them)
+  auto load_idx = [&](int64_t kk, int32_t (&ix)[PPT]) {
+    if constexpr (GATHER != 0) {
+      const int32_t* map = GATHER == 1 ? a.a.row_map : a.b.row_map;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t kr = kk + 2 * (i % 32) + h;
-        bool ok = kr < k1 && c < clim;
-        int64_t src = kr;
-        if (ok && op.row_map) {
-          const int32_t t = op.row_map[kr];
-          ok = t >= 0;
-          if (op.gather) src = t;
-        }
-        v[2 * j + h] = ok ? *reinterpret_cast<const u32x4_t*>(base + src * op.ld + c)
-                          : u32x4_t{0u, 0u, 0u, 0u};
-      }
+      for (int j = 0; j < PPT; ++j)
+        ix[j] = map[std::min<int64_t>(kk + tid / 32 + RKM * j, k1 - 1)];
     }
   };
-  auto store_km = [&](uint16_t* s, const u32x4_t* v, int np) {
-    for (int j = 0; j < np; ++j) {
-      const int i = tid + 256 * j;
-      const int kl = 2 * (i % 32), cl = (i / 32) * 8;
-      const u32x4_t lo = v[2 * j], hi = v[2 * j + 1];
+  auto load = [&](int64_t kk, const int32_t (&ix)[PPT], u32x4_t (&ra)[PPT],
+                  u32x4_t (&rb)[PPT]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = lo[e / 2], w1 = hi[e / 2];
-        const uint32_t x0 = (e & 1) ? (w0 >> 16) : (w0 & 0xFFFFu);
-        const uint32_t x1 = (e & 1) ? (w1 & 0xFFFF0000u) : (w1 << 16);
-        *reinterpret_cast<uint32_t*>(s + (cl + e) * LDSP + kl) = x0 | x1;
+    for (int j = 0; j < PPT; ++j) {
+      const int64_t kr = kk + tid / 32 + RKM * j;
+      if constexpr (!WG) {
+        ra[j] = bl16(ar, aoff[j] + (uint32_t)(kk * 2));
+      } else {
+        const int64_t src = kr < k1 ? (GATHER == 1 ? (int64_t)ix[j] : kr) : -1;
+        ra[j] = bl16(ar, src >= 0 && acol_ok ? (uint32_t)((src * a.a.ld + acol) * 2) : kNone);
       }
+      const int64_t srb = kr < k1 ? (GATHER == 2 ? (int64_t)ix[j] : kr) : -1;
+      rb[j] = bl16(br, srb >= 0 && bcol_ok ? (uint32_t)((srb * a.b.ld + bcol) * 2) : kNone);
+    }
+  };
+  auto store = [&](int buf, const u32x4_t (&ra)[PPT], const u32x4_t (&rb)[PPT]) {
+    uint16_t* sa = sA(buf);
+    uint16_t* sb = sB(buf);
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      if constexpr (!WG)
+        *reinterpret_cast<u32x4_t*>(sa + (tid / 8 + RKC * j) * PA_KC + (tid % 8) * 8) = ra[j];
+      else
+        *reinterpret_cast<u32x4_t*>(sa + (tid / 32 + RKM * j) * PKM + (tid % 32) * 8) = ra[j];
+      *reinterpret_cast<u32x4_t*>(sb + (tid / 32 + RKM * j) * PKM + (tid % 32) * 8) = rb[j];
     }
   };
 
-  constexpr int NPA = KMA ? 2 : 4;      // A: pair pieces (K-major) or 16-byte pieces
-  constexpr int NPB = 4;                // B: pair pieces (256 columns)
-  u32x4_t va[KMA ? 2 * NPA : NPA], vb[2 * NPB];
-  auto load_stage = [&](int64_t kk) {
-    if constexpr (KMA) {
-      load_km(a.a, Ab, m0, mlim, kk, va, NPA);
-    } else {
+  float16_t acc[4][JB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        va[j] = aok[j] && kk + ((tid + 256 * j) % 8) * 8 < k1
-                    ? *reinterpret_cast<const u32x4_t*>(Ab + arow[j] + kk)
-                    : u32x4_t{0u, 0u, 0u, 0u};
-    }
-    load_km(a.b, Bb, n0, nlim, kk, vb, NPB);
-  };
-  auto store_stage = [&](int buf) {
-    if constexpr (KMA) {
-      store_km(sA(buf), va, NPA);
-    } else {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = tid + 256 * j;
-        *reinterpret_cast<u32x4_t*>(sA(buf) + (i / 8) * LDSP + (i % 8) * 8) = va[j];
-      }
-    }
-    store_km(sB(buf), vb, NPB);
-  };
-
-  float16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int wm = wave / 2, wn = wave % 2;               // the wave's 64 x 128 quadrant
+  const int wm = wave % 2, wn = wave / 2;               // the wave's 128 x WNC block
   // 32-row blocks wholly past the tile's rows take no matrix work
-  const bool mv0 = m0 + wm * 64 < mlim, mv1 = m0 + wm * 64 + 32 < mlim;
-  const int64_t nst = (k1 - k0 + BK - 1) / BK;
-  if (nst > 0) {
-    load_stage(k0);
-    store_stage(0);
-  }
-  __syncthreads();
-  for (int64_t s = 0; s < nst; ++s) {
-    const int cur = (int)(s & 1);
-    const bool more = s + 1 < nst;
-    if (more) load_stage(k0 + (s + 1) * BK);
-    const uint16_t* la = sA(cur);
-    const uint16_t* lb = sB(cur);
-    if (mv0) {
+  const int64_t vrows = mlim - (m0 + wm * 128);
+  const int nvb = vrows <= 0 ? 0 : (vrows >= 128 ? 4 : (int)((vrows + 31) / 32));
+  auto compute = [&](int buf) {
+    const uint16_t* la = sA(buf);
+    const uint16_t* lb = sB(buf);
 #pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8_t fb[4];
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8_t fb[JB];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = wn * 128 + j * 32 + (lane & 31);
-          fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + col * LDSP + kk * 16 + 8 * (lane >> 5));
+      for (int j = 0; j < JB; ++j) fb[j] = frag_km(lb, PKM, wn * WNC + j * 32, kk * 16, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nvb) break;
+        bf16x8_t fa;
+        if constexpr (WG) {
+          fa = frag_km(la, PKM, wm * 128 + i * 32, kk * 16, lane);
+        } else {
+          const int row = wm * 128 + i * 32 + (lane & 31);
+          fa = *reinterpret_cast<const bf16x8_t*>(la + row * PA_KC + kk * 16 + 8 * (lane >> 5));
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          if (i == 1 && !mv1) break;
-          const int row = wm * 64 + i * 32 + (lane & 31);
-          const bf16x8_t fa =
-              *reinterpret_cast<const bf16x8_t*>(la + row * LDSP + kk * 16 + 8 * (lane >> 5));
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
-        }
+        for (int j = 0; j < JB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (more) store_stage(cur ^ 1);
+  };
+
+  // ---- main loop: stage s computes from LDS buffer s % 2 while the loads of
+  // stage s + 1 are in flight into registers (and, for a gathered operand,
+  // the rows of stage s + 2); the loads are unconditional, so the wait before
+  // the LDS store counts only them.
+  const int64_t nst = (k1 - k0 + BK - 1) / BK;
+  u32x4_t ra[PPT], rb[PPT];
+  int32_t ix[PPT];
+  if (nst > 0) {
+    if constexpr (GATHER != 0) load_idx(k0, ix);
+    load(k0, ix, ra, rb);
+    if constexpr (GATHER != 0) load_idx(k0 + BK, ix);
+    store(0, ra, rb);
+  }
+  __syncthreads();
+  for (int64_t s = 0; s + 1 < nst; ++s) {
+    load(k0 + (s + 1) * BK, ix, ra, rb);
+    if constexpr (GATHER != 0) load_idx(k0 + (s + 2) * BK, ix);
+    compute((int)(s & 1));
+    store((int)((s + 1) & 1), ra, rb);
     __syncthreads();
   }
+  if (nst > 0) compute((int)((nst - 1) & 1));
+  __syncthreads();                             // the epilogue reuses the LDS
 
   // ---- epilogue: acc[i][j][r] is row 8 (r / 4) + 4 h + r % 4 of the 32 x 32
   // block (i, j) of the wave, column l32 (h = lane / 32, l32 = lane % 32)
   const int h = lane >> 5, l32 = lane & 31;
-  auto row_of = [&](int i, int r) -> int { return wm * 64 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4); };
-  auto col_of = [&](int j) -> int64_t { return n0 + wn * 128 + j * 32 + l32; };
+  auto row_of = [&](int i, int r) -> int { return wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4); };
+  auto col_of = [&](int j) -> int64_t { return n0 + wn * WNC + j * 32 + l32; };
 
   if constexpr (MODE == BWD_WGRAD) {
     float* out = a.out_f32 + (int64_t)g * a.m * a.n;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < JB; ++j) {
         const int64_t col = col_of(j);
         if (col >= a.n) continue;
 #pragma unroll
@@ -250,11 +289,11 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
           if (row < mlim) out[row * a.n + col] = acc[i][j][r];
         }
       }
-  } else if constexpr (MODE == BWD_DGRAD_ROWS) {
+  } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < JB; ++j) {
         const int64_t col = col_of(j);
         if (col >= a.n) continue;
 #pragma unroll
@@ -265,104 +304,99 @@ __global__ __launch_bounds__(256, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
           if (a.out_f32) a.out_f32[row * a.n + col] = acc[i][j][r];
         }
       }
-  } else {
-    // SwiGLU backward.  a.n = I; C is [rows, 2I] fp32 (gate | up); the rows'
-    // router weights and whether they are routed go through LDS once.
-    float* sp = reinterpret_cast<float*>(smem);          // [128] router weight
-    int32_t* sok = reinterpret_cast<int32_t*>(sp + BM);  // [128] routed (not padding)
-    float* sdp = sp + 2 * BM;                            // [2][128] the waves' row sums
-    if (tid < BM) {
-      const int64_t r = m0 + tid;
-      const bool routed = r < mlim && a.row_src[r] >= 0;
-      sp[tid] = routed ? a.row_prob[r] : 0.0f;
-      sok[tid] = routed ? 1 : 0;
-    }
-    __syncthreads();
-    const int64_t I = a.n;
-    float part[2][16];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part[i][r] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = col_of(j);
-        if (col >= I) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = row_of(i, r);
-          const int64_t row = m0 + lr;
-          if (row >= mlim) continue;
-          const float pw = sp[lr];
-          const float d = acc[i][j][r];
-          float dg = 0.0f, du = 0.0f;
-          if (sok[lr]) {
-            const float gt = a.c[row * 2 * I + col], up = a.c[row * 2 * I + I + col];
-            const float sg = 1.0f / (1.0f + __expf(-gt));
-            const float silu = gt * sg;
-            const float dsilu = sg * (1.0f + gt * (1.0f - sg));
-            dg = d * up * pw * dsilu;
-            du = d * silu * pw;
-            part[i][r] += d * silu * up;
-          }
-          a.out_bf16[row * 2 * I + col] = f32_to_bf16(dg);
-          a.out_bf16[row * 2 * I + I + col] = f32_to_bf16(du);
-          if (a.out_f32) a.out_f32[row * I + col] = d;
-        }
-      }
-    // row sums over the wave's 128 columns: the 32 lanes of one half, then the
-    // two waves of the row in wn order (a fixed order: deterministic)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = part[i][r];
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-        if (l32 == 0) sdp[wn * BM + row_of(i, r)] = v;
-      }
-    __syncthreads();
-    if (tid < BM) {
-      const int64_t row = m0 + tid;
-      if (row < mlim) a.dp_part[row * a.dp_ld + nt] = sdp[tid] + sdp[BM + tid];
-    }
   }
 }
 
-// dprob[t, j] = sum over the n-tiles of the partial sums of the entry's row
-// (0 for entries not routed); dp_rows (nullable) receives the rows' sums.
-__global__ __launch_bounds__(256) void bwd_entry_grad_kernel(const float* dp_part, int32_t dp_ld,
+// SwiGLU backward, one wave per routed row r < rows_end, from the FC2
+// dgrad rows dD (bf16), the forward's FC1 output C = [g | u] (fp32) and the
+// row's router weight p:
+//   dC[r] = bf16([dD u p silu'(g) | dD silu(g) p])
+//   dp[r] = sum over i of dD_i silu(g_i) u_i
+// with silu(g) = g s, s = 1 / (1 + e^-g), silu'(g) = s (1 + g (1 - s));
+// padding rows (row_src < 0) get zeros.  Lane l takes columns 8 l .. 8 l + 7
+// of every 512 (16-byte dD and dC accesses, 32-byte C accesses); dp sums the
+// lane's columns in order, then a fixed butterfly (deterministic).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* dD, const float* C,
+                                                         const int32_t* row_src,
+                                                         const float* row_prob,
+                                                         const int32_t* rows_end, int64_t cap,
+                                                         int64_t I, uint16_t* dC, float* dp) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (r >= cap || r >= (int64_t)*rows_end) return;
+  const bool routed = row_src[r] >= 0;
+  const float p = routed ? row_prob[r] : 0.0f;
+  float part = 0.0f;
+  for (int64_t c = (int64_t)lane * 8; c < I; c += kWave * 8) {
+    const u32x4_t dv = *reinterpret_cast<const u32x4_t*>(dD + r * I + c);
+    const float4* gp = reinterpret_cast<const float4*>(C + r * 2 * I + c);
+    const float4* up = reinterpret_cast<const float4*>(C + r * 2 * I + I + c);
+    const float4 g0 = gp[0], g1 = gp[1], u0 = up[0], u1 = up[1];
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float u[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    float dg[8], du[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = dv[e / 2];
+      const float d = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      const float sg = 1.0f / (1.0f + __expf(-g[e]));
+      const float silu = g[e] * sg;
+      const float dsilu = sg * (1.0f + g[e] * (1.0f - sg));
+      dg[e] = routed ? d * u[e] * p * dsilu : 0.0f;
+      du[e] = routed ? d * silu * p : 0.0f;
+      part += routed ? d * silu * u[e] : 0.0f;
+    }
+    u32x4_t og, ou;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      og[q] = pack_bf16x2(dg[2 * q], dg[2 * q + 1]);
+      ou[q] = pack_bf16x2(du[2 * q], du[2 * q + 1]);
+    }
+    *reinterpret_cast<u32x4_t*>(dC + r * 2 * I + c) = og;
+    *reinterpret_cast<u32x4_t*>(dC + r * 2 * I + I + c) = ou;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, kWave);
+  if (lane == 0) dp[r] = part;
+}
+
+// dprob[t, j] = dp of the entry's row (0 for entries not routed)
+__global__ __launch_bounds__(256) void bwd_entry_grad_kernel(const float* dp,
                                                              const int32_t* dst_row, int64_t n,
-                                                             float* dprob, const int32_t* rows_end,
-                                                             int64_t cap, float* dp_rows) {
+                                                             float* dprob) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) {
-    const int32_t d = dst_row[i];
-    float s = 0.0f;
-    if (d >= 0)
-      for (int q = 0; q < dp_ld; ++q) s += dp_part[(int64_t)d * dp_ld + q];
-    dprob[i] = s;
-  }
-  if (dp_rows && i < cap && i < (int64_t)*rows_end) {
-    float s = 0.0f;
-    for (int q = 0; q < dp_ld; ++q) s += dp_part[i * dp_ld + q];
-    dp_rows[i] = s;
-  }
+  if (i >= n) return;
+  const int32_t d = dst_row[i];
+  dprob[i] = d >= 0 ? dp[d] : 0.0f;
 }
 
-// The two dgrad tile tables: workgroup 0 writes t0, workgroup 1 t1.
+// The two dgrad tile tables (workgroups 0 and 1) and the wgrads' expert
+// order (workgroup 2): experts by descending row count, ties by id.
 __global__ __launch_bounds__(256) void bwd_tables_kernel(const int32_t* offsets, int32_t G,
-                                                         TileTableSpec t0, TileTableSpec t1) {
+                                                         TileTableSpec t0, TileTableSpec t1,
+                                                         int32_t* order) {
   __shared__ TileTableLds s;
-  build_tile_table<128>(offsets, G, blockIdx.x == 0 ? t0 : t1, threadIdx.x, 256, s);
+  if (blockIdx.x < 2) {
+    build_tile_table<BM>(offsets, G, blockIdx.x == 0 ? t0 : t1, threadIdx.x, 256, s);
+    return;
+  }
+  for (int e = threadIdx.x; e <= G; e += 256) s.off[e] = offsets[e];
+  __syncthreads();
+  for (int e = threadIdx.x; e < G; e += 256) {
+    const int32_t c = s.off[e + 1] - s.off[e];
+    int rank = 0;
+    for (int f = 0; f < G; ++f) {
+      const int32_t cf = s.off[f + 1] - s.off[f];
+      rank += (cf > c || (cf == c && f < e)) ? 1 : 0;
+    }
+    order[rank] = e;
+  }
 }
 
 int bwd_lds_bytes() { return LDS_BYTES; }
 
 // Grid of a dgrad launch: every XCD's cost-balanced range of m-tiles (the
-// bound of the forward GEMM's 128-row tiles) times the n-tiles.
+// bound of the forward GEMM's schedule, for 256-row tiles) times the n-tiles.
 TileTableSpec bwd_dgrad_table_spec(int64_t rows_cap, int32_t num_groups, int64_t k, int64_t n,
                                    int4* table) {
   const int64_t ntn = (n + BN - 1) / BN;
@@ -376,44 +410,52 @@ TileTableSpec bwd_dgrad_table_spec(int64_t rows_cap, int32_t num_groups, int64_t
 }
 
 int64_t bwd_wgrad_blocks(int32_t num_groups, int64_t m, int64_t n) {
-  const int64_t total = (int64_t)num_groups * ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
-  return 8 * ((total + 7) / 8);
+  return (int64_t)num_groups * ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
 }
-
-int64_t bwd_n_tiles(int64_t n) { return (n + BN - 1) / BN; }
 
 hipError_t launch_bwd_tables(const int32_t* offsets, int32_t G, const TileTableSpec& t0,
-                             const TileTableSpec& t1, hipStream_t s) {
-  bwd_tables_kernel<<<2, 256, 0, s>>>(offsets, G, t0, t1);
+                             const TileTableSpec& t1, int32_t* order, hipStream_t s) {
+  bwd_tables_kernel<<<3, 256, 0, s>>>(offsets, G, t0, t1, order);
   return hipGetLastError();
 }
+
+// The wgrads gather one operand along K: A (dy rows, FC2) or B (x rows, FC1).
+#ifndef NVFP4_BWD_WAVES
+#define NVFP4_BWD_WAVES 8
+#endif
+constexpr int kBwdWaves = NVFP4_BWD_WAVES;
 
 hipError_t launch_bwd_gemm(int mode, const BwdGemmArgs& a, int64_t blocks, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  switch (mode) {
-    case BWD_DGRAD_SWIGLU:
-      bwd_gemm_kernel<BWD_DGRAD_SWIGLU><<<(unsigned)blocks, 256, LDS_BYTES, s>>>(a);
-      break;
-    case BWD_DGRAD_ROWS:
-      bwd_gemm_kernel<BWD_DGRAD_ROWS><<<(unsigned)blocks, 256, LDS_BYTES, s>>>(a);
-      break;
-    case BWD_WGRAD:
-      bwd_gemm_kernel<BWD_WGRAD><<<(unsigned)blocks, 256, LDS_BYTES, s>>>(a);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  const unsigned nb = (unsigned)blocks;
+  constexpr int T = 64 * kBwdWaves;
+  if (mode == BWD_DGRAD_ROWS) {
+    bwd_gemm_kernel<BWD_DGRAD_ROWS, 0, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
+  } else if (mode == BWD_WGRAD) {
+    if ((a.a.row_map && a.b.row_map) || !a.order) return hipErrorInvalidValue;
+    if (a.a.row_map) bwd_gemm_kernel<BWD_WGRAD, 1, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
+    else if (a.b.row_map) bwd_gemm_kernel<BWD_WGRAD, 2, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
+    else bwd_gemm_kernel<BWD_WGRAD, 0, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
+  } else {
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_entry_grad(const float* dp_part, int32_t dp_ld, const int32_t* dst_row,
-                                 int64_t n, float* dprob, const int32_t* rows_end, int64_t cap,
-                                 float* dp_rows, hipStream_t s) {
-  const int64_t m = std::max<int64_t>(n, dp_rows ? cap : 0);
-  if (m <= 0) return hipSuccess;
-  bwd_entry_grad_kernel<<<(unsigned)((m + 255) / 256), 256, 0, s>>>(dp_part, dp_ld, dst_row, n,
-                                                                  dprob, rows_end, cap, dp_rows);
+hipError_t launch_swiglu_bwd(const uint16_t* dD, const float* C, const int32_t* row_src,
+                             const float* row_prob, const int32_t* rows_end, int64_t cap,
+                             int64_t inter, uint16_t* dC, float* dp, hipStream_t s) {
+  if (cap <= 0) return hipSuccess;
+  swiglu_bwd_kernel<<<(unsigned)((cap + 3) / 4), 256, 0, s>>>(dD, C, row_src, row_prob, rows_end,
+                                                            cap, inter, dC, dp);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_entry_grad(const float* dp, const int32_t* dst_row, int64_t n,
+                                 float* dprob, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  bwd_entry_grad_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(dp, dst_row, n, dprob);
   return hipGetLastError();
 }
 

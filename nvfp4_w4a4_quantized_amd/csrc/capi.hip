@@ -115,13 +115,13 @@ SpLayout carve_single_pass(void* ws, int64_t T, int64_t H, int64_t I, int32_t k,
   return L;
 }
 
-// Workspace of the backward: the two dgrad tile tables, the router-weight
-// partial sums, dC and the FC1 dgrad rows.
+// Workspace of the backward: the two dgrad tile tables, the wgrads' expert
+// order, dD, dC, the rows' router-weight gradients and the FC1 dgrad rows.
 struct BwdLayout {
   int4* tab2; int4* tab1;   // FC2 / FC1 dgrad tile tables
   int64_t blocks2, blocks1;
-  float* dp_part; int32_t dp_ld;
-  uint16_t* dc; uint16_t* dxr;
+  int32_t* order;
+  uint16_t* dd; uint16_t* dc; float* dp; uint16_t* dxr;
   size_t bytes;
 };
 
@@ -132,9 +132,10 @@ BwdLayout carve_backward(void* ws, int64_t cap, int64_t H, int64_t I, int32_t E)
   L.blocks1 = bwd_dgrad_table_spec(cap, E, 2 * I, H, nullptr).blocks;
   L.tab2 = c.take<int4>((size_t)L.blocks2);
   L.tab1 = c.take<int4>((size_t)L.blocks1);
-  L.dp_ld = (int32_t)bwd_n_tiles(I);
-  L.dp_part = c.take<float>((size_t)(cap * L.dp_ld));
+  L.order = c.take<int32_t>((size_t)E);
+  L.dd = c.take<uint16_t>((size_t)(cap * I));
   L.dc = c.take<uint16_t>((size_t)(cap * 2 * I));
+  L.dp = c.take<float>((size_t)cap);
   L.dxr = c.take<uint16_t>((size_t)(cap * H));
   L.bytes = c.used;
   return L;
@@ -484,28 +485,32 @@ int moe_expert_backward(const uint16_t* dy, const uint16_t* x, int64_t tokens, i
   if (!w1 || !w2 || !dw1 || !dw2 || !expert_offsets || !workspace) return NVFP4_INVALID_ARGUMENT;
   if (rows_cap > 0 && (!fc1_out || !d || !row_src || !row_prob)) return NVFP4_INVALID_ARGUMENT;
   if (tokens > 0 && (!dy || !x || !dx || !dprob || !dst_row)) return NVFP4_INVALID_ARGUMENT;
-  const void* a16[] = {dy, x, d, w1, w2, dx, workspace};
+  const void* a16[] = {dy, x, fc1_out, d, w1, w2, dx, workspace};
   for (const void* p : a16)
     if (p && !aligned(p, 16)) return NVFP4_INVALID_ARGUMENT;
-  const void* a4[] = {fc1_out, dw1, dw2, dprob, row_src, row_prob, dst_row, expert_offsets};
+  const void* a4[] = {dw1, dw2, dprob, row_src, row_prob, dst_row, expert_offsets};
   for (const void* p : a4)
     if (p && !aligned(p, 4)) return NVFP4_INVALID_ARGUMENT;
   if (!aligned(workspace, 256)) return NVFP4_INVALID_ARGUMENT;
+  // every operand the GEMMs read is addressed with 32-bit byte offsets
+  const int64_t tok_bytes = tokens * hidden * 2, c_bytes = rows_cap * 2 * inter * 4;
+  const int64_t dc_bytes = rows_cap * 2 * inter * 2, w_bytes = 2 * inter * hidden * 2;
+  if (tok_bytes >= 0x80000000LL || c_bytes >= 0x80000000LL || dc_bytes >= 0x80000000LL ||
+      w_bytes >= 0x80000000LL)
+    return NVFP4_UNSUPPORTED;
   BwdLayout L = carve_backward(workspace, rows_cap, hidden, inter, num_experts);
   if (workspace_bytes < L.bytes) return NVFP4_WORKSPACE_TOO_SMALL;
-  float* dd_f32 = nullptr;
-  float* dp_rows = nullptr;
   float* dxr_f32 = nullptr;
   if (debug) {
+    if (debug->dd) L.dd = debug->dd;
     if (debug->dc) L.dc = debug->dc;
+    if (debug->dp_rows) L.dp = debug->dp_rows;
     if (debug->dx_rows) L.dxr = debug->dx_rows;
-    dd_f32 = debug->dd;
-    dp_rows = debug->dp_rows;
     dxr_f32 = debug->dx_rows_f32;
-    const void* p16[] = {L.dc, L.dxr};
+    const void* p16[] = {L.dd, L.dc, L.dxr};
     for (const void* p : p16)
       if (!aligned(p, 16)) return NVFP4_INVALID_ARGUMENT;
-    const void* p4[] = {dd_f32, dp_rows, dxr_f32};
+    const void* p4[] = {L.dp, dxr_f32};
     for (const void* p : p4)
       if (p && !aligned(p, 4)) return NVFP4_INVALID_ARGUMENT;
   }
@@ -518,56 +523,57 @@ int moe_expert_backward(const uint16_t* dy, const uint16_t* x, int64_t tokens, i
   // the dgrads' tile tables from the device offsets
   const TileTableSpec t2 = bwd_dgrad_table_spec(rows_cap, num_experts, hidden, inter, L.tab2);
   const TileTableSpec t1 = bwd_dgrad_table_spec(rows_cap, num_experts, 2 * inter, hidden, L.tab1);
-  if (launch_bwd_tables(expert_offsets, num_experts, t2, t1, s) != hipSuccess)
+  if (launch_bwd_tables(expert_offsets, num_experts, t2, t1, L.order, s) != hipSuccess)
     return NVFP4_HIP_ERROR;
   if (mark(1) != hipSuccess) return NVFP4_HIP_ERROR;
-  // FC2 dgrad with the SwiGLU backward: dC and the router-weight partial sums
+  // FC2 dgrad: dD = dYr W2[e] (bf16 rows), then the SwiGLU backward
   BwdGemmArgs f2{};
-  f2.a = BwdOperand{dy, hidden, 0, row_src, 1};
-  f2.b = BwdOperand{w2, inter, hidden * inter, nullptr, 0};
+  f2.a = BwdOperand{dy, hidden, 0, row_src, 1, (uint32_t)tok_bytes};
+  f2.b = BwdOperand{w2, inter, hidden * inter, nullptr, 0, (uint32_t)(hidden * inter * 2)};
   f2.offsets = expert_offsets; f2.num_groups = num_experts;
   f2.m = rows_cap; f2.n = inter; f2.k = hidden; f2.tiles = L.tab2;
-  f2.out_f32 = dd_f32; f2.out_bf16 = L.dc;
-  f2.c = fc1_out; f2.row_src = row_src; f2.row_prob = row_prob;
-  f2.dp_part = L.dp_part; f2.dp_ld = L.dp_ld;
-  if (launch_bwd_gemm(BWD_DGRAD_SWIGLU, f2, L.blocks2, s) != hipSuccess) return NVFP4_HIP_ERROR;
+  f2.out_bf16 = L.dd;
+  if (launch_bwd_gemm(BWD_DGRAD_ROWS, f2, L.blocks2, s) != hipSuccess) return NVFP4_HIP_ERROR;
   if (mark(2) != hipSuccess) return NVFP4_HIP_ERROR;
+  if (launch_swiglu_bwd(L.dd, fc1_out, row_src, row_prob, expert_offsets + num_experts, rows_cap,
+                        inter, L.dc, L.dp, s) != hipSuccess)
+    return NVFP4_HIP_ERROR;
+  if (mark(3) != hipSuccess) return NVFP4_HIP_ERROR;
   // FC2 wgrad: dW2[e] = dYr^T D over the expert's rows
   BwdGemmArgs w2g{};
-  w2g.a = BwdOperand{dy, hidden, 0, row_src, 1};
-  w2g.b = BwdOperand{d, inter, 0, row_src, 0};
-  w2g.offsets = expert_offsets; w2g.num_groups = num_experts;
+  w2g.a = BwdOperand{dy, hidden, 0, row_src, 1, (uint32_t)tok_bytes};
+  w2g.b = BwdOperand{d, inter, 0, nullptr, 0, (uint32_t)(dc_bytes / 2)};
+  w2g.offsets = expert_offsets; w2g.num_groups = num_experts; w2g.order = L.order;
   w2g.m = hidden; w2g.n = inter; w2g.out_f32 = dw2;
   if (launch_bwd_gemm(BWD_WGRAD, w2g, bwd_wgrad_blocks(num_experts, hidden, inter), s) !=
       hipSuccess)
     return NVFP4_HIP_ERROR;
-  if (mark(3) != hipSuccess) return NVFP4_HIP_ERROR;
+  if (mark(4) != hipSuccess) return NVFP4_HIP_ERROR;
   // FC1 dgrad: dXr = dC W1[e] (bf16 rows)
   BwdGemmArgs f1{};
-  f1.a = BwdOperand{L.dc, 2 * inter, 0, nullptr, 0};
-  f1.b = BwdOperand{w1, hidden, 2 * inter * hidden, nullptr, 0};
+  f1.a = BwdOperand{L.dc, 2 * inter, 0, nullptr, 0, (uint32_t)dc_bytes};
+  f1.b = BwdOperand{w1, hidden, 2 * inter * hidden, nullptr, 0, (uint32_t)w_bytes};
   f1.offsets = expert_offsets; f1.num_groups = num_experts;
   f1.m = rows_cap; f1.n = hidden; f1.k = 2 * inter; f1.tiles = L.tab1;
   f1.out_bf16 = L.dxr; f1.out_f32 = dxr_f32;
   if (launch_bwd_gemm(BWD_DGRAD_ROWS, f1, L.blocks1, s) != hipSuccess) return NVFP4_HIP_ERROR;
-  if (mark(4) != hipSuccess) return NVFP4_HIP_ERROR;
+  if (mark(5) != hipSuccess) return NVFP4_HIP_ERROR;
   // FC1 wgrad: dW1[e] = dC^T X over the expert's rows
   BwdGemmArgs w1g{};
-  w1g.a = BwdOperand{L.dc, 2 * inter, 0, nullptr, 0};
-  w1g.b = BwdOperand{x, hidden, 0, row_src, 1};
-  w1g.offsets = expert_offsets; w1g.num_groups = num_experts;
+  w1g.a = BwdOperand{L.dc, 2 * inter, 0, nullptr, 0, (uint32_t)dc_bytes};
+  w1g.b = BwdOperand{x, hidden, 0, row_src, 1, (uint32_t)tok_bytes};
+  w1g.offsets = expert_offsets; w1g.num_groups = num_experts; w1g.order = L.order;
   w1g.m = 2 * inter; w1g.n = hidden; w1g.out_f32 = dw1;
   if (launch_bwd_gemm(BWD_WGRAD, w1g, bwd_wgrad_blocks(num_experts, 2 * inter, hidden), s) !=
       hipSuccess)
     return NVFP4_HIP_ERROR;
-  if (mark(5) != hipSuccess) return NVFP4_HIP_ERROR;
+  if (mark(6) != hipSuccess) return NVFP4_HIP_ERROR;
   // dx: the sum of each token's rows; dprob: each entry's row sum
   if (launch_combine(L.dxr, 1, dst_row, tokens, topk, hidden, dx, s) != hipSuccess)
     return NVFP4_HIP_ERROR;
-  if (launch_bwd_entry_grad(L.dp_part, L.dp_ld, dst_row, tokens * topk, dprob,
-                            expert_offsets + num_experts, rows_cap, dp_rows, s) != hipSuccess)
+  if (launch_bwd_entry_grad(L.dp, dst_row, tokens * topk, dprob, s) != hipSuccess)
     return NVFP4_HIP_ERROR;
-  if (mark(6) != hipSuccess) return NVFP4_HIP_ERROR;
+  if (mark(7) != hipSuccess) return NVFP4_HIP_ERROR;
   return NVFP4_OK;
 }
 

@@ -140,17 +140,18 @@ int single_pass_lds_bytes(int64_t inter);
 hipError_t launch_single_pass(const SinglePassArgs& a, int64_t blocks, hipStream_t s);
 
 // ---- backward.hip ----
-enum { BWD_DGRAD_SWIGLU = 0, BWD_DGRAD_ROWS = 1, BWD_WGRAD = 2 };
+enum { BWD_DGRAD_ROWS = 1, BWD_WGRAD = 2 };
 
 // One bf16 operand of a backward GEMM: row-major, `ld` elements per row; per
 // group (the dgrads' B) at p + g * group_stride.  row_map (nullable) marks
 // the rows: row r is read only if row_map[r] >= 0, and from row row_map[r]
-// when `gather` is set.
+// when `gather` is set (the wgrads always gather through it).
 struct BwdOperand {
   const uint16_t* p;
   int64_t ld, group_stride;
   const int32_t* row_map;
   int32_t gather;
+  uint32_t bytes;             // readable bytes from p (per group: from its base), < 2^31
 };
 
 struct BwdGemmArgs {
@@ -159,26 +160,23 @@ struct BwdGemmArgs {
   int32_t num_groups;
   int64_t m, n, k;            // wgrad: output [G, m, n]; dgrad: n columns, K = k
   const int4* tiles;          // dgrad tile table
-  float* out_f32;             // wgrad output; dgrad: optional fp32 copy (debug)
-  uint16_t* out_bf16;         // dgrad output rows (SwiGLU mode: dC [rows, 2n])
-  const float* c;             // SwiGLU mode: the forward's FC1 output [rows, 2n]
-  const int32_t* row_src;     // SwiGLU mode: padding rows (< 0)
-  const float* row_prob;      // SwiGLU mode: router weights of the rows
-  float* dp_part;             // SwiGLU mode: [rows, dp_ld] per-n-tile row sums
-  int32_t dp_ld;
+  const int32_t* order;       // wgrad: experts, heaviest first
+  float* out_f32;             // wgrad output; dgrad: optional fp32 copy
+  uint16_t* out_bf16;         // dgrad output rows
 };
 
 int bwd_lds_bytes();
 TileTableSpec bwd_dgrad_table_spec(int64_t rows_cap, int32_t num_groups, int64_t k, int64_t n,
                                    int4* table);
 int64_t bwd_wgrad_blocks(int32_t num_groups, int64_t m, int64_t n);
-int64_t bwd_n_tiles(int64_t n);
 hipError_t launch_bwd_tables(const int32_t* offsets, int32_t G, const TileTableSpec& t0,
-                             const TileTableSpec& t1, hipStream_t s);
+                             const TileTableSpec& t1, int32_t* order, hipStream_t s);
 hipError_t launch_bwd_gemm(int mode, const BwdGemmArgs& a, int64_t blocks, hipStream_t s);
-hipError_t launch_bwd_entry_grad(const float* dp_part, int32_t dp_ld, const int32_t* dst_row,
-                                 int64_t n, float* dprob, const int32_t* rows_end, int64_t cap,
-                                 float* dp_rows, hipStream_t s);
+hipError_t launch_swiglu_bwd(const uint16_t* dD, const float* C, const int32_t* row_src,
+                             const float* row_prob, const int32_t* rows_end, int64_t cap,
+                             int64_t inter, uint16_t* dC, float* dp, hipStream_t s);
+hipError_t launch_bwd_entry_grad(const float* dp, const int32_t* dst_row, int64_t n,
+                                 float* dprob, hipStream_t s);
 
 // ---- combine.hip ----
 hipError_t launch_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,

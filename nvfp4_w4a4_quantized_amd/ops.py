@@ -411,22 +411,23 @@ def moe_expert_forward_single_pass(x, topk_idx, topk_prob, num_experts: int, int
 
 
 class BackwardTimer(StageTimer):
-    """Seven HIP events recorded by moe_expert_backward: the dgrad tile
-    tables, FC2 dgrad + SwiGLU backward, FC2 wgrad, FC1 dgrad, FC1 wgrad, and
-    the dx / dprob reductions."""
+    """Eight HIP events recorded by moe_expert_backward: the dgrad tile
+    tables, FC2 dgrad, the SwiGLU backward, FC2 wgrad, FC1 dgrad, FC1 wgrad,
+    and the dx / dprob reductions."""
 
-    NAMES = ("tables", "fc2_dgrad_swiglu", "fc2_wgrad", "fc1_dgrad", "fc1_wgrad", "reduce")
+    NAMES = ("tables", "fc2_dgrad", "swiglu_bwd", "fc2_wgrad", "fc1_dgrad", "fc1_wgrad",
+             "reduce")
 
     def __init__(self):
         L = lib()
-        self.events = (C.c_void_p * 7)()
-        for i in range(7):
+        self.events = (C.c_void_p * 8)()
+        for i in range(8):
             h = C.c_void_p()
             check(L.nvfp4_event_create(C.byref(h)), "nvfp4_event_create")
             self.events[i] = h.value
 
     def close(self):
-        for i in range(7):
+        for i in range(8):
             if self.events[i]:
                 lib().nvfp4_event_destroy(self.events[i])
                 self.events[i] = None
@@ -437,16 +438,16 @@ def moe_expert_backward_workspace_size(rows_cap, hidden, inter, num_experts) -> 
 
 
 def moe_expert_backward(dy, x, fc1_out, d, expert_offsets, row_src, row_prob, dst_row,
-                        w1, w2, workspace=None, debug: bool = False, dd: bool = False,
+                        w1, w2, workspace=None, debug: bool = False,
                         dx_rows_f32: bool = False, timer: BackwardTimer | None = None,
                         out=None):
     """Gradients of the expert layer (straight-through, BF16 GEMMs).
     dy, x: bf16 [T, H]; fc1_out: fp32 [cap, 2I] and d: bf16 [cap, I], the
     forward's FC1 output and FC2 input; the forward's routing arrays; w1 bf16
     [E, 2I, H], w2 bf16 [E, H, I].  Returns dict(dx, dw1, dw2, dprob); with
-    debug=True a second dict of the intermediates (dc, dp_rows, dx_rows, and
-    dd / dx_rows_f32 if asked).  `out`: optional dict of preallocated
-    outputs with those four names."""
+    debug=True a second dict of the intermediates (dd, dc, dp_rows, dx_rows,
+    and dx_rows_f32 if asked).  `out`: optional dict of preallocated outputs
+    with those four names."""
     for t, n in ((dy, "dy"), (x, "x"), (d, "d"), (w1, "w1"), (w2, "w2")):
         _need(t, _BF16_LIKE, n)
     _need(fc1_out, (torch.float32,), "fc1_out")
@@ -477,10 +478,8 @@ def moe_expert_backward(dy, x, fc1_out, d, expert_offsets, row_src, row_prob, ds
     inter_t = None
     if debug:
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
-        inter_t = dict(dc=e((cap, 2 * inter), torch.bfloat16), dp_rows=e(cap, torch.float32),
-                       dx_rows=e((cap, H), torch.bfloat16))
-        if dd:
-            inter_t["dd"] = e((cap, inter), torch.float32)
+        inter_t = dict(dd=e((cap, inter), torch.bfloat16), dc=e((cap, 2 * inter), torch.bfloat16),
+                       dp_rows=e(cap, torch.float32), dx_rows=e((cap, H), torch.bfloat16))
         if dx_rows_f32:
             inter_t["dx_rows_f32"] = e((cap, H), torch.float32)
         dbg = BackwardIntermediates(**{n: t.data_ptr() for n, t in inter_t.items()})
