@@ -311,6 +311,12 @@ int moe_combine(const void* y_rows, int y_rows_dtype, const int32_t* dst_row,
  *                tokens and the requantized D); the weights carry whatever
  *                rule they were quantized with ([4BIT] "Four-Over-Six ...":
  *                weights, activations or both)
+ *   act_scale_domain  outer scale of both activation quantizations
+ *                ([miniTE] §2.3, §5.1): 0 = one per token / routed row (the
+ *                per-token recipe); 1 = one per tensor: x quantized with
+ *                s_g = amax(x) / 2688 for every token (nvfp4_quantize domain 1
+ *                with one group), D with the maximum of amax_d over the routed
+ *                rows; a1_gscale and a2_gscale then hold that value per row
  *   w2           NVFP4 down weights    [E, hidden, inter]
  *                (each row-major or tiled, per its layout member)
  *   workspace    moe_expert_forward_workspace_size() bytes, 256-byte aligned;
@@ -350,6 +356,7 @@ size_t moe_expert_forward_workspace_size(int64_t tokens, int64_t hidden, int64_t
 int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
                        const int32_t* topk_idx, const float* topk_prob, int32_t topk,
                        int32_t num_experts, int32_t align, int32_t act_block_rule,
+                       int32_t act_scale_domain,
                        const nvfp4_weights* w1, const nvfp4_weights* w2, uint16_t* y,
                        void* workspace, size_t workspace_bytes,
                        const nvfp4_moe_intermediates* debug, void* const* stage_events,

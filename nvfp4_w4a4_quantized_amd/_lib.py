@@ -102,7 +102,8 @@ def _load(path):
     L.moe_expert_forward_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
     L.moe_expert_forward.restype = C.c_int
     L.moe_expert_forward.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32,
-                                     C.POINTER(Weights), C.POINTER(Weights), _vp, _vp, C.c_size_t,
+                                     _i32, C.POINTER(Weights), C.POINTER(Weights), _vp, _vp,
+                                     C.c_size_t,
                                      C.POINTER(Intermediates), _vp, _vp]
     L.moe_expert_forward_single_pass_workspace_size.restype = C.c_size_t
     L.moe_expert_forward_single_pass_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]

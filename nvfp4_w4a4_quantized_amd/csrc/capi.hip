@@ -45,6 +45,8 @@ struct MoeLayout {
   uint8_t* a2c; uint8_t* a2s; float* a2g;
   uint16_t* y_rows;
   int4* tab1; int4* tab2;   // FC1 / FC2 tile tables
+  int32_t* bounds;          // per-tensor activation scale: the reduction's row range
+  float* tamax;             // per-tensor activation scale: amax of x [0], of D [1]
   size_t bytes;
 };
 
@@ -78,6 +80,8 @@ MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_
   L.y_rows = c.take<uint16_t>((size_t)(cap * H));
   L.tab1 = c.take<int4>((size_t)gemm_grid_blocks(moe_gemm_shape(cap, H, I, E, true), true));
   L.tab2 = c.take<int4>((size_t)gemm_grid_blocks(moe_gemm_shape(cap, H, I, E, false), false));
+  L.bounds = c.take<int32_t>(2);
+  L.tamax = c.take<float>(2);
   L.bytes = c.used;
   return L;
 }
@@ -343,12 +347,13 @@ size_t moe_expert_forward_workspace_size(int64_t tokens, int64_t hidden, int64_t
 int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter,
                        const int32_t* topk_idx, const float* topk_prob, int32_t topk,
                        int32_t num_experts, int32_t align, int32_t act_block_rule,
-                       const nvfp4_weights* w1,
+                       int32_t act_scale_domain, const nvfp4_weights* w1,
                        const nvfp4_weights* w2, uint16_t* y, void* workspace,
                        size_t workspace_bytes, const nvfp4_moe_intermediates* debug,
                        void* const* stage_events, void* stream) {
   if (!route_args_ok(tokens, topk, num_experts, align)) return NVFP4_INVALID_ARGUMENT;
   if (act_block_rule < 0 || act_block_rule > 2) return NVFP4_INVALID_ARGUMENT;
+  if (act_scale_domain != 0 && act_scale_domain != 1) return NVFP4_INVALID_ARGUMENT;
   if (hidden < 128 || hidden % 128 != 0 || inter < 128 || inter % 128 != 0)
     return NVFP4_UNSUPPORTED;
   if (hidden > kMaxK || inter > kMaxK) return NVFP4_UNSUPPORTED;
@@ -432,6 +437,13 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   ra.tables[1] = gemm_tile_table_spec(g2, false, L.tab2);
   ra.num_tables = 2;
   ra.workspace = L.route_ws_i; ra.block_rule = act_block_rule;
+  if (act_scale_domain == 1 && tokens > 0) {
+    // one outer scale for the whole x ([miniTE] §2.3 per-tensor scaling)
+    if ((e = launch_tensor_amax(x, tokens, hidden, hidden, L.bounds,
+                                reinterpret_cast<uint32_t*>(L.tamax), s)) != hipSuccess)
+      return NVFP4_HIP_ERROR;
+    ra.tok_amax = L.tamax;
+  }
   if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if (debug && (debug->a1_codes || debug->a1_scales)) {   // the permuted rows, for inspection
     if ((e = launch_gather_rows(L.tokc, L.toks, L.row_src, L.offsets + num_experts, cap, hidden,
@@ -446,6 +458,14 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   // quantize the whole capacity; rows past the end are ignored downstream)
   QuantRowsArgs q{L.d, cap, inter, inter, 1, L.amax_d, nullptr, 0, L.a2c, L.a2s, L.a2g,
                   act_block_rule};
+  if (act_scale_domain == 1) {
+    // one outer scale for all routed rows of D: the maximum of their amax
+    if ((e = launch_rows_amax(L.amax_d, L.offsets + num_experts, cap, L.tamax + 1, s)) !=
+        hipSuccess)
+      return NVFP4_HIP_ERROR;
+    q.amax_kind = 3;
+    q.amax_in = L.tamax + 1;
+  }
   if ((e = launch_quantize_rows(q, s)) != hipSuccess) return NVFP4_HIP_ERROR;
   if ((e = mark(3)) != hipSuccess) return NVFP4_HIP_ERROR;
   // a6: FC2

@@ -15,8 +15,9 @@ namespace nvfp4 {
 int blocks_per_lane(int64_t k);
 
 // ---- quantize.hip ----
-// amax source of a row: reduce |x| (kind 0), amax_in[row] (kind 1), or
-// group_amax[group(row)] (kind 2, groups given by offsets).
+// amax source of a row: reduce |x| (kind 0), amax_in[row] (kind 1),
+// group_amax[group(row)] (kind 2, groups given by offsets), or amax_in[0]
+// for every row (kind 3, one outer scale per tensor, written per row).
 struct QuantRowsArgs {
   const uint16_t* x; int64_t rows; int64_t k; int64_t ld_x;
   int amax_kind; const float* amax_in; const int32_t* group_offsets; int32_t num_groups;
@@ -30,6 +31,12 @@ hipError_t launch_quantize_tiles2d(const QuantRowsArgs& a, hipStream_t s);
 hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
                              const int32_t* group_offsets, int32_t num_groups,
                              uint32_t* amax_bits, hipStream_t s);
+// amax over all rows of x into amax_bits[0] (float bits); bounds: int32[2] scratch.
+hipError_t launch_tensor_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
+                              int32_t* bounds, uint32_t* amax_bits, hipStream_t s);
+// out[0] = max of amax_rows[r] over r < min(cap, *rows_end).
+hipError_t launch_rows_amax(const float* amax_rows, const int32_t* rows_end, int64_t cap,
+                            float* out, hipStream_t s);
 // gscale[g] = amax[g] / 2688 (in place allowed: amax may alias gscale).
 hipError_t launch_group_finalize(const float* amax, float* gscale, int32_t num_groups,
                                  int rule, hipStream_t s);
@@ -59,6 +66,7 @@ struct RouteArgs {
   // token row_src[r]).
   uint8_t* tok_codes; uint8_t* tok_scales; float* tok_gscale;
   uint8_t* entry_rank;  // gather mode: [tokens * topk] scratch (rank inside the chunk)
+  const float* tok_amax; // nullable: one amax for every token (per-tensor outer scale)
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // Permuted rows r < *rows_end (device) copied from the token-major rows of

@@ -72,6 +72,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
     amax = __uint_as_float(wave_max_u32(mbits) << 16);
   } else if (a.amax_kind == 1) {
     amax = a.amax_in[row];
+  } else if (a.amax_kind == 3) {
+    amax = a.amax_in[0];
   } else {
     int g = find_group(a.group_offsets, a.num_groups, row);
     amax = a.amax_in[g];
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(QuantRowsArgs a) {
   const uint64_t total = (uint64_t)a.rows * nb;
   const uint32_t row = (uint32_t)(i < total ? i : total - 1) / nb;
   int g = 0;
-  if (a.amax_kind != 1) {
+  if (a.amax_kind == 2) {
     // a wave's rows are consecutive: one uniform search from its first row,
     // then lanes past a group boundary step forward
     g = find_group(a.group_offsets, a.num_groups, (int64_t)__builtin_amdgcn_readfirstlane(row));
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(QuantRowsArgs a) {
   }
   if (i >= total) return;
   const uint32_t b = (uint32_t)i - row * nb;
-  const float amax = a.amax_kind == 1 ? a.amax_in[row] : a.amax_in[g];
+  const float amax = a.amax_kind == 1 ? a.amax_in[row] : a.amax_in[a.amax_kind == 3 ? 0 : g];
   const float s_g = outer_scale(amax, a.block_rule);
   const uint16_t* p = a.x + (int64_t)row * a.ld_x + (int64_t)b * 16;
   const u32x4_t u0 = load_stream16(p);
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) void quantize_blocks_kernel(QuantRowsArgs a) {
   const uint2 c = quantize_block16(w, s_g, a.block_rule, &sb);
   *reinterpret_cast<uint2*>(a.codes + (int64_t)row * (a.k / 2) + (int64_t)b * 8) = c;
   a.scales[(int64_t)row * (a.k / 16) + b] = (uint8_t)sb;
-  if (a.amax_kind == 1 && b == 0) a.gscale[row] = s_g;
+  if ((a.amax_kind == 1 || a.amax_kind == 3) && b == 0) a.gscale[row] = s_g;
 }
 
 // 16x16 two-dimensional blocks (per-group outer scale from amax_in): each
@@ -255,6 +257,46 @@ hipError_t launch_group_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t
     case 16: group_amax_kernel<16><<<grid, block, 0, s>>>(x, k, ld_x, off, num_groups, amax_bits); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// The tensor's amax for one outer scale per tensor: bounds = {0, rows} for
+// the group reduction over all rows.
+__global__ void tensor_bounds_kernel(int32_t* bounds, int32_t rows) {
+  if (threadIdx.x == 0) { bounds[0] = 0; bounds[1] = rows; }
+}
+
+hipError_t launch_tensor_amax(const uint16_t* x, int64_t rows, int64_t k, int64_t ld_x,
+                              int32_t* bounds, uint32_t* amax_bits, hipStream_t s) {
+  tensor_bounds_kernel<<<1, 64, 0, s>>>(bounds, (int32_t)rows);
+  return launch_group_amax(x, rows, k, ld_x, bounds, 1, amax_bits, s);
+}
+
+// out[0] = max of amax_rows[r] over r < min(cap, *rows_end) (0 if none): one
+// workgroup, each thread a strided share, then a fixed-order reduction.
+__global__ __launch_bounds__(1024) void rows_amax_kernel(const float* amax_rows,
+                                                         const int32_t* rows_end, int64_t cap,
+                                                         float* out) {
+  __shared__ uint32_t wm[16];
+  const int64_t n = cap < (int64_t)*rows_end ? cap : (int64_t)*rows_end;
+  uint32_t m = 0u;
+  for (int64_t r = threadIdx.x; r < n; r += 1024) {
+    const uint32_t v = __float_as_uint(amax_rows[r]);   // amax >= 0: bits order as values
+    m = m > v ? m : v;
+  }
+  m = wave_max_u32(m);
+  if ((threadIdx.x & (kWave - 1)) == 0) wm[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0u;
+    for (int i = 0; i < 16; ++i) t = t > wm[i] ? t : wm[i];
+    out[0] = __uint_as_float(t);
+  }
+}
+
+hipError_t launch_rows_amax(const float* amax_rows, const int32_t* rows_end, int64_t cap,
+                            float* out, hipStream_t s) {
+  rows_amax_kernel<<<1, 1024, 0, s>>>(amax_rows, rows_end, cap, out);
   return hipGetLastError();
 }
 

@@ -335,17 +335,24 @@ __device__ __forceinline__ void load_token_row(const uint16_t* xr, int nblocks, 
 }
 
 // One token of the wave's TPW, quantized in registers (row amax, block
-// scales, codes): the lane's blocks lane + 64 i.
+// scales, codes): the lane's blocks lane + 64 i.  amax_in (nullable): the
+// tensor's amax, used instead of the row's (one outer scale per tensor).
 template <int BPL>
 __device__ __forceinline__ float quantize_token_regs(const uint32_t (&w)[BPL][8], int rule,
-                                                     uint2 (&codes)[BPL], uint32_t (&sbytes)[BPL]) {
-  uint32_t m = 0u;
+                                                     const float* amax_in, uint2 (&codes)[BPL],
+                                                     uint32_t (&sbytes)[BPL]) {
+  float amax;
+  if (amax_in) {
+    amax = *amax_in;
+  } else {
+    uint32_t m = 0u;
 #pragma unroll
-  for (int i = 0; i < BPL; ++i) {
-    const uint32_t mi = bf16_absmax_bits(w[i]);
-    m = m > mi ? m : mi;
+    for (int i = 0; i < BPL; ++i) {
+      const uint32_t mi = bf16_absmax_bits(w[i]);
+      m = m > mi ? m : mi;
+    }
+    amax = __uint_as_float(wave_max_u32(m) << 16);
   }
-  const float amax = __uint_as_float(wave_max_u32(m) << 16);
   const float s_g = outer_scale(amax, rule);
 #pragma unroll
   for (int i = 0; i < BPL; ++i) codes[i] = quantize_block16(w[i], s_g, rule, &sbytes[i]);
@@ -398,7 +405,7 @@ __device__ __forceinline__ void quantize_token_wave(const RouteArgs& a, int64_t 
 #endif
   uint2 codes[BPL];
   uint32_t sbytes[BPL];
-  const float s_g = quantize_token_regs<BPL>(w[0], a.block_rule, codes, sbytes);
+  const float s_g = quantize_token_regs<BPL>(w[0], a.block_rule, a.tok_amax, codes, sbytes);
   store_token_row<BPL>(a.tok_codes + t * (H / 2), a.tok_scales + t * (H / 16), nblocks, lane,
                        codes, sbytes);
   if (lane == 0) a.tok_gscale[t] = s_g;
@@ -679,7 +686,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
     uint32_t sbytes[BPL];
     float s_g = tok_sg[ti];
     if (a.x) {
-      s_g = quantize_token_regs<BPL>(w[ti], a.block_rule, codes, sbytes);
+      s_g = quantize_token_regs<BPL>(w[ti], a.block_rule, a.tok_amax, codes, sbytes);
       // gather mode: the token's one quantized row (the GEMM reads it through
       // row_src); otherwise a copy per destination row below
       if (a.tok_codes) {

@@ -285,9 +285,10 @@ def moe_expert_forward(x, topk_idx, topk_prob, num_experts: int, inter: int,
                        w1: NvFp4Weights, w2: NvFp4Weights, align: int = 1, workspace=None,
                        debug: bool = False, fc1_out: bool = False, y_rows_f32: bool = False,
                        timer: StageTimer | None = None, y=None, act_block_rule: int = 0,
-                       library=None):
+                       act_scale_domain: int = 0, library=None):
     """The whole expert layer.  Returns y (bf16 [T, H]); with debug=True also a
     dict of the intermediates (allocated here, written by the library).
+    act_scale_domain: 0 one activation outer scale per token, 1 per tensor.
     `library`: the loaded library to call (release build by default)."""
     L = library if library is not None else lib()
     _need(x, _BF16_LIKE, "x")
@@ -321,7 +322,8 @@ def moe_expert_forward(x, topk_idx, topk_prob, num_experts: int, inter: int,
         dbg = Intermediates(**{n: t.data_ptr() for n, t in inter_t.items()})
     ev = timer.events if timer is not None else None
     check(L.moe_expert_forward(ptr(x), T, H, inter, ptr(topk_idx), ptr(topk_prob), k,
-                                   num_experts, align, act_block_rule, C.byref(w1.c_struct()),
+                                   num_experts, align, act_block_rule, act_scale_domain,
+                                   C.byref(w1.c_struct()),
                                    C.byref(w2.c_struct()), ptr(y), ptr(workspace),
                                    workspace.numel(), C.byref(dbg) if dbg is not None else None,
                                    C.cast(ev, C.c_void_p) if ev is not None else None,

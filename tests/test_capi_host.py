@@ -125,18 +125,24 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     # expert layer: hidden not a multiple of 128, missing weights
     from nvfp4_w4a4_quantized_amd._lib import Weights
     w = Weights(0x1000, 0x1000, 0x1000)
-    assert L.moe_expert_forward(fake, 8, 200, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(w),
+    assert L.moe_expert_forward(fake, 8, 200, 128, fake, fake, 2, 4, 1, 0, 0, C.byref(w), C.byref(w),
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == UNSUPPORTED
-    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, None, C.byref(w),
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, 0, None, C.byref(w),
                                 fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
-    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(w),
-                                fake, C.c_void_p(0x10000), 16, None, None, None) == WS_SMALL
-    # unknown activation block rule
-    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 5, C.byref(w), C.byref(w),
-                                fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, 0, C.byref(w),
+                                C.byref(w), fake, C.c_void_p(0x10000), 16, None, None,
+                                None) == WS_SMALL
+    # unknown activation block rule, unknown activation scale domain
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 5, 0, C.byref(w),
+                                C.byref(w), fake, C.c_void_p(0x10000), 1 << 30, None, None,
+                                None) == INVALID
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, 2, C.byref(w),
+                                C.byref(w), fake, C.c_void_p(0x10000), 1 << 30, None, None,
+                                None) == INVALID
     wbad = Weights(0x1000, 0x1000, 0x1000, 3)   # unknown layout
-    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, C.byref(w), C.byref(wbad),
-                                fake, C.c_void_p(0x10000), 1 << 30, None, None, None) == INVALID
+    assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, 0, C.byref(w),
+                                C.byref(wbad), fake, C.c_void_p(0x10000), 1 << 30, None, None,
+                                None) == INVALID
 
 
 def test_noalloc_permute_rejects_before_any_device_call(L):

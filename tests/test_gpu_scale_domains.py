@@ -1,7 +1,8 @@
 """GPU parity of the extra outer-scale domains through the C ABI: 16x16
 two-dimensional weight blocks (scale domain 2) and the per-tensor scale (one
 group over all rows), bit for bit against the oracle; a layer run on 2D
-weights against the oracle layer on the same weights."""
+weights against the oracle layer on the same weights; the layer with one
+activation outer scale per tensor as a replay chain."""
 import numpy as np
 import pytest
 import torch
@@ -85,3 +86,64 @@ def test_layer_on_2d_weights():
     b = bf16_bits_to_f32(yo).astype(np.float64)
     rel = np.linalg.norm(a - b) / np.linalg.norm(b)
     assert rel < 1e-2, rel
+
+
+@pytest.mark.parametrize("wid,align,rule", [(0, 16, 0), (3, 1, 0), (0, 1, 1)])
+def test_layer_per_tensor_activation_scale(wid, align, rule):
+    """moe_expert_forward with one activation outer scale per tensor
+    (act_scale_domain 1), as a replay chain against the oracle: the routed A1
+    rows are the oracle's per-tensor quantization of x (domain 1, one group
+    over all tokens) bit for bit, FC1 and FC2 every element within the GEMM
+    tolerance, A2 the oracle's per-tensor quantization of the GPU's D with the
+    maximum of its row amax bit for bit, y the combine of the FC2 rows."""
+    from gpu_util import assert_gemm_full, bf16_ulp
+    from nvfp4_w4a4_quantized_amd.ops import NvFp4Weights, moe_expert_forward
+    w, W1, W2 = moe_case(wid)
+    T = w.tokens
+    say("per-tensor activation scale layer", w.name, "align", align, "rule", rule)
+    wq = [NvFp4Weights(dev(W[0]), dev(W[1]), dev(W[2])) for W in (W1, W2)]
+    y, it = moe_expert_forward(dev_bf16(w.x), dev(w.topk_idx), dev(w.topk_prob), w.experts,
+                               w.inter, wq[0], wq[1], align=align, debug=True, fc1_out=True,
+                               y_rows_f32=True, act_block_rule=rule, act_scale_domain=1)
+    torch.cuda.synchronize()
+    y = host(y)
+    it = {k: host(v) for k, v in it.items()}
+    off = it["expert_offsets"]
+    R = int(off[-1])
+    rs = it["row_src"][:R]
+    routed = rs >= 0
+    # A1: the tokens' per-tensor quantization, permuted
+    tc, ts, tg = O.quantize(w.x, domain=1, group_offsets=np.array([0, T], np.int32), rule=rule)
+    _same(it["a1_codes"][:R][routed], tc[rs[routed]], "A1 codes")
+    _same(it["a1_scales"][:R][routed], ts[rs[routed]], "A1 scales")
+    assert not it["a1_codes"][:R][~routed].any() and not it["a1_scales"][:R][~routed].any()
+    _same(it["a1_gscale"][:R][routed], np.full(routed.sum(), tg[0], np.float32), "A1 outer scale")
+    A1 = (it["a1_codes"], it["a1_scales"], it["a1_gscale"])
+    C = it["fc1_out"][:R]
+    assert_gemm_full(C, A1, W1, off, "FC1 (per-tensor A1)")
+    D = it["d"][:R]
+    dref, _ = O.swiglu(C, it["row_prob"][:R])
+    dv = bf16_bits_to_f32(D).astype(np.float64)
+    rv = bf16_bits_to_f32(dref).astype(np.float64)
+    assert np.all(np.abs(dv - rv) <= bf16_ulp(rv) * 1.0001 + 1e-40), "SwiGLU D"
+    amax = it["amax_d"][:R]
+    assert np.array_equal(amax, np.abs(bf16_bits_to_f32(D)).max(axis=1)), "amax_d"
+    # A2: one scale from the largest row amax
+    tamax = np.array([amax.max() if R else 0.0], np.float32)
+    c2, s2, g2 = O.quantize(D, domain=1, group_offsets=np.array([0, R], np.int32),
+                            amax_in=tamax, rule=rule)
+    _same(it["a2_codes"][:R], c2, "A2 codes")
+    _same(it["a2_scales"][:R], s2, "A2 scales")
+    _same(it["a2_gscale"][:R], np.full(R, g2[0], np.float32), "A2 outer scale")
+    A2 = (it["a2_codes"], it["a2_scales"], it["a2_gscale"])
+    Y = it["y_rows_f32"][:R]
+    assert_gemm_full(Y, A2, W2, off, "FC2 (per-tensor A2)")
+    ycomb = bf16_bits_to_f32(O.combine(Y, it["dst_row"])).astype(np.float64)
+    yv = bf16_bits_to_f32(y).astype(np.float64)
+    absum = np.zeros_like(yv)
+    dst = it["dst_row"]
+    for j in range(dst.shape[1]):
+        ok = dst[:, j] >= 0
+        absum[ok] += np.abs(Y[dst[ok, j]])
+    tol = absum * 2.0 ** -20 + bf16_ulp(ycomb) * 1.0001 + 1e-30
+    assert np.all(np.abs(yv - ycomb) <= tol), "combine"
