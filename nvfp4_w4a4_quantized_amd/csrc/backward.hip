@@ -37,6 +37,7 @@
 // kernel writes), so the experts with the most rows start first and the
 // light ones fill in behind them.
 #include <algorithm>
+#include <type_traits>
 
 #include "gemm_common.h"
 #include "launch.h"
@@ -47,32 +48,49 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int PA_KC = BK + 8;                 // A [m][k]
-constexpr int PKM = 256 + 32;                 // A [k][m] and B [k][n]
-constexpr int A_BYTES = BM * PA_KC * 2;       // == BK * PKM * 2
-constexpr int B_BYTES = BK * PKM * 2;
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;    // 147456
-static_assert(A_BYTES == BK * PKM * 2, "A stage");
+constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int NSTAGES = 4;                    // LDS ring: stages s .. s + 3 in flight
+constexpr int REGION = 16384;                 // one operand's stage (256 x 32 bf16)
+constexpr int STAGE_BYTES = 2 * REGION;       // A | B
+constexpr int LDS_BYTES = NSTAGES * STAGE_BYTES;   // 131072
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
 }
 
-// The matrix-core operand of a K-major LDS tile s[k][c] (row pitch `pitch`):
-// lane l receives column c0 + l % 32, rows k0 + 8 (l / 32) + 0..7.
-__device__ __forceinline__ bf16x8_t frag_km(const uint16_t* s, int pitch, int c0, int k0,
-                                            int lane) {
-  const uint16_t* p = s + (k0 + (lane >> 5) * 8 + ((lane & 15) >> 2)) * pitch + c0 +
-                      ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
-  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p);
-  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p + 4 * pitch));
+// LDS tiles are unpadded and XOR-swizzled in 16-byte chunks, because a
+// direct-to-LDS load writes one contiguous KiB per wave instruction:
+//   K-major [32 k][256 columns] (512-byte rows): chunk c of row r at c ^ 4 (r % 4)
+//   K-contiguous [256 rows][32 k] (64-byte rows): chunk c of row r at c ^ (r / 4) % 4
+// The four rows of a transposing read and the eight rows of a 16-byte
+// fragment read then fall on distinct banks.
+__device__ __forceinline__ int swz_km(int r, int c) { return c ^ (4 * (r & 3)); }
+__device__ __forceinline__ int swz_kc(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// The matrix-core operand of a K-major tile: lane l receives column
+// c0 + l % 32, rows k0 + 8 (l / 32) + 0..7 (two transposing reads; each lane
+// of a 16-lane group receives one column of the 4 x 16 block the group reads).
+__device__ __forceinline__ bf16x8_t frag_km(const uint16_t* s, int c0, int k0, int lane) {
+  const int r = k0 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+  const int col = c0 + ((lane >> 4) & 1) * 16 + 4 * (lane & 3);
+  const int off = 8 * swz_km(r, col >> 3) + (col & 7);     // rows r and r + 4 share it
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s + r * 256 + off));
+  const bf16x4_t hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(s + (r + 4) * 256 + off));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The operand of a K-contiguous tile: lane l receives row r0 + l % 32,
+// k = k0 + 8 (l / 32) + 0..7.
+__device__ __forceinline__ bf16x8_t frag_kc(const uint16_t* s, int r0, int k0, int lane) {
+  const int r = r0 + (lane & 31);
+  const int c = (k0 >> 3) + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_t*>(s + r * 32 + 8 * swz_kc(r, c));
 }
 
 // Loads go through buffer resources: an offset at or past the resource's
@@ -103,11 +121,15 @@ __device__ __forceinline__ float bl4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // Four waves, each a 128 x 128 quadrant (4 x 4 blocks of 32 x 32).
 template <int MODE, int GATHER, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
-  extern __shared__ __align__(16) uint8_t smem[];
+  // the LDS ring: one array per slot, so that the compiler sees that a load
+  // into one slot does not write the slot being read (else it waits for
+  // every load in flight before each read)
+  __shared__ __align__(16) uint8_t S0[STAGE_BYTES];
+  __shared__ __align__(16) uint8_t S1[STAGE_BYTES];
+  __shared__ __align__(16) uint8_t S2[STAGE_BYTES];
+  __shared__ __align__(16) uint8_t S3[STAGE_BYTES];
   constexpr bool WG = MODE == BWD_WGRAD;
-  constexpr int NT = 64 * NW;                 // threads
-  constexpr int PPT = BM * BK / 8 / NT;       // 16-byte pieces per thread and operand
-  constexpr int RKC = NT / 8, RKM = NT / 32;  // row steps of the K-contiguous / K-major pieces
+  static_assert(NW == 4 || NW == 8, "waves per workgroup");
   constexpr int WNC = 2 * BN / NW;            // columns of a wave (2 waves along M)
   constexpr int JB = WNC / 32;                // its 32-column blocks
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -140,20 +162,31 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
   const uint16_t* Ab = a.a.p;
   const uint16_t* Bb = a.b.p + (WG ? 0 : (int64_t)g * a.b.group_stride);
 
-  auto sA = [&](int buf) { return reinterpret_cast<uint16_t*>(smem + buf * STAGE_BYTES); };
-  auto sB = [&](int buf) {
-    return reinterpret_cast<uint16_t*>(smem + buf * STAGE_BYTES + A_BYTES);
-  };
   const __amdgpu_buffer_rsrc_t ar = rsrc(Ab, a.a.bytes);
   const __amdgpu_buffer_rsrc_t br = rsrc(Bb, a.b.bytes);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t nst = (k1 - k0 + BK - 1) / BK;           // K stages
 
-  // K-contiguous A (dgrads): piece j of a thread is row tid / 8 + RKC j, k
-  // (tid % 8) * 8 of the stage; the rows (and their gather) are fixed.
-  uint32_t aoff[PPT];
+  // ---- direct-to-LDS loads.  A stage is 32 wave instructions of one KiB
+  // (16 for A, 16 for B); wave w issues instructions w + NW q.  Lane L of an
+  // instruction writes LDS bytes 16 L of its KiB, so it loads the global
+  // chunk that the swizzle puts there.
+  constexpr int QN = 16 / NW;                   // instructions per operand and wave
+  // K-major (B; A in the wgrads): instruction i holds rows 2i and 2i + 1 of
+  // the stage; the lane's chunk is the same for all of its instructions.
+  const int km_half = lane >> 5;
+  const int km_chunk = (lane & 31) ^ (4 * ((2 * wave_u + km_half) & 3));
+  const int64_t bcol = n0 + 8 * km_chunk, acol = m0 + 8 * km_chunk;
+  const bool bcol_ok = bcol < a.n, acol_ok = acol < mlim;
+  auto km_row = [&](int q) { return 2 * (wave_u + NW * q) + km_half; };
+  // K-contiguous A (dgrads): instruction i holds rows 16 i .. 16 i + 15, the
+  // lane row 16 i + L / 4; its rows (and their gather) are fixed for the tile.
+  const int kc_chunk = (lane & 3) ^ ((lane >> 4) & 3);
+  uint32_t aoff[QN];
   if constexpr (!WG) {
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int64_t r = m0 + tid / 8 + RKC * j;
+    for (int q = 0; q < QN; ++q) {
+      const int64_t r = m0 + 16 * (wave_u + NW * q) + (lane >> 2);
       bool ok = r < mlim;
       int64_t src = r;
       if (ok && a.a.row_map) {
@@ -161,50 +194,56 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
         ok = t >= 0;
         if (a.a.gather) src = t;
       }
-      aoff[j] = ok ? (uint32_t)((src * a.a.ld + (tid % 8) * 8) * 2) : kNone;
+      aoff[q] = ok ? (uint32_t)((src * a.a.ld + 8 * kc_chunk) * 2) : kNone;
     }
   }
-  // K-major pieces (A in the wgrads, B always): rows tid / 32 + RKM j of the
-  // stage, 8 columns at (tid % 32) * 8.
-  const int64_t acol = m0 + (tid % 32) * 8;
-  const int64_t bcol = n0 + (tid % 32) * 8;
-  const bool acol_ok = acol < mlim, bcol_ok = bcol < a.n;
-
-  // the gathered rows of a stage (clamped to the group's last row; rows past
-  // it are masked where the data loads use them)
-  auto load_idx = [&](int64_t kk, int32_t (&ix)[PPT]) {
+  auto slot_ptr = [&](auto u_c) -> uint8_t* {
+    constexpr int U = decltype(u_c)::value;
+    if constexpr (U == 0) return S0;
+    else if constexpr (U == 1) return S1;
+    else if constexpr (U == 2) return S2;
+    else return S3;
+  };
+  // the gathered rows of stage st (clamped to the group's last row; rows past
+  // it are masked where the loads use them)
+  auto load_idx = [&](int64_t st, int32_t (&ix)[QN]) {
     if constexpr (GATHER != 0) {
       const int32_t* map = GATHER == 1 ? a.a.row_map : a.b.row_map;
+      const int64_t kk = k0 + st * BK;
 #pragma unroll
-      for (int j = 0; j < PPT; ++j)
-        ix[j] = map[std::min<int64_t>(kk + tid / 32 + RKM * j, k1 - 1)];
+      for (int q = 0; q < QN; ++q) ix[q] = map[std::min<int64_t>(kk + km_row(q), k1 - 1)];
     }
   };
-  auto load = [&](int64_t kk, const int32_t (&ix)[PPT], u32x4_t (&ra)[PPT],
-                  u32x4_t (&rb)[PPT]) {
+  // stage st into ring slot U = st % 4; stages past the last read nothing
+  // and write zeros (the loads stay unconditional, so every wait below
+  // counts the same instructions)
+  auto dma = [&](auto u_c, int64_t st, const int32_t (&ix)[QN]) {
+    uint8_t* sbase = slot_ptr(u_c);
+    const bool live = st < nst;
+    const int64_t kk = k0 + st * BK;
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      const int64_t kr = kk + tid / 32 + RKM * j;
+    for (int q = 0; q < QN; ++q) {
+      const int i = wave_u + NW * q;
+      uint32_t off;
       if constexpr (!WG) {
-        ra[j] = bl16(ar, aoff[j] + (uint32_t)(kk * 2));
+        off = live && aoff[q] != kNone ? aoff[q] + (uint32_t)(kk * 2) : kNone;
       } else {
-        const int64_t src = kr < k1 ? (GATHER == 1 ? (int64_t)ix[j] : kr) : -1;
-        ra[j] = bl16(ar, src >= 0 && acol_ok ? (uint32_t)((src * a.a.ld + acol) * 2) : kNone);
+        const int64_t kr = kk + km_row(q);
+        const int64_t src = kr < k1 ? (GATHER == 1 ? (int64_t)ix[q] : kr) : -1;
+        off = live && src >= 0 && acol_ok ? (uint32_t)((src * a.a.ld + acol) * 2) : kNone;
       }
-      const int64_t srb = kr < k1 ? (GATHER == 2 ? (int64_t)ix[j] : kr) : -1;
-      rb[j] = bl16(br, srb >= 0 && bcol_ok ? (uint32_t)((srb * a.b.ld + bcol) * 2) : kNone);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_t*)(sbase + i * 1024), 16, (int)off,
+                                               0, 0, 0);
     }
-  };
-  auto store = [&](int buf, const u32x4_t (&ra)[PPT], const u32x4_t (&rb)[PPT]) {
-    uint16_t* sa = sA(buf);
-    uint16_t* sb = sB(buf);
 #pragma unroll
-    for (int j = 0; j < PPT; ++j) {
-      if constexpr (!WG)
-        *reinterpret_cast<u32x4_t*>(sa + (tid / 8 + RKC * j) * PA_KC + (tid % 8) * 8) = ra[j];
-      else
-        *reinterpret_cast<u32x4_t*>(sa + (tid / 32 + RKM * j) * PKM + (tid % 32) * 8) = ra[j];
-      *reinterpret_cast<u32x4_t*>(sb + (tid / 32 + RKM * j) * PKM + (tid % 32) * 8) = rb[j];
+    for (int q = 0; q < QN; ++q) {
+      const int i = wave_u + NW * q;
+      const int64_t kr = kk + km_row(q);
+      const int64_t src = kr < k1 ? (GATHER == 2 ? (int64_t)ix[q] : kr) : -1;
+      const uint32_t off =
+          live && src >= 0 && bcol_ok ? (uint32_t)((src * a.b.ld + bcol) * 2) : kNone;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void_t*)(sbase + REGION + i * 1024), 16,
+                                               (int)off, 0, 0, 0);
     }
   };
 
@@ -220,24 +259,19 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
   // 32-row blocks wholly past the tile's rows take no matrix work
   const int64_t vrows = mlim - (m0 + wm * 128);
   const int nvb = vrows <= 0 ? 0 : (vrows >= 128 ? 4 : (int)((vrows + 31) / 32));
-  auto compute = [&](int buf) {
-    const uint16_t* la = sA(buf);
-    const uint16_t* lb = sB(buf);
+  auto compute = [&](auto u_c) {
+    const uint16_t* la = reinterpret_cast<const uint16_t*>(slot_ptr(u_c));
+    const uint16_t* lb = reinterpret_cast<const uint16_t*>(slot_ptr(u_c) + REGION);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8_t fb[JB];
 #pragma unroll
-      for (int j = 0; j < JB; ++j) fb[j] = frag_km(lb, PKM, wn * WNC + j * 32, kk * 16, lane);
+      for (int j = 0; j < JB; ++j) fb[j] = frag_km(lb, wn * WNC + j * 32, kk * 16, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (i >= nvb) break;
-        bf16x8_t fa;
-        if constexpr (WG) {
-          fa = frag_km(la, PKM, wm * 128 + i * 32, kk * 16, lane);
-        } else {
-          const int row = wm * 128 + i * 32 + (lane & 31);
-          fa = *reinterpret_cast<const bf16x8_t*>(la + row * PA_KC + kk * 16 + 8 * (lane >> 5));
-        }
+        const bf16x8_t fa = WG ? frag_km(la, wm * 128 + i * 32, kk * 16, lane)
+                               : frag_kc(la, wm * 128 + i * 32, kk * 16, lane);
 #pragma unroll
         for (int j = 0; j < JB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
@@ -245,29 +279,67 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
     }
   };
 
-  // ---- main loop: stage s computes from LDS buffer s % 2 while the loads of
-  // stage s + 1 are in flight into registers (and, for a gathered operand,
-  // the rows of stage s + 2); the loads are unconditional, so the wait before
-  // the LDS store counts only them.
-  const int64_t nst = (k1 - k0 + BK - 1) / BK;
-  u32x4_t ra[PPT], rb[PPT];
-  int32_t ix[PPT];
+  // ---- main loop: stages st + 1 .. st + 3 are in flight into the ring while
+  // the matrix cores run stage st.  Iteration st waits, synchronises, reads
+  // the rows of stage st + 5 (gathered operands), issues the loads of stage
+  // st + 3, then multiplies stage st.  Its wait lets the wave's last 2D + 2X
+  // memory instructions stay outstanding (D loads per stage, X row-index
+  // loads): exactly those issued after stage st's loads.  The row indices
+  // are read two stages before they are used, so that waiting for them never
+  // waits for a stage still in flight (the counter is in order).  The
+  // barrier carries no memory fence (a fence would wait for every load in
+  // flight); a stage's LDS reads are all consumed by MFMAs before a wave
+  // reaches the next barrier, after which its slot is reloaded.  The loop is
+  // unrolled by the ring's four slots; stages past the last only wait,
+  // synchronise and issue their (empty) loads.
+  constexpr int D = 2 * QN, X = GATHER != 0 ? QN : 0;
+  constexpr int WAIT_N = 2 * D + 2 * X;
+  static_assert(WAIT_N < 64, "vmcnt range");
+  constexpr int WAIT_IMM = (WAIT_N & 15) | ((WAIT_N >> 4) << 14) | (7 << 4) | (15 << 8);
+  constexpr int WAIT_ALL = (7 << 4) | (15 << 8);          // vmcnt(0)
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
+  int32_t ix0[QN], ix1[QN], ix2[QN], ix3[QN];              // rows of stages = 0, 1, 2, 3 mod 4
+  auto ixs = [&](auto u_c) -> int32_t (&)[QN] {
+    constexpr int U = decltype(u_c)::value;
+    if constexpr (U == 0) return ix0;
+    else if constexpr (U == 1) return ix1;
+    else if constexpr (U == 2) return ix2;
+    else return ix3;
+  };
+  auto step = [&](auto u_c, int64_t st) {
+    constexpr int U = decltype(u_c)::value;
+    using UN = std::integral_constant<int, (U + 3) & 3>;   // slot of stage st + 3
+    using UI = std::integral_constant<int, (U + 1) & 3>;   // index set of stage st + 5
+    __builtin_amdgcn_s_waitcnt(WAIT_IMM);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if constexpr (GATHER != 0) load_idx(st + 5, ixs(UI{}));
+    dma(UN{}, st + 3, ixs(UN{}));
+    if (st < nst) compute(u_c);
+  };
   if (nst > 0) {
-    if constexpr (GATHER != 0) load_idx(k0, ix);
-    load(k0, ix, ra, rb);
-    if constexpr (GATHER != 0) load_idx(k0 + BK, ix);
-    store(0, ra, rb);
+    if constexpr (GATHER != 0) {
+      load_idx(0, ix0);
+      load_idx(1, ix1);
+      load_idx(2, ix2);
+    }
+    dma(C0{}, 0, ix0);
+    if constexpr (GATHER != 0) load_idx(3, ix3);
+    dma(C1{}, 1, ix1);
+    if constexpr (GATHER != 0) load_idx(4, ix0);
+    dma(C2{}, 2, ix2);
+    for (int64_t st = 0; st < nst; st += 4) {
+      step(C0{}, st);
+      step(C1{}, st + 1);
+      step(C2{}, st + 2);
+      step(C3{}, st + 3);
+    }
   }
-  __syncthreads();
-  for (int64_t s = 0; s + 1 < nst; ++s) {
-    load(k0 + (s + 1) * BK, ix, ra, rb);
-    if constexpr (GATHER != 0) load_idx(k0 + (s + 2) * BK, ix);
-    compute((int)(s & 1));
-    store((int)((s + 1) & 1), ra, rb);
-    __syncthreads();
-  }
-  if (nst > 0) compute((int)((nst - 1) & 1));
-  __syncthreads();                             // the epilogue reuses the LDS
+  __builtin_amdgcn_s_waitcnt(WAIT_ALL);                   // no load into LDS outlives the loop
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   // ---- epilogue: acc[i][j][r] is row 8 (r / 4) + 4 h + r % 4 of the 32 x 32
   // block (i, j) of the wave, column l32 (h = lane / 32, l32 = lane % 32)
@@ -431,12 +503,12 @@ hipError_t launch_bwd_gemm(int mode, const BwdGemmArgs& a, int64_t blocks, hipSt
   const unsigned nb = (unsigned)blocks;
   constexpr int T = 64 * kBwdWaves;
   if (mode == BWD_DGRAD_ROWS) {
-    bwd_gemm_kernel<BWD_DGRAD_ROWS, 0, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
+    bwd_gemm_kernel<BWD_DGRAD_ROWS, 0, kBwdWaves><<<nb, T, 0, s>>>(a);
   } else if (mode == BWD_WGRAD) {
     if ((a.a.row_map && a.b.row_map) || !a.order) return hipErrorInvalidValue;
-    if (a.a.row_map) bwd_gemm_kernel<BWD_WGRAD, 1, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
-    else if (a.b.row_map) bwd_gemm_kernel<BWD_WGRAD, 2, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
-    else bwd_gemm_kernel<BWD_WGRAD, 0, kBwdWaves><<<nb, T, LDS_BYTES, s>>>(a);
+    if (a.a.row_map) bwd_gemm_kernel<BWD_WGRAD, 1, kBwdWaves><<<nb, T, 0, s>>>(a);
+    else if (a.b.row_map) bwd_gemm_kernel<BWD_WGRAD, 2, kBwdWaves><<<nb, T, 0, s>>>(a);
+    else bwd_gemm_kernel<BWD_WGRAD, 0, kBwdWaves><<<nb, T, 0, s>>>(a);
   } else {
     return hipErrorInvalidValue;
   }
