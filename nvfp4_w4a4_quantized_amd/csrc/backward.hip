@@ -57,7 +57,6 @@ constexpr int LDS_BYTES = NSTAGES * STAGE_BYTES;   // 131072
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
@@ -91,18 +90,6 @@ __device__ __forceinline__ bf16x8_t frag_kc(const uint16_t* s, int r0, int k0, i
   const int r = r0 + (lane & 31);
   const int c = (k0 >> 3) + (lane >> 5);
   return *reinterpret_cast<const bf16x8_t*>(s + r * 32 + 8 * swz_kc(r, c));
-}
-
-// Loads go through buffer resources: an offset at or past the resource's
-// size reads as zero without a memory access, so a masked element needs no
-// branch (a branch around a load would make the compiler wait for every load
-// in flight where the paths join).  Sizes stay below 2^31 bytes (the host
-// checks), and kNone lies past every one.
-constexpr uint32_t kNone = 0x80000000u;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
 }
 
 __device__ __forceinline__ u32x4_t bl16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -162,8 +149,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
   const uint16_t* Ab = a.a.p;
   const uint16_t* Bb = a.b.p + (WG ? 0 : (int64_t)g * a.b.group_stride);
 
-  const __amdgpu_buffer_rsrc_t ar = rsrc(Ab, a.a.bytes);
-  const __amdgpu_buffer_rsrc_t br = rsrc(Bb, a.b.bytes);
+  const __amdgpu_buffer_rsrc_t ar = buffer_rsrc(Ab, a.a.bytes);
+  const __amdgpu_buffer_rsrc_t br = buffer_rsrc(Bb, a.b.bytes);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int64_t nst = (k1 - k0 + BK - 1) / BK;           // K stages
 

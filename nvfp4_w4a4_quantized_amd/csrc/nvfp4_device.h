@@ -27,6 +27,20 @@ __device__ __forceinline__ u32x4_t load_stream16(const void* p) {
 
 constexpr int kWave = 64;
 
+// Buffer-resource loads: an offset at or past the resource's size reads as
+// zero without a memory access, so a masked element needs no branch (a
+// branch around a load makes the compiler wait, where the paths join, for
+// every load in flight).  Resources stay below 2^31 bytes (the launchers
+// check), and kNone lies past every one.
+constexpr uint32_t kNone = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
