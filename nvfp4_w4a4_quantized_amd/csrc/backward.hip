@@ -201,36 +201,60 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
       for (int q = 0; q < QN; ++q) ix[q] = map[std::min<int64_t>(kk + km_row(q), k1 - 1)];
     }
   };
+  // Per-lane offsets of stage 0 for the K-major operands that are not
+  // gathered, and the number of stages whose row (k0 + km_row + BK st) lies
+  // below k1: a stage adds BK rows, a uniform scalar step passed as the
+  // load's soffset, so the per-stage lane work is one compare and a select.
+  const uint32_t lda2 = (uint32_t)(a.a.ld * 2), ldb2 = (uint32_t)(a.b.ld * 2);
+  uint32_t am0[QN], bm0[QN];
+  int32_t kthr[QN];
+#pragma unroll
+  for (int q = 0; q < QN; ++q) {
+    const int64_t r0 = k0 + km_row(q);
+    kthr[q] = (int32_t)((k1 - r0 + BK - 1) / BK);
+    am0[q] = WG && GATHER != 1 && acol_ok && r0 < k1 ? (uint32_t)((r0 * a.a.ld + acol) * 2) : kNone;
+    bm0[q] = GATHER != 2 && bcol_ok && r0 < k1 ? (uint32_t)((r0 * a.b.ld + bcol) * 2) : kNone;
+  }
   // stage st into ring slot U = st % 4; stages past the last read nothing
   // and write zeros (the loads stay unconditional, so every wait below
-  // counts the same instructions)
+  // counts the same instructions).  An offset of kNone plus the scalar step
+  // (below 2^31) stays past the resource.
   auto dma = [&](auto u_c, int64_t st, const int32_t (&ix)[QN]) {
     uint8_t* sbase = slot_ptr(u_c);
     const bool live = st < nst;
-    const int64_t kk = k0 + st * BK;
+    const int32_t st32 = (int32_t)st;
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
       const int i = wave_u + NW * q;
-      uint32_t off;
-      if constexpr (!WG) {
-        off = live && aoff[q] != kNone ? aoff[q] + (uint32_t)(kk * 2) : kNone;
+      uint32_t vo, so;
+      if constexpr (!WG) {                     // K-contiguous rows: + BK elements a stage
+        vo = live ? aoff[q] : kNone;
+        so = live ? (uint32_t)(st * BK * 2) : 0u;
+      } else if constexpr (GATHER == 1) {
+        const bool ok = live && st32 < kthr[q] && ix[q] >= 0 && acol_ok;
+        vo = ((uint32_t)ix[q] * lda2 + (uint32_t)(acol * 2)) | (ok ? 0u : kNone);
+        so = 0u;
       } else {
-        const int64_t kr = kk + km_row(q);
-        const int64_t src = kr < k1 ? (GATHER == 1 ? (int64_t)ix[q] : kr) : -1;
-        off = live && src >= 0 && acol_ok ? (uint32_t)((src * a.a.ld + acol) * 2) : kNone;
+        vo = live && st32 < kthr[q] ? am0[q] : kNone;
+        so = live ? (uint32_t)st * (uint32_t)BK * lda2 : 0u;
       }
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_t*)(sbase + i * 1024), 16, (int)off,
-                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_t*)(sbase + i * 1024), 16, (int)vo,
+                                               (int)__builtin_amdgcn_readfirstlane(so), 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
       const int i = wave_u + NW * q;
-      const int64_t kr = kk + km_row(q);
-      const int64_t src = kr < k1 ? (GATHER == 2 ? (int64_t)ix[q] : kr) : -1;
-      const uint32_t off =
-          live && src >= 0 && bcol_ok ? (uint32_t)((src * a.b.ld + bcol) * 2) : kNone;
+      uint32_t vo, so;
+      if constexpr (GATHER == 2) {
+        const bool ok = live && st32 < kthr[q] && ix[q] >= 0 && bcol_ok;
+        vo = ((uint32_t)ix[q] * ldb2 + (uint32_t)(bcol * 2)) | (ok ? 0u : kNone);
+        so = 0u;
+      } else {
+        vo = live && st32 < kthr[q] ? bm0[q] : kNone;
+        so = live ? (uint32_t)st * (uint32_t)BK * ldb2 : 0u;
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(br, (lds_void_t*)(sbase + REGION + i * 1024), 16,
-                                               (int)off, 0, 0, 0);
+                                               (int)vo, (int)__builtin_amdgcn_readfirstlane(so), 0, 0);
     }
   };
 
@@ -243,27 +267,36 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int wm = wave % 2, wn = wave / 2;               // the wave's 128 x WNC block
-  // 32-row blocks wholly past the tile's rows take no matrix work
+  // 32-row blocks wholly past the tile's rows take no matrix work (the count
+  // is uniform in the wave: each count has its own instance of the loop)
   const int64_t vrows = mlim - (m0 + wm * 128);
-  const int nvb = vrows <= 0 ? 0 : (vrows >= 128 ? 4 : (int)((vrows + 31) / 32));
-  auto compute = [&](auto u_c) {
+  const int nvb = __builtin_amdgcn_readfirstlane(
+      vrows <= 0 ? 0 : (vrows >= 128 ? 4 : (int)((vrows + 31) / 32)));
+  // one stage of the first NVB row blocks: every fragment of both 16-k steps
+  // is read before the first MFMA, so the reads' latency runs under the
+  // MFMAs (the counter retires them in order)
+  auto compute = [&](auto u_c, auto nvb_c) {
+    constexpr int NVB = decltype(nvb_c)::value;
+    constexpr int NA = NVB > 0 ? NVB : 1;
     const uint16_t* la = reinterpret_cast<const uint16_t*>(slot_ptr(u_c));
     const uint16_t* lb = reinterpret_cast<const uint16_t*>(slot_ptr(u_c) + REGION);
+    bf16x8_t fb[BK / 16][JB], fa[BK / 16][NA];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8_t fb[JB];
 #pragma unroll
-      for (int j = 0; j < JB; ++j) fb[j] = frag_km(lb, wn * WNC + j * 32, kk * 16, lane);
+      for (int j = 0; j < JB; ++j) fb[kk][j] = frag_km(lb, wn * WNC + j * 32, kk * 16, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i >= nvb) break;
-        const bf16x8_t fa = WG ? frag_km(la, wm * 128 + i * 32, kk * 16, lane)
-                               : frag_kc(la, wm * 128 + i * 32, kk * 16, lane);
+      for (int i = 0; i < NVB; ++i)
+        fa[kk][i] = WG ? frag_km(la, wm * 128 + i * 32, kk * 16, lane)
+                       : frag_kc(la, wm * 128 + i * 32, kk * 16, lane);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < NVB; ++i)
 #pragma unroll
         for (int j = 0; j < JB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb[j], acc[i][j], 0, 0, 0);
-      }
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
   };
 
   // ---- main loop: stages st + 1 .. st + 3 are in flight into the ring while
@@ -296,7 +329,7 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
     else if constexpr (U == 2) return ix2;
     else return ix3;
   };
-  auto step = [&](auto u_c, int64_t st) {
+  auto step = [&](auto u_c, auto nvb_c, int64_t st) {
     constexpr int U = decltype(u_c)::value;
     using UN = std::integral_constant<int, (U + 3) & 3>;   // slot of stage st + 3
     using UI = std::integral_constant<int, (U + 1) & 3>;   // index set of stage st + 5
@@ -305,9 +338,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if constexpr (GATHER != 0) load_idx(st + 5, ixs(UI{}));
     dma(UN{}, st + 3, ixs(UN{}));
-    if (st < nst) compute(u_c);
+    if (st < nst) compute(u_c, nvb_c);
   };
-  if (nst > 0) {
+  auto run = [&](auto nvb_c) {
     if constexpr (GATHER != 0) {
       load_idx(0, ix0);
       load_idx(1, ix1);
@@ -319,10 +352,21 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
     if constexpr (GATHER != 0) load_idx(4, ix0);
     dma(C2{}, 2, ix2);
     for (int64_t st = 0; st < nst; st += 4) {
-      step(C0{}, st);
-      step(C1{}, st + 1);
-      step(C2{}, st + 2);
-      step(C3{}, st + 3);
+      step(C0{}, nvb_c, st);
+      step(C1{}, nvb_c, st + 1);
+      step(C2{}, nvb_c, st + 2);
+      step(C3{}, nvb_c, st + 3);
+    }
+  };
+  // every wave runs the same loads and barriers; only its matrix work
+  // depends on its valid row blocks
+  if (nst > 0) {
+    switch (nvb) {
+      case 0: run(std::integral_constant<int, 0>{}); break;
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
     }
   }
   __builtin_amdgcn_s_waitcnt(WAIT_ALL);                   // no load into LDS outlives the loop
