@@ -2,7 +2,7 @@
 import csv
 import json
 
-from nvfp4_w4a4_quantized_amd import mfma_counters, traffic
+from nvfp4_w4a4_quantized_amd import mfma_counters, stall_counters, traffic
 
 COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
         "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
@@ -46,6 +46,36 @@ def test_mfma_counters_groups_by_launch_and_drops_warmup(tmp_path):
     assert fc1[3].strip() == "2" and fc1[4].strip() == "400.0" and fc1[5].strip() == "55.0%"
     assert fc1[6].strip() == "450.0" and fc1[7].strip() == "412.3" and fc1[8].strip() == "1125"
     assert lines[1].split("|")[7].strip() == "-" and lines[2].split("|")[7].strip() == "90.0"
+
+
+def test_stall_counters_joins_passes_and_drops_warmup(tmp_path):
+    p1, p2 = tmp_path / "p1.csv", tmp_path / "p2.csv"
+    ns = 100_000
+    clock = 2.0                                   # GHz
+    cycles = clock * ns                           # shader-engine cycles per dispatch
+    first = {"SQ_BUSY_CYCLES": 1.0, "SQ_VALU_MFMA_BUSY_CYCLES": 1.0, "SQ_WAVE_CYCLES": 1.0,
+             "SQ_WAIT_ANY": 1.0, "SQ_WAIT_INST_ANY": 0.0, "SQ_ACTIVE_INST_ANY": 0.0}
+    pass1 = {"SQ_BUSY_CYCLES": stall_counters.SHADER_ENGINES * cycles,
+             "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * stall_counters.SIMDS * cycles,
+             "SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 300.0, "SQ_WAIT_INST_ANY": 200.0,
+             "SQ_ACTIVE_INST_ANY": 500.0}
+    idx = 0.1 * stall_counters.CUS * cycles
+    pass2 = {"SQ_INSTS_VALU": 4000.0, "SQ_INSTS_MFMA": 1000.0, "SQ_INSTS_LDS": 500.0,
+             "SQ_VALU_MFMA_COEXEC_CYCLES": 0.25 * 4 * 4000.0, "SQ_LDS_IDX_ACTIVE": idx,
+             "SQ_LDS_BANK_CONFLICT": 0.2 * idx}
+    # dispatch 1 is the warm-up (dropped); a non-GEMM kernel is ignored
+    rows1 = [(1, FC1, 1000, c, v, 0, 5 * ns) for c, v in first.items()]
+    rows1 += [(2, COPY, 64, "SQ_WAVE_CYCLES", 7.0, 0, 10)]
+    rows1 += [(3, FC1, 1000, c, v, 0, ns) for c, v in pass1.items()]
+    rows2 = [(1, FC1, 1000, c, 1.0, 0, 5 * ns) for c in pass2]
+    rows2 += [(3, FC1, 1000, c, v, 0, ns) for c, v in pass2.items()]
+    _write(p1, rows1)
+    _write(p2, rows2)
+    lines = [l for l in stall_counters.table([str(p1), str(p2)]).splitlines() if l.startswith("| `")]
+    assert len(lines) == 1
+    cells = [c.strip() for c in lines[0].split("|")[1:-1]]
+    assert cells == ["`gemm_w4a4_kernel<4, 2, 8, 2>`", "1000", "100.0", "2.00", "50%", "30%", "20%",
+                     "50%", "4.0", "0.50", "25%", "10%", "20%"]
 
 
 def test_traffic_scales_by_copy_calibration(tmp_path):
