@@ -463,8 +463,8 @@ int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hi
  *   stage_events nullable array of 8 hipEvent_t (as void*), recorded before
  *            the tile tables, FC2 dgrad, the SwiGLU backward, FC2 wgrad, FC1
  *            dgrad, FC1 wgrad, the dx / dprob reductions and after them
- * bf16 arrays and fc1_out 16-byte aligned, the others 4-byte aligned; rows
- * are read only inside [0, expert_offsets[num_experts]).
+ * bf16 arrays, fc1_out, dw1, dw2 and dx_rows_f32 16-byte aligned, the others
+ * 4-byte aligned; rows are read only inside [0, expert_offsets[num_experts]).
  * Limits: hidden % 128 == 0, inter % 128 == 0, hidden, inter <= 16384,
  * num_experts <= 1024, rows_cap < 2^31, and below 2^31 bytes each: dy (and
  * x), fc1_out, one expert's w1 (NVFP4_UNSUPPORTED otherwise).

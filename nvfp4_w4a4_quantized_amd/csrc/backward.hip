@@ -17,25 +17,26 @@
 // the 8 XCDs); the wgrads group K (the expert's rows) and write one fp32
 // matrix per expert.  Padding rows (row_src < 0) read as zeros.
 //
-// Tile 256 x 256, four waves of 128 x 128 (4 x 4 v_mfma_f32_32x32x16_bf16
-// blocks, the accumulators filling the 256 AGPRs), K-stage 64, both operands
-// double-buffered in LDS; the global loads of stage s + 1 are in flight in
-// registers while the matrix cores run stage s (64 MFMAs per wave), and the
-// row indices of a gathered K-major operand are read a stage earlier still.
-// Every global load goes through a buffer resource and is unconditional:
-// masked lanes read zeros, so no branch makes the compiler drain the loads
-// in flight.
-// K-major tiles are copied into LDS as they lie in memory ([k][columns], 16
-// bytes per lane) and transposed by the read: ds_read_b64_tr_b16 hands each
-// lane of a 16-lane group one column of a 4 x 16 block read by the group, so
-// two of them give a lane the 8 consecutive k of its column that the matrix
-// core takes.  K-contiguous A tiles are [m][k] and read 16 bytes per lane.
-// Row pitches (bf16): 72 for [m][64 k]; 160 and 288 for the 128- and
-// 256-column K-major tiles (80 and 144 dwords, 16 banks apart from row to
-// row: the four rows of a transposing read hit 64 distinct banks).
-// The wgrads take their tiles heaviest expert first (an order the table
-// kernel writes), so the experts with the most rows start first and the
-// light ones fill in behind them.
+// Tile 256 x 256, eight waves of 128 x 64 (4 x 2 v_mfma_f32_32x32x16_bf16
+// blocks, two waves per SIMD), K-stage 32.  Both operands go from HBM
+// straight into a four-slot LDS ring (buffer loads with the LDS destination,
+// 16 bytes per lane): three stages are in flight while the matrix cores run
+// the fourth.  Every global load is unconditional: masked lanes take an
+// offset past the buffer and read zeros, so no branch makes the compiler
+// drain the loads in flight.  K-major tiles are read from LDS with
+// ds_read_b64_tr_b16, which hands each lane of a 16-lane group one column of
+// the 4 x 16 block the group reads (two of them give a lane the 8
+// consecutive k the matrix core takes); K-contiguous tiles are read 16 bytes
+// per lane.
+// Output: the dgrads run their MFMAs with the operands swapped, so that a
+// lane holds four consecutive columns of one row and stores them as one
+// 8-byte bf16 piece; the wgrads keep one column per lane, so that each fp32
+// store writes whole 128-byte row segments, addressed by a uniform row
+// offset.
+// The dgrads take their tiles from a table (cost-balanced over the 8 XCDs);
+// the wgrads take experts heaviest first (an order the table kernel writes),
+// so the experts with the most rows start first and the light ones fill in
+// behind them.
 #include <algorithm>
 #include <type_traits>
 
@@ -57,10 +58,8 @@ constexpr int LDS_BYTES = NSTAGES * STAGE_BYTES;   // 131072
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
-  return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu);
-}
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 // LDS tiles are unpadded and XOR-swizzled in 16-byte chunks, because a
 // direct-to-LDS load writes one contiguous KiB per wave instruction:
@@ -105,7 +104,7 @@ __device__ __forceinline__ float bl4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 // The kernel.  BWD_DGRAD_*: workgroup b takes tile table entry b (group,
 // rows [r0, r1), n-tile).  BWD_WGRAD: tile b of (expert in the order table,
 // m-tile, n-tile); GATHER 1 / 2: A / B rows along K are read through row_map.
-// Four waves, each a 128 x 128 quadrant (4 x 4 blocks of 32 x 32).
+// NW waves, each a 128 x (2 BN / NW) block (4 x 2 blocks of 32 x 32 for eight).
 template <int MODE, int GATHER, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
   // the LDS ring: one array per slot, so that the compiler sees that a load
@@ -296,7 +295,8 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
       for (int i = 0; i < NVB; ++i)
 #pragma unroll
         for (int j = 0; j < JB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = WG ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0)
+                         : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk][j], fa[kk][i], acc[i][j], 0, 0, 0);
   };
 
   // ---- main loop: stages st + 1 .. st + 3 are in flight into the ring while
@@ -372,41 +372,64 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_gemm_kernel(BwdGemmArgs a) {
   __builtin_amdgcn_s_waitcnt(WAIT_ALL);                   // no load into LDS outlives the loop
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
-  // ---- epilogue: acc[i][j][r] is row 8 (r / 4) + 4 h + r % 4 of the 32 x 32
-  // block (i, j) of the wave, column l32 (h = lane / 32, l32 = lane % 32)
+  // ---- epilogue.  N is a multiple of 128, so a 32-column block is wholly
+  // inside or outside; so is a 32-row block of a wgrad (M too is a multiple
+  // of 128).
   const int h = lane >> 5, l32 = lane & 31;
-  auto row_of = [&](int i, int r) -> int { return wm * 128 + i * 32 + 8 * (r / 4) + 4 * h + (r % 4); };
-  auto col_of = [&](int j) -> int64_t { return n0 + wn * WNC + j * 32 + l32; };
-
   if constexpr (MODE == BWD_WGRAD) {
-    float* out = a.out_f32 + (int64_t)g * a.m * a.n;
+    // acc[i][j][r] is row 8 (r / 4) + 4 h + r % 4 of the 32 x 32 block (i, j)
+    // and column l32: each store writes 128 contiguous bytes of two rows.
+    // The row's offset is uniform (the store's scalar offset), the lane's
+    // column and its 4 h rows are its vector offset.
+    const int64_t mn = a.m * a.n;
+    const __amdgpu_buffer_rsrc_t orr = buffer_rsrc(a.out_f32 + (int64_t)g * mn, (uint32_t)(mn * 4));
+    const uint32_t n4 = (uint32_t)a.n * 4u;
+    const uint32_t vo = (uint32_t)(4 * h) * n4 + (uint32_t)(wn * WNC + l32) * 4u;
+    // the wave's first row and column, uniform (m < 2^15, n < 2^15)
+    const uint32_t rw = __builtin_amdgcn_readfirstlane((uint32_t)(m0 + (wave_u % 2) * 128));
+    const uint32_t cw = __builtin_amdgcn_readfirstlane((uint32_t)(n0 + (wave_u / 2) * WNC));
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if (rw + i * 32 >= (uint32_t)a.m) continue;
 #pragma unroll
       for (int j = 0; j < JB; ++j) {
-        const int64_t col = col_of(j);
-        if (col >= a.n) continue;
+        if (cw + j * 32 >= (uint32_t)a.n) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + row_of(i, r);
-          if (row < mlim) out[row * a.n + col] = acc[i][j][r];
-        }
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), orr, (int)(vo + j * 128),
+                                                (int)((rw + i * 32 + 8 * (r / 4) + (r % 4)) * n4 + 4 * n0), 0);
       }
+    }
   } else {
+    // The dgrads' MFMAs take the B fragment as their first operand (both
+    // operands share one register layout), so acc[i][j] holds the block
+    // transposed: acc[i][j][4 q + c] is row l32 and column 8 q + 4 h + c.  A
+    // lane stores four consecutive columns of one row per q (8 bytes of bf16,
+    // 16 of fp32) from one row pointer per row block.
+    const int64_t c0 = n0 + wn * WNC + 4 * h;
+    auto store = [&](auto f32_c) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm * 128 + i * 32 + l32;
+        if (row >= mlim) continue;
+        uint16_t* o = a.out_bf16 + row * a.n + c0;
+        float* of = a.out_f32 + row * a.n + c0;
 #pragma unroll
-      for (int j = 0; j < JB; ++j) {
-        const int64_t col = col_of(j);
-        if (col >= a.n) continue;
+        for (int j = 0; j < JB; ++j) {
+          if (n0 + wn * WNC + j * 32 >= a.n) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + row_of(i, r);
-          if (row >= mlim) continue;
-          a.out_bf16[row * a.n + col] = f32_to_bf16(acc[i][j][r]);
-          if (a.out_f32) a.out_f32[row * a.n + col] = acc[i][j][r];
+          for (int q = 0; q < 4; ++q) {
+            const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                               acc[i][j][4 * q + 3]};
+            *reinterpret_cast<u32x2_t*>(o + j * 32 + 8 * q) =
+                (u32x2_t){pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            if constexpr (decltype(f32_c)::value) *reinterpret_cast<f32x4_t*>(of + j * 32 + 8 * q) = v;
+          }
         }
       }
+    };
+    if (a.out_f32) store(std::true_type{});
+    else store(std::false_type{});
   }
 }
 

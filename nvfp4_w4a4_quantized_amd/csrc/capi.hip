@@ -505,10 +505,10 @@ int moe_expert_backward(const uint16_t* dy, const uint16_t* x, int64_t tokens, i
   if (!w1 || !w2 || !dw1 || !dw2 || !expert_offsets || !workspace) return NVFP4_INVALID_ARGUMENT;
   if (rows_cap > 0 && (!fc1_out || !d || !row_src || !row_prob)) return NVFP4_INVALID_ARGUMENT;
   if (tokens > 0 && (!dy || !x || !dx || !dprob || !dst_row)) return NVFP4_INVALID_ARGUMENT;
-  const void* a16[] = {dy, x, fc1_out, d, w1, w2, dx, workspace};
+  const void* a16[] = {dy, x, fc1_out, d, w1, w2, dx, dw1, dw2, workspace};
   for (const void* p : a16)
     if (p && !aligned(p, 16)) return NVFP4_INVALID_ARGUMENT;
-  const void* a4[] = {dw1, dw2, dprob, row_src, row_prob, dst_row, expert_offsets};
+  const void* a4[] = {dprob, row_src, row_prob, dst_row, expert_offsets};
   for (const void* p : a4)
     if (p && !aligned(p, 4)) return NVFP4_INVALID_ARGUMENT;
   if (!aligned(workspace, 256)) return NVFP4_INVALID_ARGUMENT;
@@ -530,7 +530,8 @@ int moe_expert_backward(const uint16_t* dy, const uint16_t* x, int64_t tokens, i
     const void* p16[] = {L.dd, L.dc, L.dxr};
     for (const void* p : p16)
       if (!aligned(p, 16)) return NVFP4_INVALID_ARGUMENT;
-    const void* p4[] = {L.dp, dxr_f32};
+    if (dxr_f32 && !aligned(dxr_f32, 16)) return NVFP4_INVALID_ARGUMENT;
+    const void* p4[] = {L.dp};
     for (const void* p : p4)
       if (p && !aligned(p, 4)) return NVFP4_INVALID_ARGUMENT;
   }
