@@ -143,6 +143,18 @@ def test_invalid_arguments_rejected_before_any_device_call(L):
     assert L.moe_expert_forward(fake, 8, 256, 128, fake, fake, 2, 4, 1, 0, 0, C.byref(w),
                                 C.byref(wbad), fake, C.c_void_p(0x10000), 1 << 30, None, None,
                                 None) == INVALID
+    # backward: hidden not a multiple of 128, dw1 / dw2 not 16-byte aligned (the
+    # weight-gradient tiles are stored in 16-byte pieces), workspace too small
+    ws = C.c_void_p(0x10000)
+
+    def bwd(hidden=256, dw1=fake, dw2=fake, ws_bytes=1 << 30):
+        return L.moe_expert_backward(fake, fake, 8, hidden, 128, 2, 4, 64, fake, fake, fake, fake,
+                                     fake, fake, fake, fake, fake, dw1, dw2, fake, ws, ws_bytes,
+                                     None, None, None)
+    assert bwd(hidden=200) == UNSUPPORTED
+    assert bwd(dw1=C.c_void_p(0x1004)) == INVALID
+    assert bwd(dw2=C.c_void_p(0x1008)) == INVALID
+    assert bwd(ws_bytes=16) == WS_SMALL
 
 
 def test_noalloc_permute_rejects_before_any_device_call(L):
