@@ -521,6 +521,17 @@ __global__ __launch_bounds__(256) void bwd_tables_kernel(const int32_t* offsets,
 
 int bwd_lds_bytes() { return LDS_BYTES; }
 
+// The dgrads' tile cost model: a tile of v valid 32-row blocks and S stages
+// costs kBwdCostFixed + S (kCostStage + v).  Measured on the Qwen3-shaped
+// layer, a 256-row tile with one valid block takes about half the time of a
+// full one (the weight stream, the transposing reads of B and the epilogue do
+// not shrink with its rows), which this fixed term reproduces; the forward
+// GEMM's smaller one left the XCD with the light experts finishing last.
+#ifndef NVFP4_BWD_COST_FIXED
+#define NVFP4_BWD_COST_FIXED 60
+#endif
+constexpr uint32_t kBwdCostFixed = NVFP4_BWD_COST_FIXED;
+
 // Grid of a dgrad launch: every XCD's cost-balanced range of m-tiles (the
 // bound of the forward GEMM's schedule, for 256-row tiles) times the n-tiles.
 TileTableSpec bwd_dgrad_table_spec(int64_t rows_cap, int32_t num_groups, int64_t k, int64_t n,
@@ -528,10 +539,12 @@ TileTableSpec bwd_dgrad_table_spec(int64_t rows_cap, int32_t num_groups, int64_t
   const int64_t ntn = (n + BN - 1) / BN;
   const int64_t mtiles = (rows_cap + BM - 1) / BM + num_groups;
   const int64_t st = std::min<int64_t>(k / kKS, kCostMaxStages);
-  const int64_t cmax = kCostFixed + st * (kCostStage + BM / 32), cmin = kCostFixed + st * (kCostStage + 1);
+  const int64_t cmax = kBwdCostFixed + st * (kCostStage + BM / 32);
+  const int64_t cmin = kBwdCostFixed + st * (kCostStage + 1);
   const int64_t per_xcd = (cmax * (mtiles + 8) + 8 * cmin - 1) / (8 * cmin) + 1;
   TileTableSpec t{};
   t.table = table; t.bm = BM; t.k = k; t.ntn = ntn; t.blocks = 8 * per_xcd * ntn;
+  t.fixed = kBwdCostFixed;
   return t;
 }
 

@@ -42,10 +42,12 @@ __device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t v) {
 // One GEMM launch's tile table: one {group, row0, row1, n-tile} entry per
 // workgroup position (group < 0: no tile), for bm-row tiles, ntn n-tiles per
 // m-tile, K (the cost model's stages) and the launch's `blocks` positions.
+// `fixed` is the cost model's per-tile term for the kernel the table serves.
 struct TileTableSpec {
   int4* table;
   int32_t bm;
   int64_t k, ntn, blocks;
+  uint32_t fixed = kCostFixed;
 };
 
 constexpr int kMaxTableGroups = 1024;
@@ -59,22 +61,25 @@ struct TileTableLds {
   uint32_t wc[4], wk[4], f0[8], f1[8];
 };
 
-// m-tiles of a group of n rows (cnt), whole ones (full) and their cost.
+// m-tiles of a group of n rows (cnt), whole ones (full) and their cost
+// (per-tile term `fixed`).
 template <int BM>
-__device__ __forceinline__ void group_tiles(int64_t n, uint32_t stages, uint32_t full_cost,
-                                            uint32_t* cnt, uint32_t* full, uint32_t* cost) {
+__device__ __forceinline__ void group_tiles(int64_t n, uint32_t stages, uint32_t fixed,
+                                            uint32_t full_cost, uint32_t* cnt, uint32_t* full,
+                                            uint32_t* cost) {
   *cnt = 0; *full = 0; *cost = 0;
   if (n > 0) {
     const uint32_t f = (uint32_t)(n / BM), rem = (uint32_t)(n % BM);
     *full = f;
     *cnt = f + (rem ? 1u : 0u);
-    *cost = f * full_cost + (rem ? tile_cost((rem + 31) / 32, stages) : 0u);
+    *cost = f * full_cost + (rem ? fixed + stages * (kCostStage + (rem + 31) / 32) : 0u);
   }
 }
 
 // Writes entries first, first + stride, ... of the table from the offsets
 // off[0..G] (global or LDS), exactly as the GEMM's own lookup derives each
-// workgroup's tile: per-group m-tile counts and costs with their inclusive
+// workgroup's tile (which uses the fixed term kCostFixed; a table may carry
+// another): per-group m-tile counts and costs with their inclusive
 // prefix sums over the groups, the 8 XCD cut points (the first m-tiles whose
 // preceding cost reaches x/8 of the total), then for every position b its
 // XCD range position, m-tile, n-tile, group and rows.  A 256-thread
@@ -86,7 +91,7 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
   constexpr int PER = kMaxTableGroups / 256;    // groups per thread, contiguous
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
   const uint32_t stages = (uint32_t)std::min<int64_t>(t.k / kKS, kCostMaxStages);
-  const uint32_t full_cost = tile_cost(BM / 32, stages);
+  const uint32_t full_cost = t.fixed + stages * (kCostStage + BM / 32);
   int32_t o[PER + 1];
 #pragma unroll
   for (int i = 0; i <= PER; ++i) {
@@ -100,7 +105,8 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
     const int gi = PER * tid + i;
     uint32_t cnt = 0, cost = 0, full = 0;
     if (gi < G) {
-      group_tiles<BM>((int64_t)o[i + 1] - (int64_t)o[i], stages, full_cost, &cnt, &full, &cost);
+      group_tiles<BM>((int64_t)o[i + 1] - (int64_t)o[i], stages, t.fixed, full_cost, &cnt, &full,
+                      &cost);
       s.off[gi] = o[i];
       if (gi == G - 1) s.off[G] = o[i + 1];
     }
@@ -129,8 +135,8 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
     }
     if (lo >= G) return tiles;
     uint32_t cnt, full, cost;
-    group_tiles<BM>((int64_t)s.off[lo + 1] - (int64_t)s.off[lo], stages, full_cost, &cnt, &full,
-                    &cost);
+    group_tiles<BM>((int64_t)s.off[lo + 1] - (int64_t)s.off[lo], stages, t.fixed, full_cost, &cnt,
+                    &full, &cost);
     const uint32_t ec = s.ic[lo] - cnt, ek = s.ik[lo] - cost;
     uint32_t j = c > ek ? (c - ek + full_cost - 1) / full_cost : 0u;
     if (j > full) j = cnt;                         // inside the partial tile: take the next one
