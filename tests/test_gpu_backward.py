@@ -184,6 +184,9 @@ CASES = {
     # skewed routing, one row alignment, two experts left empty
     "t512_h256_i256_e8_k2_empty": dict(seed=72, T=512, H=256, I=256, E=8, k=2, align=1,
                                        zipf=1.2, banned=(3, 7)),
+    # hidden 384: FC2's wgrad has a 256-row output tile half past its rows and
+    # FC1's dgrad a 256-column tile half past its columns
+    "t384_h384_i128_e4_k2": dict(seed=73, T=384, H=384, I=128, E=4, k=2, align=1),
 }
 
 
