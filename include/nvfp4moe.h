@@ -461,8 +461,9 @@ int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hi
  *            copies; dx_rows_f32 (fp32 [rows_cap, hidden], the FC1 dgrad
  *            before its bf16 rounding) is only written when given
  *   stage_events nullable array of 8 hipEvent_t (as void*), recorded before
- *            the tile tables, FC2 dgrad, the SwiGLU backward, FC2 wgrad, FC1
- *            dgrad, FC1 wgrad, the dx / dprob reductions and after them
+ *            the tile tables, FC2 dgrad, the SwiGLU backward, FC1 dgrad, the
+ *            dx / dprob reductions, FC2 wgrad, FC1 wgrad and after them (the
+ *            order the stages run in)
  * bf16 arrays, fc1_out, dw1, dw2 and dx_rows_f32 16-byte aligned, the others
  * 4-byte aligned; rows are read only inside [0, expert_offsets[num_experts]).
  * Limits: hidden % 128 == 0, inter % 128 == 0, hidden, inter <= 16384,

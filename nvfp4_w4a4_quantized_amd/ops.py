@@ -413,12 +413,12 @@ def moe_expert_forward_single_pass(x, topk_idx, topk_prob, num_experts: int, int
 
 
 class BackwardTimer(StageTimer):
-    """Eight HIP events recorded by moe_expert_backward: the dgrad tile
-    tables, FC2 dgrad, the SwiGLU backward, FC2 wgrad, FC1 dgrad, FC1 wgrad,
-    and the dx / dprob reductions."""
+    """Eight HIP events recorded by moe_expert_backward around its stages, in
+    the order they run: the dgrad tile tables, FC2 dgrad, the SwiGLU
+    backward, FC1 dgrad, the dx / dprob reductions, FC2 wgrad, FC1 wgrad."""
 
-    NAMES = ("tables", "fc2_dgrad", "swiglu_bwd", "fc2_wgrad", "fc1_dgrad", "fc1_wgrad",
-             "reduce")
+    NAMES = ("tables", "fc2_dgrad", "swiglu_bwd", "fc1_dgrad", "reduce", "fc2_wgrad",
+             "fc1_wgrad")
 
     def __init__(self):
         L = lib()
