@@ -162,6 +162,23 @@ def test_perf_path_bf16_rows_and_determinism():
     assert n == int(it["expert_offsets"][-1]) * w.hidden
 
 
+def test_decode_perf_path_matches_the_checked_path():
+    """The decode-shaped layer as the benchmark runs it (tiled weights, no
+    debug outputs, the 32-row tile) gives the checked debug path's y bit for
+    bit, on repeated calls."""
+    from nvfp4_w4a4_quantized_amd.ops import moe_expert_forward
+    w, W1, W2 = moe_case(3)
+    say("decode layer perf path x2")
+    args = (dev_bf16(w.x), dev(w.topk_idx), dev(w.topk_prob), w.experts, w.inter,
+            _weights(W1).packed(), _weights(W2).packed())
+    y1 = moe_expert_forward(*args)
+    y2 = moe_expert_forward(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    y, _ = _forward(w, W1, W2)
+    assert np.array_equal(y, host(y1))
+
+
 @pytest.mark.parametrize("tokens,experts,zipf", [(160, 300, 0.0), (2000, 300, 1.2)])
 def test_many_experts_replay_chain(tokens, experts, zipf):
     """300 experts: the layer's precomputed tile schedules span groups held by
