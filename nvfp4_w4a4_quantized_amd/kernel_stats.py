@@ -1,8 +1,15 @@
-"""Markdown table of a rocprofv3 --stats kernel summary (KERNEL_DISPATCH
-rows of the *_kernel_stats.csv file), for the profile notes.
+"""Markdown tables of rocprofv3 kernel timings, for the profile notes.
 
 Usage:
     python -m nvfp4_w4a4_quantized_amd.kernel_stats STATS_CSV [MAX_ROWS]
+        the --stats summary (KERNEL_DISPATCH rows of *_kernel_stats.csv)
+    python -m nvfp4_w4a4_quantized_amd.kernel_stats --last N TRACE_CSV [MAX_ROWS]
+        from the --kernel-trace records (*_kernel_trace.csv): per kernel and
+        grid size, the last N dispatches only (the steps a benchmark times,
+        after its warm-up)
+    python -m nvfp4_w4a4_quantized_amd.kernel_stats --window NAME GRID START COUNT TRACE_CSV
+        the dispatches START .. START + COUNT - 1 (in time order) of the
+        kernel whose name contains NAME, at grid size GRID
 """
 from __future__ import annotations
 
@@ -29,5 +36,48 @@ def table(path: str, max_rows: int = 16) -> str:
     return "\n".join(out)
 
 
+def _dispatches(path: str):
+    """{(short name, grid size): [(start, duration ns), ...]} of a trace."""
+    groups = {}
+    for r in csv.DictReader(open(path)):
+        grid = int(r["Grid_Size"]) if "Grid_Size" in r else int(r["Grid_Size_X"])   # 1-D launches
+        key = (_short(r["Kernel_Name"]), grid)
+        groups.setdefault(key, []).append(
+            (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return groups
+
+
+def window(path: str, name: str, grid: int, start: int, count: int) -> str:
+    for (kn, g), ds in _dispatches(path).items():
+        if name in kn and g == grid:
+            d = [v for _, v in sorted(ds)[start:start + count]]
+            return "`%s` grid %d, dispatches %d-%d of %d: average %.1f us, min %.1f, max %.1f" % (
+                kn, g, start, start + len(d) - 1, len(ds), sum(d) / len(d) / 1e3, min(d) / 1e3,
+                max(d) / 1e3)
+    raise SystemExit(f"no kernel containing {name!r} at grid {grid}")
+
+
+def last_table(path: str, last: int, max_rows: int = 16) -> str:
+    groups = _dispatches(path)
+    rows = []
+    for (name, grid), ds in groups.items():
+        ds.sort()
+        d = [v for _, v in ds[-last:]]
+        rows.append((sum(d), name, grid, len(ds), d))
+    rows.sort(key=lambda t: -t[0])
+    out = ["| Kernel | Grid | Calls | Last | Average (us) | Min (us) | Max (us) |",
+           "|---|---|---|---|---|---|---|"]
+    for _, name, grid, n, d in rows[:max_rows]:
+        out.append("| `%s` | %d | %d | %d | %.1f | %.1f | %.1f |" % (
+            name, grid, n, len(d), sum(d) / len(d) / 1e3, min(d) / 1e3, max(d) / 1e3))
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(table(sys.argv[1], int(sys.argv[2]) if len(sys.argv) > 2 else 16))
+    a = sys.argv[1:]
+    if a and a[0] == "--last":
+        print(last_table(a[2], int(a[1]), int(a[3]) if len(a) > 3 else 16))
+    elif a and a[0] == "--window":
+        print(window(a[5], a[1], int(a[2]), int(a[3]), int(a[4])))
+    else:
+        print(table(a[0], int(a[1]) if len(a) > 1 else 16))

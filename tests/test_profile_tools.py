@@ -2,7 +2,7 @@
 import csv
 import json
 
-from nvfp4_w4a4_quantized_amd import mfma_counters, stall_counters, traffic
+from nvfp4_w4a4_quantized_amd import kernel_stats, mfma_counters, stall_counters, traffic
 
 COLS = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
         "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
@@ -76,6 +76,25 @@ def test_stall_counters_joins_passes_and_drops_warmup(tmp_path):
     cells = [c.strip() for c in lines[0].split("|")[1:-1]]
     assert cells == ["`gemm_w4a4_kernel<4, 2, 8, 2>`", "1000", "100.0", "2.00", "50%", "30%", "20%",
                      "50%", "4.0", "0.50", "25%", "10%", "20%"]
+
+
+def test_kernel_stats_last_dispatches_per_grid(tmp_path):
+    p = tmp_path / "kt.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        # FC1: two slow warm-up dispatches, then three at 100, 110, 120 us
+        for i, d in enumerate((900, 800, 100, 110, 120)):
+            w.writerow({"Kernel_Name": FC1, "Grid_Size_X": 1000, "Start_Timestamp": 10_000_000 * i,
+                        "End_Timestamp": 10_000_000 * i + d * 1000})
+        # the same kernel at another grid size stays apart
+        w.writerow({"Kernel_Name": FC1, "Grid_Size_X": 2000, "Start_Timestamp": 5, "End_Timestamp": 5005})
+    lines = [l for l in kernel_stats.last_table(str(p), 3).splitlines() if l.startswith("| `")]
+    assert len(lines) == 2
+    cells = [c.strip() for c in lines[0].split("|")[1:-1]]
+    assert cells == ["`gemm_w4a4_kernel<4, 2, 8, 2>`", "1000", "5", "3", "110.0", "100.0", "120.0"]
+    w = kernel_stats.window(str(p), "4, 2, 8, 2>", 1000, 1, 2)
+    assert "dispatches 1-2 of 5" in w and "average 450.0 us" in w
 
 
 def test_traffic_scales_by_copy_calibration(tmp_path):
