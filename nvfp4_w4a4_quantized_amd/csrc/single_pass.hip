@@ -78,8 +78,10 @@ extern __shared__ __align__(16) uint8_t sp_smem[];
 // One FC1 slice (PHASE 0) or one FC2 slab (PHASE 1) of the workgroup's
 // m-tile.  Each is a function of its own: its registers are allocated
 // apart from the others', and nothing of one slice stays live across the
-// next slice's main loop.
-template <int PHASE>
+// next slice's main loop.  MV: the m-tile's 32-row blocks that hold a valid
+// row; the blocks past them (all padding) take no matrix work, SwiGLU,
+// quantization or stores.
+template <int PHASE, int MV>
 __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
   uint8_t* smem = sp_smem;
   const int4 te = a.tile_table[blockIdx.x];
@@ -215,7 +217,7 @@ __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
       b_load_s(clamp_st(it + 1));
       half8_t fa[WM];
 #pragma unroll
-      for (int m = 0; m < WM; ++m) fa[m] = a_frag(m, 0);
+      for (int m = 0; m < MV; ++m) fa[m] = a_frag(m, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
@@ -228,7 +230,7 @@ __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
           b_decode(bx, 0, bsn, fbn);
         }
 #pragma unroll
-        for (int m = 0; m < WM; ++m) {
+        for (int m = 0; m < MV; ++m) {
 #pragma unroll
           for (int n = 0; n < WN; ++n)
             acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[m], fbc[n], acc[m][n], 0, 0, 0);
@@ -240,7 +242,7 @@ __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
 #pragma unroll
         for (int n = 0; n < WN; ++n) fbc[n] = fbn[n];
 #pragma unroll
-        for (int m = 0; m < WM; ++m) {
+        for (int m = 0; m < MV; ++m) {
 #pragma unroll
           for (int n = 0; n < WN; ++n) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -292,7 +294,7 @@ __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
     // weighted SwiGLU of the slice -> bf16 staging [row][column in slice]
     if (wave_live) {
 #pragma unroll
-      for (int m = 0; m < WM; ++m) {
+      for (int m = 0; m < MV; ++m) {
         float sv[16], spv[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -322,8 +324,9 @@ __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
     }
     __syncthreads();
     // quantize the slice: four threads per row, each 1/4 of its 16-blocks;
-    // the row's slice maximum by two lane exchanges, then gamax, gs_i
-    {
+    // the row's slice maximum by two lane exchanges, then gamax, gs_i (rows
+    // of the valid blocks only; a wave's rows share one block)
+    if ((tid >> 2) < 32 * MV) {
       const int r = tid >> 2, qd = tid & 3;
       const int64_t width = I - (int64_t)sl * SLICE < SLICE ? I - (int64_t)sl * SLICE : SLICE;
       const int nbq = (int)(width / 64);           // blocks per thread (width % 128 == 0: 2 or 4)
@@ -397,7 +400,7 @@ __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
       if (st == 0 || (st * kKS) % SLICE != 0) return;
       const int sl = (int)(st * kKS / SLICE);
 #pragma unroll
-      for (int m = 0; m < WM; ++m) {
+      for (int m = 0; m < MV; ++m) {
         float rv[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -413,7 +416,7 @@ __device__ __noinline__ void sp_body(const SinglePassArgs& a, int idx) {
     gemm_pass(std::true_type{}, I, w2c, w2s, tiled2, bco, bso, rescale);
     // epilogue: Y = O * gs_last * gs_W2
 #pragma unroll
-    for (int m = 0; m < WM; ++m) {
+    for (int m = 0; m < MV; ++m) {
       float fv[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -471,9 +474,19 @@ __global__ __launch_bounds__(NT, 1) void single_pass_kernel(SinglePassArgs a) {
     reinterpret_cast<float*>(sp_smem + L.gam)[tid] = 0.0f;
   }
   const int nslices = (int)((a.inter + SLICE - 1) / SLICE);
-  for (int sl = 0; sl < nslices; ++sl) sp_body<0>(a, sl);
   const int nslabs = (int)((a.hidden + BN - 1) / BN);
-  for (int sb = 0; sb < nslabs; ++sb) sp_body<1>(a, sb);
+  auto run = [&](auto mv_c) {
+    constexpr int MV = decltype(mv_c)::value;
+    for (int sl = 0; sl < nslices; ++sl) sp_body<0, MV>(a, sl);
+    for (int sb = 0; sb < nslabs; ++sb) sp_body<1, MV>(a, sb);
+  };
+  const int64_t nrow = (int64_t)te.z - te.y;     // 1 .. BM valid rows
+  switch (__builtin_amdgcn_readfirstlane((int)((nrow + 31) / 32))) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    default: run(std::integral_constant<int, WM>{}); break;
+  }
 }
 
 TileTableSpec single_pass_table_spec(int64_t rows_cap, int32_t num_groups, int64_t hidden,
