@@ -489,9 +489,20 @@ __global__ __launch_bounds__(NT, 1) void single_pass_kernel(SinglePassArgs a) {
   }
 }
 
+// The 128-row blocks in cost-balanced XCD ranges, as for FC1, except that an
+// XCD's last, partial round of blocks is cut into 64-row halves when that
+// fits its 32 compute units (the kernel takes any row range up to 128 rows,
+// and a half with at most two valid 32-row blocks costs about two thirds of a
+// whole block): one workgroup per CU runs blocks of a few hundred
+// microseconds, so the last round decides the launch.
+constexpr uint32_t kXcdCUs = 32;
+
 TileTableSpec single_pass_table_spec(int64_t rows_cap, int32_t num_groups, int64_t hidden,
                                      int4* table) {
-  return gemm_mtile_table_spec(rows_cap, num_groups, hidden, table);
+  TileTableSpec t = gemm_mtile_table_spec(rows_cap, num_groups, hidden, table);
+  t.split_tail = kXcdCUs;
+  if (t.blocks > 0) t.blocks += 8 * (kXcdCUs / 2);
+  return t;
 }
 
 int single_pass_lds_bytes(int64_t inter) { return sp_lds(inter).bytes; }

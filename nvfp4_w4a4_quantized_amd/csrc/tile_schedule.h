@@ -43,11 +43,17 @@ __device__ __forceinline__ uint32_t wave_incl_sum_u32(uint32_t v) {
 // workgroup position (group < 0: no tile), for bm-row tiles, ntn n-tiles per
 // m-tile, K (the cost model's stages) and the launch's `blocks` positions.
 // `fixed` is the cost model's per-tile term for the kernel the table serves.
+// `split_tail` (tables of one n-tile, for kernels that take any row range up
+// to bm rows): the compute units of one XCD.  An XCD whose range leaves r
+// m-tiles for a last, partial round of that many workgroups, with 2 r at most
+// that many, gets those r m-tiles as 2 r half-height tiles, so its last round
+// ends sooner; the grid needs split_tail / 2 more positions per XCD.
 struct TileTableSpec {
   int4* table;
   int32_t bm;
   int64_t k, ntn, blocks;
   uint32_t fixed = kCostFixed;
+  uint32_t split_tail = 0;
 };
 
 constexpr int kMaxTableGroups = 1024;
@@ -149,13 +155,32 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
   }
   __syncthreads();
   const uint32_t un = (uint32_t)t.ntn;
+  const bool split = t.split_tail != 0 && un == 1;
   for (int64_t b = first; b < t.blocks; b += stride) {
     const int x = (int)(b % 8);
     const uint32_t pos = (uint32_t)(b / 8);
-    const uint32_t logical = s.f0[x] * un + pos;
+    // m-tile of this position, and which half of it (-1: the whole tile)
+    uint32_t mt = 0;
+    int half = -1;
+    bool live;
+    if (split) {
+      const uint32_t cnt = s.f1[x] - s.f0[x];
+      const uint32_t r = cnt % t.split_tail;
+      const uint32_t ns = 2 * r <= t.split_tail ? r : 0u;   // m-tiles cut in two
+      const uint32_t nf = cnt - ns;
+      live = pos < nf + 2 * ns;
+      if (pos < nf) {
+        mt = s.f0[x] + pos;
+      } else {
+        mt = s.f0[x] + nf + (pos - nf) / 2;
+        half = (int)((pos - nf) & 1u);
+      }
+    } else {
+      live = s.f0[x] * un + pos < s.f1[x] * un;
+      mt = (s.f0[x] * un + pos) / un;
+    }
     int4 e = make_int4(-1, 0, 0, 0);
-    if (logical < s.f1[x] * un) {
-      const uint32_t mt = logical / un;
+    if (live) {
       int lo = 0, hi = G - 1;                      // first group with ic > mt
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -163,9 +188,14 @@ __device__ void build_tile_table(const int32_t* off, int G, const TileTableSpec&
       }
       const int64_t n = (int64_t)s.off[lo + 1] - (int64_t)s.off[lo];
       const uint32_t cnt = (uint32_t)((n + BM - 1) / BM);
-      const int32_t r0 = s.off[lo] + (int32_t)(mt - (s.ic[lo] - cnt)) * BM;
-      const int32_t r1 = std::min<int32_t>(r0 + BM, s.off[lo + 1]);
-      e = make_int4(lo, r0, r1, (int)(logical - mt * un));
+      int32_t r0 = s.off[lo] + (int32_t)(mt - (s.ic[lo] - cnt)) * BM;
+      int32_t r1 = std::min<int32_t>(r0 + BM, s.off[lo + 1]);
+      if (half >= 0) {                             // rows [r0 + BM/2 h, + BM/2) of the tile
+        r0 += half * (BM / 2);
+        r1 = std::min<int32_t>(r1, r0 + BM / 2);
+      }
+      const int ntile = split ? 0 : (int)(s.f0[x] * un + pos - mt * un);
+      if (r0 < r1) e = make_int4(lo, r0, r1, ntile);
     }
     t.table[b] = e;
   }
