@@ -43,6 +43,8 @@ def _run_plain(A, W, offs, dtype=torch.float32, tiled=False):
     (513, [0, 200, 200, 513], 160, 768),
     (257, [3, 100, 257], 2048, 384),                     # rows before off[0] untouched
     (64, [0, 64], 32, 2048),
+    (160, [0, 70, 160], 64, 16384),                      # the largest K, 128-row tile
+    (40, [0, 9, 40], 96, 16384),                          # the largest K, 32-row tile
 ])
 def test_plain_fp32_full_compare(shape):
     rows, offs, n, k = shape
