@@ -204,6 +204,27 @@ def test_many_experts_replay_chain(tokens, experts, zipf):
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-2
 
 
+@pytest.mark.parametrize("H,I", [(16384, 128), (256, 16384)])
+def test_largest_hidden_and_intermediate_replay_chain(H, I):
+    """The layer at its largest hidden size (FC1's K, FC2's N) and at its
+    largest intermediate size (FC1's N, FC2's K): every step of the chain in
+    full, and y against the oracle layer."""
+    from nvfp4_w4a4_quantized_amd.workloads import MoeWorkload, random_bf16, route_topk
+    rng = np.random.default_rng(H + I)
+    tokens, experts, k = 96, 4, 2
+    idx, prob = route_topk(rng.standard_normal((tokens, experts)).astype(np.float32), k)
+    w = MoeWorkload(f"largest_h{H}_i{I}", -1, tokens, H, I, experts, k,
+                    random_bf16(rng, (tokens, H)), idx, prob, None, None, {})
+    from gpu_util import oracle_weights
+    W1 = oracle_weights(random_bf16(rng, (experts, 2 * I, H), 0.02))
+    W2 = oracle_weights(random_bf16(rng, (experts, H, I), 0.02))
+    y, it, _ = _replay_chain(w, W1, W2, 1)
+    yo, _ = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2)
+    a = bf16_bits_to_f32(y).astype(np.float64)
+    b = bf16_bits_to_f32(yo).astype(np.float64)
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-2
+
+
 @pytest.mark.parametrize("tokens,align", [(0, 1), (0, 16), (1, 1), (1, 16)])
 def test_empty_and_single_token_layer(tokens, align):
     """No tokens: the tile tables are empty and every GEMM workgroup exits;
