@@ -187,6 +187,9 @@ CASES = {
     # hidden 384: FC2's wgrad has a 256-row output tile half past its rows and
     # FC1's dgrad a 256-column tile half past its columns
     "t384_h384_i128_e4_k2": dict(seed=73, T=384, H=384, I=128, E=4, k=2, align=1),
+    # the largest hidden and intermediate sizes
+    "t96_h16384_i128_e4_k2": dict(seed=74, T=96, H=16384, I=128, E=4, k=2, align=1),
+    "t96_h256_i16384_e4_k2": dict(seed=75, T=96, H=256, I=16384, E=4, k=2, align=1),
 }
 
 
