@@ -116,10 +116,13 @@ def _multi_tile_case(tokens, experts, H, I, k, seed, zipf=1.1):
     return w, W1, W2
 
 
-@pytest.mark.parametrize("I,align,tiled", [(768, 1, True), (384, 16, False), (640, 1, False)])
+@pytest.mark.parametrize("I,align,tiled", [(768, 1, True), (384, 16, False), (640, 1, False),
+                                            (1152, 1, True)])
 def test_multi_tile_replay_chain(I, align, tiled):
     """Three tiles (768), a full and a half tile (384: 256 + 128), three
-    tiles ending in a half one (640); padding rows; both weight layouts."""
+    tiles ending in a half one (640), the largest intermediate size with
+    its FC2 input filling the LDS (1152: four tiles and a half); padding
+    rows; both weight layouts."""
     w, W1, W2 = _multi_tile_case(700, 16, 256, I, 4, I + align)
     y, it = _replay(w, W1, W2, align, tiled)
     R = int(it["expert_offsets"][-1])
