@@ -23,6 +23,15 @@
 //               of the chunk's ballot mask of tokens choosing e below t: a
 //               stable order (ascending token) without any order-dependent
 //               atomics.  Extra waves (one per expert) fill the padding rows.
+//
+// The expert layer's gather mode (tok_codes set) quantizes each token once
+// into a token-major row and writes only the row maps.  Two launches while
+// the chunk-count matrix is small enough for every workgroup to read it
+// whole (kFusedScanInts): the ranked histogram beside every token's
+// quantization, then route_scan_entries_kernel (each workgroup repeats the
+// scan's totals, then writes the entries, padding rows or tile tables).
+// Larger matrices take three: histogram + half of the quantization, scan +
+// the other half, entries.
 #include "launch.h"
 #include "nvfp4_device.h"
 
@@ -792,6 +801,151 @@ __global__ __launch_bounds__(256) void route_entries_kernel(RouteArgs a, const i
   }
 }
 
+// Gather mode, second and last launch of the two-launch path, taken when
+// the chunk-count matrix hist (E x nchunks) is small enough for every
+// workgroup to read it whole (kFusedScanInts): the scan, the entries and the
+// tile tables in one launch.  Each workgroup derives the expert offsets
+// itself: its threads sum contiguous stretches of the expert-major matrix
+// into per-expert totals in LDS (entries of the workgroup's own chunk's
+// predecessors in a second sum), then a block scan of the padded totals.
+// Workgroups [0, twg) then write the tile tables; the next nchunks take one
+// chunk each: entry i of token t (chunk c) choosing e goes to row
+// off[e] + (entries of e in chunks before c) + its rank inside the chunk.
+// The last workgroups give one wave per expert for its padding rows.  All of
+// them clear a slice of the rows' amax cells first.
+constexpr int64_t kFusedScanInts = 32768;
+constexpr int kEntryPreload = 4;    // entries per thread whose loads overlap the offsets
+
+__global__ __launch_bounds__(256) void route_scan_entries_kernel(RouteArgs a, const int32_t* hist,
+                                                                 int64_t nchunks, int64_t twg) {
+  __shared__ TileTableLds tls;
+  __shared__ int32_t off[kScanMaxE + 1];
+  __shared__ int32_t tot_s[kScanMaxE], pre_s[kScanMaxE];
+  __shared__ int32_t wsum[kScanWaves];
+  const int tid = threadIdx.x;
+  const int E = a.num_experts, k = a.topk;
+  const int64_t bx = blockIdx.x;
+  grid_zero_fill(a.zero_per_row, a.zero_rows, gridDim.x);
+  const int64_t chunk = (bx >= twg && bx < twg + nchunks) ? bx - twg : -1;
+  // this chunk's entries [i0, i1); the first kEntryPreload per thread load now
+  const int64_t i0 = chunk >= 0 ? chunk * kChunk * k : 0;
+  const int64_t i1 = chunk >= 0 ? std::min<int64_t>((chunk + 1) * kChunk, a.tokens) * k : 0;
+  int pe[kEntryPreload], pr[kEntryPreload];
+  float pp[kEntryPreload], pg[kEntryPreload];
+#pragma unroll
+  for (int u = 0; u < kEntryPreload; ++u) {
+    const int64_t i = i0 + tid + 256 * u;
+    const bool live = i < i1;
+    pe[u] = live ? a.topk_idx[i] : -1;
+    pp[u] = live ? a.topk_prob[i] : 0.0f;
+    pr[u] = live ? (int)a.entry_rank[i] : 0;
+    pg[u] = live ? a.tok_gscale[chunk * kChunk + (tid + 256 * u) / k] : 0.0f;
+  }
+  for (int e = tid; e < E; e += 256) { tot_s[e] = 0; pre_s[e] = 0; }
+  __syncthreads();
+  // thread stretch [j0, j1) of the flattened matrix (a multiple of 4 long,
+  // so with 4 | nchunks an int4 never crosses a row), walked with its row e
+  // and column c (32-bit: E * nchunks <= kFusedScanInts); a stretch spans
+  // at most a few rows, each flushed to LDS once
+  const int32_t nc = (int32_t)nchunks, cc = (int32_t)chunk;
+  const int32_t n = E * nc;
+  const int32_t per = (((n + 255) / 256) + 3) & ~3;
+  const int32_t j0 = std::min(tid * per, n), j1 = std::min(j0 + per, n);
+  int32_t e = j0 / nc, c = j0 - e * nc, ecur = e;
+  int32_t st = 0, sp = 0;
+  auto flush = [&]() {
+    if (st) atomicAdd(&tot_s[ecur], st);
+    if (sp) atomicAdd(&pre_s[ecur], sp);
+    st = 0; sp = 0;
+  };
+  if ((nc & 3) == 0) {
+    for (int32_t jb = j0; jb < j1; jb += 64) {     // sixteen 16-byte loads in flight
+      int4 q[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int32_t j = jb + 4 * u;
+        q[u] = j < j1 ? *reinterpret_cast<const int4*>(hist + j) : make_int4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (jb + 4 * u >= j1) break;
+        if (e != ecur) { flush(); ecur = e; }
+        st += q[u].x + q[u].y + q[u].z + q[u].w;
+        sp += (c < cc ? q[u].x : 0) + (c + 1 < cc ? q[u].y : 0) + (c + 2 < cc ? q[u].z : 0) +
+              (c + 3 < cc ? q[u].w : 0);
+        c += 4;
+        if (c == nc) { c = 0; ++e; }
+      }
+    }
+  } else {
+    for (int32_t j = j0; j < j1; ++j) {
+      if (e != ecur) { flush(); ecur = e; }
+      const int32_t v = hist[j];
+      st += v;
+      sp += c < cc ? v : 0;
+      if (++c == nc) { c = 0; ++e; }
+    }
+  }
+  flush();
+  __syncthreads();
+  int32_t tot[kScanPer];
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    const int e = tid + kScanThreads * i;
+    tot[i] = e < E ? tot_s[e] : 0;
+  }
+  block_expert_offsets(tot, E, a.align, off, wsum);
+  if (bx == 0)
+    for (int e = tid; e <= E; e += 256) a.offsets[e] = off[e];
+  if (bx < twg) {
+    // as in route_entries_kernel: a third of them write table 0 (FC1)
+    const int64_t w0 = a.num_tables > 1 ? twg / 3 : twg;
+    if (bx < w0)
+      build_tile_tables(off, E, a.tables[0], a.tables[0], 1, bx * 256 + tid, w0 * 256, tls);
+    else
+      build_tile_tables(off, E, a.tables[1], a.tables[1], 1, (bx - w0) * 256 + tid,
+                        (twg - w0) * 256, tls);
+    return;
+  }
+  if (chunk >= 0) {
+    // entry i = i0 + l of the chunk: token chunk * kChunk + l / k
+    auto place = [&](int64_t i, int32_t l, int e, float p, int r, float g) {
+#ifdef NVFP4_DEBUG_CHECKS
+      report_bits(a.error_word, !__builtin_isfinite(p), NVFP4_PRECONDITION_NONFINITE_PROB);
+#endif
+      int64_t d = -1;
+      if (e >= 0 && e < E) {
+        d = (int64_t)off[e] + pre_s[e] + r;
+        a.row_src[d] = (int32_t)(chunk * kChunk + l / k);
+        a.row_prob[d] = p;
+        a.gscale[d] = g;
+      }
+      a.dst_row[i] = (int32_t)d;
+    };
+#pragma unroll
+    for (int u = 0; u < kEntryPreload; ++u) {
+      const int64_t i = i0 + tid + 256 * u;
+      if (i < i1) place(i, tid + 256 * u, pe[u], pp[u], pr[u], pg[u]);
+    }
+    for (int32_t l = tid + 256 * kEntryPreload; i0 + l < i1; l += 256) {
+      const int64_t i = i0 + l;
+      place(i, l, a.topk_idx[i], a.topk_prob[i], (int)a.entry_rank[i],
+            a.tok_gscale[chunk * kChunk + l / k]);
+    }
+    return;
+  }
+  // the expert whose padding rows this wave writes
+  const int64_t ep = (bx - twg - nchunks) * 4 + tid / kWave;
+  if (ep >= E) return;
+  const int lane = tid & (kWave - 1);
+  const int64_t r1 = off[ep + 1];
+  for (int64_t r = (int64_t)off[ep] + tot_s[ep] + lane; r < r1; r += kWave) {
+    a.row_src[r] = -1;
+    a.row_prob[r] = 0.0f;
+    a.gscale[r] = 0.0f;
+  }
+}
+
 // The routed rows of the permuted layout from the token-major rows of gather
 // mode (debug intermediates): row r < *rows_end takes token row_src[r]'s
 // codes and scales, padding rows (row_src < 0) zeros.  One wave per row.
@@ -839,9 +993,11 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
   const bool small = a.tokens * a.topk <= kSmallEntries;
   const bool gather = a.tok_codes != nullptr && a.x != nullptr;
   // gather mode: tokens [0, tq_split) are quantized in the first launch, the
-  // rest in the second
+  // rest in the second (all of them in the first when the scan is fused into
+  // the entries launch)
   const int bpl_g = gather ? blocks_per_lane(a.hidden) : 1;
-  const int64_t tq_split = a.tokens / 2;
+  const bool fused = gather && (int64_t)E * nchunks <= kFusedScanInts;
+  const int64_t tq_split = fused ? a.tokens : a.tokens / 2;
   if (!small) {
     if (nchunks > 0) {
       const unsigned hg = (unsigned)((nchunks + 3) / 4);
@@ -871,6 +1027,13 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
       } else {
         route_hist_kernel<0><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
       }
+    }
+    if (fused) {
+      // the scan, the entries' rows, the padding rows and the tile tables
+      const int64_t twg = a.num_tables > 0 ? 3 * kTableWorkgroups : 0;
+      const unsigned grid = (unsigned)(twg + nchunks + (E + 3) / 4);
+      route_scan_entries_kernel<<<grid, 256, 0, s>>>(a, hist, nchunks, twg);
+      return hipGetLastError();
     }
     const int64_t scan_wgs = (E + kScanExperts - 1) / kScanExperts;
     if (gather) {

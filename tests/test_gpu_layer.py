@@ -179,13 +179,19 @@ def test_decode_perf_path_matches_the_checked_path():
     assert np.array_equal(y, host(y1))
 
 
-@pytest.mark.parametrize("tokens,experts,zipf", [(160, 300, 0.0), (2000, 300, 1.2), (600, 1024, 0.0)])
+@pytest.mark.parametrize("tokens,experts,zipf", [(160, 300, 0.0), (2000, 300, 1.2), (600, 1024, 0.0),
+                                                (2200, 1024, 0.0)])
 def test_many_experts_replay_chain(tokens, experts, zipf):
     """300 experts: the layer's precomputed tile schedules span groups held by
     several waves of their builder, on the 32-row tile (about 3 rows per
     expert) and on the 128-row tile with skewed routing (empty, tiny and
     multi-tile experts); 1024 experts, the largest count, fill every group
-    slot of the builder; every step of the chain is checked in full."""
+    slot of the builder; every step of the chain is checked in full.  At
+    2200 tokens the chunk-count matrix (1024 x 35) is past what one
+    workgroup of the fused scan-and-entries launch reads, so the routing
+    takes its three-launch form; at 600 tokens (10 chunks, not a multiple of
+    4) the fused launch sums the matrix element by element, each thread's
+    stretch crossing several experts' rows."""
     from nvfp4_w4a4_quantized_amd.workloads import MoeWorkload, random_bf16, route_topk
     rng = np.random.default_rng(tokens + experts)
     H, I, k = 256, 128, 6
