@@ -10,6 +10,11 @@ Usage:
     python -m nvfp4_w4a4_quantized_amd.kernel_stats --window NAME GRID START COUNT TRACE_CSV
         the dispatches START .. START + COUNT - 1 (in time order) of the
         kernel whose name contains NAME, at grid size GRID
+    python -m nvfp4_w4a4_quantized_amd.kernel_stats --span FIRST LAST N TRACE_CSV
+        the time from the start of a dispatch of the kernel whose name
+        contains FIRST to the end of the next dispatch whose name contains
+        LAST (a stage of back-to-back launches): median, min and max over the
+        last N such spans
 """
 from __future__ import annotations
 
@@ -73,10 +78,31 @@ def last_table(path: str, last: int, max_rows: int = 16) -> str:
     return "\n".join(out)
 
 
+def span(path: str, first: str, last: str, n: int) -> str:
+    rows = []
+    for r in csv.DictReader(open(path)):
+        rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), _short(r["Kernel_Name"])))
+    rows.sort()
+    spans, t0 = [], None
+    for st, en, name in rows:
+        if t0 is None and first in name:
+            t0 = st
+        if t0 is not None and last in name:
+            spans.append(en - t0)
+            t0 = None
+    if not spans:
+        raise SystemExit(f"no span from {first!r} to {last!r}")
+    d = sorted(spans[-n:])
+    return "%s .. %s, last %d of %d spans: median %.1f us, min %.1f, max %.1f" % (
+        first, last, len(d), len(spans), d[len(d) // 2] / 1e3, d[0] / 1e3, d[-1] / 1e3)
+
+
 if __name__ == "__main__":
     a = sys.argv[1:]
     if a and a[0] == "--last":
         print(last_table(a[2], int(a[1]), int(a[3]) if len(a) > 3 else 16))
+    elif a and a[0] == "--span":
+        print(span(a[4], a[1], a[2], int(a[3])))
     elif a and a[0] == "--window":
         print(window(a[5], a[1], int(a[2]), int(a[3]), int(a[4])))
     else:

@@ -125,3 +125,47 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_kernel_stats_span_of_back_to_back_launches(tmp_path):
+    p = tmp_path / "kt.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size_X", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        # three steps: hist at t0, entries ending 20 + i us later; an unrelated
+        # kernel in between does not end a span
+        for i in range(3):
+            t0 = 1_000_000 * i
+            w.writerow({"Kernel_Name": "void nvfp4::route_hist_quant_kernel<8, 2>(x)", "Grid_Size_X": 1,
+                        "Start_Timestamp": t0, "End_Timestamp": t0 + 10_000})
+            w.writerow({"Kernel_Name": "nvfp4::other_kernel(x)", "Grid_Size_X": 1,
+                        "Start_Timestamp": t0 + 10_500, "End_Timestamp": t0 + 11_000})
+            w.writerow({"Kernel_Name": "nvfp4::route_scan_entries_kernel(x)", "Grid_Size_X": 1,
+                        "Start_Timestamp": t0 + 12_000, "End_Timestamp": t0 + 20_000 + 1000 * i})
+    s = kernel_stats.span(str(p), "route_hist_quant", "route_scan_entries", 2)
+    assert "last 2 of 3 spans" in s and "median 22.0 us" in s and "min 21.0" in s
+
+
+def test_traffic_kernel_table_scales_per_dispatch(tmp_path):
+    mib = 8
+    f, w = tmp_path / "f.csv", tmp_path / "w.csv"
+    names = ["Kernel_Name", "Grid_Size_X", "Dispatch_Id", "Counter_Name", "Counter_Value"]
+    for path, counter, copy_kib in ((f, "FETCH_SIZE", mib * 512), (w, "WRITE_SIZE", mib * 1024)):
+        with open(path, "w", newline="") as fo:
+            wr = csv.DictWriter(fo, fieldnames=names)
+            wr.writeheader()
+            wr.writerow({"Kernel_Name": "bitwise_not_kernel", "Grid_Size_X": 1, "Dispatch_Id": 1,
+                         "Counter_Name": counter, "Counter_Value": copy_kib})
+            # first dispatch (warm-up) 999 KiB, then 100 and 300 KiB, the
+            # second split over two counter instances
+            for d, v in ((2, [999]), (3, [100]), (4, [150, 150])):
+                for x in v:
+                    wr.writerow({"Kernel_Name": "void nvfp4::route_hist_quant_kernel<8, 2>(a)",
+                                 "Grid_Size_X": 64, "Dispatch_Id": d, "Counter_Name": counter,
+                                 "Counter_Value": x})
+    t = traffic.kernel_table("route", str(f), str(w), mib)
+    row = [l for l in t.splitlines() if l.startswith("| `route")][0]
+    cells = [c.strip() for c in row.split("|")[1:-1]]
+    # fetch counts scale by 2 (the copy's 8 MiB read shows as 4 MiB), writes by 1
+    assert cells == ["`route_hist_quant_kernel<8, 2>`", "64", "%.2f" % (200 * 1024 * 2 / 1e6),
+                     "%.2f" % (200 * 1024 / 1e6)]
