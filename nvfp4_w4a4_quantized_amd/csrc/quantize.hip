@@ -59,7 +59,7 @@ __device__ __forceinline__ int find_group(const int32_t* off, int num_groups, in
 }
 
 template <int BPL>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(QuantRowsArgs a) {
+__global__ __launch_bounds__(256, BPL <= 2 ? 8 : 1) void quantize_rows_kernel(QuantRowsArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = (int64_t)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (row >= a.rows) return;

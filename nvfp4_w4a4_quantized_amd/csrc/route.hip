@@ -427,7 +427,7 @@ __device__ __forceinline__ void quantize_token_wave(const RouteArgs& a, int64_t 
 // Neither part depends on the routing offsets, so the quantization runs
 // beside the routing instead of after it.
 template <int KMAX, int BPL>
-__global__ __launch_bounds__(256) void route_hist_quant_kernel(RouteArgs a, int64_t nchunks,
+__global__ __launch_bounds__(256, BPL <= 2 ? 8 : 1) void route_hist_quant_kernel(RouteArgs a, int64_t nchunks,
                                                                int32_t* hist, int64_t hist_wgs,
                                                                int64_t tq_end) {
   extern __shared__ unsigned long long lds64[];   // [4 waves][E] (histogram workgroups)
