@@ -211,6 +211,29 @@ def test_many_experts_replay_chain(tokens, experts, zipf):
     assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-2
 
 
+@pytest.mark.parametrize("tokens,experts,k", [(400, 64, 20), (700, 40, 12)])
+def test_wide_topk_replay_chain(tokens, experts, k):
+    """Top-k above 8 through the layer: the routing's generic histogram (no
+    unrolled id list at k = 20), and at k = 20 chunks of 64 tokens holding
+    1280 entries, so the fused scan-and-entries launch also places entries
+    past the 1024 it preloads (4 per thread); k = 12 (768 per chunk) stays
+    within them.  Every step of the chain in full."""
+    from nvfp4_w4a4_quantized_amd.workloads import MoeWorkload, random_bf16, route_topk
+    rng = np.random.default_rng(tokens + experts + k)
+    H, I = 256, 128
+    idx, prob = route_topk(rng.standard_normal((tokens, experts)).astype(np.float32), k)
+    w = MoeWorkload(f"wide_topk_t{tokens}_k{k}", -1, tokens, H, I, experts, k,
+                    random_bf16(rng, (tokens, H)), idx, prob, None, None, {})
+    from gpu_util import oracle_weights
+    W1 = oracle_weights(random_bf16(rng, (experts, 2 * I, H), 0.02))
+    W2 = oracle_weights(random_bf16(rng, (experts, H, I), 0.02))
+    y, it, _ = _replay_chain(w, W1, W2, 1)
+    yo, _ = O.moe_forward(w.x, w.topk_idx, w.topk_prob, w.experts, w.inter, W1, W2)
+    a = bf16_bits_to_f32(y).astype(np.float64)
+    b = bf16_bits_to_f32(yo).astype(np.float64)
+    assert np.linalg.norm(a - b) / np.linalg.norm(b) < 1e-2
+
+
 @pytest.mark.parametrize("H,I", [(16384, 128), (256, 16384)])
 def test_largest_hidden_and_intermediate_replay_chain(H, I):
     """The layer at its largest hidden size (FC1's K, FC2's N) and at its
