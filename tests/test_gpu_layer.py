@@ -180,7 +180,7 @@ def test_decode_perf_path_matches_the_checked_path():
 
 
 @pytest.mark.parametrize("tokens,experts,zipf", [(160, 300, 0.0), (2000, 300, 1.2), (600, 1024, 0.0),
-                                                (2200, 1024, 0.0)])
+                                                (2200, 1024, 0.0), (16384, 128, 1.2), (16448, 128, 1.2)])
 def test_many_experts_replay_chain(tokens, experts, zipf):
     """300 experts: the layer's precomputed tile schedules span groups held by
     several waves of their builder, on the 32-row tile (about 3 rows per
@@ -191,7 +191,9 @@ def test_many_experts_replay_chain(tokens, experts, zipf):
     workgroup of the fused scan-and-entries launch reads, so the routing
     takes its three-launch form; at 600 tokens (10 chunks, not a multiple of
     4) the fused launch sums the matrix element by element, each thread's
-    stretch crossing several experts' rows."""
+    stretch crossing several experts' rows.  16384 and 16448 tokens with 128
+    experts sit on either side of the fused launch's limit (32768 and 32896
+    matrix entries)."""
     from nvfp4_w4a4_quantized_amd.workloads import MoeWorkload, random_bf16, route_topk
     rng = np.random.default_rng(tokens + experts)
     H, I, k = 256, 128, 6
