@@ -39,7 +39,6 @@ struct Carver {
 struct MoeLayout {
   int32_t* route_ws_i; int32_t* offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
   uint8_t* tokc; uint8_t* toks; float* tokg;   // token-major quantized activations
-  float* a1g;                                  // outer scale of each routed row
   uint8_t* rank;                               // routing entries' ranks inside their chunk
   uint16_t* d; float* amax_d;
   uint8_t* a2c; uint8_t* a2s; float* a2g;
@@ -70,7 +69,6 @@ MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_
   L.tokc = c.take<uint8_t>((size_t)((T + 1) * H / 2));   // + the zero row padding rows read
   L.toks = c.take<uint8_t>((size_t)((T + 1) * H / 16));
   L.tokg = c.take<float>((size_t)T);
-  L.a1g = c.take<float>((size_t)cap);
   L.rank = c.take<uint8_t>((size_t)(T * k));
   L.d = c.take<uint16_t>((size_t)(cap * I));
   L.amax_d = c.take<float>((size_t)cap);
@@ -90,7 +88,7 @@ MoeLayout carve_moe(void* ws, int64_t T, int64_t H, int64_t I, int32_t k, int32_
 // scales, the FC2 rows and the fused kernel's tile table.
 struct SpLayout {
   int32_t* route_ws_i; int32_t* offsets; int32_t* dst_row; int32_t* row_src; float* row_prob;
-  uint8_t* tokc; uint8_t* toks; float* tokg; float* a1g; uint8_t* rank;
+  uint8_t* tokc; uint8_t* toks; float* tokg; uint8_t* rank;
   uint16_t* y_rows;
   int4* tab;
   int64_t blocks;
@@ -110,7 +108,6 @@ SpLayout carve_single_pass(void* ws, int64_t T, int64_t H, int64_t I, int32_t k,
   L.tokc = c.take<uint8_t>((size_t)((T + 1) * H / 2));
   L.toks = c.take<uint8_t>((size_t)((T + 1) * H / 16));
   L.tokg = c.take<float>((size_t)T);
-  L.a1g = c.take<float>((size_t)cap);
   L.rank = c.take<uint8_t>((size_t)(T * k));
   L.y_rows = c.take<uint16_t>((size_t)(cap * H));
   L.blocks = single_pass_table_spec(cap, E, H, nullptr).blocks;
@@ -381,7 +378,6 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
     if (debug->row_src) L.row_src = debug->row_src;
     if (debug->row_prob) L.row_prob = debug->row_prob;
     if ((debug->a1_codes != nullptr) != (debug->a1_scales != nullptr)) return NVFP4_INVALID_ARGUMENT;
-    if (debug->a1_gscale) L.a1g = debug->a1_gscale;
     if (debug->d) L.d = debug->d;
     if (debug->amax_d) L.amax_d = debug->amax_d;
     if (debug->a2_codes) L.a2c = debug->a2_codes;
@@ -403,7 +399,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   hipError_t e;
   if ((e = mark(0)) != hipSuccess) return NVFP4_HIP_ERROR;
   GemmArgs g1{};
-  g1.a_codes = L.tokc; g1.a_scales = L.toks; g1.a_gscale = L.a1g; g1.a_row_src = L.row_src;
+  g1.a_codes = L.tokc; g1.a_scales = L.toks; g1.a_gscale = L.tokg; g1.a_row_src = L.row_src;
   g1.a_pad_row = tokens;
   g1.b_codes = w1->codes; g1.b_scales = w1->scales; g1.b_gscale = w1->gscale;
   g1.offsets = L.offsets; g1.num_groups = num_experts; g1.rows_cap = cap;
@@ -430,7 +426,7 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
   ra.num_experts = num_experts; ra.align = align;
   ra.offsets = L.offsets; ra.dst_row = L.dst_row;
   ra.row_src = L.row_src;
-  ra.row_prob = L.row_prob; ra.gscale = L.a1g;
+  ra.row_prob = L.row_prob; ra.gscale = nullptr;   // the GEMMs read tok_gscale through row_src
   ra.tok_codes = L.tokc; ra.tok_scales = L.toks; ra.tok_gscale = L.tokg; ra.entry_rank = L.rank;
   ra.zero_per_row = L.amax_d; ra.zero_rows = cap;
   ra.tables[0] = gemm_tile_table_spec(g1, true, L.tab1);
@@ -445,9 +441,10 @@ int moe_expert_forward(const uint16_t* x, int64_t tokens, int64_t hidden, int64_
     ra.tok_amax = L.tamax;
   }
   if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
-  if (debug && (debug->a1_codes || debug->a1_scales)) {   // the permuted rows, for inspection
-    if ((e = launch_gather_rows(L.tokc, L.toks, L.row_src, L.offsets + num_experts, cap, hidden,
-                                debug->a1_codes, debug->a1_scales, s)) != hipSuccess)
+  if (debug) {   // the permuted rows and their outer scales, for inspection
+    if ((e = launch_gather_rows(L.tokc, L.toks, L.tokg, L.row_src, L.offsets + num_experts, cap,
+                                hidden, debug->a1_codes, debug->a1_scales, debug->a1_gscale,
+                                s)) != hipSuccess)
       return NVFP4_HIP_ERROR;
   }
   if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
@@ -685,7 +682,6 @@ int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hi
     if (debug->dst_row) L.dst_row = debug->dst_row;
     if (debug->row_src) L.row_src = debug->row_src;
     if (debug->row_prob) L.row_prob = debug->row_prob;
-    if (debug->a1_gscale) L.a1g = debug->a1_gscale;
     if (debug->y_rows) L.y_rows = debug->y_rows;
     y_f32 = debug->y_rows_f32;
     sp.c_out = debug->fc1_out; sp.p_out = debug->p;
@@ -707,19 +703,20 @@ int moe_expert_forward_single_pass(const uint16_t* x, int64_t tokens, int64_t hi
   ra.topk_idx = topk_idx; ra.topk_prob = topk_prob; ra.topk = topk;
   ra.num_experts = num_experts; ra.align = align;
   ra.offsets = L.offsets; ra.dst_row = L.dst_row; ra.row_src = L.row_src;
-  ra.row_prob = L.row_prob; ra.gscale = L.a1g;
+  ra.row_prob = L.row_prob; ra.gscale = nullptr;   // the kernel reads tok_gscale through row_src
   ra.tok_codes = L.tokc; ra.tok_scales = L.toks; ra.tok_gscale = L.tokg; ra.entry_rank = L.rank;
   ra.tables[0] = single_pass_table_spec(cap, num_experts, hidden, L.tab);
   ra.num_tables = 1;
   ra.workspace = L.route_ws_i; ra.block_rule = 0;
   if ((e = launch_route(ra, s)) != hipSuccess) return NVFP4_HIP_ERROR;
-  if (debug && debug->a1_codes) {
-    if ((e = launch_gather_rows(L.tokc, L.toks, L.row_src, L.offsets + num_experts, cap, hidden,
-                                debug->a1_codes, debug->a1_scales, s)) != hipSuccess)
+  if (debug) {
+    if ((e = launch_gather_rows(L.tokc, L.toks, L.tokg, L.row_src, L.offsets + num_experts, cap,
+                                hidden, debug->a1_codes, debug->a1_scales, debug->a1_gscale,
+                                s)) != hipSuccess)
       return NVFP4_HIP_ERROR;
   }
   if ((e = mark(1)) != hipSuccess) return NVFP4_HIP_ERROR;
-  sp.a_codes = L.tokc; sp.a_scales = L.toks; sp.a_gscale = L.a1g;
+  sp.a_codes = L.tokc; sp.a_scales = L.toks; sp.a_gscale = L.tokg;
   sp.a_row_src = L.row_src; sp.a_pad_row = tokens; sp.row_prob = L.row_prob;
   sp.w1_codes = w1->codes; sp.w1_scales = w1->scales; sp.w1_gscale = w1->gscale;
   sp.w1_layout = w1->layout;

@@ -525,7 +525,12 @@ __global__ __launch_bounds__(64 * NW, gemm_waves_per_simd<WM>()) void gemm_w4a4_
     if (tid < BM) {
       const int64_t row = row0 + tid;
       const int64_t rr = row < row1 ? row : row1 - 1;
-      rf_sa = a.a_gscale[rr];
+      if (gather) {                              // the token's outer scale
+        const int32_t t = a.a_row_src[rr];
+        rf_sa = t >= 0 ? a.a_gscale[t] : 0.0f;
+      } else {
+        rf_sa = a.a_gscale[rr];
+      }
       if (EPI == EPI_SWIGLU) rf_p = a.row_prob[rr];
     }
     a_load(0);

@@ -70,10 +70,12 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 // Permuted rows r < *rows_end (device) copied from the token-major rows of
-// gather mode; padding rows (row_src < 0) get zeros.
+// gather mode (codes, scales and outer scale, each output nullable); padding
+// rows (row_src < 0) get zeros.
 hipError_t launch_gather_rows(const uint8_t* tok_codes, const uint8_t* tok_scales,
-                              const int32_t* row_src, const int32_t* rows_end, int64_t cap,
-                              int64_t hidden, uint8_t* codes, uint8_t* scales, hipStream_t s);
+                              const float* tok_gscale, const int32_t* row_src,
+                              const int32_t* rows_end, int64_t cap, int64_t hidden,
+                              uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s);
 // moe_permute's host-side argument checks (all but the workspace): an
 // NVFP4_* status, NVFP4_OK when the call may proceed.  No HIP call.
 int permute_args_status(const uint16_t* x, int64_t tokens, int64_t hidden,
@@ -102,8 +104,9 @@ struct GemmArgs {
   const int4* tile_table;
   // nullable: A rows gathered from token-major codes / scales (row r reads
   // token a_row_src[r]; -1, a padding row, reads row a_pad_row, all zero, so
-  // its products are +0 as in the permuted layout).  a_gscale stays per
-  // routed row.  (a_pad_row + 1) * k / 2 < 2^32.
+  // its products are +0 as in the permuted layout).  Gathering, a_gscale is
+  // per token too: row r's outer scale is a_gscale[a_row_src[r]] (0 for a
+  // padding row).  (a_pad_row + 1) * k / 2 < 2^32.
   const int32_t* a_row_src;
   int64_t a_pad_row;
 };
@@ -127,7 +130,7 @@ TileTableSpec gemm_mtile_table_spec(int64_t rows_cap, int32_t num_groups, int64_
 // kernel (one workgroup per 128-row m-tile of the tile table).
 struct SinglePassArgs {
   const uint8_t* a_codes; const uint8_t* a_scales;   // token-major quantized activations
-  const float* a_gscale;                             // [rows_cap] outer scale of each routed row
+  const float* a_gscale;                             // [tokens] outer scale of each token
   const int32_t* a_row_src; int64_t a_pad_row;       // routed row -> token row; the zero row
   const float* row_prob;
   const uint8_t* w1_codes; const uint8_t* w1_scales; const float* w1_gscale; int w1_layout;

@@ -597,7 +597,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
       if (lane == 0) {
         if (a.row_src) a.row_src[r] = -1;
         a.row_prob[r] = 0.0f;
-        if (a.x || a.tok_gscale) a.gscale[r] = 0.0f;
+        if ((a.x || a.tok_gscale) && a.gscale) a.gscale[r] = 0.0f;
       }
       if (a.x && !a.tok_codes) {
         uint8_t* cr = a.codes + r * (H / 2);
@@ -717,7 +717,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
       if (dst < 0) return;
       if (a.row_src) a.row_src[dst] = (int32_t)t;
       a.row_prob[dst] = p;
-      if (a.x || a.tok_gscale) a.gscale[dst] = s_g;
+      if ((a.x || a.tok_gscale) && a.gscale) a.gscale[dst] = s_g;
     };
     if constexpr (KMAX > 0) {
       if (lane < k) store_meta(lane, dst_l[ti], prob_l[ti]);
@@ -747,8 +747,8 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(RouteArgs a, const i
 // Gather mode, third launch of the three-launch path.  Workgroups [0, twg)
 // write the tile tables.  Then one thread per routing entry i = t*topk + j:
 // its row is dst = base[e][chunk of t] + its rank inside the chunk, and it
-// writes dst_row[i], row_src[dst] = t, row_prob[dst] and gscale[dst] (its
-// token's outer scale).  The last workgroups give one wave per expert for
+// writes dst_row[i], row_src[dst] = t and row_prob[dst] (the GEMMs read a
+// row's outer scale through row_src).  The last workgroups give one wave per expert for
 // its padding rows [offsets[e] + counts[e], offsets[e+1]).
 __global__ __launch_bounds__(256) void route_entries_kernel(RouteArgs a, const int32_t* base,
                                                             const int32_t* counts,
@@ -785,7 +785,6 @@ __global__ __launch_bounds__(256) void route_entries_kernel(RouteArgs a, const i
       d = (int64_t)base[(int64_t)e * nchunks + t / kChunk] + a.entry_rank[i];
       a.row_src[d] = (int32_t)t;
       a.row_prob[d] = p;
-      a.gscale[d] = a.tok_gscale[t];
     }
     a.dst_row[i] = (int32_t)d;
     return;
@@ -797,7 +796,6 @@ __global__ __launch_bounds__(256) void route_entries_kernel(RouteArgs a, const i
   for (int64_t r = (int64_t)a.offsets[e] + counts[e] + lane; r < r1; r += kWave) {
     a.row_src[r] = -1;
     a.row_prob[r] = 0.0f;
-    a.gscale[r] = 0.0f;
   }
 }
 
@@ -811,13 +809,17 @@ __global__ __launch_bounds__(256) void route_entries_kernel(RouteArgs a, const i
 // Workgroups [0, twg) then write the tile tables; the next nchunks take one
 // chunk each: entry i of token t (chunk c) choosing e goes to row
 // off[e] + (entries of e in chunks before c) + its rank inside the chunk.
-// The last workgroups give one wave per expert for its padding rows.  All of
-// them clear a slice of the rows' amax cells first.
+// Then one wave per expert for its padding rows; all of these clear a slice
+// of the rows' amax cells first.  The workgroups past nroute quantize tokens
+// [tq_begin, tokens): the entries no longer copy a token's outer scale (the
+// GEMMs read it through row_src), so nothing in this launch waits for them.
 constexpr int64_t kFusedScanInts = 32768;
 constexpr int kEntryPreload = 4;    // entries per thread whose loads overlap the offsets
 
+template <int BPL>
 __global__ __launch_bounds__(256) void route_scan_entries_kernel(RouteArgs a, const int32_t* hist,
-                                                                 int64_t nchunks, int64_t twg) {
+                                                                 int64_t nchunks, int64_t twg,
+                                                                 int64_t nroute, int64_t tq_begin) {
   __shared__ TileTableLds tls;
   __shared__ int32_t off[kScanMaxE + 1];
   __shared__ int32_t tot_s[kScanMaxE], pre_s[kScanMaxE];
@@ -825,13 +827,18 @@ __global__ __launch_bounds__(256) void route_scan_entries_kernel(RouteArgs a, co
   const int tid = threadIdx.x;
   const int E = a.num_experts, k = a.topk;
   const int64_t bx = blockIdx.x;
-  grid_zero_fill(a.zero_per_row, a.zero_rows, gridDim.x);
+  if (bx >= nroute) {    // the quantization of tokens [tq_begin, tokens), one per wave
+    const int64_t t = tq_begin + (bx - nroute) * 4 + threadIdx.x / kWave;
+    if (t < a.tokens) quantize_token_wave<BPL>(a, t);
+    return;
+  }
+  grid_zero_fill(a.zero_per_row, a.zero_rows, nroute);
   const int64_t chunk = (bx >= twg && bx < twg + nchunks) ? bx - twg : -1;
   // this chunk's entries [i0, i1); the first kEntryPreload per thread load now
   const int64_t i0 = chunk >= 0 ? chunk * kChunk * k : 0;
   const int64_t i1 = chunk >= 0 ? std::min<int64_t>((chunk + 1) * kChunk, a.tokens) * k : 0;
   int pe[kEntryPreload], pr[kEntryPreload];
-  float pp[kEntryPreload], pg[kEntryPreload];
+  float pp[kEntryPreload];
 #pragma unroll
   for (int u = 0; u < kEntryPreload; ++u) {
     const int64_t i = i0 + tid + 256 * u;
@@ -839,7 +846,6 @@ __global__ __launch_bounds__(256) void route_scan_entries_kernel(RouteArgs a, co
     pe[u] = live ? a.topk_idx[i] : -1;
     pp[u] = live ? a.topk_prob[i] : 0.0f;
     pr[u] = live ? (int)a.entry_rank[i] : 0;
-    pg[u] = live ? a.tok_gscale[chunk * kChunk + (tid + 256 * u) / k] : 0.0f;
   }
   for (int e = tid; e < E; e += 256) { tot_s[e] = 0; pre_s[e] = 0; }
   __syncthreads();
@@ -909,7 +915,7 @@ __global__ __launch_bounds__(256) void route_scan_entries_kernel(RouteArgs a, co
   }
   if (chunk >= 0) {
     // entry i = i0 + l of the chunk: token chunk * kChunk + l / k
-    auto place = [&](int64_t i, int32_t l, int e, float p, int r, float g) {
+    auto place = [&](int64_t i, int32_t l, int e, float p, int r) {
 #ifdef NVFP4_DEBUG_CHECKS
       report_bits(a.error_word, !__builtin_isfinite(p), NVFP4_PRECONDITION_NONFINITE_PROB);
 #endif
@@ -918,19 +924,17 @@ __global__ __launch_bounds__(256) void route_scan_entries_kernel(RouteArgs a, co
         d = (int64_t)off[e] + pre_s[e] + r;
         a.row_src[d] = (int32_t)(chunk * kChunk + l / k);
         a.row_prob[d] = p;
-        a.gscale[d] = g;
       }
       a.dst_row[i] = (int32_t)d;
     };
 #pragma unroll
     for (int u = 0; u < kEntryPreload; ++u) {
       const int64_t i = i0 + tid + 256 * u;
-      if (i < i1) place(i, tid + 256 * u, pe[u], pp[u], pr[u], pg[u]);
+      if (i < i1) place(i, tid + 256 * u, pe[u], pp[u], pr[u]);
     }
     for (int32_t l = tid + 256 * kEntryPreload; i0 + l < i1; l += 256) {
       const int64_t i = i0 + l;
-      place(i, l, a.topk_idx[i], a.topk_prob[i], (int)a.entry_rank[i],
-            a.tok_gscale[chunk * kChunk + l / k]);
+      place(i, l, a.topk_idx[i], a.topk_prob[i], (int)a.entry_rank[i]);
     }
     return;
   }
@@ -942,38 +946,43 @@ __global__ __launch_bounds__(256) void route_scan_entries_kernel(RouteArgs a, co
   for (int64_t r = (int64_t)off[ep] + tot_s[ep] + lane; r < r1; r += kWave) {
     a.row_src[r] = -1;
     a.row_prob[r] = 0.0f;
-    a.gscale[r] = 0.0f;
   }
 }
 
 // The routed rows of the permuted layout from the token-major rows of gather
 // mode (debug intermediates): row r < *rows_end takes token row_src[r]'s
-// codes and scales, padding rows (row_src < 0) zeros.  One wave per row.
+// codes, scales and outer scale, padding rows (row_src < 0) zeros; each
+// output is nullable.  One wave per row.
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* tok_codes,
                                                           const uint8_t* tok_scales,
+                                                          const float* tok_gscale,
                                                           const int32_t* row_src,
                                                           const int32_t* rows_end, int64_t cap,
                                                           int64_t H, uint8_t* codes,
-                                                          uint8_t* scales) {
+                                                          uint8_t* scales, float* gscale) {
   const int64_t r = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (r >= cap || r >= (int64_t)*rows_end) return;
   const int64_t t = row_src[r];
-  for (int64_t i = 8 * lane; i < H / 2; i += 8 * kWave) {
-    const uint2 v = t >= 0 ? *reinterpret_cast<const uint2*>(tok_codes + t * (H / 2) + i)
-                           : make_uint2(0u, 0u);
-    *reinterpret_cast<uint2*>(codes + r * (H / 2) + i) = v;
-  }
-  for (int64_t i = lane; i < H / 16; i += kWave)
-    scales[r * (H / 16) + i] = t >= 0 ? tok_scales[t * (H / 16) + i] : (uint8_t)0;
+  if (codes)
+    for (int64_t i = 8 * lane; i < H / 2; i += 8 * kWave) {
+      const uint2 v = t >= 0 ? *reinterpret_cast<const uint2*>(tok_codes + t * (H / 2) + i)
+                             : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(codes + r * (H / 2) + i) = v;
+    }
+  if (scales)
+    for (int64_t i = lane; i < H / 16; i += kWave)
+      scales[r * (H / 16) + i] = t >= 0 ? tok_scales[t * (H / 16) + i] : (uint8_t)0;
+  if (gscale && lane == 0) gscale[r] = t >= 0 ? tok_gscale[t] : 0.0f;
 }
 
 hipError_t launch_gather_rows(const uint8_t* tok_codes, const uint8_t* tok_scales,
-                              const int32_t* row_src, const int32_t* rows_end, int64_t cap,
-                              int64_t hidden, uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  if (cap <= 0) return hipSuccess;
-  gather_rows_kernel<<<(unsigned)((cap + 3) / 4), 256, 0, s>>>(tok_codes, tok_scales, row_src,
-                                                              rows_end, cap, hidden, codes, scales);
+                              const float* tok_gscale, const int32_t* row_src,
+                              const int32_t* rows_end, int64_t cap, int64_t hidden,
+                              uint8_t* codes, uint8_t* scales, float* gscale, hipStream_t s) {
+  if (cap <= 0 || (!codes && !scales && !gscale)) return hipSuccess;
+  gather_rows_kernel<<<(unsigned)((cap + 3) / 4), 256, 0, s>>>(
+      tok_codes, tok_scales, tok_gscale, row_src, rows_end, cap, hidden, codes, scales, gscale);
   return hipGetLastError();
 }
 
@@ -993,11 +1002,10 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
   const bool small = a.tokens * a.topk <= kSmallEntries;
   const bool gather = a.tok_codes != nullptr && a.x != nullptr;
   // gather mode: tokens [0, tq_split) are quantized in the first launch, the
-  // rest in the second (all of them in the first when the scan is fused into
-  // the entries launch)
+  // rest in the second
   const int bpl_g = gather ? blocks_per_lane(a.hidden) : 1;
   const bool fused = gather && (int64_t)E * nchunks <= kFusedScanInts;
-  const int64_t tq_split = fused ? a.tokens : a.tokens / 2;
+  const int64_t tq_split = a.tokens / 2;
   if (!small) {
     if (nchunks > 0) {
       const unsigned hg = (unsigned)((nchunks + 3) / 4);
@@ -1031,8 +1039,15 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
     if (fused) {
       // the scan, the entries' rows, the padding rows and the tile tables
       const int64_t twg = a.num_tables > 0 ? 3 * kTableWorkgroups : 0;
-      const unsigned grid = (unsigned)(twg + nchunks + (E + 3) / 4);
-      route_scan_entries_kernel<<<grid, 256, 0, s>>>(a, hist, nchunks, twg);
+      const int64_t nroute = twg + nchunks + (E + 3) / 4;
+      const unsigned grid = (unsigned)(nroute + (a.tokens - tq_split + 3) / 4);
+      switch (bpl_g) {
+#define NVFP4_SCANE(B) \
+        case B: route_scan_entries_kernel<B><<<grid, 256, 0, s>>>(a, hist, nchunks, twg, nroute, tq_split); break;
+        NVFP4_SCANE(1) NVFP4_SCANE(2) NVFP4_SCANE(4) NVFP4_SCANE(8) NVFP4_SCANE(16)
+#undef NVFP4_SCANE
+        default: return hipErrorInvalidValue;
+      }
       return hipGetLastError();
     }
     const int64_t scan_wgs = (E + kScanExperts - 1) / kScanExperts;

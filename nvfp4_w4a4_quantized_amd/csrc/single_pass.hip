@@ -465,7 +465,8 @@ __global__ __launch_bounds__(NT, 1) void single_pass_kernel(SinglePassArgs a) {
   if (tid < BM) {
     const int64_t row0 = te.y, nrow = (int64_t)te.z - te.y;
     const int64_t rr = row0 + (tid < nrow ? tid : nrow - 1);
-    const float sa = a.a_gscale[rr] * a.w1_gscale[te.x];
+    const int32_t tk = a.a_row_src[rr];               // the row's token (-1: padding)
+    const float sa = (tk >= 0 ? a.a_gscale[tk] : 0.0f) * a.w1_gscale[te.x];
     const float p = a.row_prob[rr];
     float* rfac = reinterpret_cast<float*>(sp_smem + L.rfac);
     rfac[tid] = sa;
