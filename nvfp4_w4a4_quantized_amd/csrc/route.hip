@@ -27,9 +27,10 @@
 // The expert layer's gather mode (tok_codes set) quantizes each token once
 // into a token-major row and writes only the row maps.  Two launches while
 // the chunk-count matrix is small enough for every workgroup to read it
-// whole (kFusedScanInts): the ranked histogram beside every token's
-// quantization, then route_scan_entries_kernel (each workgroup repeats the
-// scan's totals, then writes the entries, padding rows or tile tables).
+// whole (kFusedScanInts): the ranked histogram, then
+// route_scan_entries_kernel (each workgroup repeats the scan's totals, then
+// writes the entries, padding rows or tile tables; the others quantize the
+// tokens).
 // Larger matrices take three: histogram + half of the quantization, scan +
 // the other half, entries.
 #include "launch.h"
@@ -1002,10 +1003,12 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
   const bool small = a.tokens * a.topk <= kSmallEntries;
   const bool gather = a.tok_codes != nullptr && a.x != nullptr;
   // gather mode: tokens [0, tq_split) are quantized in the first launch, the
-  // rest in the second
+  // rest in the second.  The fused second launch takes all of them: its
+  // scan and entries are a latency-bound chain on about 200 workgroups, and
+  // the quantization fills the rest of the chip beside it.
   const int bpl_g = gather ? blocks_per_lane(a.hidden) : 1;
   const bool fused = gather && (int64_t)E * nchunks <= kFusedScanInts;
-  const int64_t tq_split = a.tokens / 2;
+  const int64_t tq_split = fused ? 0 : a.tokens / 2;
   if (!small) {
     if (nchunks > 0) {
       const unsigned hg = (unsigned)((nchunks + 3) / 4);
