@@ -31,8 +31,7 @@
 // route_scan_entries_kernel (each workgroup repeats the scan's totals, then
 // writes the entries, padding rows or tile tables; the others quantize the
 // tokens).
-// Larger matrices take three: histogram + half of the quantization, scan +
-// the other half, entries.
+// Larger matrices take three: histogram, scan + the quantization, entries.
 #include "launch.h"
 #include "nvfp4_device.h"
 
@@ -1002,13 +1001,15 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
 #endif
   const bool small = a.tokens * a.topk <= kSmallEntries;
   const bool gather = a.tok_codes != nullptr && a.x != nullptr;
-  // gather mode: tokens [0, tq_split) are quantized in the first launch, the
-  // rest in the second.  The fused second launch takes all of them: its
-  // scan and entries are a latency-bound chain on about 200 workgroups, and
-  // the quantization fills the rest of the chip beside it.
+  // gather mode: tokens [0, tq_split) would be quantized in the first
+  // launch, the rest in the second.  The second takes all of them: the
+  // entries no longer wait for the quantization, and the fused launch's scan
+  // and entries (or the three-launch form's scan) are a latency-bound chain
+  // on a few hundred workgroups, which the quantization runs beside, while
+  // the histogram launch stays short.
   const int bpl_g = gather ? blocks_per_lane(a.hidden) : 1;
   const bool fused = gather && (int64_t)E * nchunks <= kFusedScanInts;
-  const int64_t tq_split = fused ? 0 : a.tokens / 2;
+  const int64_t tq_split = 0;
   if (!small) {
     if (nchunks > 0) {
       const unsigned hg = (unsigned)((nchunks + 3) / 4);
