@@ -27,10 +27,10 @@
 // The expert layer's gather mode (tok_codes set) quantizes each token once
 // into a token-major row and writes only the row maps.  Two launches while
 // the chunk-count matrix is small enough for every workgroup to read it
-// whole (kFusedScanInts): the ranked histogram, then
-// route_scan_entries_kernel (each workgroup repeats the scan's totals, then
-// writes the entries, padding rows or tile tables; the others quantize the
-// tokens).
+// whole (kFusedScanInts): the ranked histogram (route_hist_rank_kernel),
+// then route_scan_entries_kernel (each workgroup repeats the scan's totals,
+// then writes the entries, padding rows or tile tables; the others quantize
+// the tokens).
 // Larger matrices take three: histogram, scan + the quantization, entries.
 #include "launch.h"
 #include "nvfp4_device.h"
@@ -421,22 +421,14 @@ __device__ __forceinline__ void quantize_token_wave(const RouteArgs& a, int64_t 
   if (t == a.tokens - 1) zero_pad_row(a, lane);
 }
 
-// Gather mode, first launch of the three-launch path: workgroups
-// [0, hist_wgs) count the chunks' entries and rank them inside their chunk
-// (hist_rank_chunks); the others quantize tokens [0, tq_end), one per wave.
-// Neither part depends on the routing offsets, so the quantization runs
-// beside the routing instead of after it.
-template <int KMAX, int BPL>
-__global__ __launch_bounds__(256, BPL <= 2 ? 8 : 1) void route_hist_quant_kernel(RouteArgs a, int64_t nchunks,
-                                                               int32_t* hist, int64_t hist_wgs,
-                                                               int64_t tq_end) {
-  extern __shared__ unsigned long long lds64[];   // [4 waves][E] (histogram workgroups)
-  if ((int64_t)blockIdx.x < hist_wgs) {
-    hist_rank_chunks<KMAX>(a, nchunks, hist, a.entry_rank, blockIdx.x, lds64);
-    return;
-  }
-  const int64_t t = ((int64_t)blockIdx.x - hist_wgs) * 4 + threadIdx.x / kWave;
-  if (t < tq_end) quantize_token_wave<BPL>(a, t);
+// Gather mode, first launch: each workgroup counts four chunks' entries per
+// expert and ranks them inside their chunk (hist_rank_chunks).  The tokens
+// are quantized in the next launch, beside the scan.
+template <int KMAX>
+__global__ __launch_bounds__(256) void route_hist_rank_kernel(RouteArgs a, int64_t nchunks,
+                                                              int32_t* hist) {
+  extern __shared__ unsigned long long lds64[];   // [4 waves][E]
+  hist_rank_chunks<KMAX>(a, nchunks, hist, a.entry_rank, blockIdx.x, lds64);
 }
 
 // Gather mode, second launch: workgroups [0, scan_wgs) run the scan; the
@@ -1001,36 +993,26 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
 #endif
   const bool small = a.tokens * a.topk <= kSmallEntries;
   const bool gather = a.tok_codes != nullptr && a.x != nullptr;
-  // gather mode: tokens [0, tq_split) would be quantized in the first
-  // launch, the rest in the second.  The second takes all of them: the
-  // entries no longer wait for the quantization, and the fused launch's scan
-  // and entries (or the three-launch form's scan) are a latency-bound chain
-  // on a few hundred workgroups, which the quantization runs beside, while
-  // the histogram launch stays short.
+  // gather mode: the tokens are quantized in the second launch, beside the
+  // fused launch's scan and entries (or the three-launch form's scan): a
+  // latency-bound chain on a few hundred workgroups, which the quantization
+  // runs beside, while the histogram launch stays short (the entries read
+  // no outer scale, so nothing waits for the quantization)
   const int bpl_g = gather ? blocks_per_lane(a.hidden) : 1;
   const bool fused = gather && (int64_t)E * nchunks <= kFusedScanInts;
-  const int64_t tq_split = 0;
   if (!small) {
     if (nchunks > 0) {
       const unsigned hg = (unsigned)((nchunks + 3) / 4);
       const size_t hl = 4 * E * sizeof(int32_t);
       const int kmax = a.topk <= 8 ? 8 : (a.topk <= 16 ? 16 : 0);
       if (gather) {
-        // histogram + the first part of the token quantization in one
-        // launch, the scan + the rest in the next: the per-entry kernel then
-        // only writes the maps, the rows' outer scales and the tile tables
+        // the ranked histogram
         if (bpl_g == 0) return hipErrorInvalidValue;
-        const unsigned grid = hg + (unsigned)((tq_split + 3) / 4);
         const size_t hl64 = 4 * E * sizeof(unsigned long long);
-        switch (bpl_g * 100 + kmax) {
-#define NVFP4_HISTQ(B, KM) \
-          case B * 100 + KM: \
-            route_hist_quant_kernel<KM, B><<<grid, 256, hl64, s>>>(a, nchunks, hist, (int64_t)hg, tq_split); break;
-          NVFP4_HISTQ(1, 8) NVFP4_HISTQ(2, 8) NVFP4_HISTQ(4, 8) NVFP4_HISTQ(8, 8) NVFP4_HISTQ(16, 8)
-          NVFP4_HISTQ(1, 16) NVFP4_HISTQ(2, 16) NVFP4_HISTQ(4, 16) NVFP4_HISTQ(8, 16) NVFP4_HISTQ(16, 16)
-          NVFP4_HISTQ(1, 0) NVFP4_HISTQ(2, 0) NVFP4_HISTQ(4, 0) NVFP4_HISTQ(8, 0) NVFP4_HISTQ(16, 0)
-#undef NVFP4_HISTQ
-          default: return hipErrorInvalidValue;
+        switch (kmax) {
+          case 8: route_hist_rank_kernel<8><<<hg, 256, hl64, s>>>(a, nchunks, hist); break;
+          case 16: route_hist_rank_kernel<16><<<hg, 256, hl64, s>>>(a, nchunks, hist); break;
+          default: route_hist_rank_kernel<0><<<hg, 256, hl64, s>>>(a, nchunks, hist); break;
         }
       } else if (kmax == 8) {
         route_hist_kernel<8><<<hg, 256, hl, s>>>(a.topk_idx, a.tokens, a.topk, E, nchunks, hist);
@@ -1044,10 +1026,10 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
       // the scan, the entries' rows, the padding rows and the tile tables
       const int64_t twg = a.num_tables > 0 ? 3 * kTableWorkgroups : 0;
       const int64_t nroute = twg + nchunks + (E + 3) / 4;
-      const unsigned grid = (unsigned)(nroute + (a.tokens - tq_split + 3) / 4);
+      const unsigned grid = (unsigned)(nroute + (a.tokens + 3) / 4);
       switch (bpl_g) {
 #define NVFP4_SCANE(B) \
-        case B: route_scan_entries_kernel<B><<<grid, 256, 0, s>>>(a, hist, nchunks, twg, nroute, tq_split); break;
+        case B: route_scan_entries_kernel<B><<<grid, 256, 0, s>>>(a, hist, nchunks, twg, nroute, 0); break;
         NVFP4_SCANE(1) NVFP4_SCANE(2) NVFP4_SCANE(4) NVFP4_SCANE(8) NVFP4_SCANE(16)
 #undef NVFP4_SCANE
         default: return hipErrorInvalidValue;
@@ -1056,10 +1038,10 @@ hipError_t launch_route(const RouteArgs& args, hipStream_t s) {
     }
     const int64_t scan_wgs = (E + kScanExperts - 1) / kScanExperts;
     if (gather) {
-      const unsigned grid = (unsigned)(scan_wgs + (a.tokens - tq_split + 3) / 4);
+      const unsigned grid = (unsigned)(scan_wgs + (a.tokens + 3) / 4);
       switch (bpl_g) {
 #define NVFP4_SCANQ(B) \
-        case B: route_scan_quant_kernel<B><<<grid, 256, 0, s>>>(a, hist, base, counts, nchunks, scan_wgs, tq_split); break;
+        case B: route_scan_quant_kernel<B><<<grid, 256, 0, s>>>(a, hist, base, counts, nchunks, scan_wgs, 0); break;
         NVFP4_SCANQ(1) NVFP4_SCANQ(2) NVFP4_SCANQ(4) NVFP4_SCANQ(8) NVFP4_SCANQ(16)
 #undef NVFP4_SCANQ
         default: return hipErrorInvalidValue;
